@@ -1,0 +1,354 @@
+// attn_fwd.hip -- HSTU pointwise attention forward on gfx950.
+//
+// O_i = sum_j vis(i, j) * SiLU(alpha * q_i.k_j + rab_pos[h, bucket(|i-j|)]
+//                                + rab_ts[h, bucket(|t_i-t_j|)]) / N * v_j
+// (page 1 section 2.1.2, HSTU spatial aggregation, equation (2); no softmax).
+//
+// bf16 path.  A work unit is (sequence, head, 128 query rows); each of the 4 wavefronts owns 32
+// rows.  Key tiles of 64 keys are visited in the order given by key_tiles_for_rows(): tiles that
+// the composite causal/context/candidate mask leaves empty for the whole unit are never loaded,
+// and a wavefront skips the arithmetic of tiles that are empty for its own rows (page 2, HSTU
+// acceleration operator: composite-mask skipping).  Tiles are staged global -> registers -> LDS
+// with two LDS buffers, so loading tile t+1 overlaps the matrix work on tile t (page 2: move one
+// block while computing another).
+//
+// Per tile and wavefront:
+//   S^T (64 keys x 32 rows) = K . Q^T        2 x (D/16) v_mfma_f32_32x32x16_bf16
+//   P = SiLU(alpha S + bias), masked          fp32 in registers
+//   O^T (D x 32 rows) += V^T . P^T           (D/32) x 4 v_mfma_f32_32x32x16_bf16
+// The C layout of S^T gives each lane one query row and 16 keys per 32-key block, which is the
+// B-operand layout P^T needs once keys are renumbered (perm_key) -- V is stored transposed with
+// the same renumbering, so P never leaves registers.  1/N is applied once to O.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 4 * kWaveRows;  // 128 query rows per unit
+constexpr int kBN = kKeyTile;         // 64 keys per tile
+constexpr int kToep = kRows + kBN - 1;  // 191 distinct i - j per (unit, tile)
+
+template <int D>
+struct FwdSmem {
+    static constexpr int KP = D + 8;    // K row pitch (elements)
+    static constexpr int VP = kBN + 8;  // V^T row pitch (elements)
+    bf16 k[2][kBN * KP];
+    bf16 vt[2][D * VP];
+    float rp[2][kToep + 1];             // position bias by (i - j) for the tile
+    uint32_t tk[2][kBN];                // key timestamps, biased 32-bit relative
+    int64_t tk64[2][kBN];               // key timestamps (fallback)
+    int fits[2];
+    float wt[kNumClasses];              // time bias by bucket class
+    float wp[kNumBuckets];
+};
+
+template <int D, bool RP, bool RT, bool MASK, bool FIT>
+__device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, int buf, int u0,
+                                         int g, float alpha, uint32_t ti, int64_t ti64, int j0,
+                                         int lim, int dg) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = 32 * kb + 8 * r + 4 * g;  // first of this lane's 4 keys
+            u32x4 tq;
+            if (RT && FIT) tq = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int e = 4 * r + c;
+                float bias = 0.0f;
+                if (RP) bias += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
+                if (RT) {
+                    uint32_t dt = FIT ? absdiff_u32(ti, tq[c]) : absdiff_sat(ti64, sm.tk64[buf][jj + c]);
+                    bias += sm.wt[bucket_class(dt)];
+                }
+                float x = fmaf(alpha, s[kb][e], bias);
+                float y = x * fast_sigmoid(x);
+                if (MASK) {
+                    const int j = j0 + jj + c;
+                    y = (j <= lim || j == dg) ? y : 0.0f;
+                }
+                s[kb][e] = y;
+            }
+        }
+    }
+}
+
+template <int D, bool RP, bool RT>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
+    constexpr int KP = FwdSmem<D>::KP, VP = FwdSmem<D>::VP;
+    constexpr int KCH = D / 8;                       // 16-byte chunks per row
+    constexpr int KLOADS = kBN * KCH / kThreads;     // K chunks per thread
+    constexpr int VITEMS = (kBN / 4) * KCH;          // V items of 4 keys x 8 channels
+    static_assert(KLOADS >= 1, "tile too small");
+    __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+
+    const WorkUnit wu = p.units[blockIdx.x];
+    const SeqInfo si = p.seqs[wu.seq];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+    const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
+    const int64_t tok0 = si.start;
+    const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * p.ld_in + h * D;
+    const bf16* __restrict__ kg = static_cast<const bf16*>(p.k) + tok0 * p.ld_in + h * D;
+    const bf16* __restrict__ vg = static_cast<const bf16*>(p.v) + tok0 * p.ld_in + h * D;
+    const int64_t ld = p.ld_in;
+
+    if (RP)
+        for (int e = tid; e < kNumBuckets; e += kThreads) sm.wp[e] = p.rab_pos[h * kNumBuckets + e];
+    if (RT)
+        for (int e = tid; e < kNumClasses; e += kThreads)
+            sm.wt[e] = p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+    const int64_t tbase = RT ? p.ts[tok0] : 0;
+
+    const int rhi = imin(r0 + kRows, n);
+    const KeyTiles kt = key_tiles_for_rows(r0, rhi, nc, nh);
+    const int ntiles = kt.count();
+
+    // this wavefront's rows and this lane's row
+    const int wlo = r0 + kWaveRows * wave, whi = imin(wlo + kWaveRows, rhi);
+    const int i = wlo + lr;
+    const bool row_ok = i < rhi;
+    int lim = -1, dg = -1;  // visible keys: j <= lim or j == dg
+    if (row_ok) {
+        if (i < nh) lim = imax(i, nc - 1);
+        else { lim = nh - 1; dg = i; }
+    }
+
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        if (row_ok) qf[ks] = load_bf16x8(qg + (int64_t)i * ld + 16 * ks + 8 * g);
+        else qf[ks] = bf16x8{};
+    }
+    uint32_t ti = 0;
+    int64_t ti64 = 0;
+    bool wave_qfit = true;
+    if (RT) {
+        ti64 = row_ok ? p.ts[tok0 + i] : tbase;
+        wave_qfit = __all(rel_time_fits(ti64, tbase));
+        ti = rel_time_u32(ti64, tbase);
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+
+    bf16x8 kr[KLOADS];
+    bf16x8 vr[4];
+    int64_t tkr = 0;
+
+    auto load_tile = [&](int tile) {
+        const int j0 = tile * kBN;
+#pragma unroll
+        for (int u = 0; u < KLOADS; ++u) {
+            const int id = tid + kThreads * u, row = id / KCH, ch = id % KCH, j = j0 + row;
+            kr[u] = j < n ? load_bf16x8(kg + (int64_t)j * ld + 8 * ch) : bf16x8{};
+        }
+        if (tid < VITEMS) {
+            const int kgrp = tid % (kBN / 4), ch = tid / (kBN / 4);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int j = j0 + 4 * kgrp + kk;
+                vr[kk] = j < n ? load_bf16x8(vg + (int64_t)j * ld + 8 * ch) : bf16x8{};
+            }
+        }
+        if (RT && tid < kBN) {
+            const int j = j0 + tid;
+            tkr = j < n ? p.ts[tok0 + j] : tbase;
+        }
+    };
+
+    auto store_tile = [&](int buf, int tile) {
+        const int j0 = tile * kBN;
+#pragma unroll
+        for (int u = 0; u < KLOADS; ++u) {
+            const int id = tid + kThreads * u, row = id / KCH, ch = id % KCH;
+            *reinterpret_cast<bf16x8*>(&sm.k[buf][row * KP + 8 * ch]) = kr[u];
+        }
+        if (tid < VITEMS) {
+            const int kgrp = tid % (kBN / 4), ch = tid / (kBN / 4);
+            const int col = perm_key(4 * kgrp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16x4 w = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
+                *reinterpret_cast<bf16x4*>(&sm.vt[buf][(8 * ch + e) * VP + col]) = w;
+            }
+        }
+        if (RT && tid < kBN) {  // exactly wavefront 0
+            sm.tk64[buf][tid] = tkr;
+            sm.tk[buf][tid] = rel_time_u32(tkr, tbase);
+            const bool all_fit = __all(rel_time_fits(tkr, tbase));
+            if (tid == 0) sm.fits[buf] = all_fit ? 1 : 0;
+        }
+        if (RP)
+            for (int u = tid; u < kToep; u += kThreads) {
+                const int delta = (r0 - j0) + (kRows - 1) - u;  // i - j for table slot u
+                sm.rp[buf][u] = sm.wp[bucket_of((uint32_t)(delta < 0 ? -delta : delta))];
+            }
+    };
+
+    __syncthreads();  // bias tables ready
+    load_tile(kt.tile(0));
+    store_tile(0, kt.tile(0));
+    if (ntiles > 1) load_tile(kt.tile(1));
+    __syncthreads();
+
+    // slot of (row i, key j0 + jj) in rp: u0 + (jj - 4g) + ... ; see store_tile
+    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kRows - 1);
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1, j0 = kt.tile(t) * kBN;
+        const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
+        if (kind != kEmpty) {
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                s[kb] = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        &sm.k[buf][(32 * kb + lr) * KP + 16 * ks + 8 * g]);
+                    s[kb] = mfma32(a, qf[ks], s[kb]);
+                }
+            }
+            const bool fit = !RT || (wave_qfit && sm.fits[buf]);
+            if (kind == kPartial) {
+                if (fit) epilogue<D, RP, RT, true, true>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
+                else epilogue<D, RP, RT, true, false>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
+            } else {
+                if (fit) epilogue<D, RP, RT, false, true>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
+                else epilogue<D, RP, RT, false, false>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                float tmp[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) tmp[x] = s[st >> 1][8 * (st & 1) + x];
+                const bf16x8 pb = pack8(tmp);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        &sm.vt[buf][(32 * db + lr) * VP + 16 * st + 8 * g]);
+                    o[db] = mfma32(a, pb, o[db]);
+                }
+            }
+        }
+        if (t + 1 < ntiles) store_tile(buf ^ 1, kt.tile(t + 1));
+        if (t + 2 < ntiles) load_tile(kt.tile(t + 2));
+        __syncthreads();
+    }
+
+    if (row_ok) {
+        bf16* og = static_cast<bf16*>(p.out) + (tok0 + i) * p.ld_out + h * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                bf16x4 w;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[c] = (bf16)(o[db][4 * r + c] * p.inv_n);
+                *reinterpret_cast<bf16x4*>(og + 32 * db + 8 * r + 4 * g) = w;
+            }
+    }
+}
+
+// ---- fp32 path: one thread per query row, keys streamed through the cache --------------------
+
+constexpr int kF32Rows = 64;
+
+template <int D>
+__global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(const AttnParams p) {
+    __shared__ float wp[kNumBuckets];
+    __shared__ float wt[kNumClasses];
+    const WorkUnit wu = p.units[blockIdx.x];
+    const SeqInfo si = p.seqs[wu.seq];
+    const int n = si.n, nc = si.nc, nh = si.nh, h = wu.head;
+    const int64_t tok0 = si.start, ld = p.ld_in;
+    const int i = wu.row0 + threadIdx.x;
+    const bool row_ok = i < n;
+    const bool has_rp = p.rab_pos != nullptr, has_rt = p.rab_ts != nullptr;
+    if (has_rp)
+        for (int e = threadIdx.x; e < kNumBuckets; e += kF32Rows) wp[e] = p.rab_pos[h * kNumBuckets + e];
+    if (has_rt)
+        for (int e = threadIdx.x; e < kNumClasses; e += kF32Rows)
+            wt[e] = p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+    __syncthreads();
+
+    int lim = -1, dg = -1;
+    if (row_ok) {
+        if (i < nh) lim = imax(i, nc - 1);
+        else { lim = nh - 1; dg = i; }
+    }
+    const float* qg = static_cast<const float*>(p.q) + tok0 * ld + h * D;
+    const float* kg = static_cast<const float*>(p.k) + tok0 * ld + h * D;
+    const float* vg = static_cast<const float*>(p.v) + tok0 * ld + h * D;
+    float q[D], acc[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        q[c] = row_ok ? qg[(int64_t)i * ld + c] : 0.0f;
+        acc[c] = 0.0f;
+    }
+    const int64_t ti = (has_rt && row_ok) ? p.ts[tok0 + i] : 0;
+    const int jend = __reduce_max_sync(~0ull, imax(lim, dg)) + 1;  // keys any lane sees
+    for (int j = 0; j < jend; ++j) {
+        const bool vis = j <= lim || j == dg;
+        if (!__any(vis)) continue;
+        float dot = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) dot = fmaf(q[c], kg[(int64_t)j * ld + c], dot);
+        float bias = 0.0f;
+        if (has_rp) bias += wp[bucket_of((uint32_t)(i > j ? i - j : j - i))];
+        if (has_rt && row_ok) bias += wt[bucket_class(absdiff_sat(ti, p.ts[tok0 + j]))];
+        const float x = fmaf(p.alpha, dot, bias);
+        const float w = vis ? x / (1.0f + expf(-x)) : 0.0f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(w, vg[(int64_t)j * ld + c], acc[c]);
+    }
+    if (row_ok) {
+        float* og = static_cast<float*>(p.out) + (tok0 + i) * p.ld_out + h * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) og[c] = acc[c] * p.inv_n;
+    }
+}
+
+template <int D, bool RP, bool RT>
+hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const AttnParams& p, hipStream_t s) {
+    const bool rp = p.rab_pos != nullptr, rt = p.rab_ts != nullptr;
+    if (rp && rt) return launch_bf16_t<D, true, true>(p, s);
+    if (rp) return launch_bf16_t<D, true, false>(p, s);
+    if (rt) return launch_bf16_t<D, false, true>(p, s);
+    return launch_bf16_t<D, false, false>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s) {
+    if (p.num_units == 0) return hipSuccess;
+    switch (p.head_dim) {
+        case 32: return launch_bf16_d<32>(p, s);
+        case 64: return launch_bf16_d<64>(p, s);
+        case 128: return launch_bf16_d<128>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_f32(const AttnParams& p, hipStream_t s) {
+    if (p.num_units == 0) return hipSuccess;
+    switch (p.head_dim) {
+        case 32: hipLaunchKernelGGL(fwd_f32_kernel<32>, dim3(p.num_units), dim3(kF32Rows), 0, s, p); break;
+        case 64: hipLaunchKernelGGL(fwd_f32_kernel<64>, dim3(p.num_units), dim3(kF32Rows), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(p.num_units), dim3(kF32Rows), 0, s, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hstu

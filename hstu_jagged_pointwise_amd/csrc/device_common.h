@@ -1,0 +1,100 @@
+// device_common.h -- types and small device helpers for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "geometry.h"
+
+namespace hstu {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Relative-bias bucket of a distance (exact integer rule: identity below 16, then four buckets
+// per octave, last bucket 127).  Any distance >= 2^32 lands in bucket 127, so callers may
+// saturate 64-bit distances to 0xffffffff.
+HSTU_HD int bucket_of(uint32_t x) {
+    if (x < 16u) return (int)x;
+#if defined(__HIP_DEVICE_COMPILE__)
+    int e = 31 - (int)__clz(x);
+#else
+    int e = 31 - __builtin_clz(x);
+#endif
+    int b = 16 + 4 * (e - 4) + (int)((x >> (e - 2)) & 3u);
+    return b < kNumBuckets - 1 ? b : kNumBuckets - 1;
+}
+
+// "Bucket class" of a distance: 8 * clz(x) + the three bits after the leading one.  Every class
+// lies inside one bucket, so a 264-entry table indexed by class replaces the bucket arithmetic in
+// the inner loops.  clz(0) = 32 gives class 256.
+constexpr int kNumClasses = 264;
+
+__device__ __forceinline__ uint32_t bucket_class(uint32_t x) {
+    uint32_t c = __clz(x);
+    uint32_t y = x << (c & 31u);
+    return c * 8u + ((y >> 28) & 7u);
+}
+
+// A representative distance of a class (any member gives the same bucket).
+HSTU_HD uint32_t class_representative(int cls) {
+    int c = cls >> 3, m = cls & 7;
+    if (c <= 28) return (uint32_t)(8 + m) << (28 - c);
+    if (c == 29) return 4u + (uint32_t)(m >> 1);
+    if (c == 30) return 2u + (uint32_t)(m >> 2);
+    if (c == 31) return 1u;
+    return 0u;
+}
+
+HSTU_HD int bucket_of_class(int cls) { return bucket_of(class_representative(cls)); }
+
+__device__ __forceinline__ uint32_t absdiff_u32(uint32_t a, uint32_t b) {
+    return a > b ? a - b : b - a;
+}
+
+// |a - b| for 64-bit timestamps, saturated to 32 bits (exact for bucketing, see bucket_of).
+__device__ __forceinline__ uint32_t absdiff_sat(int64_t a, int64_t b) {
+    uint64_t d = a >= b ? (uint64_t)(a - b) : (uint64_t)(b - a);
+    return d > 0xffffffffull ? 0xffffffffu : (uint32_t)d;
+}
+
+// Timestamps relative to a sequence base, biased into uint32 so that |a - b| is exact on 32-bit
+// unsigned values when both relatives fit in int32.
+__device__ __forceinline__ bool rel_time_fits(int64_t t, int64_t base) {
+    int64_t r = t - base;
+    return r >= -(int64_t)0x80000000ll && r <= (int64_t)0x7fffffffll;
+}
+__device__ __forceinline__ uint32_t rel_time_u32(int64_t t, int64_t base) {
+    return (uint32_t)(t - base) + 0x80000000u;
+}
+
+// SiLU pieces with hardware exp2 / reciprocal (about 1 ulp each).
+__device__ __forceinline__ float fast_sigmoid(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* v) {
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (bf16)v[t];
+    return r;
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Position of key k (0..63) inside a transposed tile row: bits 2 and 3 of k are swapped so that a
+// lane's eight P^T operands (keys 16s + 8(t/4) + 4g + t%4) are contiguous (16s + 8g + t).
+__device__ __forceinline__ int perm_key(int k) {
+    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+}  // namespace hstu

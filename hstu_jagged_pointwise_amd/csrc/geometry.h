@@ -1,0 +1,115 @@
+// geometry.h -- which (row block, key tile) pairs of a jagged sequence hold visible pairs.
+//
+// Shared by the host planner (work costs) and the kernels (iteration ranges), so both agree.
+// The composite mask follows page 2 ("RecSDK supports generative recommendation", HSTU
+// acceleration operator: causal + context/target masks, with whole blocks skipped) and page 1
+// section 2.1.2 (ranking: candidates at the end see the history and themselves only):
+//   nc = min(num_contexts, n), nt = min(num_targets, n - nc), nh = n - nt
+//   row i < nh (history) sees keys j <= max(i, nc - 1);  row i >= nh (candidate) sees j < nh
+//   and j == i.
+// Every key tile is BN = 64 keys wide and aligned to multiples of 64 within the sequence.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define HSTU_HD __host__ __device__ __forceinline__
+#else
+#define HSTU_HD inline
+#endif
+
+namespace hstu {
+
+constexpr int kNumBuckets = 128;
+constexpr int kKeyTile = 64;     // keys per tile in the forward / dQ kernels
+constexpr int kQueryTile = 64;   // queries per tile in the dK/dV kernel
+constexpr int kWaveRows = 32;    // rows (or keys) owned by one wavefront
+
+struct SeqInfo {
+    int32_t start;  // first token of the sequence in the packed token dimension
+    int32_t n;      // length
+    int32_t nc;     // effective number of context tokens
+    int32_t nh;     // effective number of non-candidate tokens (n - candidates)
+};
+
+struct WorkUnit {
+    int32_t seq, head, row0, cost;
+};
+
+HSTU_HD int imax(int a, int b) { return a > b ? a : b; }
+HSTU_HD int imin(int a, int b) { return a < b ? a : b; }
+HSTU_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+HSTU_HD void split_sequence(int n, int num_contexts, int num_targets, int* nc, int* nh) {
+    int c = imin(imax(num_contexts, 0), n);
+    int t = imin(imax(num_targets, 0), n - c);
+    *nc = c;
+    *nh = n - t;
+}
+
+// Key tiles visible to query rows [rlo, rhi) (rhi <= n): tiles [0, main_tiles) followed by
+// tiles [diag_first, diag_first + diag_tiles), the candidates' own diagonal.
+struct KeyTiles {
+    int main_tiles, diag_first, diag_tiles;
+    HSTU_HD int count() const { return main_tiles + diag_tiles; }
+    HSTU_HD int tile(int t) const { return t < main_tiles ? t : diag_first + (t - main_tiles); }
+};
+
+HSTU_HD KeyTiles key_tiles_for_rows(int rlo, int rhi, int nc, int nh) {
+    KeyTiles r{0, 0, 0};
+    if (rhi <= rlo) return r;
+    int kmain = 0;
+    if (rlo < nh) kmain = imax(imin(rhi, nh), nc);  // history rows: up to the last row, contexts
+    if (rhi > nh) kmain = imax(kmain, nh);          // candidate rows: the whole history
+    r.main_tiles = cdiv(kmain, kKeyTile);
+    if (rhi > nh) {
+        int first = imax(imax(rlo, nh) / kKeyTile, r.main_tiles);
+        int last = cdiv(rhi, kKeyTile);
+        r.diag_first = first;
+        r.diag_tiles = imax(0, last - first);
+    }
+    return r;
+}
+
+// Classification of the block rows [rlo, rhi) x keys [j0, j0 + 64) (rhi <= n).
+enum TileKind { kEmpty = 0, kPartial = 1, kFull = 2 };
+
+HSTU_HD int classify_row_tile(int rlo, int rhi, int j0, int n, int nc, int nh) {
+    if (rhi <= rlo) return kEmpty;
+    int j1 = j0 + kKeyTile - 1;
+    bool any = false;
+    int hhi = imin(rhi, nh);
+    if (rlo < hhi && j0 <= imax(hhi - 1, nc - 1)) any = true;          // history rows
+    int tlo = imax(rlo, nh);
+    if (tlo < rhi && (j0 < nh || (j0 < rhi && j1 >= tlo))) any = true;  // candidate rows
+    if (!any) return kEmpty;
+    if (j1 >= n) return kPartial;
+    if (rhi <= nh && j1 <= imax(rlo, nc - 1)) return kFull;             // all history rows
+    if (rlo >= nh && j1 < nh) return kFull;                             // all candidate rows
+    return kPartial;
+}
+
+// Query rows that see keys [klo, khi) (khi <= n): one contiguous range [qlo, qhi).
+HSTU_HD void rows_for_keys(int klo, int khi, int n, int nc, int nh, int* qlo, int* qhi) {
+    if (khi <= klo) { *qlo = 0; *qhi = 0; return; }
+    *qlo = klo < nc ? 0 : klo;
+    *qhi = klo < nh ? n : imin(khi, n);
+}
+
+// Classification of the block queries [i0, i0 + 64) x keys [klo, khi) (khi <= n).
+HSTU_HD int classify_key_tile(int klo, int khi, int i0, int n, int nc, int nh) {
+    if (khi <= klo) return kEmpty;
+    int i1 = i0 + kQueryTile - 1;
+    bool any = false;
+    if (klo < nc && i0 < n) any = true;                                  // context keys
+    int hlo = imax(klo, nc), hhi = imin(khi, nh);
+    if (hlo < hhi && i1 >= hlo && i0 < n) any = true;                    // history keys
+    int tlo = imax(klo, nh);
+    if (tlo < khi && i0 < khi && i1 >= tlo) any = true;                  // candidate keys
+    if (!any) return kEmpty;
+    if (i1 >= n) return kPartial;
+    if (khi <= nc) return kFull;                                         // all context keys
+    if (khi <= nh && i0 >= khi - 1) return kFull;                        // all history keys
+    return kPartial;
+}
+
+}  // namespace hstu

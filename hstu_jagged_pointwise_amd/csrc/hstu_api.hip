@@ -1,0 +1,379 @@
+// hstu_api.hip -- host side of the C ABI declared in include/hstu.h: argument validation, the
+// cost-balanced work lists (plans), and kernel dispatch.  No device memory is allocated outside
+// hstu_plan_create.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "hstu.h"
+#include "kernels.h"
+
+using hstu::SeqInfo;
+using hstu::WorkUnit;
+
+struct hstu_plan {
+    int device = -1;
+    bool on_device = false;
+    hstu_attn_args_t shape{};  // sizes only; pointer fields are cleared
+    int32_t fwd_rows = 0;      // query rows per forward / dQ work unit
+    int32_t bwd_keys = 0;      // keys per dK/dV work unit
+    int64_t pairs = 0;
+    int64_t fwd_tiles = 0;
+    std::vector<SeqInfo> seqs;
+    std::vector<WorkUnit> fwd, bwd;
+    void* dbuf = nullptr;
+    const SeqInfo* d_seqs = nullptr;
+    const WorkUnit* d_fwd = nullptr;
+    const WorkUnit* d_bwd = nullptr;
+};
+
+namespace {
+
+size_t elem_size(int32_t dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hstu_status_t check_args(const hstu_attn_args_t* a) {
+    if (!a) return HSTU_ERR_NULL_ARG;
+    if (a->dtype != HSTU_F32 && a->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+    if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128) return HSTU_ERR_UNSUPPORTED;
+    if (a->batch < 0 || a->num_heads < 1 || a->total_tokens < 0 ||
+        a->total_tokens >= (int64_t(1) << 31) || a->max_seqlen < 1 || a->num_contexts < 0 ||
+        a->reserved != 0 || !std::isfinite(a->alpha))
+        return HSTU_ERR_BAD_SHAPE;
+    int64_t hd = int64_t(a->num_heads) * a->head_dim;
+    if (a->qkv_token_stride != 0 && a->qkv_token_stride < hd) return HSTU_ERR_BAD_SHAPE;
+    if (a->qkv_token_stride % 8 != 0) return HSTU_ERR_MISALIGNED;
+    if (a->rab_ts && !a->timestamps) return HSTU_ERR_NULL_ARG;
+    return HSTU_OK;
+}
+
+// The call's sizes must be the plan's.
+hstu_status_t check_call(const hstu_plan_t* plan, const hstu_attn_args_t* a) {
+    if (!plan) return HSTU_ERR_NULL_ARG;
+    hstu_status_t s = check_args(a);
+    if (s != HSTU_OK) return s;
+    const hstu_attn_args_t& p = plan->shape;
+    if (a->dtype != p.dtype || a->batch != p.batch || a->num_heads != p.num_heads ||
+        a->head_dim != p.head_dim || a->total_tokens != p.total_tokens ||
+        a->max_seqlen != p.max_seqlen || a->num_contexts != p.num_contexts)
+        return HSTU_ERR_BAD_SHAPE;
+    if (!plan->on_device) return HSTU_ERR_NO_DEVICE_PLAN;
+    if ((a->timestamps && !aligned16(a->timestamps)) || (a->rab_pos && !aligned16(a->rab_pos)) ||
+        (a->rab_ts && !aligned16(a->rab_ts)))
+        return HSTU_ERR_MISALIGNED;
+    return HSTU_OK;
+}
+
+int64_t visible_pairs(int64_t n, int64_t nc, int64_t nh) {
+    // history rows: the first nc see nc keys, row i in [nc, nh) sees i + 1; candidates see nh + 1
+    return nc * nc + (nh * (nh + 1) - nc * (nc + 1)) / 2 + (n - nh) * (nh + 1);
+}
+
+void sort_longest_first(std::vector<WorkUnit>& u) {
+    std::stable_sort(u.begin(), u.end(),
+                     [](const WorkUnit& a, const WorkUnit& b) { return a.cost > b.cost; });
+}
+
+hstu::AttnParams base_params(const hstu_plan_t* plan, const hstu_attn_args_t* a) {
+    hstu::AttnParams p{};
+    p.seqs = plan->d_seqs;
+    p.units = plan->d_fwd;
+    p.num_units = (int32_t)plan->fwd.size();
+    p.heads = a->num_heads;
+    p.head_dim = a->head_dim;
+    int64_t hd = int64_t(a->num_heads) * a->head_dim;
+    p.ld_in = a->qkv_token_stride ? a->qkv_token_stride : hd;
+    p.ld_out = hd;
+    p.alpha = a->alpha;
+    p.inv_n = 1.0f / (float)a->max_seqlen;
+    p.ts = a->timestamps;
+    p.rab_pos = a->rab_pos;
+    p.rab_ts = a->rab_ts;
+    return p;
+}
+
+hstu_status_t hip_status(hipError_t e) { return e == hipSuccess ? HSTU_OK : HSTU_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hstu_status_str(hstu_status_t s) {
+    switch (s) {
+        case HSTU_OK: return "ok";
+        case HSTU_ERR_NULL_ARG: return "a required pointer is NULL";
+        case HSTU_ERR_BAD_SHAPE: return "sizes invalid or inconsistent with the plan";
+        case HSTU_ERR_BAD_OFFSETS: return "seq_offsets must run from 0 to T without decreasing, "
+                                          "and no length may exceed max_seqlen";
+        case HSTU_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or model width";
+        case HSTU_ERR_MISALIGNED: return "pointers must be 16-byte aligned and token strides a "
+                                         "multiple of 8 elements";
+        case HSTU_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than hstu_workspace_bytes()";
+        case HSTU_ERR_HIP: return "a HIP runtime call failed";
+        case HSTU_ERR_NO_DEVICE_PLAN: return "plan was created host-only";
+    }
+    return "unknown status";
+}
+
+hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
+                               const int32_t* num_targets, uint32_t flags, hstu_plan_t** out) {
+    if (!out) return HSTU_ERR_NULL_ARG;
+    *out = nullptr;
+    hstu_status_t st = check_args(args);
+    if (st != HSTU_OK) return st;
+    if (!off) return HSTU_ERR_NULL_ARG;
+    const int B = args->batch;
+    if (off[0] != 0 || off[B] != args->total_tokens) return HSTU_ERR_BAD_OFFSETS;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = off[b + 1] - off[b];
+        if (n < 0 || n > args->max_seqlen) return HSTU_ERR_BAD_OFFSETS;
+        if (num_targets && num_targets[b] < 0) return HSTU_ERR_BAD_SHAPE;
+    }
+
+    hstu_plan_t* plan = new (std::nothrow) hstu_plan_t();
+    if (!plan) return HSTU_ERR_HIP;
+    plan->shape = *args;
+    plan->shape.timestamps = nullptr;
+    plan->shape.rab_pos = nullptr;
+    plan->shape.rab_ts = nullptr;
+    const bool bf16 = args->dtype == HSTU_BF16;
+    plan->fwd_rows = bf16 ? 4 * hstu::kWaveRows : 64;
+    plan->bwd_keys = bf16 ? 4 * hstu::kWaveRows : 64;
+    const int H = args->num_heads;
+
+    plan->seqs.resize(B);
+    for (int b = 0; b < B; ++b) {
+        int n = (int)(off[b + 1] - off[b]);
+        int nc, nh;
+        hstu::split_sequence(n, args->num_contexts, num_targets ? num_targets[b] : 0, &nc, &nh);
+        plan->seqs[b] = SeqInfo{(int32_t)off[b], n, nc, nh};
+        plan->pairs += visible_pairs(n, nc, nh) * H;
+    }
+    for (int b = 0; b < B; ++b) {
+        const SeqInfo& s = plan->seqs[b];
+        // forward / dQ: row blocks
+        for (int r0 = 0; r0 < s.n; r0 += plan->fwd_rows) {
+            int rhi = std::min(r0 + plan->fwd_rows, s.n);
+            hstu::KeyTiles kt = hstu::key_tiles_for_rows(r0, rhi, s.nc, s.nh);
+            int64_t wave_tiles = 0;
+            for (int t = 0; t < kt.count(); ++t) {
+                int j0 = kt.tile(t) * hstu::kKeyTile;
+                for (int w0 = r0; w0 < rhi; w0 += hstu::kWaveRows)
+                    wave_tiles += hstu::classify_row_tile(w0, std::min(w0 + hstu::kWaveRows, rhi),
+                                                          j0, s.n, s.nc, s.nh) != hstu::kEmpty;
+            }
+            plan->fwd_tiles += wave_tiles * H;
+            for (int h = 0; h < H; ++h) plan->fwd.push_back(WorkUnit{b, h, r0, kt.count()});
+        }
+        // dK/dV: key blocks
+        for (int k0 = 0; k0 < s.n; k0 += plan->bwd_keys) {
+            int qlo, qhi;
+            hstu::rows_for_keys(k0, std::min(k0 + plan->bwd_keys, s.n), s.n, s.nc, s.nh, &qlo,
+                                &qhi);
+            int cost = hstu::cdiv(qhi, hstu::kQueryTile) - qlo / hstu::kQueryTile;
+            for (int h = 0; h < H; ++h) plan->bwd.push_back(WorkUnit{b, h, k0, cost});
+        }
+    }
+    sort_longest_first(plan->fwd);
+    sort_longest_first(plan->bwd);
+
+    if (!(flags & HSTU_PLAN_HOST_ONLY)) {
+        size_t nb = sizeof(SeqInfo) * plan->seqs.size();
+        size_t nf = sizeof(WorkUnit) * plan->fwd.size();
+        size_t nk = sizeof(WorkUnit) * plan->bwd.size();
+        size_t total = std::max<size_t>(nb + nf + nk, 16);
+        std::vector<char> host(total);
+        if (nb) std::memcpy(host.data(), plan->seqs.data(), nb);
+        if (nf) std::memcpy(host.data() + nb, plan->fwd.data(), nf);
+        if (nk) std::memcpy(host.data() + nb + nf, plan->bwd.data(), nk);
+        if (hipGetDevice(&plan->device) != hipSuccess ||
+            hipMalloc(&plan->dbuf, total) != hipSuccess) {
+            delete plan;
+            return HSTU_ERR_HIP;
+        }
+        if (hipMemcpy(plan->dbuf, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(plan->dbuf);
+            delete plan;
+            return HSTU_ERR_HIP;
+        }
+        char* base = static_cast<char*>(plan->dbuf);
+        plan->d_seqs = reinterpret_cast<const SeqInfo*>(base);
+        plan->d_fwd = reinterpret_cast<const WorkUnit*>(base + nb);
+        plan->d_bwd = reinterpret_cast<const WorkUnit*>(base + nb + nf);
+        plan->on_device = true;
+    }
+    *out = plan;
+    return HSTU_OK;
+}
+
+void hstu_plan_destroy(hstu_plan_t* plan) {
+    if (!plan) return;
+    if (plan->dbuf) (void)hipFree(plan->dbuf);
+    delete plan;
+}
+
+hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info) {
+    if (!plan || !info) return HSTU_ERR_NULL_ARG;
+    info->visible_pairs = plan->pairs;
+    info->fwd_units = (int64_t)plan->fwd.size();
+    info->bwd_units = (int64_t)plan->bwd.size();
+    info->fwd_tiles = plan->fwd_tiles;
+    info->fwd_row_block = plan->fwd_rows;
+    info->bwd_key_block = plan->bwd_keys;
+    return HSTU_OK;
+}
+
+hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* units, int64_t cap,
+                              int64_t* count) {
+    if (!plan || !count) return HSTU_ERR_NULL_ARG;
+    if (op != 0 && op != 1) return HSTU_ERR_BAD_SHAPE;
+    const std::vector<WorkUnit>& u = op == 0 ? plan->fwd : plan->bwd;
+    *count = (int64_t)u.size();
+    if (cap > 0 && !units) return HSTU_ERR_NULL_ARG;
+    int64_t m = std::min<int64_t>(cap, (int64_t)u.size());
+    for (int64_t i = 0; i < m; ++i) {
+        units[4 * i + 0] = u[i].seq;
+        units[4 * i + 1] = u[i].head;
+        units[4 * i + 2] = u[i].row0;
+        units[4 * i + 3] = u[i].cost;
+    }
+    return HSTU_OK;
+}
+
+size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model) {
+    if (!plan) return 0;
+    const hstu_attn_args_t& a = plan->shape;
+    size_t thd = size_t(a.total_tokens) * a.num_heads * a.head_dim;
+    switch (op) {
+        case 1: return align_up(thd * elem_size(a.dtype), 256);
+        case 3: {
+            (void)d_model;  // Z and A depend on H*d only
+            return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256);
+        }
+        default: return 0;
+    }
+}
+
+hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args, const void* q,
+                            const void* k, const void* v, const void* u, float ln_eps, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+    hstu_status_t st = check_call(plan, args);
+    if (st != HSTU_OK) return st;
+    if (args->total_tokens == 0) return HSTU_OK;  // nothing to read or write; pointers may be NULL
+    if (!q || !k || !v || !out) return HSTU_ERR_NULL_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (u && !aligned16(u)))
+        return HSTU_ERR_MISALIGNED;
+    if (u) {
+        if (!ws) return HSTU_ERR_NULL_ARG;
+        if (ws_bytes < hstu_workspace_bytes(plan, 1, 0)) return HSTU_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(ws)) return HSTU_ERR_MISALIGNED;
+        if (!(ln_eps >= 0.0f) || !std::isfinite(ln_eps)) return HSTU_ERR_BAD_SHAPE;
+    }
+    if (plan->fwd.empty()) return HSTU_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hstu::AttnParams p = base_params(plan, args);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = u ? ws : out;
+    hipError_t e = args->dtype == HSTU_BF16 ? hstu::launch_attn_fwd_bf16(p, s)
+                                            : hstu::launch_attn_fwd_f32(p, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    if (u) {
+        int64_t ldu = args->qkv_token_stride ? args->qkv_token_stride : p.ld_out;
+        int32_t width = (int32_t)p.ld_out;
+        e = args->dtype == HSTU_BF16
+                ? hstu::launch_ln_gate_bf16(ws, u, ldu, out, args->total_tokens, width, ln_eps, s)
+                : hstu::launch_ln_gate_f32(ws, u, ldu, out, args->total_tokens, width, ln_eps, s);
+    }
+    return hip_status(e);
+}
+
+hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args, const void* q,
+                            const void* k, const void* v, const void* dout, void* dq, void* dk,
+                            void* dv, float* drab_pos, float* drab_ts, void* ws, size_t ws_bytes,
+                            void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    hstu_status_t st = check_call(plan, args);
+    if (st != HSTU_OK) return st;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) {
+        if (args->total_tokens != 0) return HSTU_ERR_NULL_ARG;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || (drab_pos && !aligned16(drab_pos)) ||
+        (drab_ts && !aligned16(drab_ts)))
+        return HSTU_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hstu::AttnParams p = base_params(plan, args);
+    p.units = plan->d_bwd;
+    p.num_units = (int32_t)plan->bwd.size();
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.drab_pos = args->rab_pos ? drab_pos : nullptr;
+    p.drab_ts = args->rab_ts ? drab_ts : nullptr;
+    const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
+    hipError_t e = hipSuccess;
+    if (p.drab_pos) e = hstu::launch_zero_f32(p.drab_pos, nb, s);
+    if (e == hipSuccess && p.drab_ts) e = hstu::launch_zero_f32(p.drab_ts, nb, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    if (plan->fwd.empty()) return HSTU_OK;
+    e = args->dtype == HSTU_BF16
+            ? hstu::launch_attn_bwd_bf16(p, plan->d_fwd, (int32_t)plan->fwd.size(), s)
+            : hstu::launch_attn_bwd_f32(p, plan->d_fwd, (int32_t)plan->fwd.size(), s);
+    return hip_status(e);
+}
+
+hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                             int32_t d_model, const void* x, const void* w1, const void* w2,
+                             float ln_eps, void* y, void* ws, size_t ws_bytes, void* stream) {
+    hstu_status_t st = check_call(plan, args);
+    if (st != HSTU_OK) return st;
+    if (args->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+    if (!x || !w1 || !w2 || !y || !ws) return HSTU_ERR_NULL_ARG;
+    if (d_model < 128 || d_model % 128 != 0) return HSTU_ERR_UNSUPPORTED;
+    if ((args->num_heads * args->head_dim) % 64 != 0) return HSTU_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y) || !aligned16(ws))
+        return HSTU_ERR_MISALIGNED;
+    if (ws_bytes < hstu_workspace_bytes(plan, 3, d_model)) return HSTU_ERR_WORKSPACE_TOO_SMALL;
+    if (!(ln_eps >= 0.0f) || !std::isfinite(ln_eps)) return HSTU_ERR_BAD_SHAPE;
+    const int64_t T = args->total_tokens;
+    const int32_t hd = args->num_heads * args->head_dim;
+    if (T == 0) return HSTU_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* z = static_cast<char*>(ws);
+    char* a = z + align_up(size_t(T) * 4 * hd * 2, 256);
+    // Z = SiLU(X W1): columns [U | V | Q | K]
+    hipError_t e = hstu::launch_gemm_bf16(x, w1, z, nullptr, T, 4 * hd, d_model, 0, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    hstu::AttnParams p = base_params(plan, args);
+    const int64_t ldz = 4 * int64_t(hd);
+    p.ld_in = ldz;
+    p.v = z + size_t(hd) * 2;
+    p.q = z + size_t(2 * hd) * 2;
+    p.k = z + size_t(3 * hd) * 2;
+    p.out = a;
+    e = hstu::launch_attn_fwd_bf16(p, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    // G = LayerNorm(A) * U, in place over A
+    e = hstu::launch_ln_gate_bf16(a, z, ldz, a, T, hd, ln_eps, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    // Y = G W2 + X
+    e = hstu::launch_gemm_bf16(a, w2, y, x, T, d_model, hd, 1, s);
+    return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+"""Convenience layer over the binding: put a batch (dict of host arrays) on the GPU and call the
+library.  Only data movement and argument marshalling happen here."""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_fwd, hstu_layer_fwd,
+               hstu_plan_create, make_args)
+
+
+def to_device(batch: dict, device: str = "cuda:0") -> dict:
+    """Copy the arrays of a batch to `device` (floating tensors in the batch's dtype)."""
+    import torch
+    fdt = torch.bfloat16 if batch["dtype"] == "bf16" else torch.float32
+    out = {}
+    for key in ("q", "k", "v", "dout", "x", "w1", "w2", "u"):
+        if batch.get(key) is not None:
+            out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.float32)).to(
+                device=device, dtype=fdt)
+    for key in ("rab_pos", "rab_ts"):
+        if batch.get(key) is not None:
+            out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.float32)).to(device)
+    if batch.get("timestamps") is not None:
+        out["timestamps"] = torch.from_numpy(np.ascontiguousarray(batch["timestamps"], np.int64)).to(device)
+    return out
+
+
+def args_for(batch: dict, dev: dict, qkv_token_stride: int = 0, use_rab: bool = True):
+    return make_args(
+        dtype=HSTU_BF16 if batch["dtype"] == "bf16" else HSTU_F32,
+        batch=batch["batch"], num_heads=batch["heads"], head_dim=batch["d"],
+        total_tokens=batch["total_tokens"], max_seqlen=batch["max_seqlen"],
+        num_contexts=batch.get("num_contexts", 0), alpha=batch["alpha"],
+        qkv_token_stride=qkv_token_stride,
+        timestamps=dev.get("timestamps") if use_rab else None,
+        rab_pos=dev.get("rab_pos") if use_rab else None,
+        rab_ts=dev.get("rab_ts") if use_rab else None)
+
+
+def plan_for(batch: dict, args, flags: int = 0):
+    return hstu_plan_create(args, batch["seq_offsets"], batch.get("num_targets"), flags)
+
+
+def empty_like_thd(batch: dict, dev: dict):
+    import torch
+    T, H, d = batch["total_tokens"], batch["heads"], batch["d"]
+    fdt = torch.bfloat16 if batch["dtype"] == "bf16" else torch.float32
+    return torch.empty((T, H, d), dtype=fdt, device=dev_device(dev))
+
+
+def dev_device(dev: dict):
+    for t in dev.values():
+        return t.device
+    import torch
+    return torch.device("cuda:0")
+
+
+def attn_fwd(batch: dict, dev: dict, plan=None, args=None, u=None, ln_eps: float = 1e-5,
+             out=None, stream=None):
+    args = args_for(batch, dev) if args is None else args
+    plan = plan_for(batch, args) if plan is None else plan
+    out = empty_like_thd(batch, dev) if out is None else out
+    hstu_attn_fwd(plan, args, dev["q"], dev["k"], dev["v"], out, u=u, ln_eps=ln_eps,
+                  stream=stream)
+    return out
+
+
+def attn_bwd(batch: dict, dev: dict, plan=None, args=None, stream=None) -> dict:
+    import torch
+    args = args_for(batch, dev) if args is None else args
+    plan = plan_for(batch, args) if plan is None else plan
+    g = dict(dq=empty_like_thd(batch, dev), dk=empty_like_thd(batch, dev),
+             dv=empty_like_thd(batch, dev), drab_pos=None, drab_ts=None)
+    H = batch["heads"]
+    if dev.get("rab_pos") is not None:
+        g["drab_pos"] = torch.empty((H, 128), dtype=torch.float32, device=dev_device(dev))
+    if dev.get("rab_ts") is not None:
+        g["drab_ts"] = torch.empty((H, 128), dtype=torch.float32, device=dev_device(dev))
+    hstu_attn_bwd(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], g["dq"], g["dk"],
+                  g["dv"], g["drab_pos"], g["drab_ts"], stream=stream)
+    return g
+
+
+def layer_fwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5, y=None,
+              stream=None):
+    import torch
+    args = args_for(batch, dev) if args is None else args
+    plan = plan_for(batch, args) if plan is None else plan
+    T, D = batch["total_tokens"], batch["layer_dim"]
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=dev_device(dev)) if y is None else y
+    hstu_layer_fwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], y, ln_eps=ln_eps, stream=stream)
+    return y

@@ -1,0 +1,157 @@
+/*
+ * hstu.h -- C ABI of the MI355X (gfx950) HSTU jagged-attention library.
+ *
+ * The library computes HSTU pointwise attention over jagged user-behaviour sequences and the full
+ * HSTU layer built around it.  Sources for each operation:
+ *
+ *   - Jagged layout: sequences are stored back to back in the token dimension and located by
+ *     start offsets, as in TorchRec's KeyedJaggedTensor (page 1, "Generative recommendation:
+ *     algorithm evolution to engineering", section 3.1.2).
+ *   - Attention (page 1 section 2.1.2, HSTU, spatial aggregation, equation (2)): no softmax;
+ *     a relative attention bias from positions and timestamps is added to the scaled scores and
+ *     SiLU is applied pointwise:
+ *         S_ij = alpha * <q_i, k_j> + rab_pos[h, bucket(|i - j|)] + rab_ts[h, bucket(|t_i - t_j|)]
+ *         O_i  = sum_j vis(i, j) * SiLU(S_ij) / N * v_j           (N = max_seqlen)
+ *   - Mask (page 2, "RecSDK supports generative recommendation", HSTU acceleration operator:
+ *     composite causal + context/target mask; page 1 section 2.1.2, ranking task: candidates at
+ *     the end of a sequence must not interact).  For a sequence of length n:
+ *         nc = min(num_contexts, n), nt = min(num_targets[b], n - nc), nh = n - nt
+ *         vis(i, j) = j < nc  or  (i < nh and j <= i)  or  (i >= nh and (j < nh or j == i))
+ *   - bucket(x) = x for x < 16, else min(127, 16 + 4 (e - 4) + ((x >> (e - 2)) & 3)) with
+ *     e = floor(log2 x): exact buckets for short distances, then four per octave.
+ *   - Layer (page 1 section 2.1.2, equations (1)-(3)): Z = SiLU(X W1) split into U, V, Q, K
+ *     (column blocks of width H*d in that order, head-major inside a block); A = attention;
+ *     Y = (LayerNorm(A) * U) W2 + X, LayerNorm per token over all H*d features, biased variance,
+ *     no affine parameters.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are caller-owned device memory.  q, k, v, u, out, dout, dq, dk, dv are "THD":
+ *     element (token t, head h, channel c) sits at t * token_stride + h * head_dim + c, with
+ *     token_stride = num_heads * head_dim unless args->qkv_token_stride says otherwise (q, k, v
+ *     and u only; outputs are always dense).  Element type is args->dtype.
+ *   - Device pointers must be 16-byte aligned and token strides a multiple of 8 elements
+ *     (HSTU_ERR_MISALIGNED otherwise).
+ *   - Calls validate on the host, enqueue on `stream` (a hipStream_t; NULL = default stream) and
+ *     return without waiting.  Nothing is allocated during fwd/bwd/layer calls; scratch memory is
+ *     the caller's `ws` of at least hstu_workspace_bytes() bytes.  Kernel faults surface at the
+ *     caller's next synchronisation.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Every function is reentrant; a plan is read-only after creation and may serve calls on any
+ *     stream of the device it was created on.
+ */
+#ifndef HSTU_H
+#define HSTU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HSTU_OK = 0,
+    HSTU_ERR_NULL_ARG = 1,             /* a required pointer is NULL */
+    HSTU_ERR_BAD_SHAPE = 2,            /* sizes invalid or inconsistent with the plan */
+    HSTU_ERR_BAD_OFFSETS = 3,          /* seq_offsets not 0 .. T non-decreasing, or a length > N */
+    HSTU_ERR_UNSUPPORTED = 4,          /* head_dim / dtype combination not implemented */
+    HSTU_ERR_MISALIGNED = 5,           /* pointer or stride alignment */
+    HSTU_ERR_WORKSPACE_TOO_SMALL = 6,  /* ws_bytes < hstu_workspace_bytes() */
+    HSTU_ERR_HIP = 7,                  /* a HIP runtime call failed */
+    HSTU_ERR_NO_DEVICE_PLAN = 8        /* plan was created host-only and cannot be launched */
+} hstu_status_t;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
+
+/* Problem description shared by a plan and the calls that use it. */
+typedef struct {
+    int32_t dtype;             /* hstu_dtype_t of q, k, v, u, out, dout, dq, dk, dv, x, w1, w2, y */
+    int32_t batch;             /* B >= 0 sequences */
+    int32_t num_heads;         /* H >= 1 */
+    int32_t head_dim;          /* d = d_qk = d_v; 32, 64 or 128 */
+    int64_t total_tokens;      /* T = seq_offsets[B], < 2^31 */
+    int32_t max_seqlen;        /* N >= every length; the output scale is 1/N */
+    int32_t num_contexts;      /* >= 0 leading tokens of every sequence visible to all queries */
+    float alpha;               /* multiplies q.k only, not the bias */
+    int32_t reserved;          /* must be 0 */
+    int64_t qkv_token_stride;  /* elements between tokens of q, k, v, u; 0 means H * d */
+    const int64_t* timestamps; /* device [T] int64 seconds, or NULL (then rab_ts must be NULL) */
+    const float* rab_pos;      /* device [H][128] fp32 position-bias table, or NULL */
+    const float* rab_ts;       /* device [H][128] fp32 time-bias table, or NULL */
+} hstu_attn_args_t;
+
+typedef struct hstu_plan hstu_plan_t;
+
+/* Summary of a plan, for throughput accounting and tests. */
+typedef struct {
+    int64_t visible_pairs;     /* sum over sequences of visible (i, j) pairs, all heads */
+    int64_t fwd_units;         /* work items of the forward (and dQ) launch */
+    int64_t bwd_units;         /* work items of the dK/dV launch */
+    int64_t fwd_tiles;         /* (32-row, 64-key) tiles the forward computes, all units */
+    int64_t fwd_row_block;     /* query rows per forward work item */
+    int64_t bwd_key_block;     /* keys per dK/dV work item */
+} hstu_plan_info_t;
+
+#define HSTU_PLAN_HOST_ONLY 1u /* plan_create flag: plan on the host only (inspection, tests) */
+
+/* Build the cost-balanced work lists for one batch (page 2, HSTU acceleration operator: greedy
+ * even assignment of irregular work to cores).  seq_offsets_host: host [B+1] int64 start offsets
+ * (KeyedJaggedTensor offsets, page 1 section 3.1.2) with [0] = 0 and [B] = T.
+ * num_targets_host: host [B] int32 candidates per sequence, or NULL for none.  Work items are
+ * (sequence, head, row block) ordered by decreasing cost, so the hardware dispatcher assigns the
+ * longest first.  Unless flags has HSTU_PLAN_HOST_ONLY, the lists are copied synchronously into
+ * one device buffer owned by the plan, on the current device.  *out receives the plan, or NULL
+ * on error.  The caller frees it with hstu_plan_destroy. */
+hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* seq_offsets_host,
+                               const int32_t* num_targets_host, uint32_t flags,
+                               hstu_plan_t** out);
+
+/* Frees the plan and its device buffer (waits for nothing: the caller must not destroy a plan
+ * that queued work still uses).  NULL is ignored. */
+void hstu_plan_destroy(hstu_plan_t* plan);
+
+/* Fills *info. */
+hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info);
+
+/* Copies the work list of `op` (0 = forward / dQ, 1 = dK/dV) to host memory as int32 quadruples
+ * {sequence, head, first row (or key), cost} in launch order.  Writes at most `cap` items and
+ * returns the total count through *count. */
+hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* units, int64_t cap,
+                              int64_t* count);
+
+/* Scratch bytes a call needs: op 0 = hstu_attn_fwd without u, 1 = hstu_attn_fwd with u,
+ * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd with model width d_model (ignored otherwise). */
+size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
+
+/* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.
+ * If u is non-NULL, out instead receives LayerNorm(O) * u per token over all H*d features
+ * (the gating part of equation (3), without W2), and ws must hold hstu_workspace_bytes(plan, 1).
+ * ln_eps is used only with u. */
+hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                            const void* q, const void* k, const void* v, const void* u,
+                            float ln_eps, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention backward: given dout = dL/dO, writes dq, dk, dv (dense THD, args->dtype) and, when
+ * the pointers and the matching tables are non-NULL, drab_pos / drab_ts ([H][128] fp32,
+ * overwritten).  Bias gradients are summed with fp32 atomics, so their low bits depend on
+ * scheduling. */
+hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                            const void* q, const void* k, const void* v, const void* dout,
+                            void* dq, void* dk, void* dv, float* drab_pos, float* drab_ts,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Full HSTU layer forward, bf16 only.  x: (T, d_model) dense; w1: (d_model, 4*H*d) row-major;
+ * w2: (H*d, d_model) row-major; y: (T, d_model).  args->qkv_token_stride is ignored (Q, K, V, U
+ * are produced internally).  ws must hold hstu_workspace_bytes(plan, 3, d_model). */
+hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                             int32_t d_model, const void* x, const void* w1, const void* w2,
+                             float ln_eps, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* hstu_status_str(hstu_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H */

@@ -1,0 +1,216 @@
+"""CPU-only checks of the C-ABI library: it loads and exports every declared symbol, rejects bad
+arguments on the host with the documented status codes, and plans work lists that cover every
+visible (query, key) pair exactly as the composite mask requires (checked against the oracle's
+mask by enumeration).  No GPU call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import hstu_synth as hs
+import oracle
+import oracle.brute as brute
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+hj = pytest.importorskip("hstu_jagged_pointwise_amd")
+
+
+def _lib():
+    try:
+        return hj.load_library()
+    except RuntimeError as e:  # pragma: no cover - the build step runs before the tests
+        pytest.fail(str(e))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib()
+    names = declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(names) == sorted(hj.EXPORTS)
+
+
+def test_status_strings():
+    for s in range(9):
+        assert hj.hstu_status_str(s) and hj.hstu_status_str(s) != "unknown status"
+    assert hj.hstu_status_str(99) == "unknown status"
+
+
+def args(**kw):
+    base = dict(dtype=hj.HSTU_BF16, batch=3, num_heads=2, head_dim=64, total_tokens=30,
+                max_seqlen=16, num_contexts=1, alpha=0.125)
+    base.update(kw)
+    return hj.make_args(**base)
+
+
+OFF = np.array([0, 10, 14, 30])
+
+
+def status_of(fn, *a, **kw):
+    try:
+        fn(*a, **kw)
+    except hj.HstuError as e:
+        return e.status
+    return 0
+
+
+def test_plan_validation_codes():
+    c = hj.hstu_plan_create
+    host = hj.HSTU_PLAN_HOST_ONLY
+    assert status_of(c, args(), OFF, None, host) == 0
+    assert status_of(c, args(), np.array([1, 10, 14, 30]), None, host) == 3       # [0] != 0
+    assert status_of(c, args(), np.array([0, 10, 9, 30]), None, host) == 3        # decreasing
+    assert status_of(c, args(), np.array([0, 10, 14, 29]), None, host) == 3       # [B] != T
+    assert status_of(c, args(max_seqlen=15), OFF, None, host) == 3                # length > N
+    assert status_of(c, args(head_dim=48), OFF, None, host) == 4
+    assert status_of(c, args(dtype=7), OFF, None, host) == 4
+    assert status_of(c, args(max_seqlen=0), OFF, None, host) == 2
+    assert status_of(c, args(num_contexts=-1), OFF, None, host) == 2
+    assert status_of(c, args(num_heads=0), OFF, None, host) == 2
+    assert status_of(c, args(), OFF, np.array([1, -1, 0]), host) == 2             # targets < 0
+    assert status_of(c, args(qkv_token_stride=130), OFF, None, host) == 5         # not % 8
+    assert status_of(c, args(qkv_token_stride=64), OFF, None, host) == 2          # < H*d
+    a = args()
+    a.rab_ts = 0x1000  # a time table without timestamps
+    assert status_of(c, a, OFF, None, host) == 1
+    a = args()
+    a.alpha = float("nan")
+    assert status_of(c, a, OFF, None, host) == 2
+
+
+def test_calls_on_host_only_plan_and_mismatched_sizes():
+    plan = hj.hstu_plan_create(args(), OFF, None, hj.HSTU_PLAN_HOST_ONLY)
+    lib = _lib()
+    a = args()
+    P = ctypes.c_void_p
+    # a host-only plan cannot be launched
+    assert lib.hstu_attn_fwd(P(plan.handle), ctypes.byref(a), P(16), P(16), P(16), None, 0.0,
+                             P(16), None, 0, None) == 8
+    # sizes that differ from the plan's
+    b = args(num_heads=4)
+    assert lib.hstu_attn_fwd(P(plan.handle), ctypes.byref(b), P(16), P(16), P(16), None, 0.0,
+                             P(16), None, 0, None) == 2
+    assert lib.hstu_attn_bwd(None, ctypes.byref(a), *([P(16)] * 7), None, None, None, 0, None) == 1
+    assert lib.hstu_layer_fwd(P(plan.handle), ctypes.byref(b), 512, P(16), P(16), P(16), 1e-5,
+                              P(16), P(16), 1 << 30, None) == 2
+    assert hj.hstu_workspace_bytes(plan, hj.OP_FWD) == 0
+    assert hj.hstu_workspace_bytes(plan, hj.OP_FWD_GATED) == 30 * 2 * 64 * 2
+    plan.close()
+
+
+def _plan(batch, dtype="bf16"):
+    a = hj.make_args(dtype=hj.HSTU_BF16 if dtype == "bf16" else hj.HSTU_F32,
+                     batch=batch["batch"], num_heads=batch["heads"], head_dim=batch["d"],
+                     total_tokens=batch["total_tokens"], max_seqlen=batch["max_seqlen"],
+                     num_contexts=batch["num_contexts"], alpha=batch["alpha"])
+    return hj.hstu_plan_create(a, batch["seq_offsets"], batch["num_targets"],
+                               hj.HSTU_PLAN_HOST_ONLY)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_plan_covers_every_block_once_longest_first(dtype):
+    w = hs.make_workload("longtail_fwd")
+    plan = _plan(w, dtype)
+    info = hj.hstu_plan_info(plan)
+    H = w["heads"]
+    assert info["visible_pairs"] == H * oracle.count_pairs(w["seq_offsets"], w["num_contexts"],
+                                                           w["num_targets"])
+    rows = info["fwd_row_block"]
+    assert rows == (128 if dtype == "bf16" else 64)
+    for op, block in ((0, rows), (1, info["bwd_key_block"])):
+        u = hj.hstu_plan_units(plan, op)
+        assert np.all(np.diff(u[:, 3]) <= 0)                 # longest first
+        got = sorted(map(tuple, u[:, :3].tolist()))
+        want = sorted((b, h, r) for b, n in enumerate(w["lengths"]) for h in range(H)
+                      for r in range(0, int(n), block))
+        assert got == want
+    plan.close()
+
+
+def test_plan_of_empty_batch():
+    w = hs.make_inputs([0, 0, 0], 2, 32, dtype="fp32", rab=False, max_seqlen=4)
+    plan = _plan(w, "fp32")
+    info = hj.hstu_plan_info(plan)
+    assert info["fwd_units"] == 0 and info["bwd_units"] == 0 and info["visible_pairs"] == 0
+    plan.close()
+
+
+# ---- tile geometry against the oracle's mask ------------------------------------------------
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    d = tmp_path_factory.mktemp("shim")
+    so = str(d / "libgeom.so")
+    subprocess.check_call(["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-o", so,
+                           os.path.join(ROOT, "tests", "geometry_shim.cpp")])
+    return ctypes.CDLL(so)
+
+
+def _call3(fn, *a):
+    out = (ctypes.c_int * 3)()
+    fn(*a, out)
+    return list(out)
+
+
+def test_tile_geometry_matches_mask(shim):
+    rng = np.random.default_rng(0)
+    cases = [(n, c, t) for n in (1, 2, 31, 32, 33, 64, 65, 127, 128, 129, 200) for c in (0, 3, 70)
+             for t in (0, 1, 16, 64, 300)]
+    cases += [tuple(int(x) for x in (rng.integers(1, 400), rng.integers(0, 20), rng.integers(0, 80)))
+              for _ in range(40)]
+    for n, c, t in cases:
+        nc_, nh_ = ctypes.c_int(), ctypes.c_int()
+        shim.shim_split(n, c, t, ctypes.byref(nc_), ctypes.byref(nh_))
+        nc, nh = nc_.value, nh_.value
+        m = brute.role_mask(n, c, t, n)                      # oracle-side mask, (n, n)
+        assert nh == n - min(t, n - min(c, n))
+        ntile = (n + 63) // 64
+        # forward / dQ: 128-row units, 32-row wavefronts, 64-key tiles
+        for r0 in range(0, n, 128):
+            rhi = min(r0 + 128, n)
+            main, first, nd = _call3(shim.shim_key_tiles, r0, rhi, nc, nh)
+            listed = set(range(main)) | set(range(first, first + nd))
+            assert len(listed) == main + nd and max(listed) < ntile
+            for tile in range(ntile):
+                blk = m[r0:rhi, 64 * tile: 64 * tile + 64]
+                if tile not in listed:
+                    assert not blk.any(), (n, c, t, r0, tile)
+                for w0 in range(r0, rhi, 32):
+                    w1 = min(w0 + 32, rhi)
+                    sub = m[w0:w1, 64 * tile: 64 * tile + 64]
+                    kind = shim.shim_classify_row(w0, w1, 64 * tile, n, nc, nh)
+                    if kind == 0:
+                        assert not sub.any(), (n, c, t, w0, tile)
+                    if kind == 2:  # no mask needed: every real row sees all 64 keys
+                        assert sub.shape[1] == 64 and sub.all(), (n, c, t, w0, tile)
+                    if sub.any():
+                        assert tile in listed
+        # dK/dV: 128-key units, 32-key wavefronts, 64-query tiles
+        for k0 in range(0, n, 128):
+            khi = min(k0 + 128, n)
+            q = (ctypes.c_int * 2)()
+            shim.shim_rows_for_keys(k0, khi, n, nc, nh, q)
+            qlo, qhi = q[0], q[1]
+            rows_seen = np.nonzero(m[:, k0:khi].any(axis=1))[0]
+            assert rows_seen.min() >= qlo and rows_seen.max() < qhi
+            for i0 in range(0, n, 64):
+                for w0 in range(k0, khi, 32):
+                    w1 = min(w0 + 32, khi)
+                    sub = m[i0:i0 + 64, w0:w1]
+                    kind = shim.shim_classify_key(w0, w1, i0, n, nc, nh)
+                    if kind == 0:
+                        assert not sub.any(), (n, c, t, i0, w0)
+                    if kind == 2:
+                        assert sub.shape[0] == 64 and sub.all(), (n, c, t, i0, w0)

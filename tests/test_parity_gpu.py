@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded inputs.
+
+Tolerances: fp32 inputs, max |gpu - oracle| <= 1e-5; bf16 inputs, max |gpu - oracle| <=
+2e-2 * max |oracle| per output tensor.  Small cases are compared element by element; the
+full-size long-sequence workload is compared on sampled rows the oracle computes one by one.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import hstu_synth as hs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import hstu_jagged_pointwise_amd as hj  # noqa: E402
+from hstu_jagged_pointwise_amd import runner  # noqa: E402
+
+hj.load_library()  # fail loudly if the HIP library is missing
+
+BF16_REL = 2e-2
+F32_ABS = 1e-5
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, want, dtype):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), name
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    if dtype == "fp32":
+        assert err <= F32_ABS, f"{name}: max abs err {err:.3e} > {F32_ABS}"
+    else:
+        scale = float(np.max(np.abs(want))) if want.size else 0.0
+        assert err <= BF16_REL * scale + 1e-30, f"{name}: max err {err:.3e} vs {BF16_REL} * {scale:.3e}"
+    return err
+
+
+def run_fwd(w, **kw):
+    dev = runner.to_device(w)
+    out = runner.attn_fwd(w, dev, **kw)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+# ---- forward --------------------------------------------------------------------------------
+
+def test_tiny_fp32_workload():
+    w = hs.make_workload("tiny_fp32")
+    say("tiny_fp32 forward")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "fp32")
+
+
+EDGE_LENGTHS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 257, 0, 15, 2]
+MASKS = [(0, 0), (0, 16), (4, 16), (8, 64), (3, 300), (300, 0)]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("mask", range(len(MASKS)))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fwd_edges(d, mask, dtype):
+    nc, nt = MASKS[mask]
+    w = hs.make_inputs(EDGE_LENGTHS, 2, d, dtype=dtype, seed=100 + d + mask, rab=True,
+                       num_contexts=nc, num_targets=nt, max_seqlen=300)
+    say(f"fwd edges d={d} nc={nc} nt={nt} {dtype}")
+    check("O", run_fwd(w), oracle.attn_fwd(w), dtype)
+
+
+@pytest.mark.parametrize("which", ["none", "pos", "ts"])
+def test_fwd_bias_subsets(which):
+    w = hs.make_inputs([70, 5, 190], 3, 64, dtype="bf16", seed=7, rab=True, num_targets=8)
+    if which in ("none", "ts"):
+        w["rab_pos"] = None
+    if which in ("none", "pos"):
+        w["rab_ts"] = None
+    say(f"fwd bias subset {which}")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+
+
+def test_fwd_strided_inputs():
+    w = hs.make_inputs([50, 129, 3], 2, 64, dtype="bf16", seed=9, rab=True, num_contexts=2,
+                       num_targets=5)
+    dev = runner.to_device(w)
+    T, H, d = w["total_tokens"], 2, 64
+    big = torch.zeros((T, 3, H * d), dtype=torch.bfloat16, device="cuda:0")
+    for s, key in enumerate(("q", "k", "v")):
+        big[:, s] = dev[key].reshape(T, H * d)
+        dev[key] = big[:, s]
+    args = runner.args_for(w, dev, qkv_token_stride=3 * H * d)
+    say("fwd strided q/k/v")
+    out = runner.attn_fwd(w, dev, args=args)
+    torch.cuda.synchronize()
+    check("O", host(out), oracle.attn_fwd(w), "bf16")
+
+
+def test_fwd_wide_timestamps_take_64bit_path():
+    w = hs.make_inputs([100, 77, 300], 2, 128, dtype="bf16", seed=11, rab=True, num_targets=16)
+    ts = w["timestamps"].copy()
+    ts[100:177] = np.sort(np.random.default_rng(0).integers(-(1 << 40), 1 << 40, 77))
+    ts[200] += 3 << 31          # one token far in the future inside the third sequence
+    w["timestamps"] = ts
+    say("fwd wide timestamps")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+
+
+def test_fwd_empty_and_single():
+    w = hs.make_inputs([0, 1, 0, 0, 1], 2, 32, dtype="bf16", seed=3, rab=True, num_targets=1,
+                       max_seqlen=8)
+    say("fwd empty and single-token sequences")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+    w = hs.make_inputs([0, 0], 2, 32, dtype="bf16", seed=3, rab=True, max_seqlen=8)
+    say("fwd all-empty batch")
+    assert run_fwd(w).shape == (0, 2, 32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fwd_gated_by_u(dtype):
+    w = hs.make_inputs([40, 130, 7], 4, 32, dtype=dtype, seed=5, rab=True, num_contexts=1,
+                       num_targets=4)
+    u = np.random.default_rng(1).normal(size=(w["total_tokens"], 4 * 32)).astype(np.float32)
+    if dtype == "bf16":
+        u = hs.round_bf16(u)
+    dev = runner.to_device(w)
+    ut = torch.from_numpy(u).to("cuda:0", torch.bfloat16 if dtype == "bf16" else torch.float32)
+    say(f"fwd gated by u {dtype}")
+    out = runner.attn_fwd(w, dev, u=ut, ln_eps=1e-5)
+    torch.cuda.synchronize()
+    A = oracle.attn_fwd(w).reshape(w["total_tokens"], -1)
+    G = (A - A.mean(axis=1, keepdims=True)) / np.sqrt(A.var(axis=1, keepdims=True) + 1e-5) * u
+    check("LN(O)*u", host(out).reshape(G.shape), G, dtype)
+
+
+def test_ranking_workload_full():
+    w = hs.make_workload("ranking_fwd")
+    say("ranking_fwd full size")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+
+
+def test_longtail_workload_full():
+    w = hs.make_workload("longtail_fwd")
+    say("longtail_fwd full size")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+
+
+# ---- full layer -----------------------------------------------------------------------------
+
+def _layer_check(w):
+    dev = runner.to_device(w)
+    y = runner.layer_fwd(w, dev)
+    torch.cuda.synchronize()
+    yo, _ = oracle.layer_fwd(w)
+    got = host(y)
+    check("Y", got, yo, "bf16")
+    # The residual branch Y - X alone, so the attention path is not hidden behind X.  Y is stored
+    # in bf16, so each element also carries Y's own rounding, at most half a bf16 ulp <= 2^-8 |Y|.
+    branch = yo - w["x"]
+    err = np.abs(got - yo)
+    allowed = BF16_REL * np.max(np.abs(branch)) + 2.0 ** -8 * np.abs(yo)
+    worst = int(np.argmax(err - allowed))
+    assert np.all(err <= allowed), (f"Y - X: err {err.flat[worst]:.3e} > allowed "
+                                    f"{allowed.flat[worst]:.3e}")
+
+
+def test_layer_small():
+    w = hs.make_inputs([17, 130, 1, 64], 4, 128, dtype="bf16", seed=21, rab=True,
+                       num_contexts=4, num_targets=16, layer_dim=512)
+    say("layer small")
+    _layer_check(w)
+
+
+def test_layer_branch_dominant():
+    # W2 scaled up so that the attention / LayerNorm / gate branch dominates Y
+    w = hs.make_inputs([40, 200, 3], 4, 128, dtype="bf16", seed=22, rab=True,
+                       num_contexts=4, num_targets=16, layer_dim=512)
+    w["w2"] = hs.round_bf16(w["w2"] * 256.0)
+    say("layer with a dominant residual branch")
+    dev = runner.to_device(w)
+    y = runner.layer_fwd(w, dev)
+    torch.cuda.synchronize()
+    yo, _ = oracle.layer_fwd(w)
+    got = host(y)
+    assert np.max(np.abs(yo - w["x"])) > 4 * np.max(np.abs(w["x"]))
+    check("Y", got, yo, "bf16")
+
+
+def test_layer_workload_full():
+    w = hs.make_workload("layer_fwd")
+    say("layer_fwd full size")
+    _layer_check(w)
+
+
+# ---- backward -------------------------------------------------------------------------------
+
+def _bwd_check(w, dtype):
+    dev = runner.to_device(w)
+    g = runner.attn_bwd(w, dev)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(w)
+    for name in ("dq", "dk", "dv"):
+        check(name, host(g[name]), ref[name], dtype)
+    for name in ("drab_pos", "drab_ts"):
+        if ref[name] is not None:
+            # fp32 sums over many pairs: judge fp32 gradients relative to their scale as well
+            check(name, host(g[name]), ref[name], "bf16" if dtype == "bf16" else "fp32")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("mask", [0, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_edges(d, mask, dtype):
+    nc, nt = MASKS[mask]
+    w = hs.make_inputs(EDGE_LENGTHS, 2, d, dtype=dtype, seed=200 + d + mask, rab=True,
+                       num_contexts=nc, num_targets=nt, max_seqlen=300, backward=True)
+    say(f"bwd edges d={d} nc={nc} nt={nt} {dtype}")
+    _bwd_check(w, dtype)
+
+
+def test_bwd_no_bias_and_determinism():
+    w = hs.make_inputs([300, 64, 1], 2, 64, dtype="bf16", seed=4, rab=False, num_targets=7,
+                       backward=True)
+    dev = runner.to_device(w)
+    say("bwd without bias, twice")
+    g1 = runner.attn_bwd(w, dev)
+    g2 = runner.attn_bwd(w, dev)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv"):
+        assert torch.equal(g1[name], g2[name]), name
+    ref = oracle.attn_bwd(w)
+    for name in ("dq", "dk", "dv"):
+        check(name, host(g1[name]), ref[name], "bf16")
+
+
+def test_long_workload_reduced_full_compare():
+    w = hs.make_workload("long_fwdbwd", batch=3, len_cap=1100)
+    say("long_fwdbwd reduced: forward")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+    say("long_fwdbwd reduced: backward")
+    _bwd_check(w, "bf16")
+
+
+def test_long_workload_full_sampled():
+    w = hs.make_workload("long_fwdbwd")
+    dev = runner.to_device(w)
+    say("long_fwdbwd full size: forward + backward")
+    out = runner.attn_fwd(w, dev)
+    g = runner.attn_bwd(w, dev)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    T, H = w["total_tokens"], w["heads"]
+    off = w["seq_offsets"]
+    # rows from every sequence: first, last, candidates, contexts and random ones
+    toks = []
+    for b in range(w["batch"]):
+        s, e = int(off[b]), int(off[b + 1])
+        toks += [s, s + 3, e - 1, e - 40, e - 70] + list(rng.integers(s, e, 4))
+    toks = np.array(toks, np.int64)
+    heads = rng.integers(0, H, len(toks))
+    ref_o = oracle.attn_fwd_rows(w, toks, heads)
+    ref_g = oracle.attn_bwd_rows(w, toks, heads)
+    o = host(out)
+    # per-tensor scale from the sampled oracle rows
+    check("O rows", o[toks, heads], ref_o, "bf16")
+    for name in ("dq", "dk", "dv"):
+        check(f"{name} rows", host(g[name])[toks, heads], ref_g[name], "bf16")
+    # bias gradients: every bucket sum equals the total of dS, for both tables, per head
+    dp, dt = host(g["drab_pos"]), host(g["drab_ts"])
+    np.testing.assert_allclose(dp.sum(axis=1), dt.sum(axis=1),
+                               rtol=2e-2, atol=2e-2 * np.abs(dp).max())
