@@ -53,7 +53,7 @@ class HstuPlanInfo(ctypes.Structure):
 
 EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_info",
            "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_bwd",
-           "hstu_layer_fwd"]
+           "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd"]
 
 _lib = None
 
@@ -84,6 +84,10 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_attn_fwd.restype = I32
     lib.hstu_attn_bwd.argtypes = [P, argp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_bwd.restype = I32
+    lib.hstu_attn_bwd_dkdv.argtypes = [P, argp, P, P, P, P, P, P, P]
+    lib.hstu_attn_bwd_dkdv.restype = I32
+    lib.hstu_attn_bwd_dq.argtypes = [P, argp, P, P, P, P, P, P, P, P]
+    lib.hstu_attn_bwd_dq.restype = I32
     lib.hstu_layer_fwd.argtypes = [P, argp, I32, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
     lib.hstu_layer_fwd.restype = I32
     _lib = lib
@@ -213,6 +217,19 @@ def hstu_attn_bwd(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, dk, dv, dra
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drab_pos), _ptr(drab_ts), _ptr(ws), nbytes,
         _stream(stream)))
+
+
+def hstu_attn_bwd_dkdv(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dk, dv, stream=None) -> None:
+    _check(load_library().hstu_attn_bwd_dkdv(
+        ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+        _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def hstu_attn_bwd_dq(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, drab_pos=None,
+                     drab_ts=None, stream=None) -> None:
+    _check(load_library().hstu_attn_bwd_dq(
+        ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+        _ptr(dq), _ptr(drab_pos), _ptr(drab_ts), _stream(stream)))
 
 
 def hstu_layer_fwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, y,

@@ -304,14 +304,13 @@ __device__ __forceinline__ void run_add(float* hist, uint32_t& cur, float& sum, 
 }
 
 template <int D, bool RP, bool RT>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p,
-                                                             const WorkUnit* __restrict__ units) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p) {
     constexpr int RPt = SmemB<D>::RP, TP = SmemB<D>::TP;
     constexpr int KCH = D / 8;
     constexpr int ITEMS = (kTile / 4) * KCH;
     __shared__ __attribute__((aligned(16))) SmemB<D> sm;
 
-    const WorkUnit wu = units[blockIdx.x];
+    const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
@@ -538,10 +537,9 @@ __device__ __forceinline__ float bias_f32(const float* wp, const float* wt, bool
 }
 
 template <int D>
-__global__ __launch_bounds__(kF32) void bwd_dq_f32_kernel(const AttnParams p,
-                                                          const WorkUnit* __restrict__ units) {
+__global__ __launch_bounds__(kF32) void bwd_dq_f32_kernel(const AttnParams p) {
     __shared__ float wp[kNumBuckets], wt[kNumClasses], hp[kNumClasses], ht[kNumClasses];
-    const WorkUnit wu = units[blockIdx.x];
+    const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
     const int n = si.n, nc = si.nc, nh = si.nh, h = wu.head;
     const int64_t tok0 = si.start, ld = p.ld_in;
@@ -678,54 +676,65 @@ __global__ void zero_f32_kernel(float* p, int64_t n) {
 }
 
 template <int D, bool RP, bool RT>
-hipError_t launch_bwd_t(const AttnParams& p, const WorkUnit* units2, int32_t n2, hipStream_t s) {
-    if (p.num_units > 0)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (n2 > 0)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT>), dim3(n2), dim3(kThreads), 0, s, p, units2);
+hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_bwd_d(const AttnParams& p, const WorkUnit* u2, int32_t n2, hipStream_t s) {
-    const bool rp = p.rab_pos != nullptr, rt = p.rab_ts != nullptr;
-    if (rp && rt) return launch_bwd_t<D, true, true>(p, u2, n2, s);
-    if (rp) return launch_bwd_t<D, true, false>(p, u2, n2, s);
-    if (rt) return launch_bwd_t<D, false, true>(p, u2, n2, s);
-    return launch_bwd_t<D, false, false>(p, u2, n2, s);
+template <int D, bool RP, bool RT>
+hipError_t launch_dq_t(const AttnParams& p, hipStream_t s) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_bwd_f32_d(const AttnParams& p, const WorkUnit* u2, int32_t n2, hipStream_t s) {
-    if (p.num_units > 0)
-        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, dim3(p.num_units), dim3(kF32), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (n2 > 0) hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3(n2), dim3(kF32), 0, s, p, u2);
+template <int D, bool DQ>
+hipError_t launch_bwd_d(const AttnParams& p, hipStream_t s) {
+    const bool rp = p.rab_pos != nullptr, rt = p.rab_ts != nullptr;
+    if (rp && rt) return DQ ? launch_dq_t<D, true, true>(p, s) : launch_dkdv_t<D, true, true>(p, s);
+    if (rp) return DQ ? launch_dq_t<D, true, false>(p, s) : launch_dkdv_t<D, true, false>(p, s);
+    if (rt) return DQ ? launch_dq_t<D, false, true>(p, s) : launch_dkdv_t<D, false, true>(p, s);
+    return DQ ? launch_dq_t<D, false, false>(p, s) : launch_dkdv_t<D, false, false>(p, s);
+}
+
+template <bool DQ>
+hipError_t launch_bwd_bf16(const AttnParams& p, hipStream_t s) {
+    if (p.num_units == 0) return hipSuccess;
+    switch (p.head_dim) {
+        case 32: return launch_bwd_d<32, DQ>(p, s);
+        case 64: return launch_bwd_d<64, DQ>(p, s);
+        case 128: return launch_bwd_d<128, DQ>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool DQ>
+hipError_t launch_bwd_f32(const AttnParams& p, hipStream_t s) {
+    if (p.num_units == 0) return hipSuccess;
+    const dim3 grid(p.num_units), block(kF32);
+    switch (p.head_dim) {
+        case 32:
+            if (DQ) hipLaunchKernelGGL(bwd_dq_f32_kernel<32>, grid, block, 0, s, p);
+            else hipLaunchKernelGGL(bwd_dkdv_f32_kernel<32>, grid, block, 0, s, p);
+            break;
+        case 64:
+            if (DQ) hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, block, 0, s, p);
+            else hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, grid, block, 0, s, p);
+            break;
+        case 128:
+            if (DQ) hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, block, 0, s, p);
+            else hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, grid, block, 0, s, p);
+            break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd_bf16(const AttnParams& p, const WorkUnit* u2, int32_t n2, hipStream_t s) {
-    switch (p.head_dim) {
-        case 32: return launch_bwd_d<32>(p, u2, n2, s);
-        case 64: return launch_bwd_d<64>(p, u2, n2, s);
-        case 128: return launch_bwd_d<128>(p, u2, n2, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_attn_bwd_f32(const AttnParams& p, const WorkUnit* u2, int32_t n2, hipStream_t s) {
-    switch (p.head_dim) {
-        case 32: return launch_bwd_f32_d<32>(p, u2, n2, s);
-        case 64: return launch_bwd_f32_d<64>(p, u2, n2, s);
-        case 128: return launch_bwd_f32_d<128>(p, u2, n2, s);
-    }
-    return hipErrorInvalidValue;
-}
+hipError_t launch_attn_bwd_dkdv_bf16(const AttnParams& p, hipStream_t s) { return launch_bwd_bf16<false>(p, s); }
+hipError_t launch_attn_bwd_dq_bf16(const AttnParams& p, hipStream_t s) { return launch_bwd_bf16<true>(p, s); }
+hipError_t launch_attn_bwd_dkdv_f32(const AttnParams& p, hipStream_t s) { return launch_bwd_f32<false>(p, s); }
+hipError_t launch_attn_bwd_dq_f32(const AttnParams& p, hipStream_t s) { return launch_bwd_f32<true>(p, s); }
 
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 #include <vector>
 
@@ -50,7 +51,7 @@ hstu_status_t check_args(const hstu_attn_args_t* a) {
     int64_t hd = int64_t(a->num_heads) * a->head_dim;
     if (a->qkv_token_stride != 0 && a->qkv_token_stride < hd) return HSTU_ERR_BAD_SHAPE;
     if (a->qkv_token_stride % 8 != 0) return HSTU_ERR_MISALIGNED;
-    if (a->rab_ts && !a->timestamps) return HSTU_ERR_NULL_ARG;
+    if (a->rab_ts && !a->timestamps && a->total_tokens > 0) return HSTU_ERR_NULL_ARG;
     return HSTU_OK;
 }
 
@@ -297,44 +298,87 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
     return hip_status(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and parameters shared by the backward entry points.  Pointers that a pass does not
+// use are passed as NULL and not checked.
+hstu_status_t bwd_params(const hstu_plan_t* plan, const hstu_attn_args_t* args, const void* q,
+                         const void* k, const void* v, const void* dout,
+                         std::initializer_list<const void*> outs, hstu::AttnParams* p) {
+    hstu_status_t st = check_call(plan, args);
+    if (st != HSTU_OK) return st;
+    if (args->total_tokens != 0) {
+        if (!q || !k || !v || !dout) return HSTU_ERR_NULL_ARG;
+        for (const void* o : outs)
+            if (!o) return HSTU_ERR_NULL_ARG;
+    }
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout)) return HSTU_ERR_MISALIGNED;
+    for (const void* o : outs)
+        if (!aligned16(o)) return HSTU_ERR_MISALIGNED;
+    *p = base_params(plan, args);
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->dout = dout;
+    return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                                 const void* q, const void* k, const void* v, const void* dout,
+                                 void* dk, void* dv, void* stream) {
+    hstu::AttnParams p;
+    hstu_status_t st = bwd_params(plan, args, q, k, v, dout, {dk, dv}, &p);
+    if (st != HSTU_OK) return st;
+    if (args->total_tokens == 0) return HSTU_OK;
+    p.units = plan->d_bwd;
+    p.num_units = (int32_t)plan->bwd.size();
+    p.dk = dk;
+    p.dv = dv;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(args->dtype == HSTU_BF16 ? hstu::launch_attn_bwd_dkdv_bf16(p, s)
+                                               : hstu::launch_attn_bwd_dkdv_f32(p, s));
+}
+
+hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                               const void* q, const void* k, const void* v, const void* dout,
+                               void* dq, float* drab_pos, float* drab_ts, void* stream) {
+    hstu::AttnParams p;
+    hstu_status_t st = bwd_params(plan, args, q, k, v, dout, {dq}, &p);
+    if (st != HSTU_OK) return st;
+    if ((drab_pos && !aligned16(drab_pos)) || (drab_ts && !aligned16(drab_ts)))
+        return HSTU_ERR_MISALIGNED;
+    p.dq = dq;
+    p.drab_pos = args->rab_pos ? drab_pos : nullptr;
+    p.drab_ts = args->rab_ts ? drab_ts : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
+    hipError_t e = hipSuccess;
+    if (p.drab_pos) e = hstu::launch_zero_f32(p.drab_pos, nb, s);
+    if (e == hipSuccess && p.drab_ts) e = hstu::launch_zero_f32(p.drab_ts, nb, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    if (args->total_tokens == 0) return HSTU_OK;
+    return hip_status(args->dtype == HSTU_BF16 ? hstu::launch_attn_bwd_dq_bf16(p, s)
+                                               : hstu::launch_attn_bwd_dq_f32(p, s));
+}
+
 hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args, const void* q,
                             const void* k, const void* v, const void* dout, void* dq, void* dk,
                             void* dv, float* drab_pos, float* drab_ts, void* ws, size_t ws_bytes,
                             void* stream) {
     (void)ws;
     (void)ws_bytes;
-    hstu_status_t st = check_call(plan, args);
+    hstu::AttnParams p;
+    hstu_status_t st = bwd_params(plan, args, q, k, v, dout, {dq, dk, dv}, &p);
     if (st != HSTU_OK) return st;
-    if (!q || !k || !v || !dout || !dq || !dk || !dv) {
-        if (args->total_tokens != 0) return HSTU_ERR_NULL_ARG;
-    }
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
-        !aligned16(dk) || !aligned16(dv) || (drab_pos && !aligned16(drab_pos)) ||
-        (drab_ts && !aligned16(drab_ts)))
-        return HSTU_ERR_MISALIGNED;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hstu::AttnParams p = base_params(plan, args);
-    p.units = plan->d_bwd;
-    p.num_units = (int32_t)plan->bwd.size();
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.dout = dout;
-    p.dq = dq;
-    p.dk = dk;
-    p.dv = dv;
-    p.drab_pos = args->rab_pos ? drab_pos : nullptr;
-    p.drab_ts = args->rab_ts ? drab_ts : nullptr;
-    const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
-    hipError_t e = hipSuccess;
-    if (p.drab_pos) e = hstu::launch_zero_f32(p.drab_pos, nb, s);
-    if (e == hipSuccess && p.drab_ts) e = hstu::launch_zero_f32(p.drab_ts, nb, s);
-    if (e != hipSuccess) return HSTU_ERR_HIP;
-    if (plan->fwd.empty()) return HSTU_OK;
-    e = args->dtype == HSTU_BF16
-            ? hstu::launch_attn_bwd_bf16(p, plan->d_fwd, (int32_t)plan->fwd.size(), s)
-            : hstu::launch_attn_bwd_f32(p, plan->d_fwd, (int32_t)plan->fwd.size(), s);
-    return hip_status(e);
+    st = hstu_attn_bwd_dkdv(plan, args, q, k, v, dout, dk, dv, stream);
+    if (st != HSTU_OK) return st;
+    return hstu_attn_bwd_dq(plan, args, q, k, v, dout, dq, drab_pos, drab_ts, stream);
 }
 
 hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,

@@ -35,11 +35,12 @@ struct AttnParams {
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnParams& p, hipStream_t s);
-// dK/dV uses `units` = key-block units; dQ uses `units2` = row-block units.
-hipError_t launch_attn_bwd_bf16(const AttnParams& p, const WorkUnit* units2, int32_t num_units2,
-                                hipStream_t s);
-hipError_t launch_attn_bwd_f32(const AttnParams& p, const WorkUnit* units2, int32_t num_units2,
-                               hipStream_t s);
+// Backward passes: dK/dV over `units` = key-block units; dQ (and bias gradients, which the
+// caller has zeroed) over `units` = row-block units.
+hipError_t launch_attn_bwd_dkdv_bf16(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_bwd_dq_bf16(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_bwd_dkdv_f32(const AttnParams& p, hipStream_t s);
+hipError_t launch_attn_bwd_dq_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 
 // LayerNorm over `width` features of each row of a (bf16), times gate u (token stride ldu),

@@ -140,6 +140,16 @@ hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
                             void* dq, void* dk, void* dv, float* drab_pos, float* drab_ts,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of hstu_attn_bwd, for callers that run them on different streams (they only
+ * read the inputs, so they may overlap).  _dkdv writes dk and dv; _dq writes dq and the bias
+ * gradients exactly as hstu_attn_bwd does. */
+hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                                 const void* q, const void* k, const void* v, const void* dout,
+                                 void* dk, void* dv, void* stream);
+hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                               const void* q, const void* k, const void* v, const void* dout,
+                               void* dq, float* drab_pos, float* drab_ts, void* stream);
+
 /* Full HSTU layer forward, bf16 only.  x: (T, d_model) dense; w1: (d_model, 4*H*d) row-major;
  * w2: (H*d, d_model) row-major; y: (T, d_model).  args->qkv_token_stride is ignored (Q, K, V, U
  * are produced internally).  ws must hold hstu_workspace_bytes(plan, 3, d_model). */
