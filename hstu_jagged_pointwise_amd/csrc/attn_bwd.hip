@@ -14,10 +14,13 @@
 //     of the first two products) and transposed with renumbered rows (A operands of the last two).
 //   pass B (query-stationary): unit = (sequence, head, 128 rows) exactly like the forward;
 //     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T, and the bias-table gradients.
-// Bias-gradient sums: along a lane (one query row, keys increasing) the bucket of |i - j| and of
-// |t_i - t_j| changes rarely, so each lane keeps a running (class, sum) pair and adds it to a
-// per-unit LDS histogram only when the class changes; the histogram is flushed to the global
-// table with one atomic add per non-zero class at the end of the unit.
+// Bias-gradient sums: when all pairs of a (wavefront, tile) fall into one bucket -- the common
+// case away from the diagonal -- each lane only adds its dS values to a running sum, and the
+// wavefront flushes that sum into an LDS histogram when the tile bucket changes; other tiles add
+// each dS to an LDS histogram indexed by bucket class.  At the end of the unit each non-zero
+// histogram entry goes to the global table with one atomic add.
+// Scores are carried as -log2(e) S (folded into alpha and the staged bias tables), as in the
+// forward, so sigmoid costs one exp2 and one rcp.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -28,11 +31,10 @@ constexpr int kThreads = 256;
 constexpr int kBlk = 4 * kWaveRows;      // 128 keys (pass A) or rows (pass B) per unit
 constexpr int kTile = 64;                // queries (pass A) or keys (pass B) per tile
 constexpr int kToep = kBlk + kTile - 1;  // 191 distinct i - j per (unit, tile)
-constexpr int kHist = kNumClasses + 1;   // + one slot that absorbs the initial empty run
 
 struct ToepEntry {
-    float bias;
-    uint32_t cls;
+    float bias;     // -log2(e) * position bias
+    float bucket;   // bucket of |i - j|, as a float
 };
 
 __device__ __forceinline__ void tile_store_rowmajor_and_t(bf16* rowm, int rp_pitch, bf16* trans,
@@ -50,6 +52,25 @@ __device__ __forceinline__ void tile_store_rowmajor_and_t(bf16* rowm, int rp_pit
     }
 }
 
+// sigmoid(S) and dL/dS * N from t = -log2(e) S and dP:  P' = t s gives SiLU(S) = -ln(2) P', and
+// dS N = dP (s + x s (1 - s)) with x s = -ln(2) P'.
+struct Grad {
+    float p, ds;
+};
+__device__ __forceinline__ Grad silu_grad(float t, float dp) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+    const float pv = t * sg;
+    const float xs = -kLn2 * pv;
+    return Grad{pv, dp * (fmaf(-xs, sg, xs) + sg)};
+}
+
+// Sum over the wavefront, result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
 // ---------------------------------------------------------------------------------------------
 // pass A: dK, dV
 // ---------------------------------------------------------------------------------------------
@@ -58,17 +79,76 @@ template <int D>
 struct SmemA {
     static constexpr int RP = D + 8;     // row-major pitch
     static constexpr int TP = kTile + 8; // transposed pitch
+    float wt[kNumClasses];               // -log2(e) * time bias by class
+    float wp[kNumBuckets];               // -log2(e) * position bias by bucket
+    float wtb[kNumBuckets];              // -log2(e) * time bias by bucket
+    float rp[2][kToep + 1];
+    uint32_t tq[2][kTile];
+    int64_t tq64[2][kTile];
+    int64_t tqmin[2], tqmax[2];
+    int fits[2];
     bf16 q[2][kTile * RP];
     bf16 dout[2][kTile * RP];
     bf16 qt[2][D * TP];
     bf16 doutt[2][D * TP];
-    float rp[2][kToep + 1];
-    uint32_t tq[2][kTile];
-    int64_t tq64[2][kTile];
-    int fits[2];
-    float wt[kNumClasses];
-    float wp[kNumBuckets];
 };
+
+// Bias modes of a (wavefront, tile) as in the forward:
+//   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
+//   TM 0: time bias absent or one bucket; 1: two buckets, b1 where |dt| >= thr; 2 / 3: per-element
+//      bucket class with 32-bit / 64-bit times.
+template <int D, int PM, int TM>
+__device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemA<D>& sm,
+                                           int buf, int u0, int g, float alpha2, float b0,
+                                           float b1, uint32_t thr, uint32_t tj, int64_t tj64) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ii = 32 * qb + 8 * r + 4 * g;
+            u32x4 tq4;
+            if (TM == 1 || TM == 2) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int e = 4 * r + c;
+                float b = b0;
+                if (TM == 1) b = absdiff_u32(tj, tq4[c]) >= thr ? b1 : b0;
+                if (PM == 1) b += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
+                if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
+                if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
+                const Grad gr = silu_grad(fmaf(alpha2, s[qb][e], b), dp[qb][e]);
+                s[qb][e] = gr.p;
+                dp[qb][e] = gr.ds;
+            }
+        }
+}
+
+template <int D, int PM>
+__device__ __forceinline__ void epilogue_a_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
+                                              const SmemA<D>& sm, int buf, int u0, int g,
+                                              float alpha2, float b0, float b1, uint32_t thr,
+                                              uint32_t tj, int64_t tj64) {
+    switch (tm) {
+        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
+        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
+        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
+        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
+    }
+}
+
+// Zero P and dS of queries that do not see this lane's key (partial tiles only).
+__device__ __forceinline__ void mask_queries(f32x16 (&s)[2], f32x16 (&dp)[2], int g, int i0, int lo,
+                                             int hi) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int i = i0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
+            const bool vis = i >= lo && i <= hi;
+            s[qb][e] = vis ? s[qb][e] : 0.0f;
+            dp[qb][e] = vis ? dp[qb][e] : 0.0f;
+        }
+}
 
 template <int D, bool RP, bool RT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams p) {
@@ -88,10 +168,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
     const bf16* __restrict__ dog = static_cast<const bf16*>(p.dout) + tok0 * p.ld_out + h * D;
 
     if (RP)
-        for (int e = tid; e < kNumBuckets; e += kThreads) sm.wp[e] = p.rab_pos[h * kNumBuckets + e];
-    if (RT)
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wp[e] = -kLog2e * p.rab_pos[h * kNumBuckets + e];
+    if (RT) {
         for (int e = tid; e < kNumClasses; e += kThreads)
-            sm.wt[e] = p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+            sm.wt[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
+    }
     const int64_t tbase = RT ? p.ts[tok0] : 0;
 
     const int khi = imin(k0 + kBlk, n);
@@ -115,12 +199,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
         vf[ks] = key_ok ? load_bf16x8(vg + (int64_t)j * ld + 16 * ks + 8 * g) : bf16x8{};
     }
     uint32_t tj = 0;
-    int64_t tj64 = 0;
+    int64_t tj64 = 0, tjmin = 0, tjmax = 0;
     bool wave_kfit = true;
     if (RT) {
         tj64 = key_ok ? p.ts[tok0 + j] : tbase;
         wave_kfit = __all(rel_time_fits(tj64, tbase));
         tj = rel_time_u32(tj64, tbase);
+        tjmin = wave_min64(key_ok ? tj64 : INT64_MAX);
+        tjmax = wave_max64(key_ok ? tj64 : INT64_MIN);
     }
 
     f32x16 dvt[D / 32], dkt[D / 32];
@@ -152,11 +238,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
             tile_store_rowmajor_and_t(sm.q[buf], RPt, sm.qt[buf], TP, qr, grp, ch);
             tile_store_rowmajor_and_t(sm.dout[buf], RPt, sm.doutt[buf], TP, dr, grp, ch);
         }
-        if (RT && tid < kTile) {
+        if (RT && tid < kTile) {  // exactly wavefront 0
+            const bool real = i0 + tid < n;
             sm.tq64[buf][tid] = tqr;
             sm.tq[buf][tid] = rel_time_u32(tqr, tbase);
             const bool all_fit = __all(rel_time_fits(tqr, tbase));
-            if (tid == 0) sm.fits[buf] = all_fit ? 1 : 0;
+            const int64_t mn = wave_min64(real ? tqr : INT64_MAX);
+            const int64_t mx = wave_max64(real ? tqr : INT64_MIN);
+            if (tid == 0) {
+                sm.fits[buf] = all_fit ? 1 : 0;
+                sm.tqmin[buf] = mn;
+                sm.tqmax[buf] = mx;
+            }
         }
         if (RP)
             for (int u = tid; u < kToep; u += kThreads) {
@@ -173,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
 
     // slot of (query i0 + ii, key j) is u0 + ii - 4g with u0 below
     const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1);
-    const float alpha = p.alpha;
+    const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, i0 = (tfirst + t) * kTile;
@@ -193,39 +286,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                     dp[qb] = mfma32(ad, vf[ks], dp[qb]);
                 }
             }
-            const bool fit = !RT || (wave_kfit && sm.fits[buf]);
-            const bool masked = kind == kPartial;
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ii = 32 * qb + 8 * r + 4 * g;
-                    u32x4 tq4;
-                    if (RT) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int e = 4 * r + c;
-                        float bias = 0.0f;
-                        if (RP) bias += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
-                        if (RT) {
-                            uint32_t dt = fit ? absdiff_u32(tj, tq4[c])
-                                              : absdiff_sat(tj64, sm.tq64[buf][ii + c]);
-                            bias += sm.wt[bucket_class(dt)];
-                        }
-                        const float x = fmaf(alpha, s[qb][e], bias);
-                        const float sg = fast_sigmoid(x);
-                        float pv = x * sg;
-                        float dsv = dp[qb][e] * sg * fmaf(x, 1.0f - sg, 1.0f);
-                        if (masked) {
-                            const int i = i0 + ii + c;
-                            const bool vis = i >= lo && i <= hi;
-                            pv = vis ? pv : 0.0f;
-                            dsv = vis ? dsv : 0.0f;
-                        }
-                        s[qb][e] = pv;
-                        dp[qb][e] = dsv;
-                    }
-                }
+            float b0 = 0.0f, b1 = 0.0f;
+            uint32_t thr = 0;
+            int pm = 0, tm = 0;
+            const int ihi = imin(i0 + kTile, n) - 1;
+            if (RP) {
+                const BiasSpan sp = bias_span((int64_t)i0 - (wk1 - 1), (int64_t)ihi - wk0);
+                if (sp.kind == 0) b0 = sm.wp[sp.b_lo];
+                else pm = 1;
+            }
+            b1 = b0;
+            if (RT) {
+                const BiasSpan st = bias_span(sm.tqmin[buf] - tjmax, sm.tqmax[buf] - tjmin);
+                const bool fit = wave_kfit && sm.fits[buf];
+                if (st.kind == 0) { b0 += sm.wtb[st.b_lo]; b1 = b0; }
+                else if (st.kind == 1 && fit) {
+                    tm = 1;
+                    thr = st.thr;
+                    b1 = b0 + sm.wtb[st.b_hi];
+                    b0 += sm.wtb[st.b_lo];
+                } else tm = fit ? 2 : 3;
+            }
+            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64);
+            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64);
+            if (kind == kPartial) mask_queries(s, dp, g, i0, lo, hi);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 float tp[8], td[8];
@@ -253,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
     if (key_ok) {
         bf16* dvg = static_cast<bf16*>(p.dv) + (tok0 + j) * p.ld_out + h * D;
         bf16* dkg = static_cast<bf16*>(p.dk) + (tok0 + j) * p.ld_out + h * D;
-        const float sk = alpha * p.inv_n;
+        const float sv = -kLn2 * p.inv_n, sk = p.alpha * p.inv_n;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -261,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                 bf16x4 wv, wk;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    wv[c] = (bf16)(dvt[db][4 * r + c] * p.inv_n);
+                    wv[c] = (bf16)(dvt[db][4 * r + c] * sv);
                     wk[c] = (bf16)(dkt[db][4 * r + c] * sk);
                 }
                 *reinterpret_cast<bf16x4*>(dvg + 32 * db + 8 * r + 4 * g) = wv;
@@ -278,32 +362,136 @@ template <int D>
 struct SmemB {
     static constexpr int RP = D + 8;
     static constexpr int TP = kTile + 8;
-    bf16 k[2][kTile * RP];
-    bf16 v[2][kTile * RP];
-    bf16 kt[2][D * TP];
+    float wt[kNumClasses];
+    float wp[kNumBuckets];
+    float wtb[kNumBuckets];
     ToepEntry rp[2][kToep + 1];
     uint32_t tk[2][kTile];
     int64_t tk64[2][kTile];
+    int64_t tkmin[2], tkmax[2];
     int fits[2];
-    float wt[kNumClasses];
-    float wp[kNumBuckets];
-    float hp[kHist];
-    float ht[kHist];
+    float hct[kNumClasses];   // time-bias gradient sums of tiles spanning many buckets, by class
+    float hbp[kNumBuckets];   // position-bias gradient sums, by bucket
+    float hbt[kNumBuckets];   // time-bias gradient sums of one- or two-bucket tiles, by bucket
+    bf16 k[2][kTile * RP];
+    bf16 v[2][kTile * RP];
+    bf16 kt[2][D * TP];
 };
 
-// Adds v to the lane's running (class, sum); on a class change the finished run goes to hist.
-__device__ __forceinline__ void run_add(float* hist, uint32_t& cur, float& sum, uint32_t cls,
-                                        float v) {
-    if (cls != cur) {
-        atomicAdd(&hist[cur], sum);
-        cur = cls;
-        sum = v;
-    } else {
-        sum += v;
+// Per-element part of pass B: dS (times N) into dp.  Bias modes as in pass A.
+template <int D, int PM, int TM>
+__device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemB<D>& sm,
+                                           int buf, int u0, int g, float alpha2, float b0,
+                                           float b1, uint32_t thr, uint32_t ti, int64_t ti64) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = 32 * kb + 8 * r + 4 * g;
+            u32x4 tk4;
+            if (TM == 1 || TM == 2) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int e = 4 * r + c;
+                float b = b0;
+                if (TM == 1) b = absdiff_u32(ti, tk4[c]) >= thr ? b1 : b0;
+                if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c].bias;
+                if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tk4[c]))];
+                if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
+                dp[kb][e] = silu_grad(fmaf(alpha2, s[kb][e], b), dp[kb][e]).ds;
+            }
+        }
+}
+
+template <int D, int PM>
+__device__ __forceinline__ void epilogue_b_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
+                                              const SmemB<D>& sm, int buf, int u0, int g,
+                                              float alpha2, float b0, float b1, uint32_t thr,
+                                              uint32_t ti, int64_t ti64) {
+    switch (tm) {
+        case 0: epilogue_b<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        case 1: epilogue_b<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        case 2: epilogue_b<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        default: epilogue_b<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
     }
 }
 
-template <int D, bool RP, bool RT>
+// Bias-gradient sums of one (wavefront, tile), per lane:
+//   sum = sum of dS (serves every term whose tile lies in one bucket),
+//   mp  = sum of dS * bucket(|i - j|) (PG 1, two position buckets: the upper bucket's share is
+//         mp - b_lo * sum),
+//   th  = sum of dS over pairs with |dt| >= thr (TM 1, two time buckets),
+// plus per-element LDS histogram updates for tiles spanning more buckets (PG 2; TM 2, 3).
+struct TileSums {
+    float sum, mp, th;
+};
+template <int D, int PG, int TM, bool GP, bool GT>
+__device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& sm, int buf, int u0,
+                                              int g, uint32_t thr, uint32_t ti, int64_t ti64) {
+    TileSums ts{0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jj = 32 * kb + 8 * r + 4 * g;
+            u32x4 tk4;
+            if (GT && (TM == 1 || TM == 2)) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float ds = dp[kb][4 * r + c];
+                const int u = u0 + 32 * kb + 8 * r + c;
+                ts.sum += ds;
+                if (GP && PG == 1) ts.mp = fmaf(ds, sm.rp[buf][u].bucket, ts.mp);
+                if (GP && PG == 2) atomicAdd(&sm.hbp[(int)sm.rp[buf][u].bucket], ds);
+                if (GT && TM == 1) ts.th += absdiff_u32(ti, tk4[c]) >= thr ? ds : 0.0f;
+                if (GT && TM == 2) atomicAdd(&sm.hct[bucket_class(absdiff_u32(ti, tk4[c]))], ds);
+                if (GT && TM == 3)
+                    atomicAdd(&sm.hct[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))], ds);
+            }
+        }
+    return ts;
+}
+
+template <int D, int PG, bool GP, bool GT>
+__device__ __forceinline__ TileSums grad_sums_tm(int tm, const f32x16 (&dp)[2], SmemB<D>& sm,
+                                                 int buf, int u0, int g, uint32_t thr, uint32_t ti,
+                                                 int64_t ti64) {
+    switch (GT ? tm : 0) {
+        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
+        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
+        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
+        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
+    }
+}
+
+// Zero dS of keys this lane's row does not see (partial tiles only).
+__device__ __forceinline__ void mask_keys_b(f32x16 (&dp)[2], int g, int j0, int lim, int dg) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+            dp[kb][e] = (j <= lim || j == dg) ? dp[kb][e] : 0.0f;
+        }
+}
+
+// A per-lane running sum for one histogram bucket (the same bucket across the wavefront); a
+// change of bucket flushes the wavefront's total with one LDS atomic.
+struct Run {
+    int cur = -1;
+    float acc = 0.0f;
+    __device__ __forceinline__ void add(float* hist, int bucket, float v, int lane) {
+        if (bucket != cur) {
+            const float tot = wave_sum(acc);
+            if (cur >= 0 && lane == 0) atomicAdd(&hist[cur], tot);
+            cur = bucket;
+            acc = 0.0f;
+        }
+        acc += v;
+    }
+};
+
+template <int D, bool RP, bool RT, bool GP, bool GT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p) {
     constexpr int RPt = SmemB<D>::RP, TP = SmemB<D>::TP;
     constexpr int KCH = D / 8;
@@ -319,14 +507,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
     const bf16* __restrict__ kg = static_cast<const bf16*>(p.k) + tok0 * ld + h * D;
     const bf16* __restrict__ vg = static_cast<const bf16*>(p.v) + tok0 * ld + h * D;
     const bf16* __restrict__ dog = static_cast<const bf16*>(p.dout) + tok0 * p.ld_out + h * D;
-    const bool grad_p = RP && p.drab_pos != nullptr, grad_t = RT && p.drab_ts != nullptr;
 
     if (RP)
-        for (int e = tid; e < kNumBuckets; e += kThreads) sm.wp[e] = p.rab_pos[h * kNumBuckets + e];
-    if (RT)
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wp[e] = -kLog2e * p.rab_pos[h * kNumBuckets + e];
+    if (RT) {
         for (int e = tid; e < kNumClasses; e += kThreads)
-            sm.wt[e] = p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
-    for (int e = tid; e < kHist; e += kThreads) { sm.hp[e] = 0.0f; sm.ht[e] = 0.0f; }
+            sm.wt[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
+    }
+    for (int e = tid; e < kNumClasses; e += kThreads) sm.hct[e] = 0.0f;
+    for (int e = tid; e < kNumBuckets; e += kThreads) { sm.hbp[e] = 0.0f; sm.hbt[e] = 0.0f; }
     const int64_t tbase = RT ? p.ts[tok0] : 0;
 
     const int rhi = imin(r0 + kBlk, n);
@@ -347,18 +539,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
         dof[ks] = row_ok ? load_bf16x8(dog + (int64_t)i * p.ld_out + 16 * ks + 8 * g) : bf16x8{};
     }
     uint32_t ti = 0;
-    int64_t ti64 = 0;
+    int64_t ti64 = 0, timin = 0, timax = 0;
     bool wave_qfit = true;
     if (RT) {
         ti64 = row_ok ? p.ts[tok0 + i] : tbase;
         wave_qfit = __all(rel_time_fits(ti64, tbase));
         ti = rel_time_u32(ti64, tbase);
+        timin = wave_min64(row_ok ? ti64 : INT64_MAX);
+        timax = wave_max64(row_ok ? ti64 : INT64_MIN);
     }
     f32x16 dqt[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
-    uint32_t cur_p = kNumClasses, cur_t = kNumClasses;
-    float sum_p = 0.0f, sum_t = 0.0f;
+    Run run_p_lo, run_p_hi, run_t_lo, run_t_hi;  // bias-gradient running sums
 
     bf16x8 kr[4], vr[4];
     int64_t tkr = 0;
@@ -387,17 +580,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
             for (int kk = 0; kk < 4; ++kk)
                 *reinterpret_cast<bf16x8*>(&sm.v[buf][(4 * grp + kk) * RPt + 8 * ch]) = vr[kk];
         }
-        if (RT && tid < kTile) {
+        if (RT && tid < kTile) {  // exactly wavefront 0
+            const bool real = j0 + tid < n;
             sm.tk64[buf][tid] = tkr;
             sm.tk[buf][tid] = rel_time_u32(tkr, tbase);
             const bool all_fit = __all(rel_time_fits(tkr, tbase));
-            if (tid == 0) sm.fits[buf] = all_fit ? 1 : 0;
+            const int64_t mn = wave_min64(real ? tkr : INT64_MAX);
+            const int64_t mx = wave_max64(real ? tkr : INT64_MIN);
+            if (tid == 0) {
+                sm.fits[buf] = all_fit ? 1 : 0;
+                sm.tkmin[buf] = mn;
+                sm.tkmax[buf] = mx;
+            }
         }
         if (RP)
             for (int u = tid; u < kToep; u += kThreads) {
                 const int delta = (r0 - j0) + (kBlk - 1) - u;
                 const uint32_t ad = (uint32_t)(delta < 0 ? -delta : delta);
-                sm.rp[buf][u] = ToepEntry{sm.wp[bucket_of(ad)], bucket_class(ad)};
+                const int bk = bucket_of(ad);
+                sm.rp[buf][u] = ToepEntry{sm.wp[bk], (float)bk};
             }
     };
 
@@ -408,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
     __syncthreads();
 
     const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1);
-    const float alpha = p.alpha;
+    const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, j0 = ktl.tile(t) * kTile;
@@ -428,45 +629,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
                     dp[kb] = mfma32(av, dof[ks], dp[kb]);
                 }
             }
-            const bool fit = !RT || (wave_qfit && sm.fits[buf]);
-            const bool masked = kind == kPartial;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int jj = 32 * kb + 8 * r + 4 * g;
-                    u32x4 tk4;
-                    if (RT) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int e = 4 * r + c;
-                        float bias = 0.0f;
-                        uint32_t cls_p = 0, cls_t = 0;
-                        if (RP) {
-                            const ToepEntry te = sm.rp[buf][u0 + 32 * kb + 8 * r + c];
-                            bias += te.bias;
-                            cls_p = te.cls;
-                        }
-                        if (RT) {
-                            uint32_t dt = fit ? absdiff_u32(ti, tk4[c])
-                                              : absdiff_sat(ti64, sm.tk64[buf][jj + c]);
-                            cls_t = bucket_class(dt);
-                            bias += sm.wt[cls_t];
-                        }
-                        const float x = fmaf(alpha, s[kb][e], bias);
-                        const float sg = fast_sigmoid(x);
-                        float dsv = dp[kb][e] * sg * fmaf(x, 1.0f - sg, 1.0f);
-                        bool vis = true;
-                        if (masked) {
-                            const int jk = j0 + jj + c;
-                            vis = jk <= lim || jk == dg;
-                            dsv = vis ? dsv : 0.0f;
-                        }
-                        dp[kb][e] = dsv;
-                        if (grad_p) run_add(sm.hp, cur_p, sum_p, vis ? cls_p : cur_p, dsv);
-                        if (grad_t) run_add(sm.ht, cur_t, sum_t, vis ? cls_t : cur_t, dsv);
-                    }
+            float b0 = 0.0f, b1 = 0.0f;
+            uint32_t thr = 0;
+            int pm = 0, tm = 0;
+            BiasSpan sp{0, 0, 0, 0}, st{0, 0, 0, 0};
+            if (RP) {
+                const int jhi = imin(j0 + kTile, n) - 1;
+                sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - j0);
+                if (sp.kind == 0) b0 = sm.wp[sp.b_lo];
+                else pm = 1;
+            }
+            b1 = b0;
+            if (RT) {
+                st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
+                const bool fit = wave_qfit && sm.fits[buf];
+                if (st.kind == 0) { b0 += sm.wtb[st.b_lo]; b1 = b0; }
+                else if (st.kind == 1 && fit) {
+                    tm = 1;
+                    thr = st.thr;
+                    b1 = b0 + sm.wtb[st.b_hi];
+                    b0 += sm.wtb[st.b_lo];
+                } else tm = fit ? 2 : 3;
+            }
+            if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
+            else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
+            if (kind == kPartial) mask_keys_b(dp, g, j0, lim, dg);
+            if (GP || GT) {
+                const int pg = !GP ? 0 : (sp.kind == 0 ? 0 : (sp.kind == 1 ? 1 : 2));
+                TileSums ts;
+                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, u0, g, thr, ti, ti64);
+                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, u0, g, thr, ti, ti64);
+                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, u0, g, thr, ti, ti64);
+                if (GP && pg == 0) run_p_lo.add(sm.hbp, sp.b_lo, ts.sum, lane);
+                if (GP && pg == 1) {
+                    const float hi_part = ts.mp - (float)sp.b_lo * ts.sum;
+                    run_p_lo.add(sm.hbp, sp.b_lo, ts.sum - hi_part, lane);
+                    run_p_hi.add(sm.hbp, sp.b_hi, hi_part, lane);
                 }
+                if (GT && tm == 0) run_t_lo.add(sm.hbt, st.b_lo, ts.sum, lane);
+                if (GT && tm == 1) {
+                    run_t_lo.add(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
+                    run_t_hi.add(sm.hbt, st.b_hi, ts.th, lane);
+                }
+            }
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 float td[8];
@@ -488,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
 
     if (row_ok) {
         bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_out + h * D;
-        const float sq = alpha * p.inv_n;
+        const float sq = p.alpha * p.inv_n;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -499,14 +704,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
                 *reinterpret_cast<bf16x4*>(dqg + 32 * db + 8 * r + 4 * g) = w;
             }
     }
-    if (grad_p || grad_t) {
-        if (grad_p) atomicAdd(&sm.hp[cur_p], sum_p);
-        if (grad_t) atomicAdd(&sm.ht[cur_t], sum_t);
+    if (GP || GT) {
+        if (GP) { run_p_lo.add(sm.hbp, -2, 0.0f, lane); run_p_hi.add(sm.hbp, -2, 0.0f, lane); }  // flush
+        if (GT) { run_t_lo.add(sm.hbt, -2, 0.0f, lane); run_t_hi.add(sm.hbt, -2, 0.0f, lane); }
         __syncthreads();
         for (int e = tid; e < kNumClasses; e += kThreads) {
             const int b = bucket_of_class(e);
-            if (grad_p && sm.hp[e] != 0.0f) atomicAdd(&p.drab_pos[h * kNumBuckets + b], sm.hp[e] * p.inv_n);
-            if (grad_t && sm.ht[e] != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], sm.ht[e] * p.inv_n);
+            if (GT && sm.hct[e] != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], sm.hct[e] * p.inv_n);
+        }
+        for (int b = tid; b < kNumBuckets; b += kThreads) {
+            if (GP && sm.hbp[b] != 0.0f) atomicAdd(&p.drab_pos[h * kNumBuckets + b], sm.hbp[b] * p.inv_n);
+            if (GT && sm.hbt[b] != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], sm.hbt[b] * p.inv_n);
         }
     }
 }
@@ -683,7 +891,11 @@ hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
 
 template <int D, bool RP, bool RT>
 hipError_t launch_dq_t(const AttnParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    const bool gp = RP && p.drab_pos, gt = RT && p.drab_ts;
+    if (gp && gt) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    else if (gp) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, RP, false>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    else if (gt) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, false, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, false, false>), dim3(p.num_units), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -18,7 +18,11 @@
 //   O^T (D x 32 rows) += V^T . P^T           (D/32) x 4 v_mfma_f32_32x32x16_bf16
 // The C layout of S^T gives each lane one query row and 16 keys per 32-key block, which is the
 // B-operand layout P^T needs once keys are renumbered (perm_key) -- V is stored transposed with
-// the same renumbering, so P never leaves registers.  1/N is applied once to O.
+// the same renumbering, so P never leaves registers.  Scores are carried as -log2(e) * S (folded
+// into alpha and the staged bias tables), so SiLU costs one fma, exp2, add, rcp and mul; the
+// remaining factor -ln(2) / N is applied once to O.  Whenever every pair of a (wavefront, tile)
+// falls into one position bucket (or one time bucket), that bias is a single scalar for the tile
+// and the per-element bias work disappears -- the common case away from the diagonal.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,46 +38,70 @@ template <int D>
 struct FwdSmem {
     static constexpr int KP = D + 8;    // K row pitch (elements)
     static constexpr int VP = kBN + 8;  // V^T row pitch (elements)
-    bf16 k[2][kBN * KP];
-    bf16 vt[2][D * VP];
+    // Small tables first, so their offsets fit the 16-bit LDS instruction offset field.  Bias
+    // values are stored multiplied by -log2(e) (see silu_scaled).
+    float wt[kNumClasses];              // time bias by bucket class
+    float wp[kNumBuckets];              // position bias by bucket
+    float wtb[kNumBuckets];             // time bias by bucket
     float rp[2][kToep + 1];             // position bias by (i - j) for the tile
     uint32_t tk[2][kBN];                // key timestamps, biased 32-bit relative
     int64_t tk64[2][kBN];               // key timestamps (fallback)
+    int64_t tkmin[2], tkmax[2];         // time range of the tile's real keys
     int fits[2];
-    float wt[kNumClasses];              // time bias by bucket class
-    float wp[kNumBuckets];
+    bf16 k[2][kBN * KP];
+    bf16 vt[2][D * VP];
 };
 
-template <int D, bool RP, bool RT, bool MASK, bool FIT>
+// Bias handling of one (wavefront, tile), decided once per tile from the distance ranges:
+//   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
+//   TM 0: time bias absent or one bucket (inside b0/b1); 1: two buckets, b1 where |dt| >= thr;
+//      2: per-element bucket class, 32-bit relative times; 3: the same with 64-bit times.
+template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, int buf, int u0,
-                                         int g, float alpha, uint32_t ti, int64_t ti64, int j0,
-                                         int lim, int dg) {
+                                         int g, float alpha2, float b0, float b1, uint32_t thr,
+                                         uint32_t ti, int64_t ti64) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = 32 * kb + 8 * r + 4 * g;  // first of this lane's 4 keys
             u32x4 tq;
-            if (RT && FIT) tq = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+            if (TM == 1 || TM == 2) tq = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float bias = 0.0f;
-                if (RP) bias += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
-                if (RT) {
-                    uint32_t dt = FIT ? absdiff_u32(ti, tq[c]) : absdiff_sat(ti64, sm.tk64[buf][jj + c]);
-                    bias += sm.wt[bucket_class(dt)];
-                }
-                float x = fmaf(alpha, s[kb][e], bias);
-                float y = x * fast_sigmoid(x);
-                if (MASK) {
-                    const int j = j0 + jj + c;
-                    y = (j <= lim || j == dg) ? y : 0.0f;
-                }
-                s[kb][e] = y;
+                float b = b0;
+                if (TM == 1) b = absdiff_u32(ti, tq[c]) >= thr ? b1 : b0;
+                if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
+                if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tq[c]))];
+                if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
+                s[kb][e] = silu_scaled(fmaf(alpha2, s[kb][e], b));
             }
         }
     }
+}
+
+template <int D, int PM>
+__device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[2], const FwdSmem<D>& sm, int buf,
+                                            int u0, int g, float alpha2, float b0, float b1,
+                                            uint32_t thr, uint32_t ti, int64_t ti64) {
+    switch (tm) {
+        case 0: epilogue<D, PM, 0>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        case 1: epilogue<D, PM, 1>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        case 2: epilogue<D, PM, 2>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        default: epilogue<D, PM, 3>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+    }
+}
+
+// Zero the entries of keys this lane's row does not see (partial tiles only).
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int g, int j0, int lim, int dg) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+            s[kb][e] = (j <= lim || j == dg) ? s[kb][e] : 0.0f;
+        }
 }
 
 template <int D, bool RP, bool RT>
@@ -96,10 +124,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const int64_t ld = p.ld_in;
 
     if (RP)
-        for (int e = tid; e < kNumBuckets; e += kThreads) sm.wp[e] = p.rab_pos[h * kNumBuckets + e];
-    if (RT)
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wp[e] = -kLog2e * p.rab_pos[h * kNumBuckets + e];
+    if (RT) {
         for (int e = tid; e < kNumClasses; e += kThreads)
-            sm.wt[e] = p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+            sm.wt[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
+    }
     const int64_t tbase = RT ? p.ts[tok0] : 0;
 
     const int rhi = imin(r0 + kRows, n);
@@ -123,12 +155,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         else qf[ks] = bf16x8{};
     }
     uint32_t ti = 0;
-    int64_t ti64 = 0;
+    int64_t ti64 = 0, timin = 0, timax = 0;
     bool wave_qfit = true;
     if (RT) {
         ti64 = row_ok ? p.ts[tok0 + i] : tbase;
         wave_qfit = __all(rel_time_fits(ti64, tbase));
         ti = rel_time_u32(ti64, tbase);
+        timin = wave_min64(row_ok ? ti64 : INT64_MAX);
+        timax = wave_max64(row_ok ? ti64 : INT64_MIN);
     }
 
     f32x16 o[D / 32];
@@ -177,10 +211,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             }
         }
         if (RT && tid < kBN) {  // exactly wavefront 0
+            const bool real = j0 + tid < n;
             sm.tk64[buf][tid] = tkr;
             sm.tk[buf][tid] = rel_time_u32(tkr, tbase);
             const bool all_fit = __all(rel_time_fits(tkr, tbase));
-            if (tid == 0) sm.fits[buf] = all_fit ? 1 : 0;
+            const int64_t mn = wave_min64(real ? tkr : INT64_MAX);
+            const int64_t mx = wave_max64(real ? tkr : INT64_MIN);
+            if (tid == 0) {
+                sm.fits[buf] = all_fit ? 1 : 0;
+                sm.tkmin[buf] = mn;
+                sm.tkmax[buf] = mx;
+            }
         }
         if (RP)
             for (int u = tid; u < kToep; u += kThreads) {
@@ -195,8 +236,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     if (ntiles > 1) load_tile(kt.tile(1));
     __syncthreads();
 
-    // slot of (row i, key j0 + jj) in rp: u0 + (jj - 4g) + ... ; see store_tile
+    // slot of (row i, key j0 + jj) in rp is u0 + jj - 4g; see store_tile
     const int u0 = 4 * g - (kWaveRows * wave + lr) + (kRows - 1);
+    const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, j0 = kt.tile(t) * kBN;
@@ -213,14 +255,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                     s[kb] = mfma32(a, qf[ks], s[kb]);
                 }
             }
-            const bool fit = !RT || (wave_qfit && sm.fits[buf]);
-            if (kind == kPartial) {
-                if (fit) epilogue<D, RP, RT, true, true>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
-                else epilogue<D, RP, RT, true, false>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
-            } else {
-                if (fit) epilogue<D, RP, RT, false, true>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
-                else epilogue<D, RP, RT, false, false>(s, sm, buf, u0, g, p.alpha, ti, ti64, j0, lim, dg);
+            // bias mode of this (wavefront, tile): one bucket for the whole tile when possible
+            float b0 = 0.0f, b1 = 0.0f;
+            uint32_t thr = 0;
+            int pm = 0, tm = 0;
+            if (RP) {
+                const int jhi = imin(j0 + kBN, n) - 1;
+                const BiasSpan sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - j0);
+                if (sp.kind == 0) b0 = sm.wp[sp.b_lo];
+                else pm = 1;
             }
+            b1 = b0;
+            if (RT) {
+                const BiasSpan st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
+                const bool fit = wave_qfit && sm.fits[buf];
+                if (st.kind == 0) { b0 += sm.wtb[st.b_lo]; b1 = b0; }
+                else if (st.kind == 1 && fit) {
+                    tm = 1;
+                    thr = st.thr;
+                    b1 = b0 + sm.wtb[st.b_hi];
+                    b0 += sm.wtb[st.b_lo];
+                } else tm = fit ? 2 : 3;
+            }
+            if (pm) epilogue_tm<D, 1>(tm, s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
+            else epilogue_tm<D, 0>(tm, s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
+            if (kind == kPartial) mask_keys(s, g, j0, lim, dg);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 float tmp[8];
@@ -242,13 +301,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
 
     if (row_ok) {
         bf16* og = static_cast<bf16*>(p.out) + (tok0 + i) * p.ld_out + h * D;
+        const float oscale = -kLn2 * p.inv_n;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 bf16x4 w;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (bf16)(o[db][4 * r + c] * p.inv_n);
+                for (int c = 0; c < 4; ++c) w[c] = (bf16)(o[db][4 * r + c] * oscale);
                 *reinterpret_cast<bf16x4*>(og + 32 * db + 8 * r + 4 * g) = w;
             }
     }

@@ -72,8 +72,72 @@ __device__ __forceinline__ uint32_t rel_time_u32(int64_t t, int64_t base) {
 }
 
 // SiLU pieces with hardware exp2 / reciprocal (about 1 ulp each).
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float fast_sigmoid(float x) {
-    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+}
+
+// Scores are carried as t = -log2(e) * S, so sigmoid(S) = 1 / (1 + 2^t) and
+// SiLU(S) = -ln(2) * t * sigmoid(S): the caller folds -ln(2) into one final scale.
+__device__ __forceinline__ float silu_scaled(float t) {
+    return t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+}
+
+// Bucket range of the distances |x| for x in [lo, hi] when one bucket covers them all, else -1.
+HSTU_HD int uniform_bucket(int64_t lo, int64_t hi) {
+    if (lo < 0 && hi > 0) return -1;
+    uint64_t a = (uint64_t)(lo < 0 ? -hi : lo), b = (uint64_t)(lo < 0 ? -lo : hi);
+    uint32_t sa = a > 0xffffffffull ? 0xffffffffu : (uint32_t)a;
+    uint32_t sb = b > 0xffffffffull ? 0xffffffffu : (uint32_t)b;
+    int ba = bucket_of(sa);
+    return ba == bucket_of(sb) ? ba : -1;
+}
+
+// Smallest distance whose bucket is b.
+HSTU_HD uint32_t bucket_start(int b) {
+    if (b < 16) return (uint32_t)b;
+    const int e = 4 + (b - 16) / 4, m = (b - 16) % 4;
+    return (1u << e) + (uint32_t)m * (1u << (e - 2));
+}
+
+// How one bias term behaves over a (wavefront, tile), decided from the range [lo, hi] of the
+// signed distances it covers:
+//   kind 0: one bucket (b_lo) for every pair;
+//   kind 1: two adjacent buckets b_lo < b_hi, split at |x| >= thr;
+//   kind 2: anything else (per-element bucket lookup).
+struct BiasSpan {
+    int kind, b_lo, b_hi;
+    uint32_t thr;
+};
+HSTU_HD BiasSpan bias_span(int64_t lo, int64_t hi) {
+    BiasSpan r{2, 0, 0, 0};
+    if (lo < 0 && hi > 0) return r;
+    uint64_t a = (uint64_t)(lo < 0 ? -hi : lo), b = (uint64_t)(lo < 0 ? -lo : hi);
+    const uint32_t sa = a > 0xffffffffull ? 0xffffffffu : (uint32_t)a;
+    const uint32_t sb = b > 0xffffffffull ? 0xffffffffu : (uint32_t)b;
+    r.b_lo = bucket_of(sa);
+    r.b_hi = bucket_of(sb);
+    if (r.b_lo == r.b_hi) r.kind = 0;
+    else if (r.b_hi == r.b_lo + 1) { r.kind = 1; r.thr = bucket_start(r.b_hi); }
+    return r;
+}
+
+__device__ __forceinline__ int64_t wave_min64(int64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        int64_t o = __shfl_xor(v, m);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ int64_t wave_max64(int64_t v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        int64_t o = __shfl_xor(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
