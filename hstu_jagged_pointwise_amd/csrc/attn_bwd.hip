@@ -87,7 +87,7 @@ struct SmemA {
     int64_t tq64[2][kTile];
     int64_t tqmin[2], tqmax[2];
     int fits[2];
-    bf16 q[2][kTile * RP];
+    alignas(16) bf16 q[2][kTile * RP];
     bf16 dout[2][kTile * RP];
     bf16 qt[2][D * TP];
     bf16 doutt[2][D * TP];
@@ -272,20 +272,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
         const int buf = t & 1, i0 = (tfirst + t) * kTile;
         const int kind = wk0 < khi ? classify_key_tile(wk0, wk1, i0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
-            f32x16 s[2], dp[2];
+            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                s[qb] = f32x16{};
-                dp[qb] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const int off = (32 * qb + lr) * RPt + 16 * ks + 8 * g;
-                    bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[buf][off]);
-                    bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sm.dout[buf][off]);
-                    s[qb] = mfma32(aq, kf[ks], s[qb]);
-                    dp[qb] = mfma32(ad, vf[ks], dp[qb]);
-                }
+            for (int x = 0; x < 2 * (D / 16); ++x) {
+                const int ks = x >> 1, qb = x & 1;
+                const int off = (32 * qb + lr) * RPt + 16 * ks + 8 * g;
+                bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[buf][off]);
+                bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sm.dout[buf][off]);
+                s[qb] = mfma32(aq, kf[ks], s[qb]);
+                dp[qb] = mfma32(ad, vf[ks], dp[qb]);
             }
+            sched_mfma_lds<4 * (D / 16), 4>();
             float b0 = 0.0f, b1 = 0.0f;
             uint32_t thr = 0;
             int pm = 0, tm = 0;
@@ -328,6 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                     dkt[db] = mfma32(aq, db8, dkt[db]);
                 }
             }
+            sched_mfma_lds<8 * (D / 32), 4>();
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tfirst + t + 1);
         if (t + 2 < ntiles) load_tile(tfirst + t + 2);
@@ -373,7 +371,7 @@ struct SmemB {
     float hct[kNumClasses];   // time-bias gradient sums of tiles spanning many buckets, by class
     float hbp[kNumBuckets];   // position-bias gradient sums, by bucket
     float hbt[kNumBuckets];   // time-bias gradient sums of one- or two-bucket tiles, by bucket
-    bf16 k[2][kTile * RP];
+    alignas(16) bf16 k[2][kTile * RP];
     bf16 v[2][kTile * RP];
     bf16 kt[2][D * TP];
 };
@@ -615,20 +613,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
         const int buf = t & 1, j0 = ktl.tile(t) * kTile;
         const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
-            f32x16 s[2], dp[2];
+            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
-                dp[kb] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const int off = (32 * kb + lr) * RPt + 16 * ks + 8 * g;
-                    bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.k[buf][off]);
-                    bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.v[buf][off]);
-                    s[kb] = mfma32(ak, qf[ks], s[kb]);
-                    dp[kb] = mfma32(av, dof[ks], dp[kb]);
-                }
+            for (int x = 0; x < 2 * (D / 16); ++x) {
+                const int ks = x >> 1, kb = x & 1;
+                const int off = (32 * kb + lr) * RPt + 16 * ks + 8 * g;
+                bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.k[buf][off]);
+                bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.v[buf][off]);
+                s[kb] = mfma32(ak, qf[ks], s[kb]);
+                dp[kb] = mfma32(av, dof[ks], dp[kb]);
             }
+            sched_mfma_lds<4 * (D / 16), 4>();
             float b0 = 0.0f, b1 = 0.0f;
             uint32_t thr = 0;
             int pm = 0, tm = 0;
@@ -685,6 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
                     dqt[db] = mfma32(ak, db8, dqt[db]);
                 }
             }
+            sched_mfma_lds<4 * (D / 32), 4>();
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, ktl.tile(t + 1));
         if (t + 2 < ntiles) load_tile(ktl.tile(t + 2));

@@ -48,7 +48,7 @@ struct FwdSmem {
     int64_t tk64[2][kBN];               // key timestamps (fallback)
     int64_t tkmin[2], tkmax[2];         // time range of the tile's real keys
     int fits[2];
-    bf16 k[2][kBN * KP];
+    alignas(16) bf16 k[2][kBN * KP];
     bf16 vt[2][D * VP];
 };
 
@@ -244,17 +244,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         const int buf = t & 1, j0 = kt.tile(t) * kBN;
         const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
-            f32x16 s[2];
+            f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        &sm.k[buf][(32 * kb + lr) * KP + 16 * ks + 8 * g]);
-                    s[kb] = mfma32(a, qf[ks], s[kb]);
-                }
+            for (int x = 0; x < 2 * (D / 16); ++x) {
+                const int ks = x >> 1, kb = x & 1;
+                bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                    &sm.k[buf][(32 * kb + lr) * KP + 16 * ks + 8 * g]);
+                s[kb] = mfma32(a, qf[ks], s[kb]);
             }
+            sched_mfma_lds<2 * (D / 16), 4>();
             // bias mode of this (wavefront, tile): one bucket for the whole tile when possible
             float b0 = 0.0f, b1 = 0.0f;
             uint32_t thr = 0;
@@ -293,6 +291,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                     o[db] = mfma32(a, pb, o[db]);
                 }
             }
+            sched_mfma_lds<4 * (D / 32), 4>();
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, kt.tile(t + 1));
         if (t + 2 < ntiles) load_tile(kt.tile(t + 2));

@@ -157,6 +157,19 @@ __device__ __forceinline__ int perm_key(int k) {
     return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// Scheduling hint for a block of N MFMAs, each fed by one LDS read: issue LA reads first, then
+// alternate one MFMA and one read, so each read has LA matrix instructions to land.
+template <int N, int LA>
+__device__ __forceinline__ void sched_mfma_lds() {
+    __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < N - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
