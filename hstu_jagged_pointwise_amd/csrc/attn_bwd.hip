@@ -99,20 +99,19 @@ struct SmemA {
 //      bucket class with 32-bit / 64-bit times.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemA<D>& sm,
-                                           int buf, int u0, int g, float alpha2, float b0,
-                                           float b1, uint32_t thr, uint32_t tj, int64_t tj64) {
+                                           int buf, int u0, int g, float alpha2, const TimeSel& tb,
+                                           uint32_t tj, int64_t tj64) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ii = 32 * qb + 8 * r + 4 * g;
             u32x4 tq4;
-            if (TM == 1 || TM == 2) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
+            if (TM == 1 || TM == 2 || TM == 4) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = b0;
-                if (TM == 1) b = absdiff_u32(tj, tq4[c]) >= thr ? b1 : b0;
+                float b = tb.select<TM>(tj, tq4[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
@@ -126,13 +125,14 @@ __device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], cons
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_a_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
                                               const SmemA<D>& sm, int buf, int u0, int g,
-                                              float alpha2, float b0, float b1, uint32_t thr,
-                                              uint32_t tj, int64_t tj64) {
+                                              float alpha2, const TimeSel& tb, uint32_t tj,
+                                              int64_t tj64) {
     switch (tm) {
-        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
-        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
-        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
-        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64); break;
+        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
+        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
+        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
+        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
+        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
     }
 }
 
@@ -283,29 +283,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                 dp[qb] = mfma32(ad, vf[ks], dp[qb]);
             }
             sched_mfma_lds<4 * (D / 16), 4>();
-            float b0 = 0.0f, b1 = 0.0f;
-            uint32_t thr = 0;
-            int pm = 0, tm = 0;
+            float bpos = 0.0f;
+            int pm = 0;
             const int ihi = imin(i0 + kTile, n) - 1;
             if (RP) {
                 const BiasSpan sp = bias_span((int64_t)i0 - (wk1 - 1), (int64_t)ihi - wk0);
-                if (sp.kind == 0) b0 = sm.wp[sp.b_lo];
+                if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
-            b1 = b0;
+            TimeSel tb;
+            int tm = 0;
             if (RT) {
                 const BiasSpan st = bias_span(sm.tqmin[buf] - tjmax, sm.tqmax[buf] - tjmin);
-                const bool fit = wave_kfit && sm.fits[buf];
-                if (st.kind == 0) { b0 += sm.wtb[st.b_lo]; b1 = b0; }
-                else if (st.kind == 1 && fit) {
-                    tm = 1;
-                    thr = st.thr;
-                    b1 = b0 + sm.wtb[st.b_hi];
-                    b0 += sm.wtb[st.b_lo];
-                } else tm = fit ? 2 : 3;
-            }
-            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64);
-            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, tj, tj64);
+                tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb);
+            } else tb.set_const(bpos);
+            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64);
+            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64);
             if (kind == kPartial) mask_queries(s, dp, g, i0, lo, hi);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
@@ -368,6 +361,7 @@ struct SmemB {
     int64_t tk64[2][kTile];
     int64_t tkmin[2], tkmax[2];
     int fits[2];
+    float dg[2][kToep + 1];   // position-bias gradient sums of many-bucket tiles, by (i - j)
     float hct[kNumClasses];   // time-bias gradient sums of tiles spanning many buckets, by class
     float hbp[kNumBuckets];   // position-bias gradient sums, by bucket
     float hbt[kNumBuckets];   // time-bias gradient sums of one- or two-bucket tiles, by bucket
@@ -379,20 +373,19 @@ struct SmemB {
 // Per-element part of pass B: dS (times N) into dp.  Bias modes as in pass A.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemB<D>& sm,
-                                           int buf, int u0, int g, float alpha2, float b0,
-                                           float b1, uint32_t thr, uint32_t ti, int64_t ti64) {
+                                           int buf, int u0, int g, float alpha2, const TimeSel& tb,
+                                           uint32_t ti, int64_t ti64) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = 32 * kb + 8 * r + 4 * g;
             u32x4 tk4;
-            if (TM == 1 || TM == 2) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+            if (TM == 1 || TM == 2 || TM == 4) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = b0;
-                if (TM == 1) b = absdiff_u32(ti, tk4[c]) >= thr ? b1 : b0;
+                float b = tb.select<TM>(ti, tk4[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c].bias;
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tk4[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
@@ -404,13 +397,14 @@ __device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], cons
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_b_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
                                               const SmemB<D>& sm, int buf, int u0, int g,
-                                              float alpha2, float b0, float b1, uint32_t thr,
-                                              uint32_t ti, int64_t ti64) {
+                                              float alpha2, const TimeSel& tb, uint32_t ti,
+                                              int64_t ti64) {
     switch (tm) {
-        case 0: epilogue_b<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
-        case 1: epilogue_b<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
-        case 2: epilogue_b<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
-        default: epilogue_b<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        case 0: epilogue_b<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 1: epilogue_b<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 4: epilogue_b<D, PM, 4>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 2: epilogue_b<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        default: epilogue_b<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
     }
 }
 
@@ -418,30 +412,37 @@ __device__ __forceinline__ void epilogue_b_tm(int tm, f32x16 (&s)[2], f32x16 (&d
 //   sum = sum of dS (serves every term whose tile lies in one bucket),
 //   mp  = sum of dS * bucket(|i - j|) (PG 1, two position buckets: the upper bucket's share is
 //         mp - b_lo * sum),
-//   th  = sum of dS over pairs with |dt| >= thr (TM 1, two time buckets),
-// plus per-element LDS histogram updates for tiles spanning more buckets (PG 2; TM 2, 3).
+//   th  = sum of dS over pairs with |dt| >= thr, th2 the same for thr2 (TM 1 and 4: two or
+//         three time buckets),
+// plus, for tiles spanning more buckets, per-diagonal LDS sums for the position term (PG 2;
+// each lane adds to the slot of its own i - j, so lanes do not collide) and per-element LDS
+// histogram updates by class for the time term (TM 2, 3).
 struct TileSums {
-    float sum, mp, th;
+    float sum, mp, th, th2;
 };
 template <int D, int PG, int TM, bool GP, bool GT>
 __device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& sm, int buf, int u0,
-                                              int g, uint32_t thr, uint32_t ti, int64_t ti64) {
-    TileSums ts{0.0f, 0.0f, 0.0f};
+                                              int g, const TimeSel& tb, uint32_t ti, int64_t ti64) {
+    TileSums ts{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = 32 * kb + 8 * r + 4 * g;
             u32x4 tk4;
-            if (GT && (TM == 1 || TM == 2)) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+            if (GT && (TM == 1 || TM == 2 || TM == 4)) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float ds = dp[kb][4 * r + c];
                 const int u = u0 + 32 * kb + 8 * r + c;
                 ts.sum += ds;
                 if (GP && PG == 1) ts.mp = fmaf(ds, sm.rp[buf][u].bucket, ts.mp);
-                if (GP && PG == 2) atomicAdd(&sm.hbp[(int)sm.rp[buf][u].bucket], ds);
-                if (GT && TM == 1) ts.th += absdiff_u32(ti, tk4[c]) >= thr ? ds : 0.0f;
+                if (GP && PG == 2) atomicAdd(&sm.dg[buf][u], ds);
+                if (GT && (TM == 1 || TM == 4)) {
+                    const uint32_t d = absdiff_u32(ti, tk4[c]);
+                    ts.th += d >= tb.thr ? ds : 0.0f;
+                    if (TM == 4) ts.th2 += d >= tb.thr2 ? ds : 0.0f;
+                }
                 if (GT && TM == 2) atomicAdd(&sm.hct[bucket_class(absdiff_u32(ti, tk4[c]))], ds);
                 if (GT && TM == 3)
                     atomicAdd(&sm.hct[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))], ds);
@@ -452,13 +453,14 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& s
 
 template <int D, int PG, bool GP, bool GT>
 __device__ __forceinline__ TileSums grad_sums_tm(int tm, const f32x16 (&dp)[2], SmemB<D>& sm,
-                                                 int buf, int u0, int g, uint32_t thr, uint32_t ti,
-                                                 int64_t ti64) {
+                                                 int buf, int u0, int g, const TimeSel& tb,
+                                                 uint32_t ti, int64_t ti64) {
     switch (GT ? tm : 0) {
-        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
-        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
-        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
-        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, u0, g, thr, ti, ti64);
+        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
+        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
+        case 4: return grad_sums<D, PG, 4, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
+        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
+        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
     }
 }
 
@@ -516,6 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
             sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
     }
     for (int e = tid; e < kNumClasses; e += kThreads) sm.hct[e] = 0.0f;
+    for (int e = tid; e < 2 * (kToep + 1); e += kThreads) (&sm.dg[0][0])[e] = 0.0f;
     for (int e = tid; e < kNumBuckets; e += kThreads) { sm.hbp[e] = 0.0f; sm.hbt[e] = 0.0f; }
     const int64_t tbase = RT ? p.ts[tok0] : 0;
 
@@ -549,7 +552,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
     f32x16 dqt[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
-    Run run_p_lo, run_p_hi, run_t_lo, run_t_hi;  // bias-gradient running sums
+    Run run_p_lo, run_p_hi, run_t_lo, run_t_mid, run_t_hi;  // bias-gradient running sums
+    // Adds the per-diagonal sums of tile `tile` (buffer b) to the position histogram and clears
+    // them; called once every wavefront has finished adding to that buffer.
+    auto fold_diagonals = [&](int b, int tile) {
+        const int j0 = tile * kTile;
+        for (int u = tid; u < kToep; u += kThreads) {
+            const float v = sm.dg[b][u];
+            if (v != 0.0f) {
+                const int delta = (r0 - j0) + (kBlk - 1) - u;
+                atomicAdd(&sm.hbp[bucket_of((uint32_t)(delta < 0 ? -delta : delta))], v);
+                sm.dg[b][u] = 0.0f;
+            }
+        }
+    };
 
     bf16x8 kr[4], vr[4];
     int64_t tkr = 0;
@@ -624,37 +640,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
                 dp[kb] = mfma32(av, dof[ks], dp[kb]);
             }
             sched_mfma_lds<4 * (D / 16), 4>();
-            float b0 = 0.0f, b1 = 0.0f;
-            uint32_t thr = 0;
-            int pm = 0, tm = 0;
-            BiasSpan sp{0, 0, 0, 0}, st{0, 0, 0, 0};
+            float bpos = 0.0f;
+            int pm = 0;
+            BiasSpan sp{0, 0, 0, 0, 0}, st{0, 0, 0, 0, 0};
             if (RP) {
                 const int jhi = imin(j0 + kTile, n) - 1;
                 sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - j0);
-                if (sp.kind == 0) b0 = sm.wp[sp.b_lo];
+                if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
-            b1 = b0;
+            TimeSel tb;
+            int tm = 0;
             if (RT) {
                 st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
-                const bool fit = wave_qfit && sm.fits[buf];
-                if (st.kind == 0) { b0 += sm.wtb[st.b_lo]; b1 = b0; }
-                else if (st.kind == 1 && fit) {
-                    tm = 1;
-                    thr = st.thr;
-                    b1 = b0 + sm.wtb[st.b_hi];
-                    b0 += sm.wtb[st.b_lo];
-                } else tm = fit ? 2 : 3;
-            }
-            if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
-            else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
+                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb);
+            } else tb.set_const(bpos);
+            if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64);
+            else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64);
             if (kind == kPartial) mask_keys_b(dp, g, j0, lim, dg);
             if (GP || GT) {
                 const int pg = !GP ? 0 : (sp.kind == 0 ? 0 : (sp.kind == 1 ? 1 : 2));
                 TileSums ts;
-                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, u0, g, thr, ti, ti64);
-                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, u0, g, thr, ti, ti64);
-                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, u0, g, thr, ti, ti64);
+                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, u0, g, tb, ti, ti64);
+                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, u0, g, tb, ti, ti64);
+                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, u0, g, tb, ti, ti64);
                 if (GP && pg == 0) run_p_lo.add(sm.hbp, sp.b_lo, ts.sum, lane);
                 if (GP && pg == 1) {
                     const float hi_part = ts.mp - (float)sp.b_lo * ts.sum;
@@ -665,6 +674,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
                 if (GT && tm == 1) {
                     run_t_lo.add(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
                     run_t_hi.add(sm.hbt, st.b_hi, ts.th, lane);
+                }
+                if (GT && tm == 4) {
+                    run_t_lo.add(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
+                    run_t_mid.add(sm.hbt, st.b_lo + 1, ts.th - ts.th2, lane);
+                    run_t_hi.add(sm.hbt, st.b_hi, ts.th2, lane);
                 }
             }
 #pragma unroll
@@ -682,10 +696,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
             }
             sched_mfma_lds<4 * (D / 32), 4>();
         }
+        if (GP && t > 0) fold_diagonals(buf ^ 1, ktl.tile(t - 1));
         if (t + 1 < ntiles) store_tile(buf ^ 1, ktl.tile(t + 1));
         if (t + 2 < ntiles) load_tile(ktl.tile(t + 2));
         __syncthreads();
     }
+    if (GP && ntiles > 0) fold_diagonals((ntiles - 1) & 1, ktl.tile(ntiles - 1));
 
     if (row_ok) {
         bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_out + h * D;
@@ -702,7 +718,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
     }
     if (GP || GT) {
         if (GP) { run_p_lo.add(sm.hbp, -2, 0.0f, lane); run_p_hi.add(sm.hbp, -2, 0.0f, lane); }  // flush
-        if (GT) { run_t_lo.add(sm.hbt, -2, 0.0f, lane); run_t_hi.add(sm.hbt, -2, 0.0f, lane); }
+        if (GT) {
+            run_t_lo.add(sm.hbt, -2, 0.0f, lane);
+            run_t_mid.add(sm.hbt, -2, 0.0f, lane);
+            run_t_hi.add(sm.hbt, -2, 0.0f, lane);
+        }
         __syncthreads();
         for (int e = tid; e < kNumClasses; e += kThreads) {
             const int b = bucket_of_class(e);

@@ -54,24 +54,24 @@ struct FwdSmem {
 
 // Bias handling of one (wavefront, tile), decided once per tile from the distance ranges:
 //   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
-//   TM 0: time bias absent or one bucket (inside b0/b1); 1: two buckets, b1 where |dt| >= thr;
-//      2: per-element bucket class, 32-bit relative times; 3: the same with 64-bit times.
+//   TM 0: time bias absent or one bucket (inside tb.b0); 1: two buckets, tb.b1 where
+//      |dt| >= thr; 4: three buckets (tb.b2 where |dt| >= thr2); 2: per-element bucket class,
+//      32-bit relative times; 3: the same with 64-bit times.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, int buf, int u0,
-                                         int g, float alpha2, float b0, float b1, uint32_t thr,
-                                         uint32_t ti, int64_t ti64) {
+                                         int g, float alpha2, const TimeSel& tb, uint32_t ti,
+                                         int64_t ti64) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = 32 * kb + 8 * r + 4 * g;  // first of this lane's 4 keys
             u32x4 tq;
-            if (TM == 1 || TM == 2) tq = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
+            if (TM == 1 || TM == 2 || TM == 4) tq = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = b0;
-                if (TM == 1) b = absdiff_u32(ti, tq[c]) >= thr ? b1 : b0;
+                float b = tb.select<TM>(ti, tq[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tq[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
@@ -83,13 +83,14 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, i
 
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[2], const FwdSmem<D>& sm, int buf,
-                                            int u0, int g, float alpha2, float b0, float b1,
-                                            uint32_t thr, uint32_t ti, int64_t ti64) {
+                                            int u0, int g, float alpha2, const TimeSel& tb,
+                                            uint32_t ti, int64_t ti64) {
     switch (tm) {
-        case 0: epilogue<D, PM, 0>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
-        case 1: epilogue<D, PM, 1>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
-        case 2: epilogue<D, PM, 2>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
-        default: epilogue<D, PM, 3>(s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64); break;
+        case 0: epilogue<D, PM, 0>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 1: epilogue<D, PM, 1>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 4: epilogue<D, PM, 4>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 2: epilogue<D, PM, 2>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        default: epilogue<D, PM, 3>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
     }
 }
 
@@ -254,29 +255,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             }
             sched_mfma_lds<2 * (D / 16), 4>();
             // bias mode of this (wavefront, tile): one bucket for the whole tile when possible
-            float b0 = 0.0f, b1 = 0.0f;
-            uint32_t thr = 0;
-            int pm = 0, tm = 0;
+            float bpos = 0.0f;
+            int pm = 0;
             if (RP) {
                 const int jhi = imin(j0 + kBN, n) - 1;
                 const BiasSpan sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - j0);
-                if (sp.kind == 0) b0 = sm.wp[sp.b_lo];
+                if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
-            b1 = b0;
+            TimeSel tb;
+            int tm = 0;
             if (RT) {
                 const BiasSpan st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
-                const bool fit = wave_qfit && sm.fits[buf];
-                if (st.kind == 0) { b0 += sm.wtb[st.b_lo]; b1 = b0; }
-                else if (st.kind == 1 && fit) {
-                    tm = 1;
-                    thr = st.thr;
-                    b1 = b0 + sm.wtb[st.b_hi];
-                    b0 += sm.wtb[st.b_lo];
-                } else tm = fit ? 2 : 3;
-            }
-            if (pm) epilogue_tm<D, 1>(tm, s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
-            else epilogue_tm<D, 0>(tm, s, sm, buf, u0, g, alpha2, b0, b1, thr, ti, ti64);
+                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb);
+            } else tb.set_const(bpos);
+            if (pm) epilogue_tm<D, 1>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);
+            else epilogue_tm<D, 0>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);
             if (kind == kPartial) mask_keys(s, g, j0, lim, dg);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {

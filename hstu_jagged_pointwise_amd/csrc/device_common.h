@@ -105,13 +105,14 @@ HSTU_HD uint32_t bucket_start(int b) {
 // signed distances it covers:
 //   kind 0: one bucket (b_lo) for every pair;
 //   kind 1: two adjacent buckets b_lo < b_hi, split at |x| >= thr;
+//   kind 3: three adjacent buckets b_lo, b_lo + 1, b_hi = b_lo + 2, split at thr and thr2;
 //   kind 2: anything else (per-element bucket lookup).
 struct BiasSpan {
     int kind, b_lo, b_hi;
-    uint32_t thr;
+    uint32_t thr, thr2;
 };
 HSTU_HD BiasSpan bias_span(int64_t lo, int64_t hi) {
-    BiasSpan r{2, 0, 0, 0};
+    BiasSpan r{2, 0, 0, 0, 0xffffffffu};
     if (lo < 0 && hi > 0) return r;
     uint64_t a = (uint64_t)(lo < 0 ? -hi : lo), b = (uint64_t)(lo < 0 ? -lo : hi);
     const uint32_t sa = a > 0xffffffffull ? 0xffffffffu : (uint32_t)a;
@@ -120,8 +121,46 @@ HSTU_HD BiasSpan bias_span(int64_t lo, int64_t hi) {
     r.b_hi = bucket_of(sb);
     if (r.b_lo == r.b_hi) r.kind = 0;
     else if (r.b_hi == r.b_lo + 1) { r.kind = 1; r.thr = bucket_start(r.b_hi); }
+    else if (r.b_hi == r.b_lo + 2) {
+        r.kind = 3;
+        r.thr = bucket_start(r.b_lo + 1);
+        r.thr2 = bucket_start(r.b_hi);
+    }
     return r;
 }
+
+// Scalar part of a tile's bias plus the time-bias selection of modes 1 and 4 (see BiasSpan);
+// set() returns the time mode: 0 one bucket, 1 two buckets, 4 three buckets, 2 / 3 per-element
+// class lookup with 32-bit / 64-bit times.
+struct TimeSel {
+    float b0, b1, b2;
+    uint32_t thr, thr2;
+    __device__ __forceinline__ void set_const(float b) {
+        b0 = b1 = b2 = b;
+        thr = thr2 = 0xffffffffu;
+    }
+    __device__ __forceinline__ int set(const BiasSpan& st, bool fit, float bpos, const float* wtb) {
+        set_const(bpos);
+        if (st.kind == 0) { set_const(bpos + wtb[st.b_lo]); return 0; }
+        if (!fit) return 3;
+        if (st.kind == 2) return 2;
+        b0 = bpos + wtb[st.b_lo];
+        b1 = bpos + wtb[st.b_lo + 1];
+        b2 = bpos + wtb[st.b_hi];
+        thr = st.thr;
+        thr2 = st.thr2;
+        return st.kind == 1 ? 1 : 4;
+    }
+    template <int TM>
+    __device__ __forceinline__ float select(uint32_t ti, uint32_t tj) const {
+        if (TM == 1) return absdiff_u32(ti, tj) >= thr ? b1 : b0;
+        if (TM == 4) {
+            const uint32_t d = absdiff_u32(ti, tj);
+            return d >= thr2 ? b2 : (d >= thr ? b1 : b0);
+        }
+        return b0;
+    }
+};
 
 __device__ __forceinline__ int64_t wave_min64(int64_t v) {
 #pragma unroll
