@@ -68,6 +68,49 @@ def measured_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128", "bwd_dkdv": "bwd_dkdv_kernel<128",
+                "bwd_dq": "bwd_dq_kernel<128"}
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRAFFIC_FILE):
+    """HBM bytes per launch of the headline kernels from rocprofv3 counter runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) come from separate runs of
+    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extra`; each is scaled by bytes / counter
+    for a plain 1 GiB device copy (`bench.py --copy-calibration`) profiled with the same counter.
+    """
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] == counter:
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return vals
+
+    def copy_scale(path, counter):
+        v = [x for k, xs in per_kernel(path, counter).items() if "copyBuffer" in k for x in xs]
+        return (1 << 30) / (1024.0 * float(np.median(v)))
+
+    fs, ws = copy_scale(copy_fetch_csv, "FETCH_SIZE"), copy_scale(copy_write_csv, "WRITE_SIZE")
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    rec = {"_calibration": {"fetch_bytes_per_kib": round(1024 * fs, 3),
+                            "write_bytes_per_kib": round(1024 * ws, 3),
+                            "copy": "1 GiB device-to-device copy, 5 launches"}}
+    for kernel, pattern in KERNEL_NAMES.items():
+        f = [x for k, xs in fetch.items() if pattern in k for x in xs]
+        wr = [x for k, xs in write.items() if pattern in k for x in xs]
+        if not f or not wr:
+            continue
+        rb, wb = 1024 * fs * float(np.mean(f)), 1024 * ws * float(np.mean(wr))
+        rec[kernel] = {"bytes_per_launch": int(rb + wb), "read_bytes": int(rb), "write_bytes": int(wb),
+                       "fetch_kib_raw": float(np.mean(f)), "write_kib_raw": float(np.mean(wr)),
+                       "dispatches": len(f), "source_sha256": sha256(KERNEL_SOURCES[kernel])}
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w_full, budget_pairs=60_000_000):
     """The oracle (fp64 loops, OpenMP) on a bounded sample of the workload: the first sequence,
     with as many heads as fit the pair budget (heads are independent)."""
@@ -238,7 +281,14 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                         "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into the per-kernel "
+                         "HBM traffic record (no GPU use)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only; this implementation has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

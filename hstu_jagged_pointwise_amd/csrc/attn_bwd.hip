@@ -64,12 +64,6 @@ __device__ __forceinline__ Grad silu_grad(float t, float dp) {
     return Grad{pv, dp * (fmaf(-xs, sg, xs) + sg)};
 }
 
-// Sum over the wavefront, result in every lane.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
 
 // ---------------------------------------------------------------------------------------------
 // pass A: dK, dV
@@ -99,8 +93,9 @@ struct SmemA {
 //      bucket class with 32-bit / 64-bit times.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemA<D>& sm,
-                                           int buf, int u0, int g, float alpha2, const TimeSel& tb,
+                                           int buf, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t tj, int64_t tj64) {
+    const TimePick pick(tb);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -111,7 +106,7 @@ __device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], cons
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = tb.select<TM>(tj, tq4[c]);
+                float b = pick.get<TM>(tj, tq4[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
@@ -125,7 +120,7 @@ __device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], cons
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_a_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
                                               const SmemA<D>& sm, int buf, int u0, int g,
-                                              float alpha2, const TimeSel& tb, uint32_t tj,
+                                              float alpha2, const TimeSel tb, uint32_t tj,
                                               int64_t tj64) {
     switch (tm) {
         case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
@@ -242,13 +237,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
             const bool real = i0 + tid < n;
             sm.tq64[buf][tid] = tqr;
             sm.tq[buf][tid] = rel_time_u32(tqr, tbase);
-            const bool all_fit = __all(rel_time_fits(tqr, tbase));
-            const int64_t mn = wave_min64(real ? tqr : INT64_MAX);
-            const int64_t mx = wave_max64(real ? tqr : INT64_MIN);
+            const TimeRange tr = wave_time_range(tqr, real, tbase);
             if (tid == 0) {
-                sm.fits[buf] = all_fit ? 1 : 0;
-                sm.tqmin[buf] = mn;
-                sm.tqmax[buf] = mx;
+                sm.fits[buf] = tr.fit ? 1 : 0;
+                sm.tqmin[buf] = tr.lo;
+                sm.tqmax[buf] = tr.hi;
             }
         }
         if (RP)
@@ -373,8 +366,9 @@ struct SmemB {
 // Per-element part of pass B: dS (times N) into dp.  Bias modes as in pass A.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemB<D>& sm,
-                                           int buf, int u0, int g, float alpha2, const TimeSel& tb,
+                                           int buf, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t ti, int64_t ti64) {
+    const TimePick pick(tb);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -385,7 +379,7 @@ __device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], cons
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = tb.select<TM>(ti, tk4[c]);
+                float b = pick.get<TM>(ti, tk4[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c].bias;
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tk4[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
@@ -397,7 +391,7 @@ __device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], cons
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_b_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
                                               const SmemB<D>& sm, int buf, int u0, int g,
-                                              float alpha2, const TimeSel& tb, uint32_t ti,
+                                              float alpha2, const TimeSel tb, uint32_t ti,
                                               int64_t ti64) {
     switch (tm) {
         case 0: epilogue_b<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
@@ -422,7 +416,7 @@ struct TileSums {
 };
 template <int D, int PG, int TM, bool GP, bool GT>
 __device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& sm, int buf, int u0,
-                                              int g, const TimeSel& tb, uint32_t ti, int64_t ti64) {
+                                              int g, const TimeSel tb, uint32_t ti, int64_t ti64) {
     TileSums ts{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -453,7 +447,7 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& s
 
 template <int D, int PG, bool GP, bool GT>
 __device__ __forceinline__ TileSums grad_sums_tm(int tm, const f32x16 (&dp)[2], SmemB<D>& sm,
-                                                 int buf, int u0, int g, const TimeSel& tb,
+                                                 int buf, int u0, int g, const TimeSel tb,
                                                  uint32_t ti, int64_t ti64) {
     switch (GT ? tm : 0) {
         case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
@@ -482,7 +476,7 @@ struct Run {
     float acc = 0.0f;
     __device__ __forceinline__ void add(float* hist, int bucket, float v, int lane) {
         if (bucket != cur) {
-            const float tot = wave_sum(acc);
+            const float tot = wave_sum_dpp(acc);
             if (cur >= 0 && lane == 0) atomicAdd(&hist[cur], tot);
             cur = bucket;
             acc = 0.0f;
@@ -598,13 +592,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
             const bool real = j0 + tid < n;
             sm.tk64[buf][tid] = tkr;
             sm.tk[buf][tid] = rel_time_u32(tkr, tbase);
-            const bool all_fit = __all(rel_time_fits(tkr, tbase));
-            const int64_t mn = wave_min64(real ? tkr : INT64_MAX);
-            const int64_t mx = wave_max64(real ? tkr : INT64_MIN);
+            const TimeRange tr = wave_time_range(tkr, real, tbase);
             if (tid == 0) {
-                sm.fits[buf] = all_fit ? 1 : 0;
-                sm.tkmin[buf] = mn;
-                sm.tkmax[buf] = mx;
+                sm.fits[buf] = tr.fit ? 1 : 0;
+                sm.tkmin[buf] = tr.lo;
+                sm.tkmax[buf] = tr.hi;
             }
         }
         if (RP)

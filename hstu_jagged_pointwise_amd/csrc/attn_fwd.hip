@@ -59,8 +59,9 @@ struct FwdSmem {
 //      32-bit relative times; 3: the same with 64-bit times.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, int buf, int u0,
-                                         int g, float alpha2, const TimeSel& tb, uint32_t ti,
+                                         int g, float alpha2, const TimeSel tb, uint32_t ti,
                                          int64_t ti64) {
+    const TimePick pick(tb);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -71,7 +72,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, i
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = tb.select<TM>(ti, tq[c]);
+                float b = pick.get<TM>(ti, tq[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tq[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
@@ -83,7 +84,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, i
 
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[2], const FwdSmem<D>& sm, int buf,
-                                            int u0, int g, float alpha2, const TimeSel& tb,
+                                            int u0, int g, float alpha2, const TimeSel tb,
                                             uint32_t ti, int64_t ti64) {
     switch (tm) {
         case 0: epilogue<D, PM, 0>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
@@ -215,13 +216,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             const bool real = j0 + tid < n;
             sm.tk64[buf][tid] = tkr;
             sm.tk[buf][tid] = rel_time_u32(tkr, tbase);
-            const bool all_fit = __all(rel_time_fits(tkr, tbase));
-            const int64_t mn = wave_min64(real ? tkr : INT64_MAX);
-            const int64_t mx = wave_max64(real ? tkr : INT64_MIN);
+            const TimeRange tr = wave_time_range(tkr, real, tbase);
             if (tid == 0) {
-                sm.fits[buf] = all_fit ? 1 : 0;
-                sm.tkmin[buf] = mn;
-                sm.tkmax[buf] = mx;
+                sm.fits[buf] = tr.fit ? 1 : 0;
+                sm.tkmin[buf] = tr.lo;
+                sm.tkmax[buf] = tr.hi;
             }
         }
         if (RP)

@@ -140,8 +140,8 @@ struct TimeSel {
         thr = thr2 = 0xffffffffu;
     }
     __device__ __forceinline__ int set(const BiasSpan& st, bool fit, float bpos, const float* wtb) {
-        set_const(bpos);
         if (st.kind == 0) { set_const(bpos + wtb[st.b_lo]); return 0; }
+        set_const(bpos);
         if (!fit) return 3;
         if (st.kind == 2) return 2;
         b0 = bpos + wtb[st.b_lo];
@@ -151,16 +151,74 @@ struct TimeSel {
         thr2 = st.thr2;
         return st.kind == 1 ? 1 : 4;
     }
+};
+
+// The per-element selector of a TimeSel, built once per tile.  The third bucket is reached by
+// adding e2 = b2 - b1 (within one rounding of b2): a nested select among three values is turned
+// by the compiler into an indexed load from a scratch copy of them.
+struct TimePick {
+    float b0, b1, e2;
+    uint32_t thr, thr2;
+    __device__ __forceinline__ explicit TimePick(const TimeSel& t)
+        : b0(t.b0), b1(t.b1), e2(t.b2 - t.b1), thr(t.thr), thr2(t.thr2) {}
     template <int TM>
-    __device__ __forceinline__ float select(uint32_t ti, uint32_t tj) const {
+    __device__ __forceinline__ float get(uint32_t ti, uint32_t tj) const {
         if (TM == 1) return absdiff_u32(ti, tj) >= thr ? b1 : b0;
         if (TM == 4) {
             const uint32_t d = absdiff_u32(ti, tj);
-            return d >= thr2 ? b2 : (d >= thr ? b1 : b0);
+            const float lo = d >= thr ? b1 : b0;
+            return lo + (d >= thr2 ? e2 : 0.0f);
         }
         return b0;
     }
 };
+
+// Cross-lane reductions with DPP inside each row of 16 lanes (quad swaps, then half-row and row
+// mirrors: afterwards every lane of a row holds the row's result), then the four rows combined
+// from lanes 0, 16, 32, 48 with readlane.  Every lane of the wavefront must be active.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = umin(v, dpp_u32<kDppXor1>(v));
+    v = umin(v, dpp_u32<kDppXor2>(v));
+    v = umin(v, dpp_u32<kDppHalfMirror>(v));
+    v = umin(v, dpp_u32<kDppMirror>(v));
+    return umin(umin(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                umin(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = umax(v, dpp_u32<kDppXor1>(v));
+    v = umax(v, dpp_u32<kDppXor2>(v));
+    v = umax(v, dpp_u32<kDppHalfMirror>(v));
+    v = umax(v, dpp_u32<kDppMirror>(v));
+    return umax(umax(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+                umax(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ float fdpp_add(float v, uint32_t moved) {
+    return v + __builtin_bit_cast(float, moved);
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = fdpp_add(v, dpp_u32<kDppXor1>(__builtin_bit_cast(uint32_t, v)));
+    v = fdpp_add(v, dpp_u32<kDppXor2>(__builtin_bit_cast(uint32_t, v)));
+    v = fdpp_add(v, dpp_u32<kDppHalfMirror>(__builtin_bit_cast(uint32_t, v)));
+    v = fdpp_add(v, dpp_u32<kDppMirror>(__builtin_bit_cast(uint32_t, v)));
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(u, 48));
+    return (r0 + r1) + (r2 + r3);
+}
 
 __device__ __forceinline__ int64_t wave_min64(int64_t v) {
 #pragma unroll
@@ -177,6 +235,29 @@ __device__ __forceinline__ int64_t wave_max64(int64_t v) {
         v = o > v ? o : v;
     }
     return v;
+}
+
+// Time range and 32-bit fit of one tile's timestamps, held one per lane by a whole wavefront
+// (lanes with real = false are ignored for the range).  When every relative time fits in 32 bits
+// the range is reduced on the biased 32-bit values with DPP, else on the 64-bit values.
+struct TimeRange {
+    int64_t lo, hi;
+    bool fit;
+};
+__device__ __forceinline__ TimeRange wave_time_range(int64_t t, bool real, int64_t base) {
+    TimeRange r;
+    r.fit = __all(rel_time_fits(t, base));
+    if (r.fit) {
+        const uint32_t u = rel_time_u32(t, base);
+        const uint32_t lo = wave_min_u32(real ? u : 0xffffffffu);
+        const uint32_t hi = wave_max_u32(real ? u : 0u);
+        r.lo = base + (int64_t)(int32_t)(lo - 0x80000000u);
+        r.hi = base + (int64_t)(int32_t)(hi - 0x80000000u);
+    } else {
+        r.lo = wave_min64(real ? t : INT64_MAX);
+        r.hi = wave_max64(real ? t : INT64_MIN);
+    }
+    return r;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* v) {

@@ -118,6 +118,17 @@ def test_fwd_wide_timestamps_take_64bit_path():
     check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
 
 
+def test_bwd_wide_timestamps_take_64bit_path():
+    w = hs.make_inputs([130, 77, 300], 2, 64, dtype="bf16", seed=12, rab=True, num_targets=16,
+                       backward=True)
+    ts = w["timestamps"].copy()
+    ts[130:207] = np.sort(np.random.default_rng(1).integers(-(1 << 40), 1 << 40, 77))
+    ts[230] += 3 << 31          # one token far in the future inside the third sequence
+    w["timestamps"] = ts
+    say("bwd wide timestamps")
+    _bwd_check(w, "bf16")
+
+
 def test_fwd_empty_and_single():
     w = hs.make_inputs([0, 1, 0, 0, 1], 2, 32, dtype="bf16", seed=3, rab=True, num_targets=1,
                        max_seqlen=8)
