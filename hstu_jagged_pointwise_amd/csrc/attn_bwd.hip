@@ -10,10 +10,14 @@
 // Two passes, no atomics on dQ/dK/dV:
 //   pass A (key-stationary): unit = (sequence, head, 128 keys), 4 wavefronts x 32 keys; visits
 //     64-query tiles.  S = Q K^T and dP = dO V^T put one key per lane, which is the B-operand
-//     layout for dV^T += dO^T P and dK^T += Q^T dS; Q and dO are staged both row-major (A operands
-//     of the first two products) and transposed with renumbered rows (A operands of the last two).
+//     layout for dV^T += dO^T P and dK^T += Q^T dS; the Q and dO tiles are read along their rows
+//     for the A operands of the first two products and with transposing LDS reads for the last
+//     two.
 //   pass B (query-stationary): unit = (sequence, head, 128 rows) exactly like the forward;
-//     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T, and the bias-table gradients.
+//     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (K^T read transposed from the K tile), and the
+//     bias-table gradients.
+// Tiles are copied from memory straight into LDS by buffer loads, double-buffered, as in the
+// forward.
 // Bias-gradient sums: when all pairs of a (wavefront, tile) fall into one bucket -- the common
 // case away from the diagonal -- each lane only adds its dS values to a running sum, and the
 // wavefront flushes that sum into an LDS histogram when the tile bucket changes; other tiles add
@@ -37,21 +41,6 @@ struct ToepEntry {
     float bucket;   // bucket of |i - j|, as a float
 };
 
-__device__ __forceinline__ void tile_store_rowmajor_and_t(bf16* rowm, int rp_pitch, bf16* trans,
-                                                          int tp_pitch, const bf16x8 (&r)[4],
-                                                          int grp, int ch) {
-    // r[kk] = row 4*grp + kk, channels 8*ch .. 8*ch+7
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        *reinterpret_cast<bf16x8*>(&rowm[(4 * grp + kk) * rp_pitch + 8 * ch]) = r[kk];
-    const int col = perm_key(4 * grp);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        bf16x4 w = {r[0][e], r[1][e], r[2][e], r[3][e]};
-        *reinterpret_cast<bf16x4*>(&trans[(8 * ch + e) * tp_pitch + col]) = w;
-    }
-}
-
 // sigmoid(S) and dL/dS * N from t = -log2(e) S and dP:  P' = t s gives SiLU(S) = -ln(2) P', and
 // dS N = dP (s + x s (1 - s)) with x s = -ln(2) P'.
 struct Grad {
@@ -71,8 +60,6 @@ __device__ __forceinline__ Grad silu_grad(float t, float dp) {
 
 template <int D>
 struct SmemA {
-    static constexpr int RP = D + 8;     // row-major pitch
-    static constexpr int TP = kTile + 8; // transposed pitch
     float wt[kNumClasses];               // -log2(e) * time bias by class
     float wp[kNumBuckets];               // -log2(e) * position bias by bucket
     float wtb[kNumBuckets];              // -log2(e) * time bias by bucket
@@ -81,10 +68,8 @@ struct SmemA {
     int64_t tq64[2][kTile];
     int64_t tqmin[2], tqmax[2];
     int fits[2];
-    alignas(16) bf16 q[2][kTile * RP];
-    bf16 dout[2][kTile * RP];
-    bf16 qt[2][D * TP];
-    bf16 doutt[2][D * TP];
+    alignas(16) bf16 q[2][kTile * D];    // swizzled tiles (tile_off)
+    bf16 dout[2][kTile * D];
 };
 
 // Bias modes of a (wavefront, tile) as in the forward:
@@ -147,9 +132,6 @@ __device__ __forceinline__ void mask_queries(f32x16 (&s)[2], f32x16 (&dp)[2], in
 
 template <int D, bool RP, bool RT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams p) {
-    constexpr int RPt = SmemA<D>::RP, TP = SmemA<D>::TP;
-    constexpr int KCH = D / 8;
-    constexpr int ITEMS = (kTile / 4) * KCH;  // (4 rows x 8 channels) items per tensor
     __shared__ __attribute__((aligned(16))) SmemA<D> sm;
 
     const WorkUnit wu = p.units[blockIdx.x];
@@ -208,31 +190,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) { dvt[db] = f32x16{}; dkt[db] = f32x16{}; }
 
-    bf16x8 qr[4], dr[4];
+    const buffer_rsrc qrs = rows_rsrc(qg, n, ld, D), drs = rows_rsrc(dog, n, p.ld_out, D);
+    const TileDma<D, kThreads> qdma(tid, ld), ddma(tid, p.ld_out);
+    const RowOperand<D> rowop(lane);
+    const TrOperand<D> trop(lane);
     int64_t tqr = 0;
-    auto load_tile = [&](int tile) {
+    // starts the copy of a query tile's Q and dO rows into buffer buf and loads its timestamps
+    auto load_tile = [&](int buf, int tile) {
         const int i0 = tile * kTile;
-        if (tid < ITEMS) {
-            const int grp = tid % (kTile / 4), ch = tid / (kTile / 4);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int i = i0 + 4 * grp + kk;
-                qr[kk] = i < n ? load_bf16x8(qg + (int64_t)i * ld + 8 * ch) : bf16x8{};
-                dr[kk] = i < n ? load_bf16x8(dog + (int64_t)i * p.ld_out + 8 * ch) : bf16x8{};
-            }
-        }
+        qdma.issue(qrs, sm.q[buf], (int)((int64_t)i0 * ld * 2));
+        ddma.issue(drs, sm.dout[buf], (int)((int64_t)i0 * p.ld_out * 2));
         if (RT && tid < kTile) {
             const int i = i0 + tid;
             tqr = i < n ? p.ts[tok0 + i] : tbase;
         }
     };
+    // the tile's small tables: query times and their range, position bias by (i - j)
     auto store_tile = [&](int buf, int tile) {
         const int i0 = tile * kTile;
-        if (tid < ITEMS) {
-            const int grp = tid % (kTile / 4), ch = tid / (kTile / 4);
-            tile_store_rowmajor_and_t(sm.q[buf], RPt, sm.qt[buf], TP, qr, grp, ch);
-            tile_store_rowmajor_and_t(sm.dout[buf], RPt, sm.doutt[buf], TP, dr, grp, ch);
-        }
         if (RT && tid < kTile) {  // exactly wavefront 0
             const bool real = i0 + tid < n;
             sm.tq64[buf][tid] = tqr;
@@ -252,9 +227,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
     };
 
     __syncthreads();
-    load_tile(tfirst);
+    load_tile(0, tfirst);
     store_tile(0, tfirst);
-    if (ntiles > 1) load_tile(tfirst + 1);
+    wait_tile_dma();
     __syncthreads();
 
     // slot of (query i0 + ii, key j) is u0 + ii - 4g with u0 below
@@ -263,17 +238,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, i0 = (tfirst + t) * kTile;
+        if (t + 1 < ntiles) load_tile(buf ^ 1, tfirst + t + 1);
         const int kind = wk0 < khi ? classify_key_tile(wk0, wk1, i0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
             f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int x = 0; x < 2 * (D / 16); ++x) {
                 const int ks = x >> 1, qb = x & 1;
-                const int off = (32 * qb + lr) * RPt + 16 * ks + 8 * g;
-                bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.q[buf][off]);
-                bf16x8 ad = *reinterpret_cast<const bf16x8*>(&sm.dout[buf][off]);
-                s[qb] = mfma32(aq, kf[ks], s[qb]);
-                dp[qb] = mfma32(ad, vf[ks], dp[qb]);
+                s[qb] = mfma32(rowop.read(sm.q[buf], qb, ks), kf[ks], s[qb]);
+                dp[qb] = mfma32(rowop.read(sm.dout[buf], qb, ks), vf[ks], dp[qb]);
             }
             sched_mfma_lds<4 * (D / 16), 4>();
             float bpos = 0.0f;
@@ -304,17 +277,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                 const bf16x8 pb = pack8(tp), db8 = pack8(td);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int off = (32 * db + lr) * TP + 16 * st + 8 * g;
-                    bf16x8 ado = *reinterpret_cast<const bf16x8*>(&sm.doutt[buf][off]);
-                    bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm.qt[buf][off]);
-                    dvt[db] = mfma32(ado, pb, dvt[db]);
-                    dkt[db] = mfma32(aq, db8, dkt[db]);
+                    dvt[db] = mfma32(trop.read(sm.dout[buf], st, db), pb, dvt[db]);
+                    dkt[db] = mfma32(trop.read(sm.q[buf], st, db), db8, dkt[db]);
                 }
             }
-            sched_mfma_lds<8 * (D / 32), 4>();
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tfirst + t + 1);
-        if (t + 2 < ntiles) load_tile(tfirst + t + 2);
+        wait_tile_dma();
         __syncthreads();
     }
 
@@ -344,8 +313,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
 
 template <int D>
 struct SmemB {
-    static constexpr int RP = D + 8;
-    static constexpr int TP = kTile + 8;
     float wt[kNumClasses];
     float wp[kNumBuckets];
     float wtb[kNumBuckets];
@@ -358,9 +325,8 @@ struct SmemB {
     float hct[kNumClasses];   // time-bias gradient sums of tiles spanning many buckets, by class
     float hbp[kNumBuckets];   // position-bias gradient sums, by bucket
     float hbt[kNumBuckets];   // time-bias gradient sums of one- or two-bucket tiles, by bucket
-    alignas(16) bf16 k[2][kTile * RP];
-    bf16 v[2][kTile * RP];
-    bf16 kt[2][D * TP];
+    alignas(16) bf16 k[2][kTile * D];    // swizzled tiles (tile_off)
+    bf16 v[2][kTile * D];
 };
 
 // Per-element part of pass B: dS (times N) into dp.  Bias modes as in pass A.
@@ -487,9 +453,6 @@ struct Run {
 
 template <int D, bool RP, bool RT, bool GP, bool GT>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p) {
-    constexpr int RPt = SmemB<D>::RP, TP = SmemB<D>::TP;
-    constexpr int KCH = D / 8;
-    constexpr int ITEMS = (kTile / 4) * KCH;
     __shared__ __attribute__((aligned(16))) SmemB<D> sm;
 
     const WorkUnit wu = p.units[blockIdx.x];
@@ -561,33 +524,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
         }
     };
 
-    bf16x8 kr[4], vr[4];
+    const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
+    const TileDma<D, kThreads> dma(tid, ld);
+    const RowOperand<D> rowop(lane);
+    const TrOperand<D> trop(lane);
     int64_t tkr = 0;
-    auto load_tile = [&](int tile) {
+    // starts the copy of a key tile's K and V rows into buffer buf and loads its timestamps
+    auto load_tile = [&](int buf, int tile) {
         const int j0 = tile * kTile;
-        if (tid < ITEMS) {
-            const int grp = tid % (kTile / 4), ch = tid / (kTile / 4);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int jj = j0 + 4 * grp + kk;
-                kr[kk] = jj < n ? load_bf16x8(kg + (int64_t)jj * ld + 8 * ch) : bf16x8{};
-                vr[kk] = jj < n ? load_bf16x8(vg + (int64_t)jj * ld + 8 * ch) : bf16x8{};
-            }
-        }
+        const int row_bytes = (int)((int64_t)j0 * ld * 2);
+        dma.issue(krs, sm.k[buf], row_bytes);
+        dma.issue(vrs, sm.v[buf], row_bytes);
         if (RT && tid < kTile) {
             const int jj = j0 + tid;
             tkr = jj < n ? p.ts[tok0 + jj] : tbase;
         }
     };
+    // the tile's small tables: key times and their range, position bias and bucket by (i - j)
     auto store_tile = [&](int buf, int tile) {
         const int j0 = tile * kTile;
-        if (tid < ITEMS) {
-            const int grp = tid % (kTile / 4), ch = tid / (kTile / 4);
-            tile_store_rowmajor_and_t(sm.k[buf], RPt, sm.kt[buf], TP, kr, grp, ch);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                *reinterpret_cast<bf16x8*>(&sm.v[buf][(4 * grp + kk) * RPt + 8 * ch]) = vr[kk];
-        }
         if (RT && tid < kTile) {  // exactly wavefront 0
             const bool real = j0 + tid < n;
             sm.tk64[buf][tid] = tkr;
@@ -609,9 +564,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
     };
 
     __syncthreads();
-    load_tile(ktl.tile(0));
+    load_tile(0, ktl.tile(0));
     store_tile(0, ktl.tile(0));
-    if (ntiles > 1) load_tile(ktl.tile(1));
+    wait_tile_dma();
     __syncthreads();
 
     const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1);
@@ -619,17 +574,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, j0 = ktl.tile(t) * kTile;
+        if (t + 1 < ntiles) load_tile(buf ^ 1, ktl.tile(t + 1));
         const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
             f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int x = 0; x < 2 * (D / 16); ++x) {
                 const int ks = x >> 1, kb = x & 1;
-                const int off = (32 * kb + lr) * RPt + 16 * ks + 8 * g;
-                bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.k[buf][off]);
-                bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.v[buf][off]);
-                s[kb] = mfma32(ak, qf[ks], s[kb]);
-                dp[kb] = mfma32(av, dof[ks], dp[kb]);
+                s[kb] = mfma32(rowop.read(sm.k[buf], kb, ks), qf[ks], s[kb]);
+                dp[kb] = mfma32(rowop.read(sm.v[buf], kb, ks), dof[ks], dp[kb]);
             }
             sched_mfma_lds<4 * (D / 16), 4>();
             float bpos = 0.0f;
@@ -680,17 +633,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p)
                 for (int x = 0; x < 8; ++x) td[x] = dp[st >> 1][8 * (st & 1) + x];
                 const bf16x8 db8 = pack8(td);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    bf16x8 ak = *reinterpret_cast<const bf16x8*>(
-                        &sm.kt[buf][(32 * db + lr) * TP + 16 * st + 8 * g]);
-                    dqt[db] = mfma32(ak, db8, dqt[db]);
-                }
+                for (int db = 0; db < D / 32; ++db) dqt[db] = mfma32(trop.read(sm.k[buf], st, db), db8, dqt[db]);
             }
-            sched_mfma_lds<4 * (D / 32), 4>();
         }
         if (GP && t > 0) fold_diagonals(buf ^ 1, ktl.tile(t - 1));
         if (t + 1 < ntiles) store_tile(buf ^ 1, ktl.tile(t + 1));
-        if (t + 2 < ntiles) load_tile(ktl.tile(t + 2));
+        wait_tile_dma();
         __syncthreads();
     }
     if (GP && ntiles > 0) fold_diagonals((ntiles - 1) & 1, ktl.tile(ntiles - 1));

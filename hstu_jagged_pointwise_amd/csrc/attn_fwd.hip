@@ -8,17 +8,18 @@
 // rows.  Key tiles of 64 keys are visited in the order given by key_tiles_for_rows(): tiles that
 // the composite causal/context/candidate mask leaves empty for the whole unit are never loaded,
 // and a wavefront skips the arithmetic of tiles that are empty for its own rows (page 2, HSTU
-// acceleration operator: composite-mask skipping).  Tiles are staged global -> registers -> LDS
-// with two LDS buffers, so loading tile t+1 overlaps the matrix work on tile t (page 2: move one
-// block while computing another).
+// acceleration operator: composite-mask skipping).  K and V tiles are copied from memory straight
+// into LDS by buffer loads (rows past the sequence end read as zero), into two LDS buffers, so
+// the copy of tile t+1 runs while tile t is computed (page 2: move one block while computing
+// another).
 //
 // Per tile and wavefront:
 //   S^T (64 keys x 32 rows) = K . Q^T        2 x (D/16) v_mfma_f32_32x32x16_bf16
 //   P = SiLU(alpha S + bias), masked          fp32 in registers
 //   O^T (D x 32 rows) += V^T . P^T           (D/32) x 4 v_mfma_f32_32x32x16_bf16
 // The C layout of S^T gives each lane one query row and 16 keys per 32-key block, which is the
-// B-operand layout P^T needs once keys are renumbered (perm_key) -- V is stored transposed with
-// the same renumbering, so P never leaves registers.  Scores are carried as -log2(e) * S (folded
+// B-operand layout P^T needs; the matching V^T operand is read from the row-major V tile with
+// transposing LDS reads, so P never leaves registers.  Scores are carried as -log2(e) * S (folded
 // into alpha and the staged bias tables), so SiLU costs one fma, exp2, add, rcp and mul; the
 // remaining factor -ln(2) / N is applied once to O.  Whenever every pair of a (wavefront, tile)
 // falls into one position bucket (or one time bucket), that bias is a single scalar for the tile
@@ -36,8 +37,6 @@ constexpr int kToep = kRows + kBN - 1;  // 191 distinct i - j per (unit, tile)
 
 template <int D>
 struct FwdSmem {
-    static constexpr int KP = D + 8;    // K row pitch (elements)
-    static constexpr int VP = kBN + 8;  // V^T row pitch (elements)
     // Small tables first, so their offsets fit the 16-bit LDS instruction offset field.  Bias
     // values are stored multiplied by -log2(e) (see silu_scaled).
     float wt[kNumClasses];              // time bias by bucket class
@@ -48,8 +47,8 @@ struct FwdSmem {
     int64_t tk64[2][kBN];               // key timestamps (fallback)
     int64_t tkmin[2], tkmax[2];         // time range of the tile's real keys
     int fits[2];
-    alignas(16) bf16 k[2][kBN * KP];
-    bf16 vt[2][D * VP];
+    alignas(16) bf16 k[2][kBN * D];     // swizzled tiles (tile_off)
+    bf16 v[2][kBN * D];
 };
 
 // Bias handling of one (wavefront, tile), decided once per tile from the distance ranges:
@@ -108,11 +107,6 @@ __device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int g, int j0, int lim
 
 template <int D, bool RP, bool RT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
-    constexpr int KP = FwdSmem<D>::KP, VP = FwdSmem<D>::VP;
-    constexpr int KCH = D / 8;                       // 16-byte chunks per row
-    constexpr int KLOADS = kBN * KCH / kThreads;     // K chunks per thread
-    constexpr int VITEMS = (kBN / 4) * KCH;          // V items of 4 keys x 8 channels
-    static_assert(KLOADS >= 1, "tile too small");
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
     const WorkUnit wu = p.units[blockIdx.x];
@@ -171,47 +165,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
-    bf16x8 kr[KLOADS];
-    bf16x8 vr[4];
+    const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
+    const TileDma<D, kThreads> dma(tid, ld);
+    const RowOperand<D> kop(lane);
+    const TrOperand<D> vop(lane);
     int64_t tkr = 0;
 
-    auto load_tile = [&](int tile) {
+    // starts the copy of a tile's K and V rows into buffer buf and loads its timestamps
+    auto load_tile = [&](int buf, int tile) {
         const int j0 = tile * kBN;
-#pragma unroll
-        for (int u = 0; u < KLOADS; ++u) {
-            const int id = tid + kThreads * u, row = id / KCH, ch = id % KCH, j = j0 + row;
-            kr[u] = j < n ? load_bf16x8(kg + (int64_t)j * ld + 8 * ch) : bf16x8{};
-        }
-        if (tid < VITEMS) {
-            const int kgrp = tid % (kBN / 4), ch = tid / (kBN / 4);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int j = j0 + 4 * kgrp + kk;
-                vr[kk] = j < n ? load_bf16x8(vg + (int64_t)j * ld + 8 * ch) : bf16x8{};
-            }
-        }
+        const int row_bytes = (int)((int64_t)j0 * ld * 2);
+        dma.issue(krs, sm.k[buf], row_bytes);
+        dma.issue(vrs, sm.v[buf], row_bytes);
         if (RT && tid < kBN) {
             const int j = j0 + tid;
             tkr = j < n ? p.ts[tok0 + j] : tbase;
         }
     };
 
+    // the tile's small tables: key times and their range, position bias by (i - j)
     auto store_tile = [&](int buf, int tile) {
         const int j0 = tile * kBN;
-#pragma unroll
-        for (int u = 0; u < KLOADS; ++u) {
-            const int id = tid + kThreads * u, row = id / KCH, ch = id % KCH;
-            *reinterpret_cast<bf16x8*>(&sm.k[buf][row * KP + 8 * ch]) = kr[u];
-        }
-        if (tid < VITEMS) {
-            const int kgrp = tid % (kBN / 4), ch = tid / (kBN / 4);
-            const int col = perm_key(4 * kgrp);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                bf16x4 w = {vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
-                *reinterpret_cast<bf16x4*>(&sm.vt[buf][(8 * ch + e) * VP + col]) = w;
-            }
-        }
         if (RT && tid < kBN) {  // exactly wavefront 0
             const bool real = j0 + tid < n;
             sm.tk64[buf][tid] = tkr;
@@ -231,9 +205,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     };
 
     __syncthreads();  // bias tables ready
-    load_tile(kt.tile(0));
+    load_tile(0, kt.tile(0));
     store_tile(0, kt.tile(0));
-    if (ntiles > 1) load_tile(kt.tile(1));
+    wait_tile_dma();
     __syncthreads();
 
     // slot of (row i, key j0 + jj) in rp is u0 + jj - 4g; see store_tile
@@ -242,15 +216,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, j0 = kt.tile(t) * kBN;
+        if (t + 1 < ntiles) load_tile(buf ^ 1, kt.tile(t + 1));
         const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
             f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
             for (int x = 0; x < 2 * (D / 16); ++x) {
                 const int ks = x >> 1, kb = x & 1;
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &sm.k[buf][(32 * kb + lr) * KP + 16 * ks + 8 * g]);
-                s[kb] = mfma32(a, qf[ks], s[kb]);
+                s[kb] = mfma32(kop.read(sm.k[buf], kb, ks), qf[ks], s[kb]);
             }
             sched_mfma_lds<2 * (D / 16), 4>();
             // bias mode of this (wavefront, tile): one bucket for the whole tile when possible
@@ -278,16 +251,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                 for (int x = 0; x < 8; ++x) tmp[x] = s[st >> 1][8 * (st & 1) + x];
                 const bf16x8 pb = pack8(tmp);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        &sm.vt[buf][(32 * db + lr) * VP + 16 * st + 8 * g]);
-                    o[db] = mfma32(a, pb, o[db]);
-                }
+                for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vop.read(sm.v[buf], st, db), pb, o[db]);
             }
-            sched_mfma_lds<4 * (D / 32), 4>();
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, kt.tile(t + 1));
-        if (t + 2 < ntiles) load_tile(kt.tile(t + 2));
+        wait_tile_dma();
         __syncthreads();
     }
 

@@ -271,11 +271,140 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Position of key k (0..63) inside a transposed tile row: bits 2 and 3 of k are swapped so that a
-// lane's eight P^T operands (keys 16s + 8(t/4) + 4g + t%4) are contiguous (16s + 8g + t).
-__device__ __forceinline__ int perm_key(int k) {
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// ---- LDS tiles --------------------------------------------------------------------------------
+// A tile is kKeyTile (64) rows of D bf16, row-major without padding.  Row r is D / 8 chunks of 16
+// bytes; logical chunk c sits at chunk position c ^ tile_swz(r).  With 64 LDS banks of 4 bytes
+// this XOR pattern keeps three accesses free of bank conflicts: the 16-byte DMA writes of
+// consecutive chunks, 16-byte reads of one chunk from 16 consecutive rows (MFMA operands with
+// tile rows on lanes) and the transposing 8-byte reads of 4 rows x 64 bytes per 32 lanes (MFMA
+// operands with tile columns on lanes).  tile_swz depends on bits 0..3 of r only.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+    static_assert(D == 32 || D == 64 || D == 128, "head dim");
+    if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else if constexpr (D == 64) return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    else return (r >> 2) & 3;
 }
+// Element offset of (row r, column col) in a tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {
+    return r * D + (((col >> 3) ^ tile_swz<D>(r)) << 3) + (col & 7);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource (device pass); the host pass of a kernel only needs a placeholder of the type,
+// since kernel bodies are compiled for the device only.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buffer_rsrc;
+#else
+struct buffer_rsrc {
+    uint32_t w[4];
+};
+#endif
+
+// Transposing LDS read: within each group of 16 lanes, lane 4e + m supplies the address of 4
+// consecutive bf16 of one row, and lane i receives element i % 4 of lane 4e + i / 4 as its
+// element e (e = 0..3).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+#else
+    return bf16x4{};
+#endif
+}
+
+// Per-lane element offsets of an MFMA A operand taken transposed from a tile: A (32 x 16) has
+// A[m][k] = T[16 st + key(k)][m0 + m], where the k-slot order key(8g + t) = 8 (t / 4) + 4g + t % 4
+// matches the C layout of a 32 x 32 MFMA result (a lane's 4r + c entries are rows 8r + 4g + c).
+// Offsets are for st = 0 and one 32-column block m0; add 16 * st * D for slice st.
+template <int D>
+struct TrOperand {
+    int off[D / 32][2];
+    __device__ __forceinline__ explicit TrOperand(int lane) {
+        const int s = lane & 15, q = (lane >> 4) & 1, rr = 4 * (lane >> 5) + (s >> 2);
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) off[mb][h] = tile_off<D>(rr + 8 * h, 32 * mb + 16 * q + 4 * (s & 3));
+    }
+    __device__ __forceinline__ bf16x8 read(const bf16* tile, int st, int mb) const {
+        const bf16x4 lo = lds_read_tr4(tile + 16 * st * D + off[mb][0]);
+        const bf16x4 hi = lds_read_tr4(tile + 16 * st * D + off[mb][1]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+// Per-lane element offsets of an MFMA A operand read along tile rows: lane (lr = l % 32, g = l / 32)
+// takes row 32 blk + lr, columns 16 ks + 8g .. + 7.  Add 32 * blk * D for row block blk.
+template <int D>
+struct RowOperand {
+    int off[D / 16];
+    __device__ __forceinline__ explicit RowOperand(int lane) {
+        const int lr = lane & 31, g = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) off[ks] = tile_off<D>(lr, 16 * ks + 8 * g);
+    }
+    __device__ __forceinline__ bf16x8 read(const bf16* tile, int blk, int ks) const {
+        return *reinterpret_cast<const bf16x8*>(tile + 32 * blk * D + off[ks]);
+    }
+};
+
+// Buffer resource over rows [0, n) of a bf16 slice with row stride ld (elements) starting at base:
+// buffer loads past the last row return zeros.  The host guarantees the byte size fits 31 bits.
+__device__ __forceinline__ buffer_rsrc rows_rsrc(const bf16* base, int n, int64_t ld, int width) {
+    const int64_t bytes = n > 0 ? ((int64_t)(n - 1) * ld + width) * 2 : 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+#else
+    (void)base;
+    (void)bytes;
+    return buffer_rsrc{};
+#endif
+}
+
+// Copies tile rows [r0, r0 + 64) of one slice from memory straight into an LDS tile (buffer
+// loads with the LDS-write option, 16 bytes per lane): instruction u of wavefront w fills the
+// 1 KB block u * (THREADS / 64) + w of the tile, lane l its chunk position l, so each lane reads
+// the logical chunk that the swizzle puts there.  The copy is asynchronous: it is complete once
+// the issuing wavefront has waited for vmcnt(0).
+template <int D, int THREADS>
+struct TileDma {
+    static constexpr int C = D / 8;
+    static constexpr int N = kKeyTile * C / THREADS;
+    static_assert(N >= 1 && kKeyTile * C % THREADS == 0, "tile shape");
+    int off[N];  // byte offset of this lane's chunk, relative to tile row 0
+    int wave;
+    __device__ __forceinline__ TileDma(int tid, int64_t ld) {
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int pos = (u * (THREADS / 64) + wave) * 64 + lane;
+            const int row = pos / C, c = (pos % C) ^ tile_swz<D>(row);
+            off[u] = (int)(((int64_t)row * ld + 8 * c) * 2);
+        }
+    }
+    // row_bytes = r0 * ld * 2
+    __device__ __forceinline__ void issue(buffer_rsrc rs, bf16* tile, int row_bytes) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_void*)(tile + (u * (THREADS / 64) + wave) * 512), 16, off[u] + row_bytes, 0, 0, 0);
+#else
+        (void)rs;
+        (void)tile;
+        (void)row_bytes;
+#endif
+    }
+};
+
+__device__ __forceinline__ void wait_tile_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Scheduling hint for a block of N MFMAs, each fed by one LDS read: issue LA reads first, then
 // alternate one MFMA and one read, so each read has LA matrix instructions to land.

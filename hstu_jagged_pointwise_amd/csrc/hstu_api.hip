@@ -40,6 +40,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The bf16 kernels address one sequence's rows of a tensor with 32-bit byte offsets (tiles of 64
+// rows may run past the last row).
+bool rows_addressable(int32_t max_seqlen, int64_t token_stride) {
+    return (int64_t(max_seqlen) + 64) * token_stride * 2 < (int64_t(1) << 31);
+}
+
 hstu_status_t check_args(const hstu_attn_args_t* a) {
     if (!a) return HSTU_ERR_NULL_ARG;
     if (a->dtype != HSTU_F32 && a->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
@@ -52,6 +58,8 @@ hstu_status_t check_args(const hstu_attn_args_t* a) {
     if (a->qkv_token_stride != 0 && a->qkv_token_stride < hd) return HSTU_ERR_BAD_SHAPE;
     if (a->qkv_token_stride % 8 != 0) return HSTU_ERR_MISALIGNED;
     if (a->rab_ts && !a->timestamps && a->total_tokens > 0) return HSTU_ERR_NULL_ARG;
+    if (a->dtype == HSTU_BF16 && !rows_addressable(a->max_seqlen, a->qkv_token_stride > hd ? a->qkv_token_stride : hd))
+        return HSTU_ERR_UNSUPPORTED;
     return HSTU_OK;
 }
 
@@ -389,6 +397,8 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     if (args->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
     if (!x || !w1 || !w2 || !y || !ws) return HSTU_ERR_NULL_ARG;
     if (d_model < 128 || d_model % 128 != 0) return HSTU_ERR_UNSUPPORTED;
+    if (!rows_addressable(args->max_seqlen, 4 * int64_t(args->num_heads) * args->head_dim))
+        return HSTU_ERR_UNSUPPORTED;
     if ((args->num_heads * args->head_dim) % 64 != 0) return HSTU_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y) || !aligned16(ws))
         return HSTU_ERR_MISALIGNED;

@@ -30,7 +30,9 @@
  *     token_stride = num_heads * head_dim unless args->qkv_token_stride says otherwise (q, k, v
  *     and u only; outputs are always dense).  Element type is args->dtype.
  *   - Device pointers must be 16-byte aligned and token strides a multiple of 8 elements
- *     (HSTU_ERR_MISALIGNED otherwise).
+ *     (HSTU_ERR_MISALIGNED otherwise).  For bf16, (max_seqlen + 64) * token_stride * 2 bytes must
+ *     stay below 2^31 (HSTU_ERR_UNSUPPORTED otherwise): one sequence's rows of one tensor are
+ *     addressed with 32-bit offsets.
  *   - Calls validate on the host, enqueue on `stream` (a hipStream_t; NULL = default stream) and
  *     return without waiting.  Nothing is allocated during fwd/bwd/layer calls; scratch memory is
  *     the caller's `ws` of at least hstu_workspace_bytes() bytes.  Kernel faults surface at the
