@@ -452,7 +452,7 @@ struct Run {
 };
 
 template <int D, bool RP, bool RT, bool GP, bool GT>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) SmemB<D> sm;
 
     const WorkUnit wu = p.units[blockIdx.x];
