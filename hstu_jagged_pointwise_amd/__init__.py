@@ -48,6 +48,8 @@ class HstuPlanInfo(ctypes.Structure):
         ("fwd_tiles", ctypes.c_int64),
         ("fwd_row_block", ctypes.c_int64),
         ("bwd_key_block", ctypes.c_int64),
+        ("fwd_items", ctypes.c_int64),
+        ("fwd_split_blocks", ctypes.c_int64),
     ]
 
 
@@ -179,10 +181,11 @@ def hstu_plan_info(plan: Plan) -> dict:
 
 
 def hstu_plan_units(plan: Plan, op: int) -> np.ndarray:
+    """op 0 / 1: (count, 4) work units; op 2: (count, 8) bf16 forward items."""
     lib = load_library()
     count = ctypes.c_int64()
     _check(lib.hstu_plan_units(ctypes.c_void_p(plan.handle), int(op), None, 0, ctypes.byref(count)))
-    out = np.zeros((count.value, 4), np.int32)
+    out = np.zeros((count.value, 8 if op == 2 else 4), np.int32)
     _check(lib.hstu_plan_units(ctypes.c_void_p(plan.handle), int(op),
                                out.ctypes.data_as(ctypes.c_void_p), count.value,
                                ctypes.byref(count)))

@@ -109,7 +109,7 @@ template <int D, bool RP, bool RT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
-    const WorkUnit wu = p.units[blockIdx.x];
+    const FwdItem wu = p.items[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
@@ -131,8 +131,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const int64_t tbase = RT ? p.ts[tok0] : 0;
 
     const int rhi = imin(r0 + kRows, n);
-    const KeyTiles kt = key_tiles_for_rows(r0, rhi, nc, nh);
-    const int ntiles = kt.count();
+    const KeyTiles kl = key_tiles_for_rows(r0, rhi, nc, nh);
+    const int tbeg = wu.t0, ntiles = wu.t1 - wu.t0;  // this item's part of the tile list
+    auto tile_at = [&](int t) { return kl.tile(tbeg + t); };
 
     // this wavefront's rows and this lane's row
     const int wlo = r0 + kWaveRows * wave, whi = imin(wlo + kWaveRows, rhi);
@@ -205,8 +206,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     };
 
     __syncthreads();  // bias tables ready
-    load_tile(0, kt.tile(0));
-    store_tile(0, kt.tile(0));
+    load_tile(0, tile_at(0));
+    store_tile(0, tile_at(0));
     wait_tile_dma();
     __syncthreads();
 
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1, j0 = kt.tile(t) * kBN;
-        if (t + 1 < ntiles) load_tile(buf ^ 1, kt.tile(t + 1));
+        const int buf = t & 1, j0 = tile_at(t) * kBN;
+        if (t + 1 < ntiles) load_tile(buf ^ 1, tile_at(t + 1));
         const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
             f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -254,12 +255,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                 for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vop.read(sm.v[buf], st, db), pb, o[db]);
             }
         }
-        if (t + 1 < ntiles) store_tile(buf ^ 1, kt.tile(t + 1));
+        if (t + 1 < ntiles) store_tile(buf ^ 1, tile_at(t + 1));
         wait_tile_dma();
         __syncthreads();
     }
 
-    if (row_ok) {
+    if (row_ok && wu.part >= 0) {  // one piece of a split row block: fp32 partial sums
+        float* pg = p.part + ((size_t)wu.part * kRows + (i - r0)) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<f32x4*>(pg + 32 * db + 8 * r + 4 * g) =
+                    f32x4{o[db][4 * r], o[db][4 * r + 1], o[db][4 * r + 2], o[db][4 * r + 3]};
+    } else if (row_ok) {
         bf16* og = static_cast<bf16*>(p.out) + (tok0 + i) * p.ld_out + h * D;
         const float oscale = -kLn2 * p.inv_n;
 #pragma unroll
@@ -333,9 +342,39 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(const AttnParams p) {
     }
 }
 
+// Sums the partial slots of each split row block and writes its output rows (scaled like the
+// unsplit rows).  Workgroup (x, y) takes rows [y * kFixRows, + kFixRows) of split block x; each
+// thread owns 4 columns of one row.
+constexpr int kFixRows = 4 * kThreads / 128;
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_fix_kernel(const AttnParams p) {
+    constexpr int RPT = kThreads / (D / 4);  // rows per pass of the workgroup
+    const FixItem f = p.fix[blockIdx.x];
+    const SeqInfo si = p.seqs[f.seq];
+    const int rows = imin(kRows, si.n - f.row0);
+    const float oscale = -kLn2 * p.inv_n;
+    const int c = 4 * (threadIdx.x % (D / 4));
+#pragma unroll
+    for (int pass = 0; pass < kFixRows / RPT + (kFixRows % RPT != 0); ++pass) {
+        const int r = blockIdx.y * kFixRows + pass * RPT + threadIdx.x / (D / 4);
+        if (r >= rows || r >= (int)(blockIdx.y + 1) * kFixRows) continue;
+        f32x4 acc = f32x4{};
+        for (int k = 0; k < f.nparts; ++k)
+            acc += *reinterpret_cast<const f32x4*>(p.part + ((size_t)(f.part0 + k) * kRows + r) * D + c);
+        bf16x4 w;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = (bf16)(acc[x] * oscale);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(p.out) + (si.start + f.row0 + r) * p.ld_out +
+                                   f.head * D + c) = w;
+    }
+}
+
 template <int D, bool RP, bool RT>
 hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT>), dim3(p.num_items), dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.num_fix == 0) return e;
+    hipLaunchKernelGGL((fwd_fix_kernel<D>), dim3(p.num_fix, kRows / kFixRows), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -351,7 +390,8 @@ hipError_t launch_bf16_d(const AttnParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s) {
-    if (p.num_units == 0) return hipSuccess;
+    if (p.num_items == 0) return hipSuccess;
+    if (p.num_fix > 0 && p.part == nullptr) return hipErrorInvalidValue;
     switch (p.head_dim) {
         case 32: return launch_bf16_d<32>(p, s);
         case 64: return launch_bf16_d<64>(p, s);

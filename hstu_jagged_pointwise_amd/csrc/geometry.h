@@ -35,6 +35,17 @@ struct WorkUnit {
     int32_t seq, head, row0, cost;
 };
 
+// A forward work item: key tiles [t0, t1) of the list key_tiles_for_rows() gives for one row
+// block.  part < 0: the item covers the whole list and writes the output rows itself; otherwise
+// it writes its fp32 partial sums to partial slot `part`, and a FixItem adds the slots up.
+struct FwdItem {
+    int32_t seq, head, row0, cost, t0, t1, part, pad;
+};
+// A row block whose key tiles were split over items with slots [part0, part0 + nparts).
+struct FixItem {
+    int32_t seq, head, row0, part0, nparts, pad0, pad1, pad2;
+};
+
 HSTU_HD int imax(int a, int b) { return a > b ? a : b; }
 HSTU_HD int imin(int a, int b) { return a < b ? a : b; }
 HSTU_HD int cdiv(int a, int b) { return (a + b - 1) / b; }

@@ -15,6 +15,8 @@
 
 using hstu::SeqInfo;
 using hstu::WorkUnit;
+using hstu::FwdItem;
+using hstu::FixItem;
 
 struct hstu_plan {
     int device = -1;
@@ -26,10 +28,15 @@ struct hstu_plan {
     int64_t fwd_tiles = 0;
     std::vector<SeqInfo> seqs;
     std::vector<WorkUnit> fwd, bwd;
+    std::vector<FwdItem> items;  // bf16 forward launch (fwd, the longest split by key tiles)
+    std::vector<FixItem> fix;
+    int32_t parts = 0;           // partial slots the split items write
     void* dbuf = nullptr;
     const SeqInfo* d_seqs = nullptr;
     const WorkUnit* d_fwd = nullptr;
     const WorkUnit* d_bwd = nullptr;
+    const FwdItem* d_items = nullptr;
+    const FixItem* d_fix = nullptr;
 };
 
 namespace {
@@ -90,11 +97,52 @@ void sort_longest_first(std::vector<WorkUnit>& u) {
                      [](const WorkUnit& a, const WorkUnit& b) { return a.cost > b.cost; });
 }
 
+// Forward work items.  The forward's time is at least that of its longest row block, whose key
+// tiles run one after another in one workgroup; when a row block costs more than twice the
+// average load of a workgroup slot (two per compute unit), its key-tile list is cut into
+// near-equal pieces of at most that size (but no fewer than kMinSplit tiles) that run as separate
+// items.  (Below twice the average, the fix-up pass and the pieces' extra prologues cost more
+// than the shorter critical path saves.)
+// Because the output is a plain sum over keys (no softmax normalisation), the pieces' fp32
+// partial outputs just add up; a fix-up pass sums them.  Items are ordered longest first.
+constexpr int kMinSplit = 4;
+void build_fwd_items(hstu_plan_t* plan, int compute_units) {
+    int64_t total = 0;
+    for (const WorkUnit& u : plan->fwd) total += u.cost;
+    const int64_t slots = 2 * int64_t(compute_units);
+    const int cap = (int)std::max<int64_t>(kMinSplit, 2 * ((total + slots - 1) / slots));
+    plan->items.clear();
+    plan->fix.clear();
+    plan->parts = 0;
+    for (const WorkUnit& u : plan->fwd) {
+        if (u.cost <= cap) {
+            plan->items.push_back(FwdItem{u.seq, u.head, u.row0, u.cost, 0, u.cost, -1, 0});
+            continue;
+        }
+        const int k = (u.cost + cap - 1) / cap;
+        plan->fix.push_back(FixItem{u.seq, u.head, u.row0, plan->parts, k, 0, 0, 0});
+        for (int c = 0; c < k; ++c) {
+            const int t0 = (int)((int64_t)c * u.cost / k), t1 = (int)((int64_t)(c + 1) * u.cost / k);
+            plan->items.push_back(FwdItem{u.seq, u.head, u.row0, t1 - t0, t0, t1, plan->parts++, 0});
+        }
+    }
+    std::stable_sort(plan->items.begin(), plan->items.end(),
+                     [](const FwdItem& a, const FwdItem& b) { return a.cost > b.cost; });
+}
+
+size_t part_bytes(const hstu_plan_t* plan) {
+    return align_up(size_t(plan->parts) * plan->fwd_rows * plan->shape.head_dim * 4, 256);
+}
+
 hstu::AttnParams base_params(const hstu_plan_t* plan, const hstu_attn_args_t* a) {
     hstu::AttnParams p{};
     p.seqs = plan->d_seqs;
     p.units = plan->d_fwd;
     p.num_units = (int32_t)plan->fwd.size();
+    p.items = plan->d_items;
+    p.num_items = (int32_t)plan->items.size();
+    p.fix = plan->d_fix;
+    p.num_fix = (int32_t)plan->fix.size();
     p.heads = a->num_heads;
     p.head_dim = a->head_dim;
     int64_t hd = int64_t(a->num_heads) * a->head_dim;
@@ -193,17 +241,32 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
     sort_longest_first(plan->fwd);
     sort_longest_first(plan->bwd);
 
-    if (!(flags & HSTU_PLAN_HOST_ONLY)) {
+    const bool host_only = (flags & HSTU_PLAN_HOST_ONLY) != 0;
+    int compute_units = 256;
+    if (!host_only) {
+        if (hipGetDevice(&plan->device) != hipSuccess ||
+            hipDeviceGetAttribute(&compute_units, hipDeviceAttributeMultiprocessorCount,
+                                  plan->device) != hipSuccess) {
+            delete plan;
+            return HSTU_ERR_HIP;
+        }
+    }
+    if (bf16) build_fwd_items(plan, compute_units);
+
+    if (!host_only) {
         size_t nb = sizeof(SeqInfo) * plan->seqs.size();
         size_t nf = sizeof(WorkUnit) * plan->fwd.size();
         size_t nk = sizeof(WorkUnit) * plan->bwd.size();
-        size_t total = std::max<size_t>(nb + nf + nk, 16);
+        size_t ni = sizeof(FwdItem) * plan->items.size();
+        size_t nx = sizeof(FixItem) * plan->fix.size();
+        size_t total = std::max<size_t>(nb + nf + nk + ni + nx, 16);
         std::vector<char> host(total);
         if (nb) std::memcpy(host.data(), plan->seqs.data(), nb);
         if (nf) std::memcpy(host.data() + nb, plan->fwd.data(), nf);
         if (nk) std::memcpy(host.data() + nb + nf, plan->bwd.data(), nk);
-        if (hipGetDevice(&plan->device) != hipSuccess ||
-            hipMalloc(&plan->dbuf, total) != hipSuccess) {
+        if (ni) std::memcpy(host.data() + nb + nf + nk, plan->items.data(), ni);
+        if (nx) std::memcpy(host.data() + nb + nf + nk + ni, plan->fix.data(), nx);
+        if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
             delete plan;
             return HSTU_ERR_HIP;
         }
@@ -216,6 +279,8 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
         plan->d_seqs = reinterpret_cast<const SeqInfo*>(base);
         plan->d_fwd = reinterpret_cast<const WorkUnit*>(base + nb);
         plan->d_bwd = reinterpret_cast<const WorkUnit*>(base + nb + nf);
+        plan->d_items = reinterpret_cast<const FwdItem*>(base + nb + nf + nk);
+        plan->d_fix = reinterpret_cast<const FixItem*>(base + nb + nf + nk + ni);
         plan->on_device = true;
     }
     *out = plan;
@@ -236,13 +301,27 @@ hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info) {
     info->fwd_tiles = plan->fwd_tiles;
     info->fwd_row_block = plan->fwd_rows;
     info->bwd_key_block = plan->bwd_keys;
+    info->fwd_items = plan->shape.dtype == HSTU_BF16 ? (int64_t)plan->items.size()
+                                                     : (int64_t)plan->fwd.size();
+    info->fwd_split_blocks = (int64_t)plan->fix.size();
     return HSTU_OK;
 }
 
 hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* units, int64_t cap,
                               int64_t* count) {
     if (!plan || !count) return HSTU_ERR_NULL_ARG;
-    if (op != 0 && op != 1) return HSTU_ERR_BAD_SHAPE;
+    if (op != 0 && op != 1 && op != 2) return HSTU_ERR_BAD_SHAPE;
+    if (op == 2) {
+        *count = (int64_t)plan->items.size();
+        if (cap > 0 && !units) return HSTU_ERR_NULL_ARG;
+        int64_t m = std::min<int64_t>(cap, (int64_t)plan->items.size());
+        for (int64_t i = 0; i < m; ++i) {
+            const FwdItem& it = plan->items[i];
+            const int32_t rec[8] = {it.seq, it.head, it.row0, it.cost, it.t0, it.t1, it.part, 0};
+            std::memcpy(units + 8 * i, rec, sizeof(rec));
+        }
+        return HSTU_OK;
+    }
     const std::vector<WorkUnit>& u = op == 0 ? plan->fwd : plan->bwd;
     *count = (int64_t)u.size();
     if (cap > 0 && !units) return HSTU_ERR_NULL_ARG;
@@ -261,10 +340,11 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
     const hstu_attn_args_t& a = plan->shape;
     size_t thd = size_t(a.total_tokens) * a.num_heads * a.head_dim;
     switch (op) {
-        case 1: return align_up(thd * elem_size(a.dtype), 256);
+        case 0: return part_bytes(plan);
+        case 1: return align_up(thd * elem_size(a.dtype), 256) + part_bytes(plan);
         case 3: {
             (void)d_model;  // Z and A depend on H*d only
-            return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256);
+            return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256) + part_bytes(plan);
         }
         default: return 0;
     }
@@ -280,12 +360,13 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (u && !aligned16(u)))
         return HSTU_ERR_MISALIGNED;
-    if (u) {
+    const size_t need = hstu_workspace_bytes(plan, u ? 1 : 0, 0);
+    if (need > 0) {
         if (!ws) return HSTU_ERR_NULL_ARG;
-        if (ws_bytes < hstu_workspace_bytes(plan, 1, 0)) return HSTU_ERR_WORKSPACE_TOO_SMALL;
+        if (ws_bytes < need) return HSTU_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned16(ws)) return HSTU_ERR_MISALIGNED;
-        if (!(ln_eps >= 0.0f) || !std::isfinite(ln_eps)) return HSTU_ERR_BAD_SHAPE;
     }
+    if (u && (!(ln_eps >= 0.0f) || !std::isfinite(ln_eps))) return HSTU_ERR_BAD_SHAPE;
     if (plan->fwd.empty()) return HSTU_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hstu::AttnParams p = base_params(plan, args);
@@ -293,6 +374,9 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
     p.k = k;
     p.v = v;
     p.out = u ? ws : out;
+    // partial slots follow the gated path's attention buffer in ws
+    const size_t gated_bytes = u ? align_up(size_t(args->total_tokens) * p.ld_out * elem_size(args->dtype), 256) : 0;
+    p.part = plan->parts ? reinterpret_cast<float*>(static_cast<char*>(ws) + gated_bytes) : nullptr;
     hipError_t e = args->dtype == HSTU_BF16 ? hstu::launch_attn_fwd_bf16(p, s)
                                             : hstu::launch_attn_fwd_f32(p, s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
@@ -416,6 +500,7 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     hstu::AttnParams p = base_params(plan, args);
     const int64_t ldz = 4 * int64_t(hd);
     p.ld_in = ldz;
+    p.part = plan->parts ? reinterpret_cast<float*>(a + align_up(size_t(T) * hd * 2, 256)) : nullptr;
     p.v = z + size_t(hd) * 2;
     p.q = z + size_t(2 * hd) * 2;
     p.k = z + size_t(3 * hd) * 2;

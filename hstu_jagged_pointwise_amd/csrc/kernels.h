@@ -12,6 +12,11 @@ struct AttnParams {
     const SeqInfo* seqs;
     const WorkUnit* units;
     int32_t num_units;
+    const FwdItem* items;   // bf16 forward: work items (row blocks, the longest split by key tiles)
+    int32_t num_items;
+    const FixItem* fix;     // bf16 forward: split row blocks to sum
+    int32_t num_fix;
+    float* part;            // bf16 forward: partial slots, [slot][128 rows][head_dim] fp32
     int32_t heads;
     int32_t head_dim;
     int64_t ld_in;    // token stride of q, k, v (elements)

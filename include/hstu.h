@@ -92,6 +92,8 @@ typedef struct {
     int64_t fwd_tiles;         /* (32-row, 64-key) tiles the forward computes, all units */
     int64_t fwd_row_block;     /* query rows per forward work item */
     int64_t bwd_key_block;     /* keys per dK/dV work item */
+    int64_t fwd_items;         /* items of the forward launch (bf16: row blocks, long ones split) */
+    int64_t fwd_split_blocks;  /* row blocks whose key tiles are split over several items */
 } hstu_plan_info_t;
 
 #define HSTU_PLAN_HOST_ONLY 1u /* plan_create flag: plan on the host only (inspection, tests) */
@@ -101,9 +103,13 @@ typedef struct {
  * (KeyedJaggedTensor offsets, page 1 section 3.1.2) with [0] = 0 and [B] = T.
  * num_targets_host: host [B] int32 candidates per sequence, or NULL for none.  Work items are
  * (sequence, head, row block) ordered by decreasing cost, so the hardware dispatcher assigns the
- * longest first.  Unless flags has HSTU_PLAN_HOST_ONLY, the lists are copied synchronously into
- * one device buffer owned by the plan, on the current device.  *out receives the plan, or NULL
- * on error.  The caller frees it with hstu_plan_destroy. */
+ * longest first.  For bf16, a row block costing more than the average load of a workgroup slot
+ * (two per compute unit of the current device, 256 units for a host-only plan) runs as several
+ * forward items over disjoint key tiles whose fp32 partial outputs are summed afterwards (exact
+ * up to fp32 summation order: there is no softmax normalisation).  Unless flags has
+ * HSTU_PLAN_HOST_ONLY, the lists are copied synchronously into one device buffer owned by the
+ * plan, on the current device.  *out receives the plan, or NULL on error.  The caller frees it
+ * with hstu_plan_destroy. */
 hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* seq_offsets_host,
                                const int32_t* num_targets_host, uint32_t flags,
                                hstu_plan_t** out);
@@ -116,19 +122,23 @@ void hstu_plan_destroy(hstu_plan_t* plan);
 hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info);
 
 /* Copies the work list of `op` (0 = forward / dQ, 1 = dK/dV) to host memory as int32 quadruples
- * {sequence, head, first row (or key), cost} in launch order.  Writes at most `cap` items and
+ * {sequence, head, first row (or key), cost} in launch order; op 2 gives the bf16 forward items
+ * as int32 octets {sequence, head, first row, cost, first tile, end tile, partial slot or -1, 0}
+ * (tiles index the row block's list of visible key tiles).  Writes at most `cap` items and
  * returns the total count through *count. */
 hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* units, int64_t cap,
                               int64_t* count);
 
 /* Scratch bytes a call needs: op 0 = hstu_attn_fwd without u, 1 = hstu_attn_fwd with u,
- * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd with model width d_model (ignored otherwise). */
+ * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd with model width d_model (ignored otherwise).  The
+ * forward ops include 512 * head_dim bytes per partial slot of split row blocks (0 when the plan
+ * splits none). */
 size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
 
 /* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.
  * If u is non-NULL, out instead receives LayerNorm(O) * u per token over all H*d features
- * (the gating part of equation (3), without W2), and ws must hold hstu_workspace_bytes(plan, 1).
- * ln_eps is used only with u. */
+ * (the gating part of equation (3), without W2).  ws must hold hstu_workspace_bytes(plan, u ? 1 : 0)
+ * bytes (it may be NULL when that is 0).  ln_eps is used only with u. */
 hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                             const void* q, const void* k, const void* v, const void* u,
                             float ln_eps, void* out, void* ws, size_t ws_bytes, void* stream);

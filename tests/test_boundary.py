@@ -139,6 +139,46 @@ def test_plan_covers_every_block_once_longest_first(dtype):
     plan.close()
 
 
+@pytest.mark.parametrize("name", ["longtail_fwd", "one_long", "long_fwdbwd"])
+def test_forward_items_split_long_row_blocks(name):
+    if name == "one_long":   # one long sequence among short ones: its last row blocks split
+        w = hs.make_inputs([4000] + [60] * 50, 2, 64, dtype="bf16", seed=5, rab=True, num_targets=8)
+    else:
+        w = hs.make_workload(name)
+    plan = _plan(w, "bf16")
+    info = hj.hstu_plan_info(plan)
+    blocks = hj.hstu_plan_units(plan, 0)
+    items = hj.hstu_plan_units(plan, 2)
+    assert info["fwd_items"] == len(items)
+    assert np.all(np.diff(items[:, 3]) <= 0)                              # longest first
+    cap = max(4, 2 * -(-int(blocks[:, 3].sum()) // 512))                   # host-only: 256 CUs
+    cost = {tuple(b[:3]): int(b[3]) for b in blocks}
+    by_block = {}
+    for it in items:
+        by_block.setdefault(tuple(it[:3]), []).append(it)
+    assert set(by_block) == set(cost)
+    split, slots = 0, []
+    for key, its in by_block.items():
+        its = sorted(its, key=lambda r: r[4])
+        # the pieces tile [0, cost) exactly, in order, each of cost t1 - t0
+        assert its[0][4] == 0 and its[-1][5] == cost[key]
+        assert all(a[5] == b[4] for a, b in zip(its, its[1:]))
+        assert all(r[3] == r[5] - r[4] > 0 or cost[key] == 0 for r in its)
+        if len(its) == 1:
+            assert its[0][6] == -1
+        else:
+            split += 1
+            assert all(r[3] <= cap for r in its)
+            slots += [int(r[6]) for r in its]
+            assert cost[key] > cap
+    assert info["fwd_split_blocks"] == split
+    assert sorted(slots) == list(range(len(slots)))                        # slots used once
+    want_ws = -(-(len(slots) * 128 * w["d"] * 4) // 256) * 256
+    assert hj.hstu_workspace_bytes(plan, 0) == want_ws
+    assert (split > 0) == (name == "one_long")
+    plan.close()
+
+
 def test_plan_of_empty_batch():
     w = hs.make_inputs([0, 0, 0], 2, 32, dtype="fp32", rab=False, max_seqlen=4)
     plan = _plan(w, "fp32")

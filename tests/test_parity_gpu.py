@@ -156,6 +156,31 @@ def test_fwd_gated_by_u(dtype):
     check("LN(O)*u", host(out).reshape(G.shape), G, dtype)
 
 
+@pytest.mark.parametrize("gated", [False, True])
+def test_fwd_split_row_blocks(gated):
+    # one long sequence among short ones: its last row blocks run as several items whose fp32
+    # partial outputs a fix-up pass sums (the plan reports them)
+    w = hs.make_inputs([3000] + [60] * 40, 2, 64, dtype="bf16", seed=21, rab=True, num_contexts=2,
+                       num_targets=8)
+    dev = runner.to_device(w)
+    a = runner.args_for(w, dev)
+    plan = runner.plan_for(w, a)
+    assert hj.hstu_plan_info(plan)["fwd_split_blocks"] > 0
+    plan.close()
+    say(f"fwd split row blocks gated={gated}")
+    A = oracle.attn_fwd(w)
+    if not gated:
+        check("O", run_fwd(w), A, "bf16")
+        return
+    u = hs.round_bf16(np.random.default_rng(2).normal(size=(w["total_tokens"], 2 * 64)).astype(np.float32))
+    ut = torch.from_numpy(u).to("cuda:0", torch.bfloat16)
+    out = runner.attn_fwd(w, dev, u=ut, ln_eps=1e-5)
+    torch.cuda.synchronize()
+    A = A.reshape(w["total_tokens"], -1)
+    G = (A - A.mean(axis=1, keepdims=True)) / np.sqrt(A.var(axis=1, keepdims=True) + 1e-5) * u
+    check("LN(O)*u", host(out).reshape(G.shape), G, "bf16")
+
+
 def test_ranking_workload_full():
     w = hs.make_workload("ranking_fwd")
     say("ranking_fwd full size")
