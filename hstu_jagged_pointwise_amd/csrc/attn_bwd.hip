@@ -76,58 +76,54 @@ struct SmemA {
 //   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
 //   TM 0: time bias absent or one bucket; 1: two buckets, b1 where |dt| >= thr; 2 / 3: per-element
 //      bucket class with 32-bit / 64-bit times.
+// One 32-query half qb of the tile: queries 32 qb + (8r + 4g + c) (C layout), this lane's key.
 template <int D, int PM, int TM>
-__device__ __forceinline__ void epilogue_a(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemA<D>& sm,
-                                           int buf, int u0, int g, float alpha2, const TimeSel tb,
+__device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>& sm, int buf,
+                                           int qb, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t tj, int64_t tj64) {
     const TimePick pick(tb);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int r = 0; r < 4; ++r) {
+        const int ii = 32 * qb + 8 * r + 4 * g;
+        u32x4 tq4;
+        if (TM == 1 || TM == 2 || TM == 4) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ii = 32 * qb + 8 * r + 4 * g;
-            u32x4 tq4;
-            if (TM == 1 || TM == 2 || TM == 4) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int e = 4 * r + c;
-                float b = pick.get<TM>(tj, tq4[c]);
-                if (PM == 1) b += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
-                if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
-                if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
-                const Grad gr = silu_grad(fmaf(alpha2, s[qb][e], b), dp[qb][e]);
-                s[qb][e] = gr.p;
-                dp[qb][e] = gr.ds;
-            }
+        for (int c = 0; c < 4; ++c) {
+            const int e = 4 * r + c;
+            float b = pick.get<TM>(tj, tq4[c]);
+            if (PM == 1) b += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
+            if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
+            if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
+            const Grad gr = silu_grad(fmaf(alpha2, s[e], b), dp[e]);
+            s[e] = gr.p;
+            dp[e] = gr.ds;
         }
-}
-
-template <int D, int PM>
-__device__ __forceinline__ void epilogue_a_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
-                                              const SmemA<D>& sm, int buf, int u0, int g,
-                                              float alpha2, const TimeSel tb, uint32_t tj,
-                                              int64_t tj64) {
-    switch (tm) {
-        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
-        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
-        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
-        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
-        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64); break;
     }
 }
 
-// Zero P and dS of queries that do not see this lane's key (partial tiles only).
-__device__ __forceinline__ void mask_queries(f32x16 (&s)[2], f32x16 (&dp)[2], int g, int i0, int lo,
-                                             int hi) {
+template <int D, int PM>
+__device__ __forceinline__ void epilogue_a_tm(int tm, f32x16& s, f32x16& dp, const SmemA<D>& sm,
+                                              int buf, int qb, int u0, int g, float alpha2,
+                                              const TimeSel tb, uint32_t tj, int64_t tj64) {
+    switch (tm) {
+        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
+        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
+        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
+        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
+        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
+    }
+}
+
+// Zero P and dS of the half's queries iq0 + (8r + 4g + c) that do not see this lane's key
+// (partial tiles only).
+__device__ __forceinline__ void mask_queries(f32x16& s, f32x16& dp, int g, int iq0, int lo, int hi) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = i0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
-            const bool vis = i >= lo && i <= hi;
-            s[qb][e] = vis ? s[qb][e] : 0.0f;
-            dp[qb][e] = vis ? dp[qb][e] : 0.0f;
-        }
+    for (int e = 0; e < 16; ++e) {
+        const int i = iq0 + 8 * (e >> 2) + 4 * g + (e & 3);
+        const bool vis = i >= lo && i <= hi;
+        s[e] = vis ? s[e] : 0.0f;
+        dp[e] = vis ? dp[e] : 0.0f;
+    }
 }
 
 template <int D, bool RP, bool RT>
@@ -242,9 +238,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
         const int kind = wk0 < khi ? classify_key_tile(wk0, wk1, i0, n, nc, nh) : kEmpty;
         if (kind != kEmpty) {
             f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+            // S and dP, first query half then second
 #pragma unroll
             for (int x = 0; x < 2 * (D / 16); ++x) {
-                const int ks = x >> 1, qb = x & 1;
+                const int qb = x / (D / 16), ks = x % (D / 16);
                 s[qb] = mfma32(rowop.read(sm.q[buf], qb, ks), kf[ks], s[qb]);
                 dp[qb] = mfma32(rowop.read(sm.dout[buf], qb, ks), vf[ks], dp[qb]);
             }
@@ -263,22 +260,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                 const BiasSpan st = bias_span(sm.tqmin[buf] - tjmax, sm.tqmax[buf] - tjmin);
                 tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb);
             } else tb.set_const(bpos);
-            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64);
-            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, tb, tj, tj64);
-            if (kind == kPartial) mask_queries(s, dp, g, i0, lo, hi);
+            // Per 32-query half: epilogue, then that half's dV/dK products.  The matrix unit
+            // works through the first half's S/dP (and then its dV/dK) products while the
+            // wavefront runs the second half's epilogue.
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                float tp[8], td[8];
+            for (int qb = 0; qb < 2; ++qb) {
+                if (pm) epilogue_a_tm<D, 1>(tm, s[qb], dp[qb], sm, buf, qb, u0, g, alpha2, tb, tj, tj64);
+                else epilogue_a_tm<D, 0>(tm, s[qb], dp[qb], sm, buf, qb, u0, g, alpha2, tb, tj, tj64);
+                if (kind == kPartial) mask_queries(s[qb], dp[qb], g, i0 + 32 * qb, lo, hi);
 #pragma unroll
-                for (int x = 0; x < 8; ++x) {
-                    tp[x] = s[st >> 1][8 * (st & 1) + x];
-                    td[x] = dp[st >> 1][8 * (st & 1) + x];
-                }
-                const bf16x8 pb = pack8(tp), db8 = pack8(td);
+                for (int sl = 0; sl < 2; ++sl) {
+                    float tp[8], td[8];
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    dvt[db] = mfma32(trop.read(sm.dout[buf], st, db), pb, dvt[db]);
-                    dkt[db] = mfma32(trop.read(sm.q[buf], st, db), db8, dkt[db]);
+                    for (int x = 0; x < 8; ++x) {
+                        tp[x] = s[qb][8 * sl + x];
+                        td[x] = dp[qb][8 * sl + x];
+                    }
+                    const bf16x8 pb = pack8(tp), db8 = pack8(td);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qb + sl, db), pb, dvt[db]);
+                        dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qb + sl, db), db8, dkt[db]);
+                    }
                 }
             }
         }

@@ -369,14 +369,15 @@ __device__ __forceinline__ buffer_rsrc rows_rsrc(const bf16* base, int n, int64_
 
 // Copies tile rows [r0, r0 + 64) of one slice from memory straight into an LDS tile (buffer
 // loads with the LDS-write option, 16 bytes per lane): instruction u of wavefront w fills the
-// 1 KB block u * (THREADS / 64) + w of the tile, lane l its chunk position l, so each lane reads
-// the logical chunk that the swizzle puts there.  The copy is asynchronous: it is complete once
-// the issuing wavefront has waited for vmcnt(0).
+// 1 KB block u * W + w of the tile (W wavefronts; blocks past the tile's D / 8 are skipped), lane
+// l its chunk position l, so each lane reads the logical chunk that the swizzle puts there.  The
+// copy is asynchronous: it is complete once the issuing wavefront has waited for vmcnt(0).
 template <int D, int THREADS>
 struct TileDma {
-    static constexpr int C = D / 8;
-    static constexpr int N = kKeyTile * C / THREADS;
-    static_assert(N >= 1 && kKeyTile * C % THREADS == 0, "tile shape");
+    static constexpr int C = D / 8;            // 16-byte chunks per row = 1 KB blocks per tile
+    static constexpr int W = THREADS / 64;
+    static constexpr int N = (C + W - 1) / W;  // blocks per wavefront
+    static_assert(kKeyTile == 64, "a 1 KB block is 64 chunks");
     int off[N];  // byte offset of this lane's chunk, relative to tile row 0
     int wave;
     __device__ __forceinline__ TileDma(int tid, int64_t ld) {
@@ -384,7 +385,7 @@ struct TileDma {
         const int lane = tid & 63;
 #pragma unroll
         for (int u = 0; u < N; ++u) {
-            const int pos = (u * (THREADS / 64) + wave) * 64 + lane;
+            const int pos = (u * W + wave) * 64 + lane;
             const int row = pos / C, c = (pos % C) ^ tile_swz<D>(row);
             off[u] = (int)(((int64_t)row * ld + 8 * c) * 2);
         }
@@ -394,8 +395,9 @@ struct TileDma {
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
         for (int u = 0; u < N; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rs, (lds_void*)(tile + (u * (THREADS / 64) + wave) * 512), 16, off[u] + row_bytes, 0, 0, 0);
+            if (C % W == 0 || u * W + wave < C)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (lds_void*)(tile + (u * W + wave) * 512), 16, off[u] + row_bytes, 0, 0, 0);
 #else
         (void)rs;
         (void)tile;

@@ -106,10 +106,11 @@ HSTU_HD void rows_for_keys(int klo, int khi, int n, int nc, int nh, int* qlo, in
     *qhi = klo < nh ? n : imin(khi, n);
 }
 
-// Classification of the block queries [i0, i0 + 64) x keys [klo, khi) (khi <= n).
-HSTU_HD int classify_key_tile(int klo, int khi, int i0, int n, int nc, int nh) {
+// Classification of the block queries [i0, i0 + rows) x keys [klo, khi) (khi <= n).
+HSTU_HD int classify_key_tile(int klo, int khi, int i0, int n, int nc, int nh,
+                              int rows = kQueryTile) {
     if (khi <= klo) return kEmpty;
-    int i1 = i0 + kQueryTile - 1;
+    int i1 = i0 + rows - 1;
     bool any = false;
     if (klo < nc && i0 < n) any = true;                                  // context keys
     int hlo = imax(klo, nc), hhi = imin(khi, nh);

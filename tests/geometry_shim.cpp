@@ -14,7 +14,7 @@ int shim_classify_row(int rlo, int rhi, int j0, int n, int nc, int nh) {
 void shim_rows_for_keys(int klo, int khi, int n, int nc, int nh, int* out2) {
     hstu::rows_for_keys(klo, khi, n, nc, nh, &out2[0], &out2[1]);
 }
-int shim_classify_key(int klo, int khi, int i0, int n, int nc, int nh) {
-    return hstu::classify_key_tile(klo, khi, i0, n, nc, nh);
+int shim_classify_key(int klo, int khi, int i0, int n, int nc, int nh, int rows) {
+    return hstu::classify_key_tile(klo, khi, i0, n, nc, nh, rows);
 }
 }

@@ -245,12 +245,14 @@ def test_tile_geometry_matches_mask(shim):
             qlo, qhi = q[0], q[1]
             rows_seen = np.nonzero(m[:, k0:khi].any(axis=1))[0]
             assert rows_seen.min() >= qlo and rows_seen.max() < qhi
-            for i0 in range(0, n, 64):
-                for w0 in range(k0, khi, 32):
-                    w1 = min(w0 + 32, khi)
-                    sub = m[i0:i0 + 64, w0:w1]
-                    kind = shim.shim_classify_key(w0, w1, i0, n, nc, nh)
-                    if kind == 0:
-                        assert not sub.any(), (n, c, t, i0, w0)
-                    if kind == 2:
-                        assert sub.shape[0] == 64 and sub.all(), (n, c, t, i0, w0)
+            # 64-query tiles, and their 32-query halves (the two wavefronts sharing a key group)
+            for rows in (64, 32):
+                for i0 in range(0, n, rows):
+                    for w0 in range(k0, khi, 32):
+                        w1 = min(w0 + 32, khi)
+                        sub = m[i0:i0 + rows, w0:w1]
+                        kind = shim.shim_classify_key(w0, w1, i0, n, nc, nh, rows)
+                        if kind == 0:
+                            assert not sub.any(), (n, c, t, i0, w0, rows)
+                        if kind == 2:
+                            assert sub.shape[0] == rows and sub.all(), (n, c, t, i0, w0, rows)
