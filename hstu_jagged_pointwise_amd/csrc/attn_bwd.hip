@@ -8,11 +8,13 @@
 //   (and likewise d rab_ts over time buckets).
 //
 // Two passes, no atomics on dQ/dK/dV:
-//   pass A (key-stationary): unit = (sequence, head, 128 keys), 4 wavefronts x 32 keys; visits
-//     64-query tiles.  S = Q K^T and dP = dO V^T put one key per lane, which is the B-operand
-//     layout for dV^T += dO^T P and dK^T += Q^T dS; the Q and dO tiles are read along their rows
-//     for the A operands of the first two products and with transposing LDS reads for the last
-//     two.
+//   pass A (key-stationary): unit = (sequence, head, 128 keys), 8 wavefronts: wavefront w owns
+//     keys 32 (w % 4) .. + 31 and the query half 32 (w / 4) .. + 31 of each visited 64-query tile
+//     (two wavefronts per SIMD; the two halves' dK, dV partial sums are added through LDS at the
+//     end).  The unit's K and V rows stay in LDS and are read as MFMA B operands, which keeps a
+//     wavefront within the 256 registers that two wavefronts per SIMD allow.  S = Q K^T and dP = dO V^T put one key per lane, which is the B-operand layout for
+//     dV^T += dO^T P and dK^T += Q^T dS; the Q and dO tiles are read along their rows for the A
+//     operands of the first two products and with transposing LDS reads for the last two.
 //   pass B (query-stationary): unit = (sequence, head, 128 rows) exactly like the forward;
 //     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (K^T read transposed from the K tile), and the
 //     bias-table gradients.
@@ -31,7 +33,8 @@
 namespace hstu {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;           // pass B
+constexpr int kThreadsA = 512;          // pass A: 8 wavefronts
 constexpr int kBlk = 4 * kWaveRows;      // 128 keys (pass A) or rows (pass B) per unit
 constexpr int kTile = 64;                // queries (pass A) or keys (pass B) per tile
 constexpr int kToep = kBlk + kTile - 1;  // 191 distinct i - j per (unit, tile)
@@ -70,28 +73,31 @@ struct SmemA {
     int fits[2];
     alignas(16) bf16 q[2][kTile * D];    // swizzled tiles (tile_off)
     bf16 dout[2][kTile * D];
+    bf16 kb[kBlk * D];                   // the unit's keys and values, swizzled like the tiles
+    bf16 vb[kBlk * D];
 };
 
 // Bias modes of a (wavefront, tile) as in the forward:
 //   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
 //   TM 0: time bias absent or one bucket; 1: two buckets, b1 where |dt| >= thr; 2 / 3: per-element
 //      bucket class with 32-bit / 64-bit times.
-// One 32-query half qb of the tile: queries 32 qb + (8r + 4g + c) (C layout), this lane's key.
+// One wavefront's 32 x 32 block: queries q0 + (8r + 4g + c) of the tile (C layout), its key per
+// lane; u0 is the Toeplitz slot of the block's first query for this lane.
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>& sm, int buf,
-                                           int qb, int u0, int g, float alpha2, const TimeSel tb,
+                                           int q0, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t tj, int64_t tj64) {
     const TimePick pick(tb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int ii = 32 * qb + 8 * r + 4 * g;
+        const int ii = q0 + 8 * r + 4 * g;
         u32x4 tq4;
         if (TM == 1 || TM == 2 || TM == 4) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int e = 4 * r + c;
             float b = pick.get<TM>(tj, tq4[c]);
-            if (PM == 1) b += sm.rp[buf][u0 + 32 * qb + 8 * r + c];
+            if (PM == 1) b += sm.rp[buf][u0 + 8 * r + c];
             if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
             if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
             const Grad gr = silu_grad(fmaf(alpha2, s[e], b), dp[e]);
@@ -103,18 +109,18 @@ __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>
 
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_a_tm(int tm, f32x16& s, f32x16& dp, const SmemA<D>& sm,
-                                              int buf, int qb, int u0, int g, float alpha2,
+                                              int buf, int q0, int u0, int g, float alpha2,
                                               const TimeSel tb, uint32_t tj, int64_t tj64) {
     switch (tm) {
-        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
-        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
-        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
-        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
-        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, qb, u0, g, alpha2, tb, tj, tj64); break;
+        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
+        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
+        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
+        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
+        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
     }
 }
 
-// Zero P and dS of the half's queries iq0 + (8r + 4g + c) that do not see this lane's key
+// Zero P and dS of the block's queries iq0 + (8r + 4g + c) that do not see this lane's key
 // (partial tiles only).
 __device__ __forceinline__ void mask_queries(f32x16& s, f32x16& dp, int g, int iq0, int lo, int hi) {
 #pragma unroll
@@ -127,12 +133,14 @@ __device__ __forceinline__ void mask_queries(f32x16& s, f32x16& dp, int g, int i
 }
 
 template <int D, bool RP, bool RT>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams p) {
+    constexpr int kThreads = kThreadsA;  // the helpers below stride over the whole workgroup
     __shared__ __attribute__((aligned(16))) SmemA<D> sm;
 
     const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+    const int wave = (tid >> 6) & 3, qh = tid >> 8;  // key group, query half
     const int n = si.n, nc = si.nc, nh = si.nh, k0 = wu.row0, h = wu.head;
     const int64_t tok0 = si.start, ld = p.ld_in;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * ld + h * D;
@@ -155,6 +163,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
     int qlo, qhi;
     rows_for_keys(k0, khi, n, nc, nh, &qlo, &qhi);
     const int tfirst = qlo / kTile, ntiles = cdiv(qhi, kTile) - tfirst;
+    // partial dK, dV of the second query half go through the (then idle) tile buffers
+    static_assert(sizeof(sm.q) + sizeof(sm.dout) >= 4 * (D / 32) * 16 * 64 * sizeof(float),
+                  "reduction buffer");
 
     const int wk0 = k0 + kWaveRows * wave, wk1 = imin(wk0 + kWaveRows, khi);
     const int j = wk0 + lr;
@@ -164,12 +175,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
         if (j < nc) { lo = 0; hi = n - 1; }
         else if (j < nh) { lo = j; hi = n - 1; }
         else { lo = j; hi = j; }
-    }
-    bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        kf[ks] = key_ok ? load_bf16x8(kg + (int64_t)j * ld + 16 * ks + 8 * g) : bf16x8{};
-        vf[ks] = key_ok ? load_bf16x8(vg + (int64_t)j * ld + 16 * ks + 8 * g) : bf16x8{};
     }
     uint32_t tj = 0;
     int64_t tj64 = 0, tjmin = 0, tjmax = 0;
@@ -222,35 +227,44 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
             }
     };
 
+    {  // the unit's 128 keys and values (rows past the sequence end read as zero)
+        const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
+        const TileDma<D, kThreads> kvdma(tid, ld);
+#pragma unroll
+        for (int half = 0; half < kBlk / kTile; ++half) {
+            const int row_bytes = (int)((int64_t)(k0 + kTile * half) * ld * 2);
+            kvdma.issue(krs, sm.kb + kTile * half * D, row_bytes);
+            kvdma.issue(vrs, sm.vb + kTile * half * D, row_bytes);
+        }
+    }
     __syncthreads();
     load_tile(0, tfirst);
     store_tile(0, tfirst);
     wait_tile_dma();
     __syncthreads();
 
-    // slot of (query i0 + ii, key j) is u0 + ii - 4g with u0 below
-    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1);
+    // slot of (query i0 + ii, key j) is u0 + ii - 4g; this wavefront's queries start at ii = q0
+    const int q0 = kWaveRows * qh;
+    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1) + q0;
     const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1, i0 = (tfirst + t) * kTile;
+        const int buf = t & 1, i0 = (tfirst + t) * kTile, iq0 = i0 + q0;
         if (t + 1 < ntiles) load_tile(buf ^ 1, tfirst + t + 1);
-        const int kind = wk0 < khi ? classify_key_tile(wk0, wk1, i0, n, nc, nh) : kEmpty;
+        const int kind = wk0 < khi && iq0 < n ? classify_key_tile(wk0, wk1, iq0, n, nc, nh, kWaveRows)
+                                              : kEmpty;
         if (kind != kEmpty) {
-            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-            // S and dP, first query half then second
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int x = 0; x < 2 * (D / 16); ++x) {
-                const int qb = x / (D / 16), ks = x % (D / 16);
-                s[qb] = mfma32(rowop.read(sm.q[buf], qb, ks), kf[ks], s[qb]);
-                dp[qb] = mfma32(rowop.read(sm.dout[buf], qb, ks), vf[ks], dp[qb]);
+            for (int ks = 0; ks < D / 16; ++ks) {
+                s = mfma32(rowop.read(sm.q[buf], qh, ks), rowop.read(sm.kb, wave, ks), s);
+                dp = mfma32(rowop.read(sm.dout[buf], qh, ks), rowop.read(sm.vb, wave, ks), dp);
             }
-            sched_mfma_lds<4 * (D / 16), 4>();
             float bpos = 0.0f;
             int pm = 0;
-            const int ihi = imin(i0 + kTile, n) - 1;
+            const int ihi = imin(iq0 + kWaveRows, n) - 1;
             if (RP) {
-                const BiasSpan sp = bias_span((int64_t)i0 - (wk1 - 1), (int64_t)ihi - wk0);
+                const BiasSpan sp = bias_span((int64_t)iq0 - (wk1 - 1), (int64_t)ihi - wk0);
                 if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
@@ -260,28 +274,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
                 const BiasSpan st = bias_span(sm.tqmin[buf] - tjmax, sm.tqmax[buf] - tjmin);
                 tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb);
             } else tb.set_const(bpos);
-            // Per 32-query half: epilogue, then that half's dV/dK products.  The matrix unit
-            // works through the first half's S/dP (and then its dV/dK) products while the
-            // wavefront runs the second half's epilogue.
+            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
+            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
+            if (kind == kPartial) mask_queries(s, dp, g, iq0, lo, hi);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                if (pm) epilogue_a_tm<D, 1>(tm, s[qb], dp[qb], sm, buf, qb, u0, g, alpha2, tb, tj, tj64);
-                else epilogue_a_tm<D, 0>(tm, s[qb], dp[qb], sm, buf, qb, u0, g, alpha2, tb, tj, tj64);
-                if (kind == kPartial) mask_queries(s[qb], dp[qb], g, i0 + 32 * qb, lo, hi);
+            for (int sl = 0; sl < 2; ++sl) {
+                float tp[8], td[8];
 #pragma unroll
-                for (int sl = 0; sl < 2; ++sl) {
-                    float tp[8], td[8];
+                for (int x = 0; x < 8; ++x) {
+                    tp[x] = s[8 * sl + x];
+                    td[x] = dp[8 * sl + x];
+                }
+                const bf16x8 pb = pack8(tp), db8 = pack8(td);
 #pragma unroll
-                    for (int x = 0; x < 8; ++x) {
-                        tp[x] = s[qb][8 * sl + x];
-                        td[x] = dp[qb][8 * sl + x];
-                    }
-                    const bf16x8 pb = pack8(tp), db8 = pack8(td);
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qb + sl, db), pb, dvt[db]);
-                        dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qb + sl, db), db8, dkt[db]);
-                    }
+                for (int db = 0; db < D / 32; ++db) {
+                    dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qh + sl, db), pb, dvt[db]);
+                    dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qh + sl, db), db8, dkt[db]);
                 }
             }
         }
@@ -290,7 +298,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(const AttnParams 
         __syncthreads();
     }
 
-    if (key_ok) {
+    // add the second query half's partial sums into the first's, dV then dK, through LDS laid
+    // out [key group][db][element][lane] (lanes consecutive: no bank conflicts)
+    float* red = reinterpret_cast<float*>(&sm.q[0][0]);
+    auto exchange = [&](f32x16 (&acc)[D / 32]) {
+        float* mine = red + ((size_t)wave * (D / 32) * 16) * 64 + lane;
+        if (qh == 1)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[(db * 16 + e) * 64] = acc[db][e];
+        __syncthreads();
+        if (qh == 0)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[db][e] += mine[(db * 16 + e) * 64];
+        __syncthreads();
+    };
+    exchange(dvt);
+    exchange(dkt);
+
+    if (key_ok && qh == 0) {
         bf16* dvg = static_cast<bf16*>(p.dv) + (tok0 + j) * p.ld_out + h * D;
         bf16* dkg = static_cast<bf16*>(p.dk) + (tok0 + j) * p.ld_out + h * D;
         const float sv = -kLn2 * p.inv_n, sk = p.alpha * p.inv_n;
@@ -844,7 +873,7 @@ __global__ void zero_f32_kernel(float* p, int64_t n) {
 
 template <int D, bool RP, bool RT>
 hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, RP, RT>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
     return hipGetLastError();
 }
 
