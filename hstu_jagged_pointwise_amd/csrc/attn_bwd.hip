@@ -15,9 +15,11 @@
 //     wavefront within the 256 registers that two wavefronts per SIMD allow.  S = Q K^T and dP = dO V^T put one key per lane, which is the B-operand layout for
 //     dV^T += dO^T P and dK^T += Q^T dS; the Q and dO tiles are read along their rows for the A
 //     operands of the first two products and with transposing LDS reads for the last two.
-//   pass B (query-stationary): unit = (sequence, head, 128 rows) exactly like the forward;
-//     S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (K^T read transposed from the K tile), and the
-//     bias-table gradients.
+//   pass B (query-stationary): unit = (sequence, head, 128 rows) like the forward, 8 wavefronts:
+//     wavefront w owns rows 32 (w % 4) .. + 31 and the key half 32 (w / 4) .. + 31 of each
+//     64-key tile; S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (K^T read transposed from the K
+//     tile), and the bias-table gradients.  The unit's Q and dO rows stay in LDS (B operands),
+//     two wavefronts per SIMD; the key halves' dQ partial sums are added through LDS at the end.
 // Tiles are copied from memory straight into LDS by buffer loads, double-buffered, as in the
 // forward.
 // Bias-gradient sums: when all pairs of a (wavefront, tile) fall into one bucket -- the common
@@ -359,44 +361,46 @@ struct SmemB {
     float hbt[kNumBuckets];   // time-bias gradient sums of one- or two-bucket tiles, by bucket
     alignas(16) bf16 k[2][kTile * D];    // swizzled tiles (tile_off)
     bf16 v[2][kTile * D];
+    bf16 qb[kBlk * D];                   // the unit's query and dO rows, swizzled like the tiles
+    bf16 dob[kBlk * D];
 };
 
-// Per-element part of pass B: dS (times N) into dp.  Bias modes as in pass A.
+// Per-element part of pass B for one wavefront's 32 x 32 block: keys k0 + (8r + 4g + c) of the
+// tile (C layout), this lane's row; u0 is the Toeplitz slot of the block's first key for this
+// lane.  dS (times N) into dp.  Bias modes as in pass A.
 template <int D, int PM, int TM>
-__device__ __forceinline__ void epilogue_b(f32x16 (&s)[2], f32x16 (&dp)[2], const SmemB<D>& sm,
-                                           int buf, int u0, int g, float alpha2, const TimeSel tb,
+__device__ __forceinline__ void epilogue_b(const f32x16& s, f32x16& dp, const SmemB<D>& sm, int buf,
+                                           int k0, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t ti, int64_t ti64) {
     const TimePick pick(tb);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < 4; ++r) {
+        const int jj = k0 + 8 * r + 4 * g;
+        u32x4 tk4;
+        if (TM == 1 || TM == 2 || TM == 4) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int jj = 32 * kb + 8 * r + 4 * g;
-            u32x4 tk4;
-            if (TM == 1 || TM == 2 || TM == 4) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int e = 4 * r + c;
-                float b = pick.get<TM>(ti, tk4[c]);
-                if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c].bias;
-                if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tk4[c]))];
-                if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
-                dp[kb][e] = silu_grad(fmaf(alpha2, s[kb][e], b), dp[kb][e]).ds;
-            }
+        for (int c = 0; c < 4; ++c) {
+            const int e = 4 * r + c;
+            float b = pick.get<TM>(ti, tk4[c]);
+            if (PM == 1) b += sm.rp[buf][u0 + 8 * r + c].bias;
+            if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tk4[c]))];
+            if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
+            dp[e] = silu_grad(fmaf(alpha2, s[e], b), dp[e]).ds;
         }
+    }
 }
 
 template <int D, int PM>
-__device__ __forceinline__ void epilogue_b_tm(int tm, f32x16 (&s)[2], f32x16 (&dp)[2],
-                                              const SmemB<D>& sm, int buf, int u0, int g,
+__device__ __forceinline__ void epilogue_b_tm(int tm, const f32x16& s, f32x16& dp,
+                                              const SmemB<D>& sm, int buf, int k0, int u0, int g,
                                               float alpha2, const TimeSel tb, uint32_t ti,
                                               int64_t ti64) {
     switch (tm) {
-        case 0: epilogue_b<D, PM, 0>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        case 1: epilogue_b<D, PM, 1>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        case 4: epilogue_b<D, PM, 4>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        case 2: epilogue_b<D, PM, 2>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        default: epilogue_b<D, PM, 3>(s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 0: epilogue_b<D, PM, 0>(s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64); break;
+        case 1: epilogue_b<D, PM, 1>(s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64); break;
+        case 4: epilogue_b<D, PM, 4>(s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64); break;
+        case 2: epilogue_b<D, PM, 2>(s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64); break;
+        default: epilogue_b<D, PM, 3>(s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64); break;
     }
 }
 
@@ -413,20 +417,19 @@ struct TileSums {
     float sum, mp, th, th2;
 };
 template <int D, int PG, int TM, bool GP, bool GT>
-__device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& sm, int buf, int u0,
-                                              int g, const TimeSel tb, uint32_t ti, int64_t ti64) {
+__device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, int buf, int k0,
+                                              int u0, int g, const TimeSel tb, uint32_t ti,
+                                              int64_t ti64) {
     TileSums ts{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int jj = 32 * kb + 8 * r + 4 * g;
+            const int jj = k0 + 8 * r + 4 * g;
             u32x4 tk4;
             if (GT && (TM == 1 || TM == 2 || TM == 4)) tk4 = *reinterpret_cast<const u32x4*>(&sm.tk[buf][jj]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float ds = dp[kb][4 * r + c];
-                const int u = u0 + 32 * kb + 8 * r + c;
+                const float ds = dp[4 * r + c];
+                const int u = u0 + 8 * r + c;
                 ts.sum += ds;
                 if (GP && PG == 1) ts.mp = fmaf(ds, sm.rp[buf][u].bucket, ts.mp);
                 if (GP && PG == 2) atomicAdd(&sm.dg[buf][u], ds);
@@ -444,27 +447,26 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16 (&dp)[2], SmemB<D>& s
 }
 
 template <int D, int PG, bool GP, bool GT>
-__device__ __forceinline__ TileSums grad_sums_tm(int tm, const f32x16 (&dp)[2], SmemB<D>& sm,
-                                                 int buf, int u0, int g, const TimeSel tb,
+__device__ __forceinline__ TileSums grad_sums_tm(int tm, const f32x16& dp, SmemB<D>& sm, int buf,
+                                                 int k0, int u0, int g, const TimeSel tb,
                                                  uint32_t ti, int64_t ti64) {
     switch (GT ? tm : 0) {
-        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
-        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
-        case 4: return grad_sums<D, PG, 4, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
-        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
-        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, u0, g, tb, ti, ti64);
+        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
+        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
+        case 4: return grad_sums<D, PG, 4, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
+        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
+        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
     }
 }
 
-// Zero dS of keys this lane's row does not see (partial tiles only).
-__device__ __forceinline__ void mask_keys_b(f32x16 (&dp)[2], int g, int j0, int lim, int dg) {
+// Zero dS of the block's keys jk0 + (8r + 4g + c) that this lane's row does not see (partial
+// tiles only).
+__device__ __forceinline__ void mask_keys_b(f32x16& dp, int g, int jk0, int lim, int dg) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-            dp[kb][e] = (j <= lim || j == dg) ? dp[kb][e] : 0.0f;
-        }
+    for (int e = 0; e < 16; ++e) {
+        const int j = jk0 + 8 * (e >> 2) + 4 * g + (e & 3);
+        dp[e] = (j <= lim || j == dg) ? dp[e] : 0.0f;
+    }
 }
 
 // A per-lane running sum for one histogram bucket (the same bucket across the wavefront); a
@@ -484,12 +486,14 @@ struct Run {
 };
 
 template <int D, bool RP, bool RT, bool GP, bool GT>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p) {
+    constexpr int kThreads = kThreadsA;  // the helpers below stride over the whole workgroup
     __shared__ __attribute__((aligned(16))) SmemB<D> sm;
 
     const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+    const int wave = (tid >> 6) & 3, kh = tid >> 8;  // row group, key half
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = si.start, ld = p.ld_in;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * ld + h * D;
@@ -521,12 +525,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p)
     if (row_ok) {
         if (i < nh) lim = imax(i, nc - 1);
         else { lim = nh - 1; dg = i; }
-    }
-    bf16x8 qf[D / 16], dof[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        qf[ks] = row_ok ? load_bf16x8(qg + (int64_t)i * ld + 16 * ks + 8 * g) : bf16x8{};
-        dof[ks] = row_ok ? load_bf16x8(dog + (int64_t)i * p.ld_out + 16 * ks + 8 * g) : bf16x8{};
     }
     uint32_t ti = 0;
     int64_t ti64 = 0, timin = 0, timax = 0;
@@ -595,34 +593,44 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p)
             }
     };
 
+    {  // the unit's 128 query and dO rows (rows past the sequence end read as zero)
+        const buffer_rsrc qrs = rows_rsrc(qg, n, ld, D), drs = rows_rsrc(dog, n, p.ld_out, D);
+        const TileDma<D, kThreads> qdma(tid, ld), ddma(tid, p.ld_out);
+#pragma unroll
+        for (int half = 0; half < kBlk / kTile; ++half) {
+            qdma.issue(qrs, sm.qb + kTile * half * D, (int)((int64_t)(r0 + kTile * half) * ld * 2));
+            ddma.issue(drs, sm.dob + kTile * half * D, (int)((int64_t)(r0 + kTile * half) * p.ld_out * 2));
+        }
+    }
     __syncthreads();
     load_tile(0, ktl.tile(0));
     store_tile(0, ktl.tile(0));
     wait_tile_dma();
     __syncthreads();
 
-    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1);
+    // slot of (row i, key j0 + jj) is u0 + jj - 4g; this wavefront's keys start at jj = k0
+    const int k0 = kWaveRows * kh;
+    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1) + k0;
     const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1, j0 = ktl.tile(t) * kTile;
+        const int buf = t & 1, j0 = ktl.tile(t) * kTile, jk0 = j0 + k0;
         if (t + 1 < ntiles) load_tile(buf ^ 1, ktl.tile(t + 1));
-        const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
+        const int kind = wlo < rhi && jk0 < n ? classify_row_tile(wlo, whi, jk0, n, nc, nh, kWaveRows)
+                                              : kEmpty;
         if (kind != kEmpty) {
-            f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int x = 0; x < 2 * (D / 16); ++x) {
-                const int ks = x >> 1, kb = x & 1;
-                s[kb] = mfma32(rowop.read(sm.k[buf], kb, ks), qf[ks], s[kb]);
-                dp[kb] = mfma32(rowop.read(sm.v[buf], kb, ks), dof[ks], dp[kb]);
+            for (int ks = 0; ks < D / 16; ++ks) {
+                s = mfma32(rowop.read(sm.k[buf], kh, ks), rowop.read(sm.qb, wave, ks), s);
+                dp = mfma32(rowop.read(sm.v[buf], kh, ks), rowop.read(sm.dob, wave, ks), dp);
             }
-            sched_mfma_lds<4 * (D / 16), 4>();
             float bpos = 0.0f;
             int pm = 0;
             BiasSpan sp{0, 0, 0, 0, 0}, st{0, 0, 0, 0, 0};
             if (RP) {
-                const int jhi = imin(j0 + kTile, n) - 1;
-                sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - j0);
+                const int jhi = imin(jk0 + kWaveRows, n) - 1;
+                sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - jk0);
                 if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
@@ -632,15 +640,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p)
                 st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
                 tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb);
             } else tb.set_const(bpos);
-            if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64);
-            else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, u0, g, alpha2, tb, ti, ti64);
-            if (kind == kPartial) mask_keys_b(dp, g, j0, lim, dg);
+            if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);
+            else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);
+            if (kind == kPartial) mask_keys_b(dp, g, jk0, lim, dg);
             if (GP || GT) {
                 const int pg = !GP ? 0 : (sp.kind == 0 ? 0 : (sp.kind == 1 ? 1 : 2));
                 TileSums ts;
-                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, u0, g, tb, ti, ti64);
-                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, u0, g, tb, ti, ti64);
-                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, u0, g, tb, ti, ti64);
+                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, k0, u0, g, tb, ti, ti64);
+                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, k0, u0, g, tb, ti, ti64);
+                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, k0, u0, g, tb, ti, ti64);
                 if (GP && pg == 0) run_p_lo.add(sm.hbp, sp.b_lo, ts.sum, lane);
                 if (GP && pg == 1) {
                     const float hi_part = ts.mp - (float)sp.b_lo * ts.sum;
@@ -659,13 +667,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p)
                 }
             }
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int sl = 0; sl < 2; ++sl) {
                 float td[8];
 #pragma unroll
-                for (int x = 0; x < 8; ++x) td[x] = dp[st >> 1][8 * (st & 1) + x];
+                for (int x = 0; x < 8; ++x) td[x] = dp[8 * sl + x];
                 const bf16x8 db8 = pack8(td);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) dqt[db] = mfma32(trop.read(sm.k[buf], st, db), db8, dqt[db]);
+                for (int db = 0; db < D / 32; ++db)
+                    dqt[db] = mfma32(trop.read(sm.k[buf], 2 * kh + sl, db), db8, dqt[db]);
             }
         }
         if (GP && t > 0) fold_diagonals(buf ^ 1, ktl.tile(t - 1));
@@ -675,7 +684,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const AttnParams p)
     }
     if (GP && ntiles > 0) fold_diagonals((ntiles - 1) & 1, ktl.tile(ntiles - 1));
 
-    if (row_ok) {
+    // add the second key half's partial dQ into the first's through the idle K and V tile
+    // buffers (adjacent), laid out [row group][db][element][lane]
+    static_assert(sizeof(sm.k) + sizeof(sm.v) >= 4 * (D / 32) * 16 * 64 * sizeof(float),
+                  "reduction buffer");
+    {
+        float* mine = reinterpret_cast<float*>(&sm.k[0][0]) + ((size_t)wave * (D / 32) * 16) * 64 + lane;
+        if (kh == 1)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[(db * 16 + e) * 64] = dqt[db][e];
+        __syncthreads();
+        if (kh == 0)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) dqt[db][e] += mine[(db * 16 + e) * 64];
+    }
+
+    if (row_ok && kh == 0) {
         bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_out + h * D;
         const float sq = p.alpha * p.inv_n;
 #pragma unroll
@@ -880,10 +908,10 @@ hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
 template <int D, bool RP, bool RT>
 hipError_t launch_dq_t(const AttnParams& p, hipStream_t s) {
     const bool gp = RP && p.drab_pos, gt = RT && p.drab_ts;
-    if (gp && gt) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, RP, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
-    else if (gp) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, RP, false>), dim3(p.num_units), dim3(kThreads), 0, s, p);
-    else if (gt) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, false, RT>), dim3(p.num_units), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, false, false>), dim3(p.num_units), dim3(kThreads), 0, s, p);
+    if (gp && gt) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, RP, RT>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
+    else if (gp) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, RP, false>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
+    else if (gt) hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, false, RT>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, RP, RT, false, false>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
     return hipGetLastError();
 }
 

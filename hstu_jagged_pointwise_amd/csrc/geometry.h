@@ -81,12 +81,13 @@ HSTU_HD KeyTiles key_tiles_for_rows(int rlo, int rhi, int nc, int nh) {
     return r;
 }
 
-// Classification of the block rows [rlo, rhi) x keys [j0, j0 + 64) (rhi <= n).
+// Classification of the block rows [rlo, rhi) x keys [j0, j0 + keys) (rhi <= n).
 enum TileKind { kEmpty = 0, kPartial = 1, kFull = 2 };
 
-HSTU_HD int classify_row_tile(int rlo, int rhi, int j0, int n, int nc, int nh) {
+HSTU_HD int classify_row_tile(int rlo, int rhi, int j0, int n, int nc, int nh,
+                              int keys = kKeyTile) {
     if (rhi <= rlo) return kEmpty;
-    int j1 = j0 + kKeyTile - 1;
+    int j1 = j0 + keys - 1;
     bool any = false;
     int hhi = imin(rhi, nh);
     if (rlo < hhi && j0 <= imax(hhi - 1, nc - 1)) any = true;          // history rows

@@ -8,8 +8,8 @@ void shim_key_tiles(int rlo, int rhi, int nc, int nh, int* out3) {
     hstu::KeyTiles k = hstu::key_tiles_for_rows(rlo, rhi, nc, nh);
     out3[0] = k.main_tiles; out3[1] = k.diag_first; out3[2] = k.diag_tiles;
 }
-int shim_classify_row(int rlo, int rhi, int j0, int n, int nc, int nh) {
-    return hstu::classify_row_tile(rlo, rhi, j0, n, nc, nh);
+int shim_classify_row(int rlo, int rhi, int j0, int n, int nc, int nh, int keys) {
+    return hstu::classify_row_tile(rlo, rhi, j0, n, nc, nh, keys);
 }
 void shim_rows_for_keys(int klo, int khi, int n, int nc, int nh, int* out2) {
     hstu::rows_for_keys(klo, khi, n, nc, nh, &out2[0], &out2[1]);

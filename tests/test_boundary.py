@@ -230,13 +230,21 @@ def test_tile_geometry_matches_mask(shim):
                 for w0 in range(r0, rhi, 32):
                     w1 = min(w0 + 32, rhi)
                     sub = m[w0:w1, 64 * tile: 64 * tile + 64]
-                    kind = shim.shim_classify_row(w0, w1, 64 * tile, n, nc, nh)
+                    kind = shim.shim_classify_row(w0, w1, 64 * tile, n, nc, nh, 64)
                     if kind == 0:
                         assert not sub.any(), (n, c, t, w0, tile)
                     if kind == 2:  # no mask needed: every real row sees all 64 keys
                         assert sub.shape[1] == 64 and sub.all(), (n, c, t, w0, tile)
                     if sub.any():
                         assert tile in listed
+                    for kh in range(2):  # the tile's 32-key halves
+                        j0 = 64 * tile + 32 * kh
+                        sub = m[w0:w1, j0:j0 + 32]
+                        kind = shim.shim_classify_row(w0, w1, j0, n, nc, nh, 32)
+                        if kind == 0:
+                            assert not sub.any(), (n, c, t, w0, j0)
+                        if kind == 2:
+                            assert sub.shape[1] == 32 and sub.all(), (n, c, t, w0, j0)
         # dK/dV: 128-key units, 32-key wavefronts, 64-query tiles
         for k0 in range(0, n, 128):
             khi = min(k0 + 128, n)
