@@ -71,7 +71,7 @@ struct SmemA {
     float rp[2][kToep + 1];
     uint32_t tq[2][kTile];
     int64_t tq64[2][kTile];
-    int64_t tqmin[2], tqmax[2];
+    int64_t tqmin[2][2], tqmax[2][2];  // time range of the real queries of each 32-query half
     int fits[2];
     alignas(16) bf16 q[2][kTile * D];    // swizzled tiles (tile_off)
     bf16 dout[2][kTile * D];
@@ -218,8 +218,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             const TimeRange tr = wave_time_range(tqr, real, tbase);
             if (tid == 0) {
                 sm.fits[buf] = tr.fit ? 1 : 0;
-                sm.tqmin[buf] = tr.lo;
-                sm.tqmax[buf] = tr.hi;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    sm.tqmin[buf][hf] = tr.lo[hf];
+                    sm.tqmax[buf][hf] = tr.hi[hf];
+                }
             }
         }
         if (RP)
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                const BiasSpan st = bias_span(sm.tqmin[buf] - tjmax, sm.tqmax[buf] - tjmin);
+                const BiasSpan st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
                 tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb);
             } else tb.set_const(bpos);
             if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
@@ -353,12 +356,13 @@ struct SmemB {
     ToepEntry rp[2][kToep + 1];
     uint32_t tk[2][kTile];
     int64_t tk64[2][kTile];
-    int64_t tkmin[2], tkmax[2];
+    int64_t tkmin[2][2], tkmax[2][2];  // time range of the real keys of each 32-key half
     int fits[2];
     float dg[2][kToep + 1];   // position-bias gradient sums of many-bucket tiles, by (i - j)
-    float hct[kNumClasses];   // time-bias gradient sums of tiles spanning many buckets, by class
     float hbp[kNumBuckets];   // position-bias gradient sums, by bucket
-    float hbt[kNumBuckets];   // time-bias gradient sums of one- or two-bucket tiles, by bucket
+    // time-bias gradient sums by (bucket, lane % 32): at most two lanes of a wavefront share an
+    // address, whatever their buckets
+    float hbt[kNumBuckets][32];
     alignas(16) bf16 k[2][kTile * D];    // swizzled tiles (tile_off)
     bf16 v[2][kTile * D];
     bf16 qb[kBlk * D];                   // the unit's query and dO rows, swizzled like the tiles
@@ -418,8 +422,8 @@ struct TileSums {
 };
 template <int D, int PG, int TM, bool GP, bool GT>
 __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, int buf, int k0,
-                                              int u0, int g, const TimeSel tb, uint32_t ti,
-                                              int64_t ti64) {
+                                              int u0, int g, int lane, const TimeSel tb,
+                                              uint32_t ti, int64_t ti64) {
     TileSums ts{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -438,9 +442,9 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, in
                     ts.th += d >= tb.thr ? ds : 0.0f;
                     if (TM == 4) ts.th2 += d >= tb.thr2 ? ds : 0.0f;
                 }
-                if (GT && TM == 2) atomicAdd(&sm.hct[bucket_class(absdiff_u32(ti, tk4[c]))], ds);
+                if (GT && TM == 2) atomicAdd(&sm.hbt[bucket_of(absdiff_u32(ti, tk4[c]))][lane & 31], ds);
                 if (GT && TM == 3)
-                    atomicAdd(&sm.hct[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))], ds);
+                    atomicAdd(&sm.hbt[bucket_of(absdiff_sat(ti64, sm.tk64[buf][jj + c]))][lane & 31], ds);
             }
         }
     return ts;
@@ -448,14 +452,14 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, in
 
 template <int D, int PG, bool GP, bool GT>
 __device__ __forceinline__ TileSums grad_sums_tm(int tm, const f32x16& dp, SmemB<D>& sm, int buf,
-                                                 int k0, int u0, int g, const TimeSel tb,
+                                                 int k0, int u0, int g, int lane, const TimeSel tb,
                                                  uint32_t ti, int64_t ti64) {
     switch (GT ? tm : 0) {
-        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
-        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
-        case 4: return grad_sums<D, PG, 4, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
-        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
-        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, k0, u0, g, tb, ti, ti64);
+        case 0: return grad_sums<D, PG, 0, GP, GT>(dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
+        case 1: return grad_sums<D, PG, 1, GP, GT>(dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
+        case 4: return grad_sums<D, PG, 4, GP, GT>(dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
+        case 2: return grad_sums<D, PG, 2, GP, GT>(dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
+        default: return grad_sums<D, PG, 3, GP, GT>(dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
     }
 }
 
@@ -469,8 +473,9 @@ __device__ __forceinline__ void mask_keys_b(f32x16& dp, int g, int jk0, int lim,
     }
 }
 
-// A per-lane running sum for one histogram bucket (the same bucket across the wavefront); a
-// change of bucket flushes the wavefront's total with one LDS atomic.
+// A per-lane running sum for one histogram bucket (the same bucket across the wavefront).  A
+// change of bucket flushes it: add() into a per-bucket histogram as the wavefront's total (one
+// LDS atomic), add_cols() into a (bucket, lane % 32) histogram lane by lane (no reduction).
 struct Run {
     int cur = -1;
     float acc = 0.0f;
@@ -478,6 +483,14 @@ struct Run {
         if (bucket != cur) {
             const float tot = wave_sum_dpp(acc);
             if (cur >= 0 && lane == 0) atomicAdd(&hist[cur], tot);
+            cur = bucket;
+            acc = 0.0f;
+        }
+        acc += v;
+    }
+    __device__ __forceinline__ void add_cols(float (*hist)[32], int bucket, float v, int lane) {
+        if (bucket != cur) {
+            if (cur >= 0) atomicAdd(&hist[cur][lane & 31], acc);
             cur = bucket;
             acc = 0.0f;
         }
@@ -510,9 +523,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         for (int e = tid; e < kNumBuckets; e += kThreads)
             sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
     }
-    for (int e = tid; e < kNumClasses; e += kThreads) sm.hct[e] = 0.0f;
     for (int e = tid; e < 2 * (kToep + 1); e += kThreads) (&sm.dg[0][0])[e] = 0.0f;
-    for (int e = tid; e < kNumBuckets; e += kThreads) { sm.hbp[e] = 0.0f; sm.hbt[e] = 0.0f; }
+    for (int e = tid; e < kNumBuckets; e += kThreads) sm.hbp[e] = 0.0f;
+    for (int e = tid; e < kNumBuckets * 32; e += kThreads) (&sm.hbt[0][0])[e] = 0.0f;
     const int64_t tbase = RT ? p.ts[tok0] : 0;
 
     const int rhi = imin(r0 + kBlk, n);
@@ -580,8 +593,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
             const TimeRange tr = wave_time_range(tkr, real, tbase);
             if (tid == 0) {
                 sm.fits[buf] = tr.fit ? 1 : 0;
-                sm.tkmin[buf] = tr.lo;
-                sm.tkmax[buf] = tr.hi;
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    sm.tkmin[buf][hf] = tr.lo[hf];
+                    sm.tkmax[buf][hf] = tr.hi[hf];
+                }
             }
         }
         if (RP)
@@ -637,7 +653,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
+                st = bias_span(timin - sm.tkmax[buf][kh], timax - sm.tkmin[buf][kh]);
                 tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb);
             } else tb.set_const(bpos);
             if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);
@@ -646,24 +662,24 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
             if (GP || GT) {
                 const int pg = !GP ? 0 : (sp.kind == 0 ? 0 : (sp.kind == 1 ? 1 : 2));
                 TileSums ts;
-                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, k0, u0, g, tb, ti, ti64);
-                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, k0, u0, g, tb, ti, ti64);
-                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, k0, u0, g, tb, ti, ti64);
+                if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
+                else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
+                else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, buf, k0, u0, g, lane, tb, ti, ti64);
                 if (GP && pg == 0) run_p_lo.add(sm.hbp, sp.b_lo, ts.sum, lane);
                 if (GP && pg == 1) {
                     const float hi_part = ts.mp - (float)sp.b_lo * ts.sum;
                     run_p_lo.add(sm.hbp, sp.b_lo, ts.sum - hi_part, lane);
                     run_p_hi.add(sm.hbp, sp.b_hi, hi_part, lane);
                 }
-                if (GT && tm == 0) run_t_lo.add(sm.hbt, st.b_lo, ts.sum, lane);
+                if (GT && tm == 0) run_t_lo.add_cols(sm.hbt, st.b_lo, ts.sum, lane);
                 if (GT && tm == 1) {
-                    run_t_lo.add(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
-                    run_t_hi.add(sm.hbt, st.b_hi, ts.th, lane);
+                    run_t_lo.add_cols(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
+                    run_t_hi.add_cols(sm.hbt, st.b_hi, ts.th, lane);
                 }
                 if (GT && tm == 4) {
-                    run_t_lo.add(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
-                    run_t_mid.add(sm.hbt, st.b_lo + 1, ts.th - ts.th2, lane);
-                    run_t_hi.add(sm.hbt, st.b_hi, ts.th2, lane);
+                    run_t_lo.add_cols(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
+                    run_t_mid.add_cols(sm.hbt, st.b_lo + 1, ts.th - ts.th2, lane);
+                    run_t_hi.add_cols(sm.hbt, st.b_hi, ts.th2, lane);
                 }
             }
 #pragma unroll
@@ -719,18 +735,20 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
     if (GP || GT) {
         if (GP) { run_p_lo.add(sm.hbp, -2, 0.0f, lane); run_p_hi.add(sm.hbp, -2, 0.0f, lane); }  // flush
         if (GT) {
-            run_t_lo.add(sm.hbt, -2, 0.0f, lane);
-            run_t_mid.add(sm.hbt, -2, 0.0f, lane);
-            run_t_hi.add(sm.hbt, -2, 0.0f, lane);
+            run_t_lo.add_cols(sm.hbt, -2, 0.0f, lane);
+            run_t_mid.add_cols(sm.hbt, -2, 0.0f, lane);
+            run_t_hi.add_cols(sm.hbt, -2, 0.0f, lane);
         }
         __syncthreads();
-        for (int e = tid; e < kNumClasses; e += kThreads) {
-            const int b = bucket_of_class(e);
-            if (GT && sm.hct[e] != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], sm.hct[e] * p.inv_n);
-        }
         for (int b = tid; b < kNumBuckets; b += kThreads) {
             if (GP && sm.hbp[b] != 0.0f) atomicAdd(&p.drab_pos[h * kNumBuckets + b], sm.hbp[b] * p.inv_n);
-            if (GT && sm.hbt[b] != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], sm.hbt[b] * p.inv_n);
+            if (GT) {
+                // sum the 32 columns, starting at a different column per bucket (no bank clashes)
+                float v = 0.0f;
+#pragma unroll 8
+                for (int l = 0; l < 32; ++l) v += sm.hbt[b][(l + b) & 31];
+                if (v != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], v * p.inv_n);
+            }
         }
     }
 }

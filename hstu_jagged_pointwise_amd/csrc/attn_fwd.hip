@@ -194,8 +194,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             const TimeRange tr = wave_time_range(tkr, real, tbase);
             if (tid == 0) {
                 sm.fits[buf] = tr.fit ? 1 : 0;
-                sm.tkmin[buf] = tr.lo;
-                sm.tkmax[buf] = tr.hi;
+                sm.tkmin[buf] = tr.lo[0] < tr.lo[1] ? tr.lo[0] : tr.lo[1];
+                sm.tkmax[buf] = tr.hi[0] > tr.hi[1] ? tr.hi[0] : tr.hi[1];
             }
         }
         if (RP)

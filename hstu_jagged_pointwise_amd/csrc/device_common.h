@@ -188,6 +188,24 @@ constexpr int kDppMirror = 0x140;     // row_mirror
 __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Minimum / maximum over each half (lanes 0..31, 32..63) of the wavefront.
+__device__ __forceinline__ void half_min_max_u32(uint32_t lo_in, uint32_t hi_in, uint32_t (&lo)[2],
+                                                 uint32_t (&hi)[2]) {
+    uint32_t a = lo_in, b = hi_in;
+    a = umin(a, dpp_u32<kDppXor1>(a));
+    b = umax(b, dpp_u32<kDppXor1>(b));
+    a = umin(a, dpp_u32<kDppXor2>(a));
+    b = umax(b, dpp_u32<kDppXor2>(b));
+    a = umin(a, dpp_u32<kDppHalfMirror>(a));
+    b = umax(b, dpp_u32<kDppHalfMirror>(b));
+    a = umin(a, dpp_u32<kDppMirror>(a));
+    b = umax(b, dpp_u32<kDppMirror>(b));
+    lo[0] = umin(__builtin_amdgcn_readlane(a, 0), __builtin_amdgcn_readlane(a, 16));
+    lo[1] = umin(__builtin_amdgcn_readlane(a, 32), __builtin_amdgcn_readlane(a, 48));
+    hi[0] = umax(__builtin_amdgcn_readlane(b, 0), __builtin_amdgcn_readlane(b, 16));
+    hi[1] = umax(__builtin_amdgcn_readlane(b, 32), __builtin_amdgcn_readlane(b, 48));
+}
+
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     v = umin(v, dpp_u32<kDppXor1>(v));
     v = umin(v, dpp_u32<kDppXor2>(v));
@@ -237,11 +255,12 @@ __device__ __forceinline__ int64_t wave_max64(int64_t v) {
     return v;
 }
 
-// Time range and 32-bit fit of one tile's timestamps, held one per lane by a whole wavefront
-// (lanes with real = false are ignored for the range).  When every relative time fits in 32 bits
-// the range is reduced on the biased 32-bit values with DPP, else on the 64-bit values.
+// Time range of each half (rows 0..31, 32..63) of one tile's timestamps, held one per lane by a
+// whole wavefront (lanes with real = false are ignored; a half with no real lane gets an empty
+// range lo > hi), and whether every relative time fits in 32 bits.  When they fit the ranges are
+// reduced on the biased 32-bit values with DPP, else on the 64-bit values.
 struct TimeRange {
-    int64_t lo, hi;
+    int64_t lo[2], hi[2];
     bool fit;
 };
 __device__ __forceinline__ TimeRange wave_time_range(int64_t t, bool real, int64_t base) {
@@ -249,13 +268,20 @@ __device__ __forceinline__ TimeRange wave_time_range(int64_t t, bool real, int64
     r.fit = __all(rel_time_fits(t, base));
     if (r.fit) {
         const uint32_t u = rel_time_u32(t, base);
-        const uint32_t lo = wave_min_u32(real ? u : 0xffffffffu);
-        const uint32_t hi = wave_max_u32(real ? u : 0u);
-        r.lo = base + (int64_t)(int32_t)(lo - 0x80000000u);
-        r.hi = base + (int64_t)(int32_t)(hi - 0x80000000u);
+        uint32_t lo[2], hi[2];
+        half_min_max_u32(real ? u : 0xffffffffu, real ? u : 0u, lo, hi);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            r.lo[h] = base + (int64_t)(int32_t)(lo[h] - 0x80000000u);
+            r.hi[h] = base + (int64_t)(int32_t)(hi[h] - 0x80000000u);
+        }
     } else {
-        r.lo = wave_min64(real ? t : INT64_MAX);
-        r.hi = wave_max64(real ? t : INT64_MIN);
+        const int half = (int)(__lane_id() >> 5);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            r.lo[h] = wave_min64(real && half == h ? t : INT64_MAX);
+            r.hi[h] = wave_max64(real && half == h ? t : INT64_MIN);
+        }
     }
     return r;
 }
