@@ -358,7 +358,6 @@ struct SmemB {
     int64_t tk64[2][kTile];
     int64_t tkmin[2][2], tkmax[2][2];  // time range of the real keys of each 32-key half
     int fits[2];
-    float dg[2][kToep + 1];   // position-bias gradient sums of many-bucket tiles, by (i - j)
     float hbp[kNumBuckets];   // position-bias gradient sums, by bucket
     // time-bias gradient sums by (bucket, lane % 32): at most two lanes of a wavefront share an
     // address, whatever their buckets
@@ -414,9 +413,10 @@ __device__ __forceinline__ void epilogue_b_tm(int tm, const f32x16& s, f32x16& d
 //         mp - b_lo * sum),
 //   th  = sum of dS over pairs with |dt| >= thr, th2 the same for thr2 (TM 1 and 4: two or
 //         three time buckets),
-// plus, for tiles spanning more buckets, per-diagonal LDS sums for the position term (PG 2;
-// each lane adds to the slot of its own i - j, so lanes do not collide) and per-element LDS
-// histogram updates by class for the time term (TM 2, 3).
+// plus, for tiles spanning more buckets, per-lane runs along the lane's keys (which come in
+// increasing order): a lane adds its run sum to the LDS histogram only when its own bucket
+// changes (PG 2 position, TM 2 and 3 time).  LDS float atomics cost a few cycles per active
+// lane, so few changes per lane keep them cheap.
 struct TileSums {
     float sum, mp, th, th2;
 };
@@ -425,6 +425,24 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, in
                                               int u0, int g, int lane, const TimeSel tb,
                                               uint32_t ti, int64_t ti64) {
     TileSums ts{0.0f, 0.0f, 0.0f, 0.0f};
+    int pcur = -1, tcur = -1;  // per-lane runs of the many-bucket modes
+    float pacc = 0.0f, tacc = 0.0f;
+    auto prun = [&](int b, float ds) {
+        if (b != pcur) {
+            if (pcur >= 0) atomicAdd(&sm.hbp[pcur], pacc);
+            pcur = b;
+            pacc = 0.0f;
+        }
+        pacc += ds;
+    };
+    auto trun = [&](int b, float ds) {
+        if (b != tcur) {
+            if (tcur >= 0) atomicAdd(&sm.hbt[tcur][lane & 31], tacc);
+            tcur = b;
+            tacc = 0.0f;
+        }
+        tacc += ds;
+    };
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = k0 + 8 * r + 4 * g;
@@ -436,17 +454,18 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, in
                 const int u = u0 + 8 * r + c;
                 ts.sum += ds;
                 if (GP && PG == 1) ts.mp = fmaf(ds, sm.rp[buf][u].bucket, ts.mp);
-                if (GP && PG == 2) atomicAdd(&sm.dg[buf][u], ds);
+                if (GP && PG == 2) prun((int)sm.rp[buf][u].bucket, ds);
                 if (GT && (TM == 1 || TM == 4)) {
                     const uint32_t d = absdiff_u32(ti, tk4[c]);
                     ts.th += d >= tb.thr ? ds : 0.0f;
                     if (TM == 4) ts.th2 += d >= tb.thr2 ? ds : 0.0f;
                 }
-                if (GT && TM == 2) atomicAdd(&sm.hbt[bucket_of(absdiff_u32(ti, tk4[c]))][lane & 31], ds);
-                if (GT && TM == 3)
-                    atomicAdd(&sm.hbt[bucket_of(absdiff_sat(ti64, sm.tk64[buf][jj + c]))][lane & 31], ds);
+                if (GT && TM == 2) trun(bucket_of(absdiff_u32(ti, tk4[c])), ds);
+                if (GT && TM == 3) trun(bucket_of(absdiff_sat(ti64, sm.tk64[buf][jj + c])), ds);
             }
         }
+    if (GP && PG == 2 && pcur >= 0) atomicAdd(&sm.hbp[pcur], pacc);
+    if (GT && (TM == 2 || TM == 3) && tcur >= 0) atomicAdd(&sm.hbt[tcur][lane & 31], tacc);
     return ts;
 }
 
@@ -523,7 +542,6 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         for (int e = tid; e < kNumBuckets; e += kThreads)
             sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
     }
-    for (int e = tid; e < 2 * (kToep + 1); e += kThreads) (&sm.dg[0][0])[e] = 0.0f;
     for (int e = tid; e < kNumBuckets; e += kThreads) sm.hbp[e] = 0.0f;
     for (int e = tid; e < kNumBuckets * 32; e += kThreads) (&sm.hbt[0][0])[e] = 0.0f;
     const int64_t tbase = RT ? p.ts[tok0] : 0;
@@ -553,19 +571,6 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
     Run run_p_lo, run_p_hi, run_t_lo, run_t_mid, run_t_hi;  // bias-gradient running sums
-    // Adds the per-diagonal sums of tile `tile` (buffer b) to the position histogram and clears
-    // them; called once every wavefront has finished adding to that buffer.
-    auto fold_diagonals = [&](int b, int tile) {
-        const int j0 = tile * kTile;
-        for (int u = tid; u < kToep; u += kThreads) {
-            const float v = sm.dg[b][u];
-            if (v != 0.0f) {
-                const int delta = (r0 - j0) + (kBlk - 1) - u;
-                atomicAdd(&sm.hbp[bucket_of((uint32_t)(delta < 0 ? -delta : delta))], v);
-                sm.dg[b][u] = 0.0f;
-            }
-        }
-    };
 
     const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
     const TileDma<D, kThreads> dma(tid, ld);
@@ -693,12 +698,10 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
                     dqt[db] = mfma32(trop.read(sm.k[buf], 2 * kh + sl, db), db8, dqt[db]);
             }
         }
-        if (GP && t > 0) fold_diagonals(buf ^ 1, ktl.tile(t - 1));
         if (t + 1 < ntiles) store_tile(buf ^ 1, ktl.tile(t + 1));
         wait_tile_dma();
         __syncthreads();
     }
-    if (GP && ntiles > 0) fold_diagonals((ntiles - 1) & 1, ktl.tile(ntiles - 1));
 
     // add the second key half's partial dQ into the first's through the idle K and V tile
     // buffers (adjacent), laid out [row group][db][element][lane]
