@@ -493,23 +493,15 @@ __device__ __forceinline__ void mask_keys_b(f32x16& dp, int g, int jk0, int lim,
 }
 
 // A per-lane running sum for one histogram bucket (the same bucket across the wavefront).  A
-// change of bucket flushes it: add() into a per-bucket histogram as the wavefront's total (one
-// LDS atomic), add_cols() into a (bucket, lane % 32) histogram lane by lane (no reduction).
+// change of bucket flushes the wavefront's total (DPP reduction) with one single-lane LDS atomic
+// at hist[bucket * stride].
 struct Run {
     int cur = -1;
     float acc = 0.0f;
-    __device__ __forceinline__ void add(float* hist, int bucket, float v, int lane) {
+    __device__ __forceinline__ void add(float* hist, int bucket, float v, int lane, int stride = 1) {
         if (bucket != cur) {
             const float tot = wave_sum_dpp(acc);
-            if (cur >= 0 && lane == 0) atomicAdd(&hist[cur], tot);
-            cur = bucket;
-            acc = 0.0f;
-        }
-        acc += v;
-    }
-    __device__ __forceinline__ void add_cols(float (*hist)[32], int bucket, float v, int lane) {
-        if (bucket != cur) {
-            if (cur >= 0) atomicAdd(&hist[cur][lane & 31], acc);
+            if (cur >= 0 && lane == 0) atomicAdd(&hist[cur * stride], tot);
             cur = bucket;
             acc = 0.0f;
         }
@@ -676,15 +668,15 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
                     run_p_lo.add(sm.hbp, sp.b_lo, ts.sum - hi_part, lane);
                     run_p_hi.add(sm.hbp, sp.b_hi, hi_part, lane);
                 }
-                if (GT && tm == 0) run_t_lo.add_cols(sm.hbt, st.b_lo, ts.sum, lane);
+                if (GT && tm == 0) run_t_lo.add(&sm.hbt[0][0], st.b_lo, ts.sum, lane, 32);
                 if (GT && tm == 1) {
-                    run_t_lo.add_cols(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
-                    run_t_hi.add_cols(sm.hbt, st.b_hi, ts.th, lane);
+                    run_t_lo.add(&sm.hbt[0][0], st.b_lo, ts.sum - ts.th, lane, 32);
+                    run_t_hi.add(&sm.hbt[0][0], st.b_hi, ts.th, lane, 32);
                 }
                 if (GT && tm == 4) {
-                    run_t_lo.add_cols(sm.hbt, st.b_lo, ts.sum - ts.th, lane);
-                    run_t_mid.add_cols(sm.hbt, st.b_lo + 1, ts.th - ts.th2, lane);
-                    run_t_hi.add_cols(sm.hbt, st.b_hi, ts.th2, lane);
+                    run_t_lo.add(&sm.hbt[0][0], st.b_lo, ts.sum - ts.th, lane, 32);
+                    run_t_mid.add(&sm.hbt[0][0], st.b_lo + 1, ts.th - ts.th2, lane, 32);
+                    run_t_hi.add(&sm.hbt[0][0], st.b_hi, ts.th2, lane, 32);
                 }
             }
 #pragma unroll
@@ -738,9 +730,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
     if (GP || GT) {
         if (GP) { run_p_lo.add(sm.hbp, -2, 0.0f, lane); run_p_hi.add(sm.hbp, -2, 0.0f, lane); }  // flush
         if (GT) {
-            run_t_lo.add_cols(sm.hbt, -2, 0.0f, lane);
-            run_t_mid.add_cols(sm.hbt, -2, 0.0f, lane);
-            run_t_hi.add_cols(sm.hbt, -2, 0.0f, lane);
+            run_t_lo.add(&sm.hbt[0][0], -2, 0.0f, lane, 32);
+            run_t_mid.add(&sm.hbt[0][0], -2, 0.0f, lane, 32);
+            run_t_hi.add(&sm.hbt[0][0], -2, 0.0f, lane, 32);
         }
         __syncthreads();
         for (int b = tid; b < kNumBuckets; b += kThreads) {
