@@ -119,52 +119,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const bf16* __restrict__ vg = static_cast<const bf16*>(p.v) + tok0 * p.ld_in + h * D;
     const int64_t ld = p.ld_in;
 
-    if (RP)
-        for (int e = tid; e < kNumBuckets; e += kThreads)
-            sm.wp[e] = -kLog2e * p.rab_pos[h * kNumBuckets + e];
-    if (RT) {
-        for (int e = tid; e < kNumClasses; e += kThreads)
-            sm.wt[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
-        for (int e = tid; e < kNumBuckets; e += kThreads)
-            sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
-    }
     const int64_t tbase = RT ? p.ts[tok0] : 0;
-
     const int rhi = imin(r0 + kRows, n);
     const KeyTiles kl = key_tiles_for_rows(r0, rhi, nc, nh);
     const int tbeg = wu.t0, ntiles = wu.t1 - wu.t0;  // this item's part of the tile list
     auto tile_at = [&](int t) { return kl.tile(tbeg + t); };
-
-    // this wavefront's rows and this lane's row
-    const int wlo = r0 + kWaveRows * wave, whi = imin(wlo + kWaveRows, rhi);
-    const int i = wlo + lr;
-    const bool row_ok = i < rhi;
-    int lim = -1, dg = -1;  // visible keys: j <= lim or j == dg
-    if (row_ok) {
-        if (i < nh) lim = imax(i, nc - 1);
-        else { lim = nh - 1; dg = i; }
-    }
-
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        if (row_ok) qf[ks] = load_bf16x8(qg + (int64_t)i * ld + 16 * ks + 8 * g);
-        else qf[ks] = bf16x8{};
-    }
-    uint32_t ti = 0;
-    int64_t ti64 = 0, timin = 0, timax = 0;
-    bool wave_qfit = true;
-    if (RT) {
-        ti64 = row_ok ? p.ts[tok0 + i] : tbase;
-        wave_qfit = __all(rel_time_fits(ti64, tbase));
-        ti = rel_time_u32(ti64, tbase);
-        timin = wave_min64(row_ok ? ti64 : INT64_MAX);
-        timax = wave_max64(row_ok ? ti64 : INT64_MIN);
-    }
-
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
     const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
     const TileDma<D, kThreads> dma(tid, ld);
@@ -205,8 +164,51 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             }
     };
 
-    __syncthreads();  // bias tables ready
+    // the first tile's copy runs while the bias tables, Q and the row times load
     load_tile(0, tile_at(0));
+
+    if (RP)
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wp[e] = -kLog2e * p.rab_pos[h * kNumBuckets + e];
+    if (RT) {
+        for (int e = tid; e < kNumClasses; e += kThreads)
+            sm.wt[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
+        for (int e = tid; e < kNumBuckets; e += kThreads)
+            sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
+    }
+
+    // this wavefront's rows and this lane's row
+    const int wlo = r0 + kWaveRows * wave, whi = imin(wlo + kWaveRows, rhi);
+    const int i = wlo + lr;
+    const bool row_ok = i < rhi;
+    int lim = -1, dg = -1;  // visible keys: j <= lim or j == dg
+    if (row_ok) {
+        if (i < nh) lim = imax(i, nc - 1);
+        else { lim = nh - 1; dg = i; }
+    }
+
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        if (row_ok) qf[ks] = load_bf16x8(qg + (int64_t)i * ld + 16 * ks + 8 * g);
+        else qf[ks] = bf16x8{};
+    }
+    uint32_t ti = 0;
+    int64_t ti64 = 0, timin = 0, timax = 0;
+    bool wave_qfit = true;
+    if (RT) {
+        ti64 = row_ok ? p.ts[tok0 + i] : tbase;
+        wave_qfit = __all(rel_time_fits(ti64, tbase));
+        ti = rel_time_u32(ti64, tbase);
+        timin = wave_min64(row_ok ? ti64 : INT64_MAX);
+        timax = wave_max64(row_ok ? ti64 : INT64_MIN);
+    }
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+
+    __syncthreads();  // bias tables ready
     store_tile(0, tile_at(0));
     wait_tile_dma();
     __syncthreads();
