@@ -58,6 +58,8 @@ def _load():
         lib.hstu_ref_attn_bwd_rows.argtypes = common + [p, i64, p, p, p, p, p, i32]
         lib.hstu_ref_layer_fwd.argtypes = [i64, i64, i64, i64, p, i64, i64, p, p, p, p, f64,
                                            p, p, p, f64, p, p, i32]
+        lib.hstu_ref_layer_bwd.argtypes = [i64, i64, i64, i64, p, i64, i64, p, p, p, p, f64,
+                                           p, p, p, p, f64, p, p, p, p, p, i32]
         lib.hstu_ref_num_threads.restype = i32
         _lib = lib
     return _lib
@@ -176,3 +178,23 @@ def layer_fwd(w: dict, eps: float = 1e-5, nthreads: int = 0):
                                _ptr(rt), float(w["alpha"]), _ptr(x), _ptr(w1), _ptr(w2), eps,
                                _ptr(y), _ptr(attn), nthreads)
     return y, attn
+
+
+def layer_bwd(w: dict, dy=None, eps: float = 1e-5, nthreads: int = 0) -> dict:
+    """Gradients of sum(dy * Y) for Y = layer_fwd(w): dx (T, D), dw1 (D, 4Hd), dw2 (Hd, D) and the
+    bias-table gradients (H, 128) when the tables are present; fp64."""
+    off = _i64(w["seq_offsets"])
+    B, H, d, D = len(off) - 1, int(w["heads"]), int(w["d"]), int(w["layer_dim"])
+    T = int(off[-1])
+    x, w1, w2 = _f64(w["x"]), _f64(w["w1"]), _f64(w["w2"])
+    g = _f64(w["dy"] if dy is None else dy)
+    nt, ts = _i32(w.get("num_targets")), _i64(w.get("timestamps"))
+    rp, rt = _f64(w.get("rab_pos")), _f64(w.get("rab_ts"))
+    dx = np.zeros((T, D)); dw1 = np.zeros((D, 4 * H * d)); dw2 = np.zeros((H * d, D))
+    drp = np.zeros((H, 128)) if rp is not None else None
+    drt = np.zeros((H, 128)) if rt is not None else None
+    _load().hstu_ref_layer_bwd(B, H, d, D, _ptr(off), int(w["max_seqlen"]),
+                               int(w.get("num_contexts", 0)), _ptr(nt), _ptr(ts), _ptr(rp),
+                               _ptr(rt), float(w["alpha"]), _ptr(x), _ptr(w1), _ptr(w2), _ptr(g),
+                               eps, _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(drp), _ptr(drt), nthreads)
+    return dict(dx=dx, dw1=dw1, dw2=dw2, drab_pos=drp, drab_ts=drt)

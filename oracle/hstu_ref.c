@@ -379,6 +379,136 @@ void hstu_ref_layer_fwd(int64_t B, int64_t H, int64_t d, int64_t D, const int64_
     free(z); free(u); free(qq); free(kk); free(vv); free(a);
 }
 
+/* Layer backward: gradients of sum(dy * Y) for Y = layer_fwd(x, w1, w2), by the chain rule through
+ * the steps of the forward in reverse (page 1 section 2.1.2, equations (1)-(3)):
+ *   H = X W1, Z = SiLU(H) = [U | V | Q | K], A = attention(Q, K, V),
+ *   xh = (A - mean) / sqrt(var + eps) per token, G = xh * U, Y = G W2 + X.
+ * Backward:
+ *   dW2 = G^T dy,  dG = dy W2^T,  dU = dG * xh,  dxh = dG * U,
+ *   dA = (dxh - mean(dxh) - xh * mean(dxh * xh)) / sqrt(var + eps)      (per token, over H*d)
+ *   (dQ, dK, dV, d rab) = attention backward with dout = dA,
+ *   dH = [dU | dV | dQ | dK] * SiLU'(H),  SiLU'(h) = s (1 + h (1 - s)), s = sigmoid(h),
+ *   dW1 = X^T dH,  dX = dy + dH W1^T.
+ * Outputs: dx (T x D), dw1 (D x 4Hd), dw2 (Hd x D); drab_* (H x 128) when the table is given. */
+void hstu_ref_layer_bwd(int64_t B, int64_t H, int64_t d, int64_t D, const int64_t* off, int64_t N,
+                        int64_t num_contexts, const int32_t* num_targets, const int64_t* ts,
+                        const double* rab_pos, const double* rab_ts, double alpha,
+                        const double* x, const double* w1, const double* w2, const double* dy,
+                        double eps, double* dx, double* dw1, double* dw2, double* drab_pos,
+                        double* drab_ts, int nthreads) {
+    int64_t T = off[B], Hd = H * d, W = 4 * Hd;
+    size_t nz = (size_t)(T * W + 1), na = (size_t)(T * Hd + 1);
+    double* hpre = (double*)malloc(sizeof(double) * nz);
+    double* u = (double*)malloc(sizeof(double) * na);
+    double* qq = (double*)malloc(sizeof(double) * na);
+    double* kk = (double*)malloc(sizeof(double) * na);
+    double* vv = (double*)malloc(sizeof(double) * na);
+    double* a = (double*)malloc(sizeof(double) * na);
+    double* xh = (double*)malloc(sizeof(double) * na);
+    double* rstd = (double*)malloc(sizeof(double) * (size_t)(T + 1));
+    double* g = (double*)malloc(sizeof(double) * na);
+    double* da = (double*)malloc(sizeof(double) * na);
+    double* du = (double*)malloc(sizeof(double) * na);
+    double* dq = (double*)malloc(sizeof(double) * na);
+    double* dk = (double*)malloc(sizeof(double) * na);
+    double* dv = (double*)malloc(sizeof(double) * na);
+    double* dh = (double*)malloc(sizeof(double) * nz);
+    set_threads(nthreads);
+    /* forward, keeping H (before SiLU), xh and 1/sqrt(var + eps) */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double* ht = hpre + t * W;
+        for (int64_t c = 0; c < W; ++c) ht[c] = 0.0;
+        for (int64_t e = 0; e < D; ++e) {
+            double xe = x[t * D + e];
+            const double* wr = w1 + e * W;
+            for (int64_t c = 0; c < W; ++c) ht[c] += xe * wr[c];
+        }
+        for (int64_t c = 0; c < Hd; ++c) {
+            u[t * Hd + c] = ht[c] * sigmoid(ht[c]);
+            vv[t * Hd + c] = ht[Hd + c] * sigmoid(ht[Hd + c]);
+            qq[t * Hd + c] = ht[2 * Hd + c] * sigmoid(ht[2 * Hd + c]);
+            kk[t * Hd + c] = ht[3 * Hd + c] * sigmoid(ht[3 * Hd + c]);
+        }
+    }
+    hstu_ref_attn_fwd(B, H, d, d, off, N, num_contexts, num_targets, ts, rab_pos, rab_ts, alpha,
+                      qq, kk, vv, a, nthreads);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double* at = a + t * Hd;
+        double mean = 0.0, var = 0.0;
+        for (int64_t c = 0; c < Hd; ++c) mean += at[c];
+        mean /= (double)Hd;
+        for (int64_t c = 0; c < Hd; ++c) var += (at[c] - mean) * (at[c] - mean);
+        var /= (double)Hd;
+        rstd[t] = 1.0 / sqrt(var + eps);
+        for (int64_t c = 0; c < Hd; ++c) {
+            xh[t * Hd + c] = (at[c] - mean) * rstd[t];
+            g[t * Hd + c] = xh[t * Hd + c] * u[t * Hd + c];
+        }
+    }
+    /* dW2 = G^T dy (rows of W2 independent) */
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < Hd; ++e) {
+        double* wr = dw2 + e * D;
+        for (int64_t c = 0; c < D; ++c) wr[c] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            double ge = g[t * Hd + e];
+            for (int64_t c = 0; c < D; ++c) wr[c] += ge * dy[t * D + c];
+        }
+    }
+    /* dG = dy W2^T, then the gate and LayerNorm backward, per token */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double* dxh = da + t * Hd;  /* dxh first, turned into dA in place */
+        double m1 = 0.0, m2 = 0.0;
+        for (int64_t e = 0; e < Hd; ++e) {
+            double dg = 0.0;
+            for (int64_t c = 0; c < D; ++c) dg += dy[t * D + c] * w2[e * D + c];
+            du[t * Hd + e] = dg * xh[t * Hd + e];
+            dxh[e] = dg * u[t * Hd + e];
+            m1 += dxh[e];
+            m2 += dxh[e] * xh[t * Hd + e];
+        }
+        m1 /= (double)Hd;
+        m2 /= (double)Hd;
+        for (int64_t e = 0; e < Hd; ++e) dxh[e] = (dxh[e] - m1 - xh[t * Hd + e] * m2) * rstd[t];
+    }
+    hstu_ref_attn_bwd(B, H, d, d, off, N, num_contexts, num_targets, ts, rab_pos, rab_ts, alpha,
+                      qq, kk, vv, da, dq, dk, dv, drab_pos, drab_ts, nthreads);
+    /* dH = [dU | dV | dQ | dK] * SiLU'(H) */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t c = 0; c < W; ++c) {
+            int64_t blk = c / Hd, e = c % Hd;
+            double dz = blk == 0 ? du[t * Hd + e] : blk == 1 ? dv[t * Hd + e]
+                      : blk == 2 ? dq[t * Hd + e] : dk[t * Hd + e];
+            double h = hpre[t * W + c], s = sigmoid(h);
+            dh[t * W + c] = dz * s * (1.0 + h * (1.0 - s));
+        }
+    }
+    /* dW1 = X^T dH */
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < D; ++e) {
+        double* wr = dw1 + e * W;
+        for (int64_t c = 0; c < W; ++c) wr[c] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            double xe = x[t * D + e];
+            for (int64_t c = 0; c < W; ++c) wr[c] += xe * dh[t * W + c];
+        }
+    }
+    /* dX = dy + dH W1^T */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t e = 0; e < D; ++e) {
+            double acc = dy[t * D + e];
+            for (int64_t c = 0; c < W; ++c) acc += dh[t * W + c] * w1[e * W + c];
+            dx[t * D + e] = acc;
+        }
+    free(hpre); free(u); free(qq); free(kk); free(vv); free(a); free(xh); free(rstd); free(g);
+    free(da); free(du); free(dq); free(dk); free(dv); free(dh);
+}
+
 /* ---- counting ----------------------------------------------------------------------------- */
 
 /* Number of visible (i, j) pairs of the batch for one head, by enumerating vis(). */

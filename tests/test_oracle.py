@@ -375,6 +375,48 @@ def test_layer_matches_library_routines():
     np.testing.assert_allclose(y, yb, rtol=0, atol=1e-12)
 
 
+def test_layer_backward_finite_differences():
+    # Central differences of L = sum(dy * Y) through the (separately pinned) layer forward, for
+    # every entry of x, w1, w2 and of both bias tables.  Weights are drawn large enough that the
+    # attention, LayerNorm and gate terms all carry weight in the gradients.
+    rng = np.random.default_rng(5)
+    w = hs.make_inputs([5, 8], 2, 3, dtype="fp32", seed=31, rab=True, num_contexts=1,
+                       num_targets=2, layer_dim=6, max_seqlen=9)
+    w["w1"] = rng.normal(0.0, 0.6, w["w1"].shape)
+    w["w2"] = rng.normal(0.0, 0.6, w["w2"].shape)
+    w["rab_pos"] = rng.normal(0.0, 0.5, w["rab_pos"].shape)
+    w["rab_ts"] = rng.normal(0.0, 0.5, w["rab_ts"].shape)
+    dy = rng.normal(size=(w["total_tokens"], 6))
+    g = oracle.layer_bwd(w, dy=dy)
+
+    def loss(**over):
+        return float(np.sum(oracle.layer_fwd(dict(w, **over))[0] * dy))
+
+    eps = 1e-6
+    for name, key in (("dx", "x"), ("dw1", "w1"), ("dw2", "w2"), ("drab_pos", "rab_pos"),
+                      ("drab_ts", "rab_ts")):
+        base = np.asarray(w[key], dtype=np.float64)
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            p = base.copy(); p[idx] += eps
+            m = base.copy(); m[idx] -= eps
+            num[idx] = (loss(**{key: p}) - loss(**{key: m})) / (2 * eps)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+    assert np.all(g["drab_pos"][:, 16:] == 0.0)    # no position distance reaches 16 here
+    assert np.abs(g["dw1"]).max() > 1e-2 and np.abs(g["drab_ts"]).max() > 1e-3
+
+
+def test_layer_backward_linear_in_dy():
+    w = hs.make_inputs([7, 12], 2, 4, dtype="fp32", seed=32, rab=True, num_targets=3,
+                       layer_dim=8)
+    rng = np.random.default_rng(6)
+    d1 = rng.normal(size=(19, 8)); d2 = rng.normal(size=(19, 8))
+    g1, g2 = oracle.layer_bwd(w, dy=d1), oracle.layer_bwd(w, dy=d2)
+    g3 = oracle.layer_bwd(w, dy=2.0 * d1 - d2)
+    for name in ("dx", "dw1", "dw2", "drab_pos", "drab_ts"):
+        np.testing.assert_allclose(g3[name], 2.0 * g1[name] - g2[name], rtol=1e-9, atol=1e-13)
+
+
 # ---- workload recipe --------------------------------------------------------------------------
 
 def test_workload_shapes():
