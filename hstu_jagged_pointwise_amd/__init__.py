@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libhstu_amd.so")
 HSTU_F32 = 0
 HSTU_BF16 = 1
 HSTU_PLAN_HOST_ONLY = 1
-OP_FWD, OP_FWD_GATED, OP_BWD, OP_LAYER = 0, 1, 2, 3
+OP_FWD, OP_FWD_GATED, OP_BWD, OP_LAYER, OP_LAYER_BWD = 0, 1, 2, 3, 4
 
 
 class HstuAttnArgs(ctypes.Structure):
@@ -55,7 +55,7 @@ class HstuPlanInfo(ctypes.Structure):
 
 EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_info",
            "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_bwd",
-           "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd"]
+           "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd", "hstu_layer_bwd"]
 
 _lib = None
 
@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_attn_bwd_dq.restype = I32
     lib.hstu_layer_fwd.argtypes = [P, argp, I32, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
     lib.hstu_layer_fwd.restype = I32
+    lib.hstu_layer_bwd.argtypes = [P, argp, I32, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
+                                   ctypes.c_size_t, P]
+    lib.hstu_layer_bwd.restype = I32
     _lib = lib
     return lib
 
@@ -241,3 +244,13 @@ def hstu_layer_fwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, y,
     _check(load_library().hstu_layer_fwd(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), int(d_model), _ptr(x), _ptr(w1),
         _ptr(w2), float(ln_eps), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+
+
+def hstu_layer_bwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, dy, dx, dw1, dw2,
+                   drab_pos=None, drab_ts=None, ln_eps: float = 1e-5, ws=None,
+                   stream=None) -> None:
+    ws, nbytes = _workspace(plan, OP_LAYER_BWD, d_model, ws, x.device)
+    _check(load_library().hstu_layer_bwd(
+        ctypes.c_void_p(plan.handle), ctypes.byref(args), int(d_model), _ptr(x), _ptr(w1),
+        _ptr(w2), _ptr(dy), float(ln_eps), _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(drab_pos),
+        _ptr(drab_ts), _ptr(ws), nbytes, _stream(stream)))

@@ -325,8 +325,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     exchange(dkt);
 
     if (key_ok && qh == 0) {
-        bf16* dvg = static_cast<bf16*>(p.dv) + (tok0 + j) * p.ld_out + h * D;
-        bf16* dkg = static_cast<bf16*>(p.dk) + (tok0 + j) * p.ld_out + h * D;
+        bf16* dvg = static_cast<bf16*>(p.dv) + (tok0 + j) * p.ld_grad + h * D;
+        bf16* dkg = static_cast<bf16*>(p.dk) + (tok0 + j) * p.ld_grad + h * D;
         const float sv = -kLn2 * p.inv_n, sk = p.alpha * p.inv_n;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
     }
 
     if (row_ok && kh == 0) {
-        bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_out + h * D;
+        bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
         const float sq = p.alpha * p.inv_n;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -828,7 +828,7 @@ __global__ __launch_bounds__(kF32) void bwd_dq_f32_kernel(const AttnParams p) {
         if (vis && gt) atomicAdd(&ht[bucket_class(absdiff_sat(ti, tj))], ds);
     }
     if (row_ok) {
-        float* dqg = static_cast<float*>(p.dq) + (tok0 + i) * p.ld_out + h * D;
+        float* dqg = static_cast<float*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
 #pragma unroll
         for (int c = 0; c < D; ++c) dqg[c] = acc[c] * p.alpha * p.inv_n;
     }
@@ -897,8 +897,8 @@ __global__ __launch_bounds__(kF32) void bwd_dkdv_f32_kernel(const AttnParams p) 
         }
     }
     if (key_ok) {
-        float* dkg = static_cast<float*>(p.dk) + (tok0 + j) * p.ld_out + h * D;
-        float* dvg = static_cast<float*>(p.dv) + (tok0 + j) * p.ld_out + h * D;
+        float* dkg = static_cast<float*>(p.dk) + (tok0 + j) * p.ld_grad + h * D;
+        float* dvg = static_cast<float*>(p.dv) + (tok0 + j) * p.ld_grad + h * D;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
             dkg[c] = gk[c] * p.alpha * p.inv_n;

@@ -1,0 +1,198 @@
+// gemm.hip -- the dense products of an HSTU layer and of its backward on gfx950 (page 1 section
+// 2.1.2, equations (1) and (3): Z = SiLU(X W1) and Y = (LayerNorm(A) * U) W2 + X; their
+// gradients dW1 = X^T dH, dX = dH W1^T + dY, dW2 = G^T dY and dG = dY W2^T).
+//
+// C (M x N) = epilogue(op(A) op(B)) in bf16 with fp32 accumulation on v_mfma_f32_32x32x16_bf16.
+// Each workgroup (4 wavefronts, 64 x 64 outputs each) computes a 128 x 128 tile over a range of
+// K, 64 at a time.  Operand tiles go from memory straight into LDS with buffer loads that write
+// LDS (no register staging), double buffered, in the XOR-swizzled tile layout of the attention
+// kernels:
+//   * an operand whose rows are the MFMA's row index and whose columns are K (A row-major,
+//     or B given as B^T row-major) is stored as 128 rows x 64 K and read 16 bytes per lane;
+//   * an operand stored K-major (A given as A^T, or B row-major) is stored as 64 K rows x 128
+//     and read with transposing 8-byte LDS reads in natural K order.
+// K-major operands may have any K (rows past the end read as zero), so the token dimension of
+// the weight gradients can be the reduction dimension and can be split over blockIdx.z; those
+// launches add their fp32 partial results atomically into an output the caller has cleared.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kGT = 256;               // threads
+constexpr int kGM = 128, kGN = 128, kGK = 64;
+constexpr int kGTile = kGM * kGK;      // elements of one operand stage (either form)
+
+// Transposed operand in natural K order: lane (lr = l % 32, g = l / 32) receives columns
+// c0 + lr of K rows 16 st + 8g + 0..7 from a 64 x D tile.  In each group of 16 lanes, lane s
+// supplies the address of row 8g + 4h + s / 4, columns 16 q + 4 (s % 4) .. + 3 (q = bit 4 of
+// the lane), so that after the transposing read lane i holds row 8g + 4h + e, column 16 q + i.
+template <int D>
+struct TrOperandNat {
+    int off[D / 32][2];
+    __device__ __forceinline__ explicit TrOperandNat(int lane) {
+        const int s = lane & 15, q = (lane >> 4) & 1, g = lane >> 5;
+#pragma unroll
+        for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                off[cb][h] = tile_off<D>(8 * g + 4 * h + (s >> 2), 32 * cb + 16 * q + 4 * (s & 3));
+    }
+    __device__ __forceinline__ bf16x8 read(const bf16* tile, int st, int cb) const {
+        const bf16x4 lo = lds_read_tr4(tile + 16 * st * D + off[cb][0]);
+        const bf16x4 hi = lds_read_tr4(tile + 16 * st * D + off[cb][1]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+struct GemmSmem {
+    bf16 a[2][kGTile];
+    bf16 b[2][kGTile];
+};
+
+__device__ __forceinline__ float silu_f(float x) { return x * fast_sigmoid(x); }
+
+// AT: A is given as A^T (K x M, row stride lda); else A is M x K.  BT: B is given as B^T (N x K,
+// row stride ldb); else B is K x N.
+template <bool AT, bool BT, int EPI>
+__global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) GemmSmem sm;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 5, lr = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kGM;
+    const int n0 = blockIdx.x * kGN;
+    const int64_t kbeg = (int64_t)blockIdx.z * g.kchunk;
+    const int64_t kend = min(g.K, kbeg + g.kchunk);
+    if (kbeg >= kend) return;  // uniform: whole workgroup
+    const int nk = (int)((kend - kbeg + kGK - 1) / kGK);
+    const bf16* A = static_cast<const bf16*>(g.a);
+    const bf16* B = static_cast<const bf16*>(g.b);
+
+    // A operand source
+    buffer_rsrc ars, brs;
+    if constexpr (AT) ars = rows_rsrc(A + kbeg * g.lda + m0, (int)(kend - kbeg), g.lda, kGM);
+    else ars = rows_rsrc(A + m0 * g.lda, (int)min<int64_t>(g.M - m0, kGM), g.lda, (int)g.K);
+    if constexpr (BT) brs = rows_rsrc(B + (int64_t)n0 * g.ldb, kGN, g.ldb, (int)g.K);
+    else brs = rows_rsrc(B + kbeg * g.ldb + n0, (int)(kend - kbeg), g.ldb, kGN);
+    const TileDma<AT ? 128 : 64, kGT> adma(tid, g.lda);
+    const TileDma<BT ? 64 : 128, kGT> bdma(tid, g.ldb);
+
+    auto issue = [&](int t, int buf) {
+        const int kk = t * kGK;  // relative to kbeg
+        if constexpr (AT) {
+            adma.issue(ars, sm.a[buf], (int)((int64_t)kk * g.lda * 2));
+        } else {
+            adma.issue(ars, sm.a[buf], (int)((kbeg + kk) * 2));
+            adma.issue(ars, sm.a[buf] + 64 * kGK, (int)((kbeg + kk + 64 * g.lda) * 2));
+        }
+        if constexpr (BT) {
+            bdma.issue(brs, sm.b[buf], (int)((kbeg + kk) * 2));
+            bdma.issue(brs, sm.b[buf] + 64 * kGK, (int)((kbeg + kk + 64 * g.ldb) * 2));
+        } else {
+            bdma.issue(brs, sm.b[buf], (int)((int64_t)kk * g.ldb * 2));
+        }
+    };
+
+    const RowOperand<64> rowop(lane);
+    const TrOperandNat<128> trop(lane);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+
+    issue(0, 0);
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t & 1;
+        wait_tile_dma();
+        __syncthreads();
+        if (t + 1 < nk) issue(t + 1, buf ^ 1);
+#pragma unroll
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                a[mb] = AT ? trop.read(sm.a[buf], ks, 2 * wm + mb)
+                           : rowop.read(sm.a[buf], 2 * wm + mb, ks);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                b[nb] = BT ? rowop.read(sm.b[buf], 2 * wn + nb, ks)
+                           : trop.read(sm.b[buf], ks, 2 * wn + nb);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
+        }
+    }
+
+    // lane holds C[64 wm + 32 mb + 8 r + 4 gq + c][64 wn + 32 nb + lr]
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t m = m0 + 64 * wm + 32 * mb + 8 * r + 4 * gq + c;
+                    const int64_t n = n0 + 64 * wn + 32 * nb + lr;
+                    if (m >= g.M) continue;
+                    const float x = acc[mb][nb][4 * r + c];
+                    if constexpr (EPI == kEpiSilu) {
+                        static_cast<bf16*>(g.c)[m * g.ldc + n] = (bf16)silu_f(x);
+                        if (g.c2) static_cast<bf16*>(g.c2)[m * g.ldc + n] = (bf16)x;
+                    } else if constexpr (EPI == kEpiResidual) {
+                        static_cast<bf16*>(g.c)[m * g.ldc + n] =
+                            (bf16)(x + (float)static_cast<const bf16*>(g.r)[m * g.ldr + n]);
+                    } else if constexpr (EPI == kEpiStoreF32) {
+                        static_cast<float*>(g.c)[m * g.ldc + n] = x;
+                    } else {
+                        unsafeAtomicAdd(static_cast<float*>(g.c) + m * g.ldc + n, x);
+                    }
+                }
+}
+
+template <bool AT, bool BT>
+hipError_t launch_t(const GemmArgs& g, dim3 grid, hipStream_t s) {
+    switch (g.epilogue) {
+        case kEpiSilu: hipLaunchKernelGGL((gemm_kernel<AT, BT, kEpiSilu>), grid, dim3(kGT), 0, s, g); break;
+        case kEpiResidual: hipLaunchKernelGGL((gemm_kernel<AT, BT, kEpiResidual>), grid, dim3(kGT), 0, s, g); break;
+        case kEpiStoreF32: hipLaunchKernelGGL((gemm_kernel<AT, BT, kEpiStoreF32>), grid, dim3(kGT), 0, s, g); break;
+        case kEpiAtomicF32: hipLaunchKernelGGL((gemm_kernel<AT, BT, kEpiAtomicF32>), grid, dim3(kGT), 0, s, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+    if (g.M <= 0 || g.K <= 0) return hipSuccess;
+    if (!g.a || !g.b || !g.c || g.N <= 0 || g.N % kGN != 0) return hipErrorInvalidValue;
+    if (g.epilogue == kEpiResidual && !g.r) return hipErrorInvalidValue;
+    // operands read along K (row form) need whole 64-wide K steps and no K split
+    const bool k_ragged_ok = g.at && !g.bt;
+    int64_t kchunk = g.kchunk <= 0 ? g.K : g.kchunk;
+    if (!k_ragged_ok && (g.K % kGK != 0 || kchunk < g.K)) return hipErrorInvalidValue;
+    if (kchunk % kGK != 0 && kchunk < g.K) return hipErrorInvalidValue;
+    if (g.at && g.M % kGM != 0) return hipErrorInvalidValue;
+    if (kchunk < g.K && g.epilogue != kEpiAtomicF32) return hipErrorInvalidValue;
+    // 32-bit buffer offsets: a K-major operand spans kchunk rows, a row-form operand 128 rows
+    const int64_t kspan_a = g.at ? kchunk * g.lda : kGM * g.lda + g.K;
+    const int64_t kspan_b = g.bt ? kGN * g.ldb + g.K : kchunk * g.ldb;
+    if ((kspan_a + kGK * g.lda) * 2 >= (int64_t(1) << 31) ||
+        (kspan_b + kGK * g.ldb) * 2 >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    const int64_t splits = (g.K + kchunk - 1) / kchunk;
+    if (splits > 65535) return hipErrorInvalidValue;
+    GemmArgs a = g;
+    a.kchunk = kchunk;
+    dim3 grid(g.N / kGN, (unsigned)((g.M + kGM - 1) / kGM), (unsigned)splits);
+    if (!g.at && !g.bt) return launch_t<false, false>(a, grid, s);
+    if (!g.at && g.bt) return launch_t<false, true>(a, grid, s);
+    if (g.at && !g.bt) return launch_t<true, false>(a, grid, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace hstu

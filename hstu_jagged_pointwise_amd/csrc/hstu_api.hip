@@ -31,6 +31,7 @@ struct hstu_plan {
     std::vector<FwdItem> items;  // bf16 forward launch (fwd, the longest split by key tiles)
     std::vector<FixItem> fix;
     int32_t parts = 0;           // partial slots the split items write
+    int32_t compute_units = 256;
     void* dbuf = nullptr;
     const SeqInfo* d_seqs = nullptr;
     const WorkUnit* d_fwd = nullptr;
@@ -148,6 +149,7 @@ hstu::AttnParams base_params(const hstu_plan_t* plan, const hstu_attn_args_t* a)
     int64_t hd = int64_t(a->num_heads) * a->head_dim;
     p.ld_in = a->qkv_token_stride ? a->qkv_token_stride : hd;
     p.ld_out = hd;
+    p.ld_grad = hd;
     p.alpha = a->alpha;
     p.inv_n = 1.0f / (float)a->max_seqlen;
     p.ts = a->timestamps;
@@ -251,6 +253,7 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
             return HSTU_ERR_HIP;
         }
     }
+    plan->compute_units = compute_units;
     if (bf16) build_fwd_items(plan, compute_units);
 
     if (!host_only) {
@@ -345,6 +348,12 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
         case 3: {
             (void)d_model;  // Z and A depend on H*d only
             return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256) + part_bytes(plan);
+        }
+        case 4: {
+            (void)d_model;
+            // Z, H (pre-activation), dH: T x 4Hd bf16; A, G, dA: T x Hd bf16; dG: T x Hd fp32
+            return 3 * align_up(4 * thd * 2, 256) + 3 * align_up(thd * 2, 256) +
+                   align_up(thd * 4, 256) + part_bytes(plan);
         }
         default: return 0;
     }
@@ -473,21 +482,67 @@ hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
     return hstu_attn_bwd_dq(plan, args, q, k, v, dout, dq, drab_pos, drab_ts, stream);
 }
 
-hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
-                             int32_t d_model, const void* x, const void* w1, const void* w2,
-                             float ln_eps, void* y, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+hstu_status_t layer_checks(const hstu_plan_t* plan, const hstu_attn_args_t* args, int32_t d_model,
+                           std::initializer_list<const void*> ptrs, float ln_eps) {
     hstu_status_t st = check_call(plan, args);
     if (st != HSTU_OK) return st;
     if (args->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
-    if (!x || !w1 || !w2 || !y || !ws) return HSTU_ERR_NULL_ARG;
+    for (const void* q : ptrs)
+        if (!q) return HSTU_ERR_NULL_ARG;
     if (d_model < 128 || d_model % 128 != 0) return HSTU_ERR_UNSUPPORTED;
     if (!rows_addressable(args->max_seqlen, 4 * int64_t(args->num_heads) * args->head_dim))
         return HSTU_ERR_UNSUPPORTED;
-    if ((args->num_heads * args->head_dim) % 64 != 0) return HSTU_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y) || !aligned16(ws))
-        return HSTU_ERR_MISALIGNED;
-    if (ws_bytes < hstu_workspace_bytes(plan, 3, d_model)) return HSTU_ERR_WORKSPACE_TOO_SMALL;
+    if ((args->num_heads * args->head_dim) % 64 != 0 || args->num_heads * args->head_dim > 4096)
+        return HSTU_ERR_UNSUPPORTED;
+    for (const void* q : ptrs)
+        if (!aligned16(q)) return HSTU_ERR_MISALIGNED;
     if (!(ln_eps >= 0.0f) || !std::isfinite(ln_eps)) return HSTU_ERR_BAD_SHAPE;
+    return HSTU_OK;
+}
+
+hstu::GemmArgs gemm_args(const void* a, int64_t lda, bool at, const void* b, int64_t ldb, bool bt,
+                         int64_t M, int32_t N, int64_t K, void* c, int64_t ldc, int32_t epi) {
+    hstu::GemmArgs g{};
+    g.a = a;
+    g.lda = lda;
+    g.at = at;
+    g.b = b;
+    g.ldb = ldb;
+    g.bt = bt;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.ldc = ldc;
+    g.epilogue = epi;
+    return g;
+}
+
+// Tokens per workgroup for a weight gradient (M x N outputs summed over T tokens): enough
+// splits for about four workgroups per compute unit, at least 256 tokens each.
+int64_t token_chunk(const hstu_plan_t* plan, int64_t T, int64_t M, int64_t N) {
+    const int64_t tiles = (M / 128) * (N / 128);
+    const int64_t want = std::max<int64_t>(1, (4 * int64_t(plan->compute_units) + tiles - 1) / tiles);
+    int64_t chunk = (T + want - 1) / want;
+    chunk = std::max<int64_t>(256, (chunk + 63) / 64 * 64);
+    while ((T + chunk - 1) / chunk > 65535) chunk *= 2;
+    return chunk;
+}
+
+}  // namespace
+
+extern "C" {
+
+hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                             int32_t d_model, const void* x, const void* w1, const void* w2,
+                             float ln_eps, void* y, void* ws, size_t ws_bytes, void* stream) {
+    hstu_status_t st = layer_checks(plan, args, d_model, {x, w1, w2, y, ws}, ln_eps);
+    if (st != HSTU_OK) return st;
+    if (ws_bytes < hstu_workspace_bytes(plan, 3, d_model)) return HSTU_ERR_WORKSPACE_TOO_SMALL;
     const int64_t T = args->total_tokens;
     const int32_t hd = args->num_heads * args->head_dim;
     if (T == 0) return HSTU_OK;
@@ -495,7 +550,8 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     char* z = static_cast<char*>(ws);
     char* a = z + align_up(size_t(T) * 4 * hd * 2, 256);
     // Z = SiLU(X W1): columns [U | V | Q | K]
-    hipError_t e = hstu::launch_gemm_bf16(x, w1, z, nullptr, T, 4 * hd, d_model, 0, s);
+    hipError_t e = hstu::launch_gemm(
+        gemm_args(x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z, 4 * hd, hstu::kEpiSilu), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     hstu::AttnParams p = base_params(plan, args);
     const int64_t ldz = 4 * int64_t(hd);
@@ -511,7 +567,117 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     e = hstu::launch_ln_gate_bf16(a, z, ldz, a, T, hd, ln_eps, s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     // Y = G W2 + X
-    e = hstu::launch_gemm_bf16(a, w2, y, x, T, d_model, hd, 1, s);
+    hstu::GemmArgs g = gemm_args(a, hd, false, w2, d_model, false, T, d_model, hd, y, d_model,
+                                 hstu::kEpiResidual);
+    g.r = x;
+    g.ldr = d_model;
+    return hip_status(hstu::launch_gemm(g, s));
+}
+
+hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                             int32_t d_model, const void* x, const void* w1, const void* w2,
+                             const void* dy, float ln_eps, void* dx, float* dw1, float* dw2,
+                             float* drab_pos, float* drab_ts, void* ws, size_t ws_bytes,
+                             void* stream) {
+    // with no tokens only the gradients that are cleared need to exist
+    hstu_status_t st = args && args->total_tokens == 0
+                           ? layer_checks(plan, args, d_model, {dw1, dw2}, ln_eps)
+                           : layer_checks(plan, args, d_model, {x, w1, w2, dy, dx, dw1, dw2, ws}, ln_eps);
+    if (st != HSTU_OK) return st;
+    const int64_t T = args->total_tokens;
+    const int32_t hd = args->num_heads * args->head_dim;
+    if (hd % 128 != 0) return HSTU_ERR_UNSUPPORTED;
+    if ((drab_pos && !aligned16(drab_pos)) || (drab_ts && !aligned16(drab_ts)))
+        return HSTU_ERR_MISALIGNED;
+    if (T > 0 && ws_bytes < hstu_workspace_bytes(plan, 4, d_model))
+        return HSTU_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // weight and bias-table gradients are sums over tokens: clear them (also when T == 0)
+    drab_pos = args->rab_pos ? drab_pos : nullptr;
+    drab_ts = args->rab_ts ? drab_ts : nullptr;
+    const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
+    hipError_t e = hstu::launch_zero_f32(dw1, int64_t(d_model) * 4 * hd, s);
+    if (e == hipSuccess) e = hstu::launch_zero_f32(dw2, int64_t(hd) * d_model, s);
+    if (e == hipSuccess && drab_pos) e = hstu::launch_zero_f32(drab_pos, nb, s);
+    if (e == hipSuccess && drab_ts) e = hstu::launch_zero_f32(drab_ts, nb, s);
+    if (e != hipSuccess) return HSTU_ERR_HIP;
+    if (T == 0) return HSTU_OK;
+    const size_t wide = align_up(size_t(T) * 4 * hd * 2, 256), narrow = align_up(size_t(T) * hd * 2, 256);
+    char* z = static_cast<char*>(ws);
+    char* hpre = z + wide;
+    char* dh = hpre + wide;
+    char* a = dh + wide;
+    char* g = a + narrow;
+    char* da = g + narrow;
+    float* dg = reinterpret_cast<float*>(da + narrow);
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(dg) + align_up(size_t(T) * hd * 4, 256));
+    const int64_t ldz = 4 * int64_t(hd);
+
+    // recompute H = X W1 and Z = SiLU(H), columns [U | V | Q | K]
+    hstu::GemmArgs ga = gemm_args(x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z,
+                                  ldz, hstu::kEpiSilu);
+    ga.c2 = hpre;
+    e = hstu::launch_gemm(ga, s);
+    // recompute A = attention(Q, K, V)
+    hstu::AttnParams p = base_params(plan, args);
+    p.ld_in = ldz;
+    p.ld_out = hd;
+    p.ld_grad = ldz;
+    p.v = z + size_t(hd) * 2;
+    p.q = z + size_t(2 * hd) * 2;
+    p.k = z + size_t(3 * hd) * 2;
+    p.out = a;
+    p.part = plan->parts ? part : nullptr;
+    if (e == hipSuccess) e = hstu::launch_attn_fwd_bf16(p, s);
+    // dG = dY W2^T (fp32)
+    if (e == hipSuccess)
+        e = hstu::launch_gemm(gemm_args(dy, d_model, false, w2, d_model, true, T, hd, d_model, dg,
+                                        hd, hstu::kEpiStoreF32), s);
+    // G, dA and the U-slot gradient of H
+    if (e == hipSuccess)
+        e = hstu::launch_ln_gate_bwd_bf16(a, z, hpre, ldz, dg, g, da, dh, ldz, T, hd, ln_eps, s);
+    // dW2 = G^T dY, split over tokens
+    if (e == hipSuccess) {
+        hstu::GemmArgs gw = gemm_args(g, hd, true, dy, d_model, false, hd, d_model, T, dw2,
+                                      d_model, hstu::kEpiAtomicF32);
+        gw.kchunk = token_chunk(plan, T, hd, d_model);
+        e = hstu::launch_gemm(gw, s);
+    }
+    // attention backward with dout = dA: dV, dQ, dK into their slots of dH
+    if (e == hipSuccess) {
+        p.dout = da;
+        p.dv = dh + size_t(hd) * 2;
+        p.dq = dh + size_t(2 * hd) * 2;
+        p.dk = dh + size_t(3 * hd) * 2;
+        p.units = plan->d_bwd;
+        p.num_units = (int32_t)plan->bwd.size();
+        e = hstu::launch_attn_bwd_dkdv_bf16(p, s);
+    }
+    if (e == hipSuccess) {
+        p.units = plan->d_fwd;
+        p.num_units = (int32_t)plan->fwd.size();
+        p.drab_pos = drab_pos;
+        p.drab_ts = drab_ts;
+        e = hstu::launch_attn_bwd_dq_bf16(p, s);
+    }
+    // dH = dZ * SiLU'(H) on the V, Q, K slots (the U slot is already done)
+    if (e == hipSuccess)
+        e = hstu::launch_silu_bwd_bf16(dh + size_t(hd) * 2, hpre + size_t(hd) * 2, ldz, T, 3 * hd, s);
+    // dW1 = X^T dH, split over tokens
+    if (e == hipSuccess) {
+        hstu::GemmArgs gw = gemm_args(x, d_model, true, dh, ldz, false, d_model, 4 * hd, T, dw1,
+                                      ldz, hstu::kEpiAtomicF32);
+        gw.kchunk = token_chunk(plan, T, d_model, 4 * hd);
+        e = hstu::launch_gemm(gw, s);
+    }
+    // dX = dH W1^T + dY
+    if (e == hipSuccess) {
+        hstu::GemmArgs gx = gemm_args(dh, ldz, false, w1, ldz, true, T, d_model, ldz, dx, d_model,
+                                      hstu::kEpiResidual);
+        gx.r = dy;
+        gx.ldr = d_model;
+        e = hstu::launch_gemm(gx, s);
+    }
     return hip_status(e);
 }
 

@@ -20,7 +20,8 @@ struct AttnParams {
     int32_t heads;
     int32_t head_dim;
     int64_t ld_in;    // token stride of q, k, v (elements)
-    int64_t ld_out;   // token stride of out / dout / dq / dk / dv (elements)
+    int64_t ld_out;   // token stride of out / dout (elements)
+    int64_t ld_grad;  // token stride of dq / dk / dv (elements)
     float alpha;
     float inv_n;      // 1 / max_seqlen
     const int64_t* ts;
@@ -55,9 +56,42 @@ hipError_t launch_ln_gate_bf16(const void* a, const void* u, int64_t ldu, void* 
 hipError_t launch_ln_gate_f32(const void* a, const void* u, int64_t ldu, void* out,
                               int64_t rows, int32_t width, float eps, hipStream_t s);
 
-// C = epilogue(A (M x K) * B (K x N)); row-major bf16; epilogue 0 = SiLU, 1 = + R (residual,
-// M x N).  Requires K % 64 == 0 and N % 128 == 0.
-hipError_t launch_gemm_bf16(const void* A, const void* B, void* C, const void* R, int64_t M,
-                            int32_t N, int32_t K, int32_t epilogue, hipStream_t s);
+// Layer backward, per token row of width Hd: recomputes LayerNorm(a), writes the gate product
+// g = xhat * u (bf16), the attention-output gradient da (bf16) and the U-slot gradient before
+// the projection, dhu = dg * xhat * SiLU'(hu) (bf16, token stride lddh).  u and hu have token
+// stride ldz; a, g, da stride width; dg is fp32 with stride width.
+hipError_t launch_ln_gate_bwd_bf16(const void* a, const void* u, const void* hu, int64_t ldz,
+                                   const float* dg, void* g, void* da, void* dhu, int64_t lddh,
+                                   int64_t rows, int32_t width, float eps, hipStream_t s);
+// In place dz *= SiLU'(h) over rows x width elements with token strides ld (both).
+hipError_t launch_silu_bwd_bf16(void* dz, const void* h, int64_t ld, int64_t rows, int32_t width,
+                                hipStream_t s);
+
+// C (M x N) = epilogue(op(A) op(B)), bf16 operands, fp32 accumulation.
+enum GemmEpilogue : int32_t {
+    kEpiSilu = 0,       // C = SiLU(acc) (bf16); if c2, also c2 = acc (bf16, stride ldc)
+    kEpiResidual = 1,   // C = acc + R (bf16)
+    kEpiStoreF32 = 2,   // C = acc (fp32)
+    kEpiAtomicF32 = 3,  // C += acc (fp32, atomic; K may be split over workgroups)
+};
+struct GemmArgs {
+    const void* a;      // at ? A^T (K x M) : A (M x K), row stride lda
+    int64_t lda;
+    const void* b;      // bt ? B^T (N x K) : B (K x N), row stride ldb
+    int64_t ldb;
+    int64_t M;
+    int32_t N;          // multiple of 128
+    int64_t K;          // multiple of 64 unless (at && !bt)
+    int64_t kchunk;     // K per workgroup (0 = all); a split needs at && !bt and kEpiAtomicF32
+    void* c;
+    int64_t ldc;
+    void* c2;
+    const void* r;
+    int64_t ldr;
+    bool at;
+    bool bt;            // at && bt is not supported
+    int32_t epilogue;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 
 }  // namespace hstu

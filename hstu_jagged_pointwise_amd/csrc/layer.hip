@@ -1,122 +1,21 @@
-// layer.hip -- the dense parts of an HSTU layer on gfx950 (page 1 section 2.1.2, equations (1)
-// and (3): pointwise projection Z = SiLU(X W1), pointwise transformation
-// Y = (LayerNorm(A) * U) W2 + X; page 1 section 2.1.3: only two linear layers, fused
-// elementwise work).
-//
-// gemm_kernel: C = epilogue(A B), A (M x K) and B (K x N) row-major bf16, fp32 accumulation with
-// v_mfma_f32_32x32x16_bf16.  128 x 128 output tile per workgroup (4 wavefronts, 64 x 64 each),
-// K advanced 64 at a time through two LDS buffers.  B tiles are stored transposed (n-major) so
-// both MFMA operands read 16 contiguous bytes per lane.  The epilogue applies SiLU (projection)
-// or adds the residual before the single bf16 store.
+// layer.hip -- the row-wise parts of an HSTU layer on gfx950 (page 1 section 2.1.2, equation (3):
+// pointwise transformation LayerNorm(A) * U; page 1 section 2.1.3: fused elementwise work) and
+// of its backward.  The matrix products are in gemm.hip.
 //
 // ln_gate_kernel: one wavefront per token; mean and biased variance over the row in fp32 with
 // cross-lane reductions, then (a - mean) * rsqrt(var + eps) * u.
+//
+// ln_gate_bwd_kernel: one wavefront per token.  With xhat = (a - mean) * rstd and the incoming
+// gradient dg of g = xhat * u: du = dg * xhat, dxhat = dg * u and the LayerNorm backward
+// da = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)).  The same pass writes g (for
+// dW2 = G^T dY) and turns du into the gradient before the U projection's SiLU.
+//
+// silu_bwd_kernel: dz * SiLU'(h) in place, SiLU'(h) = s (1 + h (1 - s)), s = sigmoid(h).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace hstu {
 namespace {
-
-constexpr int kGT = 256;  // threads
-constexpr int kGM = 128, kGN = 128, kGK = 64;
-constexpr int kGP = kGK + 8;  // LDS pitch (elements) of both tiles
-
-struct GemmSmem {
-    bf16 a[2][kGM * kGP];
-    bf16 b[2][kGN * kGP];  // transposed: [n][k]
-};
-
-template <int EPI>
-__global__ __launch_bounds__(kGT, 2) void gemm_kernel(const bf16* __restrict__ A,
-                                                      const bf16* __restrict__ B,
-                                                      bf16* __restrict__ C,
-                                                      const bf16* __restrict__ R, int64_t M,
-                                                      int N, int K) {
-    __shared__ __attribute__((aligned(16))) GemmSmem sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kGM;
-    const int n0 = blockIdx.x * kGN;
-
-    bf16x8 ar[4], br[4];
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int id = tid + kGT * u, row = id >> 3, ch = id & 7;
-            const int64_t m = m0 + row;
-            ar[u] = m < M ? load_bf16x8(A + m * K + k0 + 8 * ch) : bf16x8{};
-        }
-        const int kg = tid & 15, ch = tid >> 4;  // 4 k-rows x 8 columns
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            br[kk] = load_bf16x8(B + (int64_t)(k0 + 4 * kg + kk) * N + n0 + 8 * ch);
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int id = tid + kGT * u, row = id >> 3, ch = id & 7;
-            *reinterpret_cast<bf16x8*>(&sm.a[buf][row * kGP + 8 * ch]) = ar[u];
-        }
-        const int kg = tid & 15, ch = tid >> 4;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 w = {br[0][e], br[1][e], br[2][e], br[3][e]};
-            *reinterpret_cast<bf16x4*>(&sm.b[buf][(8 * ch + e) * kGP + 4 * kg]) = w;
-        }
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
-
-    const int nk = K / kGK;
-    load(0);
-    store(0);
-    if (nk > 1) load(kGK);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-        const int buf = t & 1;
-#pragma unroll
-        for (int ks = 0; ks < kGK / 16; ++ks) {
-            bf16x8 a[2], b[2];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                a[mb] = *reinterpret_cast<const bf16x8*>(
-                    &sm.a[buf][(64 * wm + 32 * mb + lr) * kGP + 16 * ks + 8 * g]);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                b[nb] = *reinterpret_cast<const bf16x8*>(
-                    &sm.b[buf][(64 * wn + 32 * nb + lr) * kGP + 16 * ks + 8 * g]);
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
-        }
-        if (t + 1 < nk) store(buf ^ 1);
-        if (t + 2 < nk) load((t + 2) * kGK);
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int64_t m = m0 + 64 * wm + 32 * mb + 8 * r + 4 * g + c;
-                    const int nn = n0 + 64 * wn + 32 * nb + lr;
-                    if (m < M) {
-                        float x = acc[mb][nb][4 * r + c];
-                        if (EPI == 0) x = x * fast_sigmoid(x);
-                        else x += (float)R[m * N + nn];
-                        C[m * N + nn] = (bf16)x;
-                    }
-                }
-}
 
 // ---- LayerNorm x gate ------------------------------------------------------------------------
 
@@ -199,6 +98,95 @@ __global__ __launch_bounds__(64 * kLnRowsPerBlock) void ln_gate_kernel(
     }
 }
 
+__device__ __forceinline__ float silu_grad(float h) {
+    const float sg = fast_sigmoid(h);
+    return sg * (1.0f + h * (1.0f - sg));
+}
+
+__global__ __launch_bounds__(64 * kLnRowsPerBlock) void ln_gate_bwd_kernel(
+    const bf16* a, const bf16* __restrict__ u, const bf16* __restrict__ hu, int64_t ldz,
+    const float* __restrict__ dg, bf16* __restrict__ g, bf16* __restrict__ da,
+    bf16* __restrict__ dhu, int64_t lddh, int64_t rows, int width, float eps) {
+    const int64_t row = (int64_t)blockIdx.x * kLnRowsPerBlock + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const bf16* ar = a + row * width;
+    float x[kLnMaxChunks][8], dx[kLnMaxChunks][8];
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kLnMaxChunks; ++k) {
+        const int c = 8 * (lane + 64 * k);
+        if (c < width) {
+            load8(ar + c, x[k]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += x[k][e];
+        }
+    }
+    const float mean = wave_sum(s) / (float)width;
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kLnMaxChunks; ++k) {
+        const int c = 8 * (lane + 64 * k);
+        if (c < width)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = x[k][e] - mean;
+                v = fmaf(d, d, v);
+            }
+    }
+    const float rstd = rsqrtf(wave_sum(v) / (float)width + eps);
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kLnMaxChunks; ++k) {
+        const int c = 8 * (lane + 64 * k);
+        if (c < width) {
+            float uu[8], hh[8], gg[8], gout[8], dh[8];
+            load8(u + row * ldz + c, uu);
+            load8(hu + row * ldz + c, hh);
+            load8(dg + row * width + c, gg);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xh = (x[k][e] - mean) * rstd;
+                x[k][e] = xh;
+                gout[e] = xh * uu[e];
+                dx[k][e] = gg[e] * uu[e];
+                dh[e] = gg[e] * xh * silu_grad(hh[e]);
+                s1 += dx[k][e];
+                s2 = fmaf(dx[k][e], xh, s2);
+            }
+            store8(g + row * width + c, gout);
+            store8(dhu + row * lddh + c, dh);
+        }
+    }
+    const float m1 = wave_sum(s1) / (float)width, m2 = wave_sum(s2) / (float)width;
+#pragma unroll
+    for (int k = 0; k < kLnMaxChunks; ++k) {
+        const int c = 8 * (lane + 64 * k);
+        if (c < width) {
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (dx[k][e] - m1 - x[k][e] * m2) * rstd;
+            store8(da + row * width + c, o);
+        }
+    }
+}
+
+constexpr int kSiluThreads = 256;
+
+__global__ __launch_bounds__(kSiluThreads) void silu_bwd_kernel(bf16* dz, const bf16* __restrict__ h,
+                                                               int64_t ld, int64_t rows, int chunks) {
+    const int64_t i = (int64_t)blockIdx.x * kSiluThreads + threadIdx.x;
+    if (i >= rows * chunks) return;
+    const int64_t row = i / chunks;
+    const int c = 8 * (int)(i - row * chunks);
+    float zz[8], hh[8];
+    load8(dz + row * ld + c, zz);
+    load8(h + row * ld + c, hh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zz[e] *= silu_grad(hh[e]);
+    store8(dz + row * ld + c, zz);
+}
+
 template <typename T>
 hipError_t launch_ln(const void* a, const void* u, int64_t ldu, void* out, int64_t rows, int width,
                      float eps, hipStream_t s) {
@@ -213,21 +201,6 @@ hipError_t launch_ln(const void* a, const void* u, int64_t ldu, void* out, int64
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const void* A, const void* B, void* C, const void* R, int64_t M,
-                            int32_t N, int32_t K, int32_t epilogue, hipStream_t s) {
-    if (M <= 0) return hipSuccess;
-    if (N % kGN != 0 || K % kGK != 0 || (epilogue == 1 && !R)) return hipErrorInvalidValue;
-    dim3 grid(N / kGN, (unsigned)((M + kGM - 1) / kGM));
-    if (epilogue == 0)
-        hipLaunchKernelGGL(gemm_kernel<0>, grid, dim3(kGT), 0, s, static_cast<const bf16*>(A),
-                           static_cast<const bf16*>(B), static_cast<bf16*>(C), nullptr, M, N, K);
-    else
-        hipLaunchKernelGGL(gemm_kernel<1>, grid, dim3(kGT), 0, s, static_cast<const bf16*>(A),
-                           static_cast<const bf16*>(B), static_cast<bf16*>(C),
-                           static_cast<const bf16*>(R), M, N, K);
-    return hipGetLastError();
-}
-
 hipError_t launch_ln_gate_bf16(const void* a, const void* u, int64_t ldu, void* out, int64_t rows,
                                int32_t width, float eps, hipStream_t s) {
     return launch_ln<bf16>(a, u, ldu, out, rows, width, eps, s);
@@ -236,6 +209,31 @@ hipError_t launch_ln_gate_bf16(const void* a, const void* u, int64_t ldu, void* 
 hipError_t launch_ln_gate_f32(const void* a, const void* u, int64_t ldu, void* out, int64_t rows,
                               int32_t width, float eps, hipStream_t s) {
     return launch_ln<float>(a, u, ldu, out, rows, width, eps, s);
+}
+
+hipError_t launch_ln_gate_bwd_bf16(const void* a, const void* u, const void* hu, int64_t ldz,
+                                   const float* dg, void* g, void* da, void* dhu, int64_t lddh,
+                                   int64_t rows, int32_t width, float eps, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (width % 8 != 0 || width > 64 * 8 * kLnMaxChunks) return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)((rows + kLnRowsPerBlock - 1) / kLnRowsPerBlock);
+    hipLaunchKernelGGL(ln_gate_bwd_kernel, dim3(blocks), dim3(64 * kLnRowsPerBlock), 0, s,
+                       static_cast<const bf16*>(a), static_cast<const bf16*>(u),
+                       static_cast<const bf16*>(hu), ldz, dg, static_cast<bf16*>(g),
+                       static_cast<bf16*>(da), static_cast<bf16*>(dhu), lddh, rows, width, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_bwd_bf16(void* dz, const void* h, int64_t ld, int64_t rows, int32_t width,
+                                hipStream_t s) {
+    if (rows <= 0 || width <= 0) return hipSuccess;
+    if (width % 8 != 0) return hipErrorInvalidValue;
+    const int chunks = width / 8;
+    const int64_t n = rows * chunks;
+    hipLaunchKernelGGL(silu_bwd_kernel, dim3((unsigned)((n + kSiluThreads - 1) / kSiluThreads)),
+                       dim3(kSiluThreads), 0, s, static_cast<bf16*>(dz),
+                       static_cast<const bf16*>(h), ld, rows, chunks);
+    return hipGetLastError();
 }
 
 }  // namespace hstu

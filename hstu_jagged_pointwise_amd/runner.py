@@ -6,8 +6,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_fwd, hstu_layer_fwd,
-               hstu_plan_create, make_args)
+from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_fwd, hstu_layer_bwd,
+               hstu_layer_fwd, hstu_plan_create, make_args)
 
 
 def to_device(batch: dict, device: str = "cuda:0") -> dict:
@@ -15,7 +15,7 @@ def to_device(batch: dict, device: str = "cuda:0") -> dict:
     import torch
     fdt = torch.bfloat16 if batch["dtype"] == "bf16" else torch.float32
     out = {}
-    for key in ("q", "k", "v", "dout", "x", "w1", "w2", "u"):
+    for key in ("q", "k", "v", "dout", "x", "w1", "w2", "u", "dy"):
         if batch.get(key) is not None:
             out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.float32)).to(
                 device=device, dtype=fdt)
@@ -92,3 +92,25 @@ def layer_fwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5
     y = torch.empty((T, D), dtype=torch.bfloat16, device=dev_device(dev)) if y is None else y
     hstu_layer_fwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], y, ln_eps=ln_eps, stream=stream)
     return y
+
+
+def layer_bwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5, ws=None,
+              stream=None) -> dict:
+    """Gradients of sum(dy * Y) for the layer: dx (bf16), dw1, dw2 and bias tables (fp32)."""
+    import torch
+    args = args_for(batch, dev) if args is None else args
+    plan = plan_for(batch, args) if plan is None else plan
+    T, D, H = batch["total_tokens"], batch["layer_dim"], batch["heads"]
+    Hd = H * batch["d"]
+    device = dev_device(dev)
+    g = dict(dx=torch.empty((T, D), dtype=torch.bfloat16, device=device),
+             dw1=torch.empty((D, 4 * Hd), dtype=torch.float32, device=device),
+             dw2=torch.empty((Hd, D), dtype=torch.float32, device=device),
+             drab_pos=None, drab_ts=None)
+    if dev.get("rab_pos") is not None:
+        g["drab_pos"] = torch.empty((H, 128), dtype=torch.float32, device=device)
+    if dev.get("rab_ts") is not None:
+        g["drab_ts"] = torch.empty((H, 128), dtype=torch.float32, device=device)
+    hstu_layer_bwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], dev["dy"], g["dx"], g["dw1"],
+                   g["dw2"], g["drab_pos"], g["drab_ts"], ln_eps=ln_eps, ws=ws, stream=stream)
+    return g

@@ -17,7 +17,8 @@ Recipe (one ``numpy.random.default_rng(seed)`` per workload, draws in this order
   3. relative-bias tables, position table then time table, each N(0, 0.02^2) of shape (H, 128);
   4. q, k, v each N(0, 0.5^2) of shape (T, H, d)  -- or, for the layer workload, X ~ N(0, 1) of
      shape (T, D), W1 ~ N(0, 0.02^2) of shape (D, 4*H*d), W2 ~ N(0, 0.02^2) of shape (H*d, D);
-  5. for the forward+backward workload, the upstream gradient dO ~ N(0, 1) of shape (T, H, d).
+  5. for the forward+backward workload, the upstream gradient dO ~ N(0, 1) of shape (T, H, d);
+     for a layer backward, dY ~ N(0, 1) of shape (T, D).
 bf16 workloads round every floating-point tensor except the bias tables to bf16 (round to
 nearest even, done by torch) and return the rounded values as float32 arrays, so both sides see
 the same numbers.
@@ -136,7 +137,10 @@ def make_inputs(lengths: Sequence[int], heads: int, d: int, *, dtype: str = "bf1
         for key in ("q", "k", "v"):
             out[key] = rnd(rng.normal(0.0, 0.5, (T, heads, d)).astype(np.float32))
     if backward:
-        out["dout"] = rnd(rng.normal(0.0, 1.0, (T, heads, d)).astype(np.float32))
+        if layer_dim:
+            out["dy"] = rnd(rng.normal(0.0, 1.0, (T, layer_dim)).astype(np.float32))
+        else:
+            out["dout"] = rnd(rng.normal(0.0, 1.0, (T, heads, d)).astype(np.float32))
     return out
 
 

@@ -130,9 +130,9 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
                               int64_t* count);
 
 /* Scratch bytes a call needs: op 0 = hstu_attn_fwd without u, 1 = hstu_attn_fwd with u,
- * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd with model width d_model (ignored otherwise).  The
- * forward ops include 512 * head_dim bytes per partial slot of split row blocks (0 when the plan
- * splits none). */
+ * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd, 4 = hstu_layer_bwd (d_model is the model width; it
+ * does not change the result at present).  The forward ops, and op 4, include 512 * head_dim
+ * bytes per partial slot of split row blocks (0 when the plan splits none). */
 size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
 
 /* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.
@@ -168,6 +168,27 @@ hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* 
 hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                              int32_t d_model, const void* x, const void* w1, const void* w2,
                              float ln_eps, void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Full HSTU layer backward, bf16 only: the gradients of sum(dy * Y) for Y = hstu_layer_fwd(x)
+ * (page 1 section 2.1.2, equations (1)-(3), by the chain rule; the forward's intermediates are
+ * recomputed, not stored).  With H = x w1, Z = SiLU(H) = [U | V | Q | K], A = attention(Q, K, V),
+ * xhat = LayerNorm(A), G = xhat * U:
+ *     dw2 = G^T dy,  dG = dy w2^T,  dU = dG * xhat,
+ *     dA = rstd * (dG*U - mean(dG*U) - xhat * mean(dG*U*xhat))          (per token),
+ *     dQ, dK, dV, drab_* = attention backward with dout = dA,
+ *     dH = [dU | dV | dQ | dK] * SiLU'(H),  dw1 = x^T dH,  dx = dy + dH w1^T.
+ * x, dy, dx: (T, d_model) bf16; w1: (d_model, 4*H*d), w2: (H*d, d_model) bf16 row-major, as in
+ * hstu_layer_fwd.  dw1 and dw2 (same shapes, fp32) and drab_pos / drab_ts ([H][128] fp32, when
+ * non-NULL and the matching table is given) are overwritten; they are summed over tokens with
+ * fp32 atomics, so their low bits depend on scheduling.  H*d must be a multiple of 128 and at
+ * most 4096, d_model a multiple of 128 (HSTU_ERR_UNSUPPORTED otherwise).  ws must hold
+ * hstu_workspace_bytes(plan, 4, d_model) bytes.  ln_eps must equal the forward's.  With no
+ * tokens only dw1 and dw2 must be non-NULL (the gradients are cleared and nothing else runs). */
+hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                             int32_t d_model, const void* x, const void* w1, const void* w2,
+                             const void* dy, float ln_eps, void* dx, float* dw1, float* dw2,
+                             float* drab_pos, float* drab_ts, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /* Static string naming a status code. */
 const char* hstu_status_str(hstu_status_t status);

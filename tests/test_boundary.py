@@ -36,7 +36,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = _lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(names) == sorted(hj.EXPORTS)
@@ -107,6 +107,14 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
                               P(16), P(16), 1 << 30, None) == 2
     assert hj.hstu_workspace_bytes(plan, hj.OP_FWD) == 0
     assert hj.hstu_workspace_bytes(plan, hj.OP_FWD_GATED) == 30 * 2 * 64 * 2
+    assert lib.hstu_layer_bwd(P(plan.handle), ctypes.byref(b), 512, *([P(16)] * 4), 1e-5,
+                              *([P(16)] * 6), 1 << 30, None) == 2
+    assert lib.hstu_layer_bwd(P(plan.handle), ctypes.byref(a), 512, *([P(16)] * 4), 1e-5,
+                              *([P(16)] * 6), 1 << 30, None) == 8   # host-only plan
+    # layer backward: Z, H and dH (T x 4Hd bf16), A, G, dA (T x Hd bf16), dG (T x Hd fp32)
+    hd = 2 * 64
+    want = 3 * (30 * 4 * hd * 2) + 3 * (30 * hd * 2) + 30 * hd * 4
+    assert hj.hstu_workspace_bytes(plan, hj.OP_LAYER_BWD, 512) == want
     plan.close()
 
 

@@ -240,6 +240,78 @@ def test_layer_workload_full():
     _layer_check(w)
 
 
+# ---- full layer backward ---------------------------------------------------------------------
+
+def _layer_bwd_check(w):
+    dev = runner.to_device(w)
+    g = runner.layer_bwd(w, dev)
+    torch.cuda.synchronize()
+    ref = oracle.layer_bwd(w)
+    errs = {}
+    for name in ("dx", "dw1", "dw2", "drab_pos", "drab_ts"):
+        if ref[name] is not None:
+            errs[name] = check(name, host(g[name]), ref[name], "bf16")
+    # dx = dy + (branch through the layer): judge the branch on its own scale too; dx is stored
+    # in bf16, so each element also carries half a bf16 ulp of |dx|.
+    got = host(g["dx"])
+    branch = ref["dx"] - w["dy"]
+    err = np.abs(got - ref["dx"])
+    allowed = BF16_REL * np.max(np.abs(branch)) + 2.0 ** -8 * np.abs(ref["dx"])
+    worst = int(np.argmax(err - allowed))
+    assert np.all(err <= allowed), (f"dx - dy: err {err.flat[worst]:.3e} > allowed "
+                                    f"{allowed.flat[worst]:.3e}")
+    say("  relative errors " + ", ".join(
+        f"{k} {v / max(np.max(np.abs(ref[k])), 1e-30):.2e}" for k, v in errs.items()))
+    return errs
+
+
+def test_layer_bwd_small():
+    w = hs.make_inputs([17, 130, 1, 64], 4, 128, dtype="bf16", seed=41, rab=True,
+                       num_contexts=4, num_targets=16, layer_dim=512, backward=True)
+    say("layer backward small")
+    _layer_bwd_check(w)
+
+
+@pytest.mark.parametrize("heads,d,D", [(2, 64, 128), (4, 32, 256), (1, 128, 384)])
+def test_layer_bwd_shapes(heads, d, D):
+    # weights scaled so that the attention, LayerNorm and gate terms carry the gradients
+    w = hs.make_inputs([5, 70, 129, 2, 64], heads, d, dtype="bf16", seed=42 + d, rab=True,
+                       num_contexts=2, num_targets=5, layer_dim=D, backward=True)
+    w["w1"] = hs.round_bf16(w["w1"] * 8.0)
+    w["w2"] = hs.round_bf16(w["w2"] * 16.0)
+    say(f"layer backward H={heads} d={d} D={D}")
+    _layer_bwd_check(w)
+
+
+def test_layer_bwd_without_time_bias():
+    w = hs.make_inputs([33, 250], 4, 128, dtype="bf16", seed=43, rab=True, num_targets=8,
+                       layer_dim=512, backward=True)
+    w["rab_ts"] = None
+    say("layer backward, position bias only")
+    _layer_bwd_check(w)
+
+
+def test_layer_bwd_empty_batch_clears_gradients():
+    w = hs.make_inputs([0, 0], 4, 128, dtype="bf16", seed=44, rab=True, layer_dim=512,
+                       backward=True, max_seqlen=8)
+    say("layer backward, no tokens")
+    dev = runner.to_device(w)
+    dev["x"] = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    dev["dy"] = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    g = runner.layer_bwd(w, dev)
+    torch.cuda.synchronize()
+    for name in ("dw1", "dw2", "drab_pos", "drab_ts"):
+        assert torch.all(g[name] == 0), name
+
+
+def test_layer_bwd_workload_full():
+    w = hs.make_workload("layer_fwd")
+    w["dy"] = hs.round_bf16(np.random.default_rng(7).normal(
+        0.0, 1.0, (w["total_tokens"], w["layer_dim"])).astype(np.float32))
+    say(f"layer backward full size, T={w['total_tokens']}")
+    _layer_bwd_check(w)
+
+
 # ---- backward -------------------------------------------------------------------------------
 
 def _bwd_check(w, dtype):
