@@ -144,6 +144,40 @@ def make_inputs(lengths: Sequence[int], heads: int, d: int, *, dtype: str = "bf1
     return out
 
 
+def make_cached_inputs(cache_lengths: Sequence[int], num_cands: Sequence[int], heads: int, d: int,
+                       *, seed: int = 0, rab: bool = True, max_seqlen: Optional[int] = None,
+                       alpha: Optional[float] = None, name: str = "cached") -> dict:
+    """Candidate scoring against a key/value cache, bf16: per user a cached history of
+    cache_lengths[b] tokens (k_cache, v_cache, cache_timestamps) and num_cands[b] candidates
+    (q, k, v, timestamps) that follow it.  Timestamps run through history then candidates as in
+    step 2 of the recipe; then the bias tables, the cached k and v, then candidate q, k, v, all
+    drawn as in steps 3-4."""
+    rng = np.random.default_rng(seed)
+    hl = np.asarray(cache_lengths, dtype=np.int64)
+    mc = np.asarray(num_cands, dtype=np.int64)
+    B = len(hl)
+    full = draw_timestamps(rng, hl + mc) if rab else None
+    out = dict(name=name, dtype="bf16", batch=B, heads=heads, d=d,
+               cache_offsets=offsets_from_lengths(hl), cand_offsets=offsets_from_lengths(mc),
+               total_tokens=int(mc.sum()), cache_tokens=int(hl.sum()),
+               max_seqlen=int(max_seqlen if max_seqlen is not None
+                              else (int((hl + mc).max()) if B else 1)),
+               alpha=float(alpha if alpha is not None else 1.0 / math.sqrt(d)),
+               timestamps=None, cache_timestamps=None, rab_pos=None, rab_ts=None)
+    if rab:
+        fo = offsets_from_lengths(hl + mc)
+        out["cache_timestamps"] = np.concatenate(
+            [full[fo[b]:fo[b] + hl[b]] for b in range(B)] or [np.zeros(0, np.int64)])
+        out["timestamps"] = np.concatenate(
+            [full[fo[b] + hl[b]:fo[b + 1]] for b in range(B)] or [np.zeros(0, np.int64)])
+        out["rab_pos"] = rng.normal(0.0, 0.02, (heads, NUM_BUCKETS)).astype(np.float32)
+        out["rab_ts"] = rng.normal(0.0, 0.02, (heads, NUM_BUCKETS)).astype(np.float32)
+    Tc, T = int(hl.sum()), int(mc.sum())
+    for key, n in (("k_cache", Tc), ("v_cache", Tc), ("q", T), ("k", T), ("v", T)):
+        out[key] = round_bf16(rng.normal(0.0, 0.5, (n, heads, d)).astype(np.float32))
+    return out
+
+
 def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
                   len_cap: Optional[int] = None) -> dict:
     """Draw one of the named workloads.

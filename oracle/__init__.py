@@ -60,6 +60,8 @@ def _load():
                                            p, p, p, f64, p, p, i32]
         lib.hstu_ref_layer_bwd.argtypes = [i64, i64, i64, i64, p, i64, i64, p, p, p, p, f64,
                                            p, p, p, p, f64, p, p, p, p, p, i32]
+        lib.hstu_ref_attn_fwd_cached.argtypes = [i64, i64, i64, p, p, i64, p, p, p, p, f64,
+                                                 p, p, p, p, p, p, i32]
         lib.hstu_ref_num_threads.restype = i32
         _lib = lib
     return _lib
@@ -137,6 +139,23 @@ def attn_fwd_rows(w: dict, row_tok, row_head, nthreads: int = 0) -> np.ndarray:
     rt, rh = _i64(row_tok), _i64(row_head)
     out = np.zeros((len(rt), a.dv), np.float64)
     _load().hstu_ref_attn_fwd_rows(*a.head, len(rt), _ptr(rt), _ptr(rh), _ptr(out), nthreads)
+    return out
+
+
+def attn_fwd_cached(w: dict, nthreads: int = 0) -> np.ndarray:
+    """Candidate rows scored against cached history keys and values (see hstu_ref.c); w holds
+    cand_offsets / cache_offsets, q, k, v (candidates), k_cache, v_cache, timestamps (candidates),
+    cache_timestamps and the bias tables.  Returns (T_cand, H, d), fp64."""
+    co, ho = _i64(w["cand_offsets"]), _i64(w["cache_offsets"])
+    q, k, v = _f64(w["q"]), _f64(w["k"]), _f64(w["v"])
+    kc, vc = _f64(w["k_cache"]), _f64(w["v_cache"])
+    B, H, d = len(co) - 1, int(w["heads"]), int(w["d"])
+    ts, tsc = _i64(w.get("timestamps")), _i64(w.get("cache_timestamps"))
+    rp, rt = _f64(w.get("rab_pos")), _f64(w.get("rab_ts"))
+    out = np.zeros((int(co[-1]), H, d))
+    _load().hstu_ref_attn_fwd_cached(B, H, d, _ptr(co), _ptr(ho), int(w["max_seqlen"]), _ptr(ts),
+                                     _ptr(tsc), _ptr(rp), _ptr(rt), float(w["alpha"]), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(kc), _ptr(vc), _ptr(out), nthreads)
     return out
 
 

@@ -110,6 +110,8 @@ static double score(const prob_t* p, int64_t s, int64_t h, int64_t i, int64_t j)
 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
+static double dot_rows(const double* a, const double* b, int64_t d);
+
 /* ---- scheduling helper: (b, h) units, longest first --------------------------------------- */
 
 typedef struct { int64_t n, b, h; } unit_t;
@@ -194,6 +196,50 @@ void hstu_ref_attn_fwd_rows(int64_t B, int64_t H, int64_t dqk, int64_t dv, const
     for (int64_t r = 0; r < nrows; ++r) {
         int64_t b = seq_of(off, B, row_tok[r]);
         fwd_row(&p, b, row_head[r], row_tok[r] - off[b], out_rows + r * dv);
+    }
+}
+
+/* ---- candidate scoring against cached history -------------------------------------------- */
+
+/* Ranking with a key/value cache (page 2 "RecSDK supports generative recommendation", HSTU
+ * acceleration operator: KV-cache support; page 1 section 2.1.2, ranking: candidates appended
+ * after the history see the whole history and themselves, never each other).  User b has nh
+ * history tokens held in the cache (rows cache_off[b] .. cache_off[b + 1] of kc / vc, positions
+ * 0 .. nh - 1, times ts_cache) and m candidates (rows cand_off[b] .. of q / k / v, positions
+ * nh + c, times ts_cand).  For candidate c and head h:
+ *     S_cj = alpha <q_c, k_j> + Wp[h, bucket(nh + c - j)] + Wt[h, bucket(|t_c - t_j|)]  (j < nh)
+ *     S_cc = alpha <q_c, k_c> + Wp[h, bucket(0)] + Wt[h, bucket(0)]
+ *     O_c  = sum_{j < nh} SiLU(S_cj) / N v_j + SiLU(S_cc) / N v_c
+ * These are the candidate rows of the full forward over [history | candidates] with the
+ * candidates as targets.  out is (T_cand, H, d). */
+void hstu_ref_attn_fwd_cached(int64_t B, int64_t H, int64_t d, const int64_t* cand_off,
+                              const int64_t* cache_off, int64_t N, const int64_t* ts_cand,
+                              const int64_t* ts_cache, const double* rab_pos,
+                              const double* rab_ts, double alpha, const double* q,
+                              const double* k, const double* v, const double* kc,
+                              const double* vc, double* out, int nthreads) {
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t x = 0; x < B * H; ++x) {
+        int64_t b = x / H, h = x % H;
+        int64_t s = cand_off[b], m = cand_off[b + 1] - s;
+        int64_t sc = cache_off[b], nh = cache_off[b + 1] - sc;
+        for (int64_t c = 0; c < m; ++c) {
+            const double* qc = q + ((s + c) * H + h) * d;
+            double* o = out + ((s + c) * H + h) * d;
+            for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
+            for (int64_t j = 0; j <= nh; ++j) {  /* j == nh stands for the candidate itself */
+                int self = j == nh;
+                const double* kj = self ? k + ((s + c) * H + h) * d : kc + ((sc + j) * H + h) * d;
+                const double* vj = self ? v + ((s + c) * H + h) * d : vc + ((sc + j) * H + h) * d;
+                double xs = alpha * dot_rows(qc, kj, d);
+                if (rab_pos) xs += rab_pos[h * NB + hstu_ref_bucket(self ? 0 : nh + c - j)];
+                if (rab_ts)
+                    xs += rab_ts[h * NB + hstu_ref_bucket(self ? 0 : absdiff64(ts_cand[s + c], ts_cache[sc + j]))];
+                double w = xs * sigmoid(xs) / (double)N;
+                for (int64_t e = 0; e < d; ++e) o[e] += w * vj[e];
+            }
+        }
     }
 }
 

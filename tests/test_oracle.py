@@ -364,6 +364,84 @@ def test_backward_is_thread_count_independent():
         np.testing.assert_array_equal(a[name], b[name])
 
 
+# ---- candidate scoring against cached history -----------------------------------------------
+
+def _as_full_sequences(w, num_contexts=0, seed=0):
+    """The same users as one jagged batch [history | candidates] with the candidates as targets;
+    history queries (whose rows are not compared) are random."""
+    rng = np.random.default_rng(seed)
+    ho, co = w["cache_offsets"], w["cand_offsets"]
+    H, d = w["heads"], w["d"]
+    parts = {k: [] for k in ("q", "k", "v", "timestamps")}
+    lengths, cand_rows = [], []
+    pos = 0
+    for b in range(w["batch"]):
+        nh, m = ho[b + 1] - ho[b], co[b + 1] - co[b]
+        parts["q"] += [rng.normal(size=(nh, H, d)), w["q"][co[b]:co[b + 1]]]
+        parts["k"] += [w["k_cache"][ho[b]:ho[b + 1]], w["k"][co[b]:co[b + 1]]]
+        parts["v"] += [w["v_cache"][ho[b]:ho[b + 1]], w["v"][co[b]:co[b + 1]]]
+        if w["timestamps"] is not None:
+            parts["timestamps"] += [w["cache_timestamps"][ho[b]:ho[b + 1]],
+                                    w["timestamps"][co[b]:co[b + 1]]]
+        cand_rows += list(range(pos + nh, pos + nh + m))
+        lengths.append(nh + m)
+        pos += nh + m
+    full = dict(w, seq_offsets=hs.offsets_from_lengths(lengths), total_tokens=pos,
+                num_contexts=num_contexts,
+                num_targets=np.diff(co).astype(np.int32))
+    for key, val in parts.items():
+        full[key] = np.concatenate(val) if val else None
+    if w["timestamps"] is None:
+        full["timestamps"] = None
+    return full, np.array(cand_rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("rab", [True, False])
+def test_cached_equals_target_rows_of_full_forward(rab):
+    w = hs.make_cached_inputs([37, 1, 5, 130, 1], [4, 3, 0, 17, 1], 2, 8, seed=51, rab=rab)
+    for key in ("q", "k", "v", "k_cache", "v_cache"):
+        w[key] = w[key].astype(np.float64)
+    got = oracle.attn_fwd_cached(w)
+    # Leading contexts change nothing for candidates, who see the whole history anyway, as long
+    # as the history is at least as long as the contexts (else candidates become contexts).
+    for nc in (0, 1):
+        full, rows = _as_full_sequences(w, num_contexts=nc)
+        want = oracle.attn_fwd(full)[rows]
+        np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+def test_cached_closed_form_constant_bias():
+    c = 0.3
+    w = hs.make_cached_inputs([9, 0, 20], [3, 2, 5], 1, 4, seed=52, rab=False, alpha=0.0)
+    # (a user without history: its candidates see only themselves)
+    w["rab_pos"] = np.full((1, 128), c)
+    got = oracle.attn_fwd_cached(w)
+    scale = silu(c) / w["max_seqlen"]
+    ho, co = w["cache_offsets"], w["cand_offsets"]
+    for b in range(3):
+        hist = w["v_cache"][ho[b]:ho[b + 1], 0].astype(np.float64).sum(axis=0)
+        for r in range(co[b], co[b + 1]):
+            np.testing.assert_allclose(got[r, 0], scale * (hist + w["v"][r, 0]), rtol=1e-12,
+                                       atol=1e-15)
+
+
+def test_cached_candidates_do_not_see_each_other():
+    w = hs.make_cached_inputs([25, 40], [6, 5], 2, 8, seed=53)
+    base = oracle.attn_fwd_cached(w)
+    w2 = dict(w)
+    for key in ("q", "k", "v"):
+        w2[key] = w[key].copy()
+    w2["timestamps"] = w["timestamps"].copy()
+    # replace candidate 2 of user 0 entirely; the others must not change
+    for key in ("q", "k", "v"):
+        w2[key][2] = -w[key][2] + 0.5
+    w2["timestamps"][2] += 1000
+    got = oracle.attn_fwd_cached(w2)
+    keep = [r for r in range(11) if r != 2]
+    np.testing.assert_array_equal(got[keep], base[keep])
+    assert not np.allclose(got[2], base[2])
+
+
 # ---- full layer ----------------------------------------------------------------------------
 
 def test_layer_matches_library_routines():
