@@ -10,8 +10,9 @@ backward passes.  Inputs are resident in HBM before timing starts.
 FLOPs are counted on visible (unmasked) pairs only: 4d per pair per head forward, 10d backward.
 
 Prints one JSON line.  Besides the headline workload it reports the forward-only workloads
-(ranking-shaped, long-tail, full layer) with warm and cold-cache timings, the dominant kernel's
-roofline, and the fp64 CPU oracle timed on a bounded sample of the same workload.
+(ranking-shaped, long-tail, full layer) with warm and cold-cache timings, the full layer's
+backward, candidate scoring against cached history, the dominant kernel's roofline, and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -272,6 +273,76 @@ def bench_forward(torch, hj, runner, name, iters=20, cold=False):
             "visible_pairs": info["visible_pairs"], "flops": flops, "bytes": nbytes}
 
 
+def bench_cached(torch, hj, runner, iters=20):
+    """Candidate scoring against cached history: 128 users with long-tail history lengths, 64
+    candidates each (4 heads of width 128).  FLOPs: 4d per visible (candidate, key) pair per
+    head; bytes: candidate q, k, v and output, cached k and v, and the timestamps."""
+    import hstu_synth as hs
+    w = hs.make_cached_workload()
+    dev = runner.to_device(w)
+    a = runner.args_for(w, dev)
+    plan = hj.hstu_plan_create_cached(a, w["cand_offsets"], w["cache_offsets"])
+    info = hj.hstu_plan_info(plan)
+    out = runner.empty_like_thd(w, dev)
+    ws = torch.empty(max(hj.hstu_workspace_bytes(plan, hj.OP_CACHED), 16), dtype=torch.uint8,
+                     device="cuda:0")
+    call = lambda: hj.hstu_attn_fwd_cached(plan, a, dev["q"], dev["k"], dev["v"], dev["k_cache"],
+                                           dev["v_cache"], dev["cache_timestamps"], out, ws=ws)
+    T, Tc, H, d = w["total_tokens"], w["cache_tokens"], w["heads"], w["d"]
+    flops = info["visible_pairs"] * 4 * d
+    nbytes = (4 * T + 2 * Tc) * H * d * 2 + 8 * (T + Tc)
+    for _ in range(5):
+        call()
+    timer = Timer(torch)
+    for _ in range(iters):
+        timer.record("x", call)
+    torch.cuda.synchronize()
+    med = float(np.median(timer.ms("x")))
+    plan.close()
+    return {"ms_median": round(med, 4), "tflops": round(flops / med / 1e9, 2),
+            "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "candidates_per_s": round(T / med * 1e3, 1),
+            "algorithmic_GBps": round(nbytes / med / 1e6, 1),
+            "pct_hbm_peak": round(100 * nbytes / med / 1e6 / PEAK_HBM_GBS, 2),
+            "visible_pairs": info["visible_pairs"], "flops": flops, "bytes": nbytes}
+
+
+def bench_layer_bwd(torch, hj, runner, iters=20):
+    """Full layer backward (recompute of the forward's intermediates included) on the full-layer
+    workload with dY ~ N(0, 1).  FLOPs counted: the backward's own products only, i.e. dG, dW2,
+    dW1, dX (2 T D Hd (1 + 1 + 4 + 4)) and 10d per visible pair per head for the attention; the
+    recomputed X W1 and attention forward are work done but not counted."""
+    import hstu_synth as hs
+    w = hs.make_workload("layer_fwd")
+    T, H, d, D = w["total_tokens"], w["heads"], w["d"], w["layer_dim"]
+    w["dy"] = hs.round_bf16(np.random.default_rng(1).normal(0.0, 1.0, (T, D)).astype(np.float32))
+    dev = runner.to_device(w)
+    a = runner.args_for(w, dev)
+    plan = runner.plan_for(w, a)
+    info = hj.hstu_plan_info(plan)
+    ws = torch.empty(hj.hstu_workspace_bytes(plan, hj.OP_LAYER_BWD, D), dtype=torch.uint8,
+                     device="cuda:0")
+    f32 = dict(dtype=torch.float32, device="cuda:0")
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device="cuda:0")
+    dw1, dw2 = torch.empty((D, 4 * H * d), **f32), torch.empty((H * d, D), **f32)
+    drp, drt = torch.empty((H, 128), **f32), torch.empty((H, 128), **f32)
+    call = lambda: hj.hstu_layer_bwd(plan, a, D, dev["x"], dev["w1"], dev["w2"], dev["dy"], dx,
+                                     dw1, dw2, drp, drt, ws=ws)
+    flops = 20 * T * D * H * d + 10 * d * info["visible_pairs"]
+    for _ in range(5):
+        call()
+    timer = Timer(torch)
+    for _ in range(iters):
+        timer.record("x", call)
+    torch.cuda.synchronize()
+    med = float(np.median(timer.ms("x")))
+    plan.close()
+    return {"ms_median": round(med, 4), "tflops": round(flops / med / 1e9, 2),
+            "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "tokens_per_s": round(T / med * 1e3, 1), "flops": flops,
+            "flops_counted": "dG, dW2, dW1, dX products and 10d per visible pair per head"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,6 +419,8 @@ def main():
             extra[name] = {"warm": bench_forward(torch, hj, runner, name)}
         extra["longtail_fwd"]["cold"] = bench_forward(torch, hj, runner, "longtail_fwd", cold=True)
         result["forward_workloads"] = extra
+        result["layer_backward"] = bench_layer_bwd(torch, hj, runner)
+        result["cached_scoring"] = bench_cached(torch, hj, runner)
     print(json.dumps(result))
 
 

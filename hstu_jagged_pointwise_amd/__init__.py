@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "_build", "libhstu_amd.so")
 HSTU_F32 = 0
 HSTU_BF16 = 1
 HSTU_PLAN_HOST_ONLY = 1
-OP_FWD, OP_FWD_GATED, OP_BWD, OP_LAYER, OP_LAYER_BWD = 0, 1, 2, 3, 4
+OP_FWD, OP_FWD_GATED, OP_BWD, OP_LAYER, OP_LAYER_BWD, OP_CACHED = 0, 1, 2, 3, 4, 5
 
 
 class HstuAttnArgs(ctypes.Structure):
@@ -55,7 +55,8 @@ class HstuPlanInfo(ctypes.Structure):
 
 EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_info",
            "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_bwd",
-           "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd", "hstu_layer_bwd"]
+           "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd", "hstu_layer_bwd",
+           "hstu_plan_create_cached", "hstu_attn_fwd_cached"]
 
 _lib = None
 
@@ -95,6 +96,10 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_layer_bwd.argtypes = [P, argp, I32, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
                                    ctypes.c_size_t, P]
     lib.hstu_layer_bwd.restype = I32
+    lib.hstu_plan_create_cached.argtypes = [argp, P, P, U32, ctypes.POINTER(P)]
+    lib.hstu_plan_create_cached.restype = I32
+    lib.hstu_attn_fwd_cached.argtypes = [P, argp, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.hstu_attn_fwd_cached.restype = I32
     _lib = lib
     return lib
 
@@ -170,6 +175,18 @@ def hstu_plan_create(args: HstuAttnArgs, seq_offsets, num_targets=None, flags: i
         ctypes.byref(args), off.ctypes.data_as(ctypes.c_void_p),
         None if nt is None else nt.ctypes.data_as(ctypes.c_void_p), int(flags),
         ctypes.byref(handle)))
+    return Plan(handle.value, args)
+
+
+def hstu_plan_create_cached(args: HstuAttnArgs, cand_offsets, cache_offsets,
+                            flags: int = 0) -> Plan:
+    """Plan for candidate scoring against cached history; offsets are host arrays."""
+    co = np.ascontiguousarray(np.asarray(cand_offsets), dtype=np.int64)
+    ho = np.ascontiguousarray(np.asarray(cache_offsets), dtype=np.int64)
+    handle = ctypes.c_void_p()
+    _check(load_library().hstu_plan_create_cached(
+        ctypes.byref(args), co.ctypes.data_as(ctypes.c_void_p),
+        ho.ctypes.data_as(ctypes.c_void_p), int(flags), ctypes.byref(handle)))
     return Plan(handle.value, args)
 
 
@@ -254,3 +271,12 @@ def hstu_layer_bwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, dy, 
         ctypes.c_void_p(plan.handle), ctypes.byref(args), int(d_model), _ptr(x), _ptr(w1),
         _ptr(w2), _ptr(dy), float(ln_eps), _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(drab_pos),
         _ptr(drab_ts), _ptr(ws), nbytes, _stream(stream)))
+
+
+def hstu_attn_fwd_cached(plan: Plan, args: HstuAttnArgs, q, k, v, k_cache, v_cache,
+                         cache_timestamps, out, ws=None, stream=None) -> None:
+    ws, nbytes = _workspace(plan, OP_CACHED, 0, ws, q.device)
+    _check(load_library().hstu_attn_fwd_cached(
+        ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(k_cache), _ptr(v_cache), _ptr(cache_timestamps), _ptr(out), _ptr(ws), nbytes,
+        _stream(stream)))

@@ -105,7 +105,11 @@ __device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int g, int j0, int lim
         }
 }
 
-template <int D, bool RP, bool RT>
+// CACHED: candidate scoring.  The item's rows are candidates (positions nk + i, where nk is the
+// user's cached history length) and its key tiles run over the cache; every cached key is
+// visible (rows past the cache end read as zero, and zero V rows add nothing), and each row's
+// own key is added after the tiles by the item that holds the first tile.
+template <int D, bool RP, bool RT, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
@@ -115,17 +119,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = si.start;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * p.ld_in + h * D;
-    const bf16* __restrict__ kg = static_cast<const bf16*>(p.k) + tok0 * p.ld_in + h * D;
-    const bf16* __restrict__ vg = static_cast<const bf16*>(p.v) + tok0 * p.ld_in + h * D;
-    const int64_t ld = p.ld_in;
+    const CacheSeq cs = CACHED ? p.cache[wu.seq] : CacheSeq{0, 0};
+    const int64_t ktok0 = CACHED ? cs.start : tok0;
+    const int64_t ld = CACHED ? p.ld_cache : p.ld_in;  // key / value token stride
+    const bf16* __restrict__ kg = static_cast<const bf16*>(CACHED ? p.kc : p.k) + ktok0 * ld + h * D;
+    const bf16* __restrict__ vg = static_cast<const bf16*>(CACHED ? p.vc : p.v) + ktok0 * ld + h * D;
+    const int nk = CACHED ? cs.n : n;     // keys
+    const int rpos0 = CACHED ? cs.n : 0;  // position of row 0
+    const int64_t* __restrict__ tsk = (CACHED ? p.ts_cache : p.ts) + ktok0;
 
-    const int64_t tbase = RT ? p.ts[tok0] : 0;
+    const int64_t tbase = RT ? (nk > 0 ? tsk[0] : p.ts[tok0]) : 0;
     const int rhi = imin(r0 + kRows, n);
     const KeyTiles kl = key_tiles_for_rows(r0, rhi, nc, nh);
     const int tbeg = wu.t0, ntiles = wu.t1 - wu.t0;  // this item's part of the tile list
-    auto tile_at = [&](int t) { return kl.tile(tbeg + t); };
+    auto tile_at = [&](int t) { return CACHED ? tbeg + t : kl.tile(tbeg + t); };
 
-    const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
+    const buffer_rsrc krs = rows_rsrc(kg, nk, ld, D), vrs = rows_rsrc(vg, nk, ld, D);
     const TileDma<D, kThreads> dma(tid, ld);
     const RowOperand<D> kop(lane);
     const TrOperand<D> vop(lane);
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         dma.issue(vrs, sm.v[buf], row_bytes);
         if (RT && tid < kBN) {
             const int j = j0 + tid;
-            tkr = j < n ? p.ts[tok0 + j] : tbase;
+            tkr = j < nk ? tsk[j] : tbase;
         }
     };
 
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     auto store_tile = [&](int buf, int tile) {
         const int j0 = tile * kBN;
         if (RT && tid < kBN) {  // exactly wavefront 0
-            const bool real = j0 + tid < n;
+            const bool real = j0 + tid < nk;
             sm.tk64[buf][tid] = tkr;
             sm.tk[buf][tid] = rel_time_u32(tkr, tbase);
             const TimeRange tr = wave_time_range(tkr, real, tbase);
@@ -159,13 +168,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         }
         if (RP)
             for (int u = tid; u < kToep; u += kThreads) {
-                const int delta = (r0 - j0) + (kRows - 1) - u;  // i - j for table slot u
+                const int delta = (r0 + rpos0 - j0) + (kRows - 1) - u;  // i - j for table slot u
                 sm.rp[buf][u] = sm.wp[bucket_of((uint32_t)(delta < 0 ? -delta : delta))];
             }
     };
 
     // the first tile's copy runs while the bias tables, Q and the row times load
-    load_tile(0, tile_at(0));
+    if (ntiles > 0) load_tile(0, tile_at(0));
 
     if (RP)
         for (int e = tid; e < kNumBuckets; e += kThreads)
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const int i = wlo + lr;
     const bool row_ok = i < rhi;
     int lim = -1, dg = -1;  // visible keys: j <= lim or j == dg
-    if (row_ok) {
+    if (row_ok && !CACHED) {
         if (i < nh) lim = imax(i, nc - 1);
         else { lim = nh - 1; dg = i; }
     }
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
 
     __syncthreads();  // bias tables ready
-    store_tile(0, tile_at(0));
+    if (ntiles > 0) store_tile(0, tile_at(0));
     wait_tile_dma();
     __syncthreads();
 
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, j0 = tile_at(t) * kBN;
         if (t + 1 < ntiles) load_tile(buf ^ 1, tile_at(t + 1));
-        const int kind = wlo < rhi ? classify_row_tile(wlo, whi, j0, n, nc, nh) : kEmpty;
+        const int kind = wlo >= rhi ? kEmpty : CACHED ? kFull : classify_row_tile(wlo, whi, j0, n, nc, nh);
         if (kind != kEmpty) {
             f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -233,8 +242,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             float bpos = 0.0f;
             int pm = 0;
             if (RP) {
-                const int jhi = imin(j0 + kBN, n) - 1;
-                const BiasSpan sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - j0);
+                const int jhi = imin(j0 + kBN, nk) - 1;
+                const BiasSpan sp = bias_span((int64_t)wlo + rpos0 - jhi, (int64_t)(whi - 1 + rpos0) - j0);
                 if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
@@ -260,6 +269,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         if (t + 1 < ntiles) store_tile(buf ^ 1, tile_at(t + 1));
         wait_tile_dma();
         __syncthreads();
+    }
+
+    if (CACHED && row_ok && wu.t0 == 0) {  // the row's own key and value
+        const bf16* kr = static_cast<const bf16*>(p.k) + (tok0 + i) * p.ld_in + h * D;
+        const bf16* vr = static_cast<const bf16*>(p.v) + (tok0 + i) * p.ld_in + h * D;
+        float dot = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 kv = load_bf16x8(kr + 16 * ks + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[ks][e], (float)kv[e], dot);
+        }
+        dot += __shfl_xor(dot, 32);
+        float b = 0.0f;  // distance 0 in position and time: bucket 0
+        if (RP) b += sm.wp[0];
+        if (RT) b += sm.wtb[0];
+        const float pw = silu_scaled(fmaf(alpha2, dot, b));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bf16x4 vv = *reinterpret_cast<const bf16x4*>(vr + 32 * db + 8 * r + 4 * g);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[db][4 * r + c] = fmaf(pw, (float)vv[c], o[db][4 * r + c]);
+            }
     }
 
     if (row_ok && wu.part >= 0) {  // one piece of a split row block: fp32 partial sums
@@ -373,7 +407,10 @@ __global__ __launch_bounds__(kThreads) void fwd_fix_kernel(const AttnParams p) {
 
 template <int D, bool RP, bool RT>
 hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT>), dim3(p.num_items), dim3(kThreads), 0, s, p);
+    if (p.cache)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, true>), dim3(p.num_items), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, false>), dim3(p.num_items), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.num_fix == 0) return e;
     hipLaunchKernelGGL((fwd_fix_kernel<D>), dim3(p.num_fix, kRows / kFixRows), dim3(kThreads), 0, s, p);

@@ -31,6 +31,12 @@ struct SeqInfo {
     int32_t nh;     // effective number of non-candidate tokens (n - candidates)
 };
 
+// Cached history of one user for candidate scoring: rows [start, start + n) of the cache.
+struct CacheSeq {
+    int32_t start;
+    int32_t n;
+};
+
 struct WorkUnit {
     int32_t seq, head, row0, cost;
 };

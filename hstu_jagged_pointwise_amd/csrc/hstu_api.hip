@@ -17,6 +17,7 @@ using hstu::SeqInfo;
 using hstu::WorkUnit;
 using hstu::FwdItem;
 using hstu::FixItem;
+using hstu::CacheSeq;
 
 struct hstu_plan {
     int device = -1;
@@ -32,12 +33,15 @@ struct hstu_plan {
     std::vector<FixItem> fix;
     int32_t parts = 0;           // partial slots the split items write
     int32_t compute_units = 256;
+    bool cached = false;         // candidate scoring against cached history
+    std::vector<CacheSeq> cache;
     void* dbuf = nullptr;
     const SeqInfo* d_seqs = nullptr;
     const WorkUnit* d_fwd = nullptr;
     const WorkUnit* d_bwd = nullptr;
     const FwdItem* d_items = nullptr;
     const FixItem* d_fix = nullptr;
+    const CacheSeq* d_cache = nullptr;
 };
 
 namespace {
@@ -82,6 +86,7 @@ hstu_status_t check_call(const hstu_plan_t* plan, const hstu_attn_args_t* a) {
         a->max_seqlen != p.max_seqlen || a->num_contexts != p.num_contexts)
         return HSTU_ERR_BAD_SHAPE;
     if (!plan->on_device) return HSTU_ERR_NO_DEVICE_PLAN;
+    if (plan->cached) return HSTU_ERR_BAD_SHAPE;
     if ((a->timestamps && !aligned16(a->timestamps)) || (a->rab_pos && !aligned16(a->rab_pos)) ||
         (a->rab_ts && !aligned16(a->rab_ts)))
         return HSTU_ERR_MISALIGNED;
@@ -159,6 +164,62 @@ hstu::AttnParams base_params(const hstu_plan_t* plan, const hstu_attn_args_t* a)
 }
 
 hstu_status_t hip_status(hipError_t e) { return e == hipSuccess ? HSTU_OK : HSTU_ERR_HIP; }
+
+// Builds the bf16 forward items and, unless HSTU_PLAN_HOST_ONLY, copies every list into one
+// device buffer.  Takes ownership of plan (deleted on failure).
+hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) {
+    const bool host_only = (flags & HSTU_PLAN_HOST_ONLY) != 0;
+    int compute_units = 256;
+    if (!host_only) {
+        if (hipGetDevice(&plan->device) != hipSuccess ||
+            hipDeviceGetAttribute(&compute_units, hipDeviceAttributeMultiprocessorCount,
+                                  plan->device) != hipSuccess) {
+            delete plan;
+            return HSTU_ERR_HIP;
+        }
+    }
+    plan->compute_units = compute_units;
+    if (plan->shape.dtype == HSTU_BF16) build_fwd_items(plan, compute_units);
+
+    if (!host_only) {
+        const size_t sizes[6] = {sizeof(SeqInfo) * plan->seqs.size(),
+                                 sizeof(WorkUnit) * plan->fwd.size(),
+                                 sizeof(WorkUnit) * plan->bwd.size(),
+                                 sizeof(FwdItem) * plan->items.size(),
+                                 sizeof(FixItem) * plan->fix.size(),
+                                 sizeof(CacheSeq) * plan->cache.size()};
+        const void* srcs[6] = {plan->seqs.data(), plan->fwd.data(), plan->bwd.data(),
+                               plan->items.data(), plan->fix.data(), plan->cache.data()};
+        size_t offs[6], total = 0;
+        for (int i = 0; i < 6; ++i) {
+            offs[i] = total;
+            total += align_up(sizes[i], 16);
+        }
+        total = std::max<size_t>(total, 16);
+        std::vector<char> host(total);
+        for (int i = 0; i < 6; ++i)
+            if (sizes[i]) std::memcpy(host.data() + offs[i], srcs[i], sizes[i]);
+        if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
+            delete plan;
+            return HSTU_ERR_HIP;
+        }
+        if (hipMemcpy(plan->dbuf, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipFree(plan->dbuf);
+            delete plan;
+            return HSTU_ERR_HIP;
+        }
+        char* base = static_cast<char*>(plan->dbuf);
+        plan->d_seqs = reinterpret_cast<const SeqInfo*>(base + offs[0]);
+        plan->d_fwd = reinterpret_cast<const WorkUnit*>(base + offs[1]);
+        plan->d_bwd = reinterpret_cast<const WorkUnit*>(base + offs[2]);
+        plan->d_items = reinterpret_cast<const FwdItem*>(base + offs[3]);
+        plan->d_fix = reinterpret_cast<const FixItem*>(base + offs[4]);
+        plan->d_cache = reinterpret_cast<const CacheSeq*>(base + offs[5]);
+        plan->on_device = true;
+    }
+    *out = plan;
+    return HSTU_OK;
+}
 
 }  // namespace
 
@@ -242,52 +303,7 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
     }
     sort_longest_first(plan->fwd);
     sort_longest_first(plan->bwd);
-
-    const bool host_only = (flags & HSTU_PLAN_HOST_ONLY) != 0;
-    int compute_units = 256;
-    if (!host_only) {
-        if (hipGetDevice(&plan->device) != hipSuccess ||
-            hipDeviceGetAttribute(&compute_units, hipDeviceAttributeMultiprocessorCount,
-                                  plan->device) != hipSuccess) {
-            delete plan;
-            return HSTU_ERR_HIP;
-        }
-    }
-    plan->compute_units = compute_units;
-    if (bf16) build_fwd_items(plan, compute_units);
-
-    if (!host_only) {
-        size_t nb = sizeof(SeqInfo) * plan->seqs.size();
-        size_t nf = sizeof(WorkUnit) * plan->fwd.size();
-        size_t nk = sizeof(WorkUnit) * plan->bwd.size();
-        size_t ni = sizeof(FwdItem) * plan->items.size();
-        size_t nx = sizeof(FixItem) * plan->fix.size();
-        size_t total = std::max<size_t>(nb + nf + nk + ni + nx, 16);
-        std::vector<char> host(total);
-        if (nb) std::memcpy(host.data(), plan->seqs.data(), nb);
-        if (nf) std::memcpy(host.data() + nb, plan->fwd.data(), nf);
-        if (nk) std::memcpy(host.data() + nb + nf, plan->bwd.data(), nk);
-        if (ni) std::memcpy(host.data() + nb + nf + nk, plan->items.data(), ni);
-        if (nx) std::memcpy(host.data() + nb + nf + nk + ni, plan->fix.data(), nx);
-        if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
-            delete plan;
-            return HSTU_ERR_HIP;
-        }
-        if (hipMemcpy(plan->dbuf, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
-            (void)hipFree(plan->dbuf);
-            delete plan;
-            return HSTU_ERR_HIP;
-        }
-        char* base = static_cast<char*>(plan->dbuf);
-        plan->d_seqs = reinterpret_cast<const SeqInfo*>(base);
-        plan->d_fwd = reinterpret_cast<const WorkUnit*>(base + nb);
-        plan->d_bwd = reinterpret_cast<const WorkUnit*>(base + nb + nf);
-        plan->d_items = reinterpret_cast<const FwdItem*>(base + nb + nf + nk);
-        plan->d_fix = reinterpret_cast<const FixItem*>(base + nb + nf + nk + ni);
-        plan->on_device = true;
-    }
-    *out = plan;
-    return HSTU_OK;
+    return finish_plan(plan, flags, out);
 }
 
 void hstu_plan_destroy(hstu_plan_t* plan) {
@@ -349,6 +365,7 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
             (void)d_model;  // Z and A depend on H*d only
             return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256) + part_bytes(plan);
         }
+        case 5: return plan->cached ? part_bytes(plan) : 0;
         case 4: {
             (void)d_model;
             // Z, H (pre-activation), dH: T x 4Hd bf16; A, G, dA: T x Hd bf16; dG: T x Hd fp32
@@ -679,6 +696,94 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         e = hstu::launch_gemm(gx, s);
     }
     return hip_status(e);
+}
+
+hstu_status_t hstu_plan_create_cached(const hstu_attn_args_t* args, const int64_t* cand_off,
+                                      const int64_t* cache_off, uint32_t flags,
+                                      hstu_plan_t** out) {
+    if (!out) return HSTU_ERR_NULL_ARG;
+    *out = nullptr;
+    hstu_status_t st = check_args(args);
+    if (st != HSTU_OK) return st;
+    if (args->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+    if (!cand_off || !cache_off) return HSTU_ERR_NULL_ARG;
+    const int B = args->batch;
+    if (cand_off[0] != 0 || cand_off[B] != args->total_tokens || cache_off[0] != 0)
+        return HSTU_ERR_BAD_OFFSETS;
+    for (int b = 0; b < B; ++b) {
+        const int64_t m = cand_off[b + 1] - cand_off[b], nk = cache_off[b + 1] - cache_off[b];
+        if (m < 0 || nk < 0 || m + nk > args->max_seqlen) return HSTU_ERR_BAD_OFFSETS;
+    }
+    if (cache_off[B] >= (int64_t(1) << 31)) return HSTU_ERR_BAD_SHAPE;
+    hstu_plan_t* plan = new (std::nothrow) hstu_plan_t();
+    if (!plan) return HSTU_ERR_HIP;
+    plan->shape = *args;
+    plan->shape.timestamps = nullptr;
+    plan->shape.rab_pos = nullptr;
+    plan->shape.rab_ts = nullptr;
+    plan->cached = true;
+    plan->fwd_rows = 4 * hstu::kWaveRows;
+    plan->bwd_keys = 0;
+    const int H = args->num_heads;
+    plan->seqs.resize(B);
+    plan->cache.resize(B);
+    for (int b = 0; b < B; ++b) {
+        const int m = (int)(cand_off[b + 1] - cand_off[b]), nk = (int)(cache_off[b + 1] - cache_off[b]);
+        plan->seqs[b] = SeqInfo{(int32_t)cand_off[b], m, 0, m};
+        plan->cache[b] = CacheSeq{(int32_t)cache_off[b], nk};
+        plan->pairs += int64_t(nk + 1) * m * H;
+        const int tiles = hstu::cdiv(nk, hstu::kKeyTile);
+        for (int r0 = 0; r0 < m; r0 += plan->fwd_rows) {
+            plan->fwd_tiles += int64_t(tiles) * hstu::cdiv(std::min(plan->fwd_rows, m - r0), hstu::kWaveRows) * H;
+            for (int h = 0; h < H; ++h) plan->fwd.push_back(WorkUnit{b, h, r0, tiles});
+        }
+    }
+    sort_longest_first(plan->fwd);
+    return finish_plan(plan, flags, out);
+}
+
+hstu_status_t hstu_attn_fwd_cached(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                                   const void* q, const void* k, const void* v,
+                                   const void* k_cache, const void* v_cache,
+                                   const int64_t* cache_timestamps, void* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    if (!plan) return HSTU_ERR_NULL_ARG;
+    hstu_status_t st = check_args(args);
+    if (st != HSTU_OK) return st;
+    const hstu_attn_args_t& ps = plan->shape;
+    if (!plan->cached || args->dtype != ps.dtype || args->batch != ps.batch ||
+        args->num_heads != ps.num_heads || args->head_dim != ps.head_dim ||
+        args->total_tokens != ps.total_tokens || args->max_seqlen != ps.max_seqlen)
+        return HSTU_ERR_BAD_SHAPE;
+    if (!plan->on_device) return HSTU_ERR_NO_DEVICE_PLAN;
+    if (args->total_tokens == 0) return HSTU_OK;
+    if (!q || !k || !v || !out) return HSTU_ERR_NULL_ARG;
+    int64_t cache_tokens = 0;
+    for (const CacheSeq& c : plan->cache) cache_tokens += c.n;
+    if (cache_tokens > 0 && (!k_cache || !v_cache)) return HSTU_ERR_NULL_ARG;
+    if (args->rab_ts && cache_tokens > 0 && !cache_timestamps) return HSTU_ERR_NULL_ARG;
+    for (const void* ptr : {q, k, v, (const void*)out, k_cache, v_cache, (const void*)cache_timestamps,
+                            (const void*)args->timestamps, (const void*)args->rab_pos,
+                            (const void*)args->rab_ts})
+        if (ptr && !aligned16(ptr)) return HSTU_ERR_MISALIGNED;
+    const size_t need = hstu_workspace_bytes(plan, 5, 0);
+    if (need > 0) {
+        if (!ws) return HSTU_ERR_NULL_ARG;
+        if (ws_bytes < need) return HSTU_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(ws)) return HSTU_ERR_MISALIGNED;
+    }
+    hstu::AttnParams p = base_params(plan, args);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.part = plan->parts ? static_cast<float*>(ws) : nullptr;
+    p.cache = plan->d_cache;
+    p.kc = k_cache;
+    p.vc = v_cache;
+    p.ts_cache = args->rab_ts ? cache_timestamps : nullptr;
+    p.ld_cache = int64_t(args->num_heads) * args->head_dim;
+    return hip_status(hstu::launch_attn_fwd_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

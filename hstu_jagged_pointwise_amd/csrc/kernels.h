@@ -37,6 +37,15 @@ struct AttnParams {
     void* dv;
     float* drab_pos;
     float* drab_ts;
+    // Candidate scoring against cached history (bf16 forward only).  When cache is set, seqs[b]
+    // describes user b's candidates (start, n) and cache[b] its cached history; keys and values
+    // come from kc / vc (token stride ld_cache) with times ts_cache, and each candidate row also
+    // sees its own k and v.
+    const CacheSeq* cache;
+    const void* kc;
+    const void* vc;
+    const int64_t* ts_cache;
+    int64_t ld_cache;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s);

@@ -6,8 +6,9 @@ from typing import Optional
 
 import numpy as np
 
-from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_fwd, hstu_layer_bwd,
-               hstu_layer_fwd, hstu_plan_create, make_args)
+from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_fwd, hstu_attn_fwd_cached,
+               hstu_layer_bwd, hstu_layer_fwd, hstu_plan_create, hstu_plan_create_cached,
+               make_args)
 
 
 def to_device(batch: dict, device: str = "cuda:0") -> dict:
@@ -15,15 +16,16 @@ def to_device(batch: dict, device: str = "cuda:0") -> dict:
     import torch
     fdt = torch.bfloat16 if batch["dtype"] == "bf16" else torch.float32
     out = {}
-    for key in ("q", "k", "v", "dout", "x", "w1", "w2", "u", "dy"):
+    for key in ("q", "k", "v", "dout", "x", "w1", "w2", "u", "dy", "k_cache", "v_cache"):
         if batch.get(key) is not None:
             out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.float32)).to(
                 device=device, dtype=fdt)
     for key in ("rab_pos", "rab_ts"):
         if batch.get(key) is not None:
             out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.float32)).to(device)
-    if batch.get("timestamps") is not None:
-        out["timestamps"] = torch.from_numpy(np.ascontiguousarray(batch["timestamps"], np.int64)).to(device)
+    for key in ("timestamps", "cache_timestamps"):
+        if batch.get(key) is not None:
+            out[key] = torch.from_numpy(np.ascontiguousarray(batch[key], np.int64)).to(device)
     return out
 
 
@@ -114,3 +116,14 @@ def layer_bwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5
     hstu_layer_bwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], dev["dy"], g["dx"], g["dw1"],
                    g["dw2"], g["drab_pos"], g["drab_ts"], ln_eps=ln_eps, ws=ws, stream=stream)
     return g
+
+
+def attn_fwd_cached(batch: dict, dev: dict, plan=None, args=None, out=None, stream=None):
+    """Candidate rows scored against the cached history of each user."""
+    args = args_for(batch, dev) if args is None else args
+    if plan is None:
+        plan = hstu_plan_create_cached(args, batch["cand_offsets"], batch["cache_offsets"])
+    out = empty_like_thd(batch, dev) if out is None else out
+    hstu_attn_fwd_cached(plan, args, dev["q"], dev["k"], dev["v"], dev.get("k_cache"),
+                         dev.get("v_cache"), dev.get("cache_timestamps"), out, stream=stream)
+    return out

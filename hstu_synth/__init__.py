@@ -178,6 +178,17 @@ def make_cached_inputs(cache_lengths: Sequence[int], num_cands: Sequence[int], h
     return out
 
 
+def make_cached_workload(seed: int = 0, batch: int = 128, num_cands: int = 64) -> dict:
+    """Candidate scoring at ranking scale: per user a cached history with the long-tail length
+    mix (lognormal(5, 1) clipped to [8, 4096], as the long-tail forward workload), 64
+    candidates, 4 heads of width 128, position and time bias."""
+    rng = np.random.default_rng(seed)
+    spec = WORKLOADS["longtail_fwd"]
+    hl = draw_lengths(rng, spec, batch)
+    return make_cached_inputs(hl, np.full(batch, num_cands), spec.heads, spec.d,
+                              seed=seed + 1, name="cached_scoring")
+
+
 def make_workload(name: str, seed: int = 0, *, batch: Optional[int] = None,
                   len_cap: Optional[int] = None) -> dict:
     """Draw one of the named workloads.

@@ -130,9 +130,10 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
                               int64_t* count);
 
 /* Scratch bytes a call needs: op 0 = hstu_attn_fwd without u, 1 = hstu_attn_fwd with u,
- * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd, 4 = hstu_layer_bwd (d_model is the model width; it
- * does not change the result at present).  The forward ops, and op 4, include 512 * head_dim
- * bytes per partial slot of split row blocks (0 when the plan splits none). */
+ * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd, 4 = hstu_layer_bwd, 5 = hstu_attn_fwd_cached (d_model
+ * is the model width; it does not change the result at present).  The forward ops, and op 4,
+ * include 512 * head_dim bytes per partial slot of split row blocks (0 when the plan splits
+ * none). */
 size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
 
 /* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.
@@ -189,6 +190,36 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
                              const void* dy, float ln_eps, void* dx, float* dw1, float* dw2,
                              float* drab_pos, float* drab_ts, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* Candidate scoring against cached history (page 2, "RecSDK supports generative
+ * recommendation", HSTU acceleration operator: KV-cache support; page 1 section 2.1.2, ranking:
+ * candidates appended after a user's history are all scored in one pass, each seeing the whole
+ * history and itself, never another candidate).  User b has cache_off[b + 1] - cache_off[b]
+ * history tokens whose keys and values were computed earlier (the cache) and
+ * cand_off[b + 1] - cand_off[b] new candidates.  A candidate at index c of user b has position
+ * nk + c (nk = the user's cache length) and, with S defined as for hstu_attn_fwd,
+ *     O_c = sum_{j < nk} SiLU(S_cj) / N v_j + SiLU(S_cc) / N v_c,
+ * i.e. exactly the candidate rows of hstu_attn_fwd over [history | candidates] with the
+ * candidates as targets.  bf16 only (HSTU_ERR_UNSUPPORTED otherwise).
+ *
+ * hstu_plan_create_cached: args describe the candidates (total_tokens = cand_off[B]; timestamps
+ * = candidate times) and max_seqlen = N must be >= nk + m for every user (HSTU_ERR_BAD_OFFSETS
+ * otherwise).  num_contexts is ignored: candidates see every cached key anyway.  cand_off and
+ * cache_off are host arrays of B + 1 non-decreasing offsets starting at 0.  The plan serves only
+ * hstu_attn_fwd_cached (other calls return HSTU_ERR_BAD_SHAPE). */
+hstu_status_t hstu_plan_create_cached(const hstu_attn_args_t* args, const int64_t* cand_off,
+                                      const int64_t* cache_off, uint32_t flags,
+                                      hstu_plan_t** plan);
+
+/* q, k, v: candidate THD tensors (token stride args->qkv_token_stride or H*d); k_cache, v_cache:
+ * dense THD cache (cache_off[B] rows); cache_timestamps: [cache_off[B]] int64, needed when
+ * args->rab_ts is set; out: dense THD (T, H, d).  ws must hold hstu_workspace_bytes(plan, 5, 0)
+ * bytes (partial sums of long caches split over several workgroups; 0 when nothing is split). */
+hstu_status_t hstu_attn_fwd_cached(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                                   const void* q, const void* k, const void* v,
+                                   const void* k_cache, const void* v_cache,
+                                   const int64_t* cache_timestamps, void* out, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* Static string naming a status code. */
 const char* hstu_status_str(hstu_status_t status);

@@ -240,6 +240,64 @@ def test_layer_workload_full():
     _layer_check(w)
 
 
+# ---- candidate scoring against cached history ------------------------------------------------
+
+def _cached_check(w):
+    dev = runner.to_device(w)
+    out = runner.attn_fwd_cached(w, dev)
+    torch.cuda.synchronize()
+    return check("O", host(out), oracle.attn_fwd_cached(w), "bf16")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_cached_small(d):
+    # users without history, without candidates, more than one row block of candidates, and a
+    # cache that is not a whole number of key tiles
+    w = hs.make_cached_inputs([37, 1, 5, 130, 0, 700], [4, 3, 0, 17, 2, 150], 2, d, seed=61 + d)
+    say(f"cached scoring small d={d}")
+    _cached_check(w)
+
+
+@pytest.mark.parametrize("rab", ["none", "pos"])
+def test_cached_bias_subsets(rab):
+    w = hs.make_cached_inputs([64, 200, 3], [16, 9, 130], 4, 128, seed=62, rab=True)
+    if rab == "none":
+        w["rab_pos"] = w["rab_ts"] = w["timestamps"] = w["cache_timestamps"] = None
+    else:
+        w["rab_ts"] = None
+    say(f"cached scoring bias {rab}")
+    _cached_check(w)
+
+
+def test_cached_long_cache_is_split():
+    lengths = [8000] + [50] * 200
+    w = hs.make_cached_inputs(lengths, [16] * len(lengths), 4, 128, seed=63)
+    dev = runner.to_device(w)
+    a = runner.args_for(w, dev)
+    plan = hj.hstu_plan_create_cached(a, w["cand_offsets"], w["cache_offsets"])
+    assert hj.hstu_plan_info(plan)["fwd_split_blocks"] > 0
+    say("cached scoring with a split long cache")
+    out = runner.attn_fwd_cached(w, dev, plan=plan, args=a)
+    torch.cuda.synchronize()
+    check("O", host(out), oracle.attn_fwd_cached(w), "bf16")
+
+
+def test_cached_workload_full():
+    w = hs.make_cached_workload()
+    say(f"cached scoring workload, {w['total_tokens']} candidates, {w['cache_tokens']} cached")
+    _cached_check(w)
+
+
+def test_cached_rejects_regular_calls():
+    w = hs.make_cached_inputs([10], [2], 2, 64, seed=64)
+    dev = runner.to_device(w)
+    a = runner.args_for(w, dev)
+    plan = hj.hstu_plan_create_cached(a, w["cand_offsets"], w["cache_offsets"])
+    out = runner.empty_like_thd(w, dev)
+    with pytest.raises(hj.HstuError):
+        hj.hstu_attn_fwd(plan, a, dev["q"], dev["k"], dev["v"], out)
+
+
 # ---- full layer backward ---------------------------------------------------------------------
 
 def _layer_bwd_check(w):
