@@ -159,6 +159,23 @@ def attn_fwd_cached(w: dict, nthreads: int = 0) -> np.ndarray:
     return out
 
 
+def jagged_select(src, src_offsets, dst_offsets, keep_start=None) -> np.ndarray:
+    """Stochastic Length compaction (page 1 section 2.1.3, algorithm-level optimisation: each
+    training sequence is cut to a randomly drawn length before the encoder runs).  Sequence b
+    keeps the dst_offsets[b + 1] - dst_offsets[b] consecutive tokens starting at keep_start[b]
+    within it (default: the most recent ones, i.e. its last tokens), in order; the result is the
+    jagged tensor of the kept tokens.  Plain slicing of the rows."""
+    so, do = np.asarray(src_offsets, np.int64), np.asarray(dst_offsets, np.int64)
+    src = np.asarray(src)
+    out = np.zeros((int(do[-1]),) + src.shape[1:], dtype=src.dtype)
+    for b in range(len(so) - 1):
+        n, m = so[b + 1] - so[b], do[b + 1] - do[b]
+        st = n - m if keep_start is None else int(keep_start[b])
+        assert 0 <= st and st + m <= n, "window outside the sequence"
+        out[do[b]:do[b + 1]] = src[so[b] + st:so[b] + st + m]
+    return out
+
+
 def attn_bwd(w: dict, dout=None, q=None, k=None, v=None, nthreads: int = 0) -> dict:
     """Gradients of sum(dout * O) w.r.t. q, k, v and the two bias tables (fp64)."""
     a = _Args(w, q, k, v)

@@ -442,6 +442,34 @@ def test_cached_candidates_do_not_see_each_other():
     assert not np.allclose(got[2], base[2])
 
 
+# ---- Stochastic Length compaction -------------------------------------------------------------
+
+def test_jagged_select_on_the_printed_example():
+    # The KeyedJaggedTensor example printed on the pages, each sequence cut to its last
+    # min(n, 2) tokens, then to one token at a chosen start; results written out by hand from
+    # the printed grouping [[101, 102], [201, 202, 203], [1001], [1002, 1003]].
+    with open(os.path.join(GOLDEN, "kjt_example.json")) as f:
+        ex = json.load(f)
+    vals = np.array(ex["values"], dtype=np.int64)[:, None]
+    got = oracle.jagged_select(vals, ex["offsets"], [0, 2, 4, 5, 7])
+    assert got[:, 0].tolist() == [101, 102, 202, 203, 1001, 1002, 1003]
+    got = oracle.jagged_select(vals, ex["offsets"], [0, 1, 2, 3, 4], keep_start=[0, 1, 0, 1])
+    assert got[:, 0].tolist() == [101, 202, 1001, 1003]
+    got = oracle.jagged_select(vals, ex["offsets"], [0, 0, 0, 0, 0])
+    assert got.shape == (0, 1)
+
+
+def test_jagged_select_identity_and_rows():
+    rng = np.random.default_rng(3)
+    lengths = np.array([5, 0, 9, 1])
+    off = hs.offsets_from_lengths(lengths)
+    x = rng.normal(size=(int(off[-1]), 3, 4))
+    np.testing.assert_array_equal(oracle.jagged_select(x, off, off), x)
+    keep = np.minimum(lengths, 3)
+    got = oracle.jagged_select(x, off, hs.offsets_from_lengths(keep))
+    np.testing.assert_array_equal(got, np.concatenate([x[0:5][-3:], x[5:14][-3:], x[14:15]]))
+
+
 # ---- full layer ----------------------------------------------------------------------------
 
 def test_layer_matches_library_routines():
