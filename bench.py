@@ -11,7 +11,8 @@ FLOPs are counted on visible (unmasked) pairs only: 4d per pair per head forward
 
 Prints one JSON line.  Besides the headline workload it reports the forward-only workloads
 (ranking-shaped, long-tail, full layer) with warm and cold-cache timings, the full layer's
-backward, candidate scoring against cached history, the dominant kernel's roofline, and the fp64 CPU oracle timed on a bounded sample of
+backward, candidate scoring against cached history, Stochastic Length compaction, the dominant
+kernel's roofline, and the fp64 CPU oracle timed on a bounded sample of
 the same workload.
 """
 from __future__ import annotations
@@ -307,6 +308,34 @@ def bench_cached(torch, hj, runner, iters=20):
             "visible_pairs": info["visible_pairs"], "flops": flops, "bytes": nbytes}
 
 
+def bench_select(torch, hj, iters=20):
+    """Stochastic Length compaction of one THD tensor of the long-sequence workload (74k tokens,
+    8 x 128 bf16 per token), every sequence cut to its 2048 most recent tokens.  Bytes: the kept
+    rows read once and written once (an HBM-bound copy)."""
+    import hstu_synth as hs
+    spec = hs.WORKLOADS[HEADLINE]
+    L = hs.draw_lengths(np.random.default_rng(0), spec, spec.batch)
+    keep = np.minimum(L, 2048)
+    so, do = hs.offsets_from_lengths(L), hs.offsets_from_lengths(keep)
+    row = (spec.heads, spec.d)
+    src = torch.empty((int(so[-1]),) + row, dtype=torch.bfloat16, device="cuda:0").normal_()
+    dst = torch.empty((int(do[-1]),) + row, dtype=torch.bfloat16, device="cuda:0")
+    dso = torch.from_numpy(so).cuda()
+    ddo = torch.from_numpy(do).cuda()
+    call = lambda: hj.hstu_jagged_select(dso, ddo, src, dst)
+    for _ in range(5):
+        call()
+    timer = Timer(torch)
+    for _ in range(iters):
+        timer.record("x", call)
+    torch.cuda.synchronize()
+    med = float(np.median(timer.ms("x")))
+    nbytes = 2 * dst.numel() * dst.element_size()
+    return {"ms_median": round(med, 4), "algorithmic_GBps": round(nbytes / med / 1e6, 1),
+            "pct_hbm_peak": round(100 * nbytes / med / 1e6 / PEAK_HBM_GBS, 2),
+            "rows_kept": int(do[-1]), "rows_in": int(so[-1]), "bytes": nbytes}
+
+
 def bench_layer_bwd(torch, hj, runner, iters=20):
     """Full layer backward (recompute of the forward's intermediates included) on the full-layer
     workload with dY ~ N(0, 1).  FLOPs counted: the backward's own products only, i.e. dG, dW2,
@@ -421,6 +450,7 @@ def main():
         result["forward_workloads"] = extra
         result["layer_backward"] = bench_layer_bwd(torch, hj, runner)
         result["cached_scoring"] = bench_cached(torch, hj, runner)
+        result["stochastic_length_select"] = bench_select(torch, hj)
     print(json.dumps(result))
 
 

@@ -56,7 +56,7 @@ class HstuPlanInfo(ctypes.Structure):
 EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_info",
            "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_bwd",
            "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd", "hstu_layer_bwd",
-           "hstu_plan_create_cached", "hstu_attn_fwd_cached"]
+           "hstu_plan_create_cached", "hstu_attn_fwd_cached", "hstu_jagged_select"]
 
 _lib = None
 
@@ -100,6 +100,8 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_plan_create_cached.restype = I32
     lib.hstu_attn_fwd_cached.argtypes = [P, argp, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_fwd_cached.restype = I32
+    lib.hstu_jagged_select.argtypes = [I32, P, I64, P, I64, P, I64, P, P, P]
+    lib.hstu_jagged_select.restype = I32
     _lib = lib
     return lib
 
@@ -280,3 +282,15 @@ def hstu_attn_fwd_cached(plan: Plan, args: HstuAttnArgs, q, k, v, k_cache, v_cac
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v),
         _ptr(k_cache), _ptr(v_cache), _ptr(cache_timestamps), _ptr(out), _ptr(ws), nbytes,
         _stream(stream)))
+
+
+def hstu_jagged_select(src_offsets, dst_offsets, src, dst, keep_start=None, stream=None) -> None:
+    """Stochastic Length compaction: device int64 offsets (B + 1), contiguous src / dst tensors
+    whose first dimension is the token; keep_start (device int64 [B]) or None for the last
+    rows of each sequence."""
+    B = int(src_offsets.numel()) - 1
+    row_bytes = int(src[0].numel() * src.element_size()) if src.shape[0] else \
+        int(np.prod(src.shape[1:], dtype=np.int64)) * src.element_size()
+    _check(load_library().hstu_jagged_select(
+        B, _ptr(src_offsets), int(src.shape[0]), _ptr(dst_offsets), int(dst.shape[0]),
+        _ptr(keep_start), row_bytes, _ptr(src), _ptr(dst), _stream(stream)))

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD, "libhstu_amd.so")
-SOURCES = ["hstu_api.hip", "attn_fwd.hip", "attn_bwd.hip", "layer.hip", "gemm.hip"]
+SOURCES = ["hstu_api.hip", "attn_fwd.hip", "attn_bwd.hip", "layer.hip", "gemm.hip", "jagged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for all device code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

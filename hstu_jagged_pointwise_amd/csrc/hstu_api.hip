@@ -786,4 +786,21 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_plan_t* plan, const hstu_attn_args
     return hip_status(hstu::launch_attn_fwd_bf16(p, static_cast<hipStream_t>(stream)));
 }
 
+hstu_status_t hstu_jagged_select(int32_t batch, const int64_t* src_offsets, int64_t src_rows,
+                                 const int64_t* dst_offsets, int64_t dst_rows,
+                                 const int64_t* keep_start, int64_t row_bytes, const void* src,
+                                 void* dst, void* stream) {
+    if (batch < 0 || src_rows < 0 || dst_rows < 0 || row_bytes <= 0) return HSTU_ERR_BAD_SHAPE;
+    if (row_bytes % 8 != 0) return HSTU_ERR_MISALIGNED;
+    if (dst_rows == 0) return HSTU_OK;
+    if (batch == 0) return HSTU_ERR_BAD_SHAPE;
+    if (!src_offsets || !dst_offsets || !src || !dst) return HSTU_ERR_NULL_ARG;
+    for (const void* ptr : {(const void*)src_offsets, (const void*)dst_offsets,
+                            (const void*)keep_start, src, (const void*)dst})
+        if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 7) != 0) return HSTU_ERR_MISALIGNED;
+    return hip_status(hstu::launch_jagged_select(batch, src_offsets, src_rows, dst_offsets, dst_rows,
+                                                 keep_start, row_bytes, src, dst,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

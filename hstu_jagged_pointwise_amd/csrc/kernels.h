@@ -103,4 +103,11 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 
+// Stochastic Length compaction: rows of jagged src (offsets so, src_rows rows of row_bytes)
+// gathered into jagged dst (offsets dof); sequence b keeps the rows starting at keep_start[b]
+// (NULL: its last rows).  Offsets and keep_start are device arrays.
+hipError_t launch_jagged_select(int32_t B, const int64_t* so, int64_t src_rows, const int64_t* dof,
+                                int64_t dst_rows, const int64_t* keep_start, int64_t row_bytes,
+                                const void* src, void* dst, hipStream_t s);
+
 }  // namespace hstu

@@ -221,6 +221,23 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_plan_t* plan, const hstu_attn_args
                                    const int64_t* cache_timestamps, void* out, void* ws,
                                    size_t ws_bytes, void* stream);
 
+/* Stochastic Length compaction (page 1 section 2.1.3, algorithm-level optimisation: each
+ * training sequence is cut to a randomly drawn length before the encoder runs, which lowers the
+ * cost without a visible loss in quality).  The draw is the caller's (the pages give its rule
+ * only in a figure); this call moves the kept tokens on the device.  Sequence b of the jagged
+ * tensor src (device offsets src_offsets[batch + 1], src_rows rows of row_bytes bytes) keeps
+ * dst_offsets[b + 1] - dst_offsets[b] consecutive rows starting at row keep_start[b] of the
+ * sequence (device int64[batch]; NULL keeps its last rows, the most recent tokens), and dst
+ * (dst_rows = dst_offsets[batch] rows) receives them packed in sequence order.  Offsets are
+ * device arrays and are not checked on the host: a window that leaves its sequence or the
+ * source tensor yields zero rows there.  row_bytes must be a multiple of 8, pointers 8-byte
+ * aligned (16-byte aligned rows of a multiple of 16 bytes take the wide path).  Call it once
+ * per tensor (x or q / k / v / u, timestamps) with the same offsets. */
+hstu_status_t hstu_jagged_select(int32_t batch, const int64_t* src_offsets, int64_t src_rows,
+                                 const int64_t* dst_offsets, int64_t dst_rows,
+                                 const int64_t* keep_start, int64_t row_bytes, const void* src,
+                                 void* dst, void* stream);
+
 /* Static string naming a status code. */
 const char* hstu_status_str(hstu_status_t status);
 

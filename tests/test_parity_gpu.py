@@ -298,6 +298,45 @@ def test_cached_rejects_regular_calls():
         hj.hstu_attn_fwd(plan, a, dev["q"], dev["k"], dev["v"], out)
 
 
+# ---- Stochastic Length compaction -----------------------------------------------------------
+
+def _select_case(lengths, keep, starts, row_shape, dtype, seed):
+    rng = np.random.default_rng(seed)
+    so = hs.offsets_from_lengths(lengths)
+    do = hs.offsets_from_lengths(keep)
+    src = rng.normal(size=(int(so[-1]),) + row_shape)
+    if dtype == torch.int64:
+        src = rng.integers(-2 ** 62, 2 ** 62, size=src.shape)
+    want = oracle.jagged_select(src, so, do, starts)
+    ts = torch.from_numpy(np.ascontiguousarray(src)).to(device="cuda", dtype=dtype)
+    dst = torch.full((int(do[-1]),) + row_shape, 7, dtype=dtype, device="cuda")
+    dev = lambda a: torch.from_numpy(np.asarray(a, np.int64)).cuda()
+    hj.hstu_jagged_select(dev(so), dev(do), ts, dst,
+                          keep_start=None if starts is None else dev(starts))
+    torch.cuda.synchronize()
+    exp = torch.from_numpy(np.ascontiguousarray(want)).to(dtype)  # same rounding as the source
+    assert torch.equal(dst.cpu(), exp), "compaction is not bit-exact"
+
+
+@pytest.mark.parametrize("row_shape,dtype", [((512,), torch.bfloat16), ((4, 128), torch.float32),
+                                             ((), torch.int64), ((4,), torch.float16)])
+def test_jagged_select_tail_and_windows(row_shape, dtype):
+    lengths = np.array([40, 0, 7, 300, 1, 64])
+    keep = np.array([10, 0, 7, 0, 1, 33])
+    say(f"jagged select {row_shape} {dtype}")
+    _select_case(lengths, keep, None, row_shape, dtype, 71)
+    starts = np.array([30, 0, 0, 17, 0, 31])
+    _select_case(lengths, keep, starts, row_shape, dtype, 72)
+
+
+def test_jagged_select_workload_full():
+    w = hs.make_workload("longtail_fwd")
+    L = w["lengths"]
+    keep = np.minimum(L, 256)   # every sequence cut to its 256 most recent tokens
+    say("jagged select, long-tail lengths cut to 256")
+    _select_case(L, keep, None, (4, 128), torch.bfloat16, 73)
+
+
 # ---- full layer backward ---------------------------------------------------------------------
 
 def _layer_bwd_check(w):
