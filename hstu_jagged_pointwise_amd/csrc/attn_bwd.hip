@@ -89,7 +89,7 @@ template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>& sm, int buf,
                                            int q0, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t tj, int64_t tj64) {
-    const TimePick pick(tb);
+    const TimePickAbs pick(tb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int ii = q0 + 8 * r + 4 * g;
@@ -276,8 +276,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             TimeSel tb;
             int tm = 0;
             if (RT) {
+                // TimePickAbs compares |t_key - t_query| itself: no sign or overflow condition
                 const BiasSpan st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
-                tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb);
+                tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb, true, 0u);
             } else tb.set_const(bpos);
             if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
             else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
@@ -375,7 +376,7 @@ template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_b(const f32x16& s, f32x16& dp, const SmemB<D>& sm, int buf,
                                            int k0, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t ti, int64_t ti64) {
-    const TimePick pick(tb);
+    const TimePick pick(tb, ti);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int jj = k0 + 8 * r + 4 * g;
@@ -384,9 +385,9 @@ __device__ __forceinline__ void epilogue_b(const f32x16& s, f32x16& dp, const Sm
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int e = 4 * r + c;
-            float b = pick.get<TM>(ti, tk4[c]);
+            float b = pick.get<TM>(tk4[c]);
             if (PM == 1) b += sm.rp[buf][u0 + 8 * r + c].bias;
-            if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tk4[c]))];
+            if (TM == 2) b += sm.wt[bucket_class(absdiff_sad(ti, tk4[c]))];
             if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
             dp[e] = silu_grad(fmaf(alpha2, s[e], b), dp[e]).ds;
         }
@@ -412,7 +413,7 @@ __device__ __forceinline__ void epilogue_b_tm(int tm, const f32x16& s, f32x16& d
 //   mp  = sum of dS * bucket(|i - j|) (PG 1, two position buckets: the upper bucket's share is
 //         mp - b_lo * sum),
 //   th  = sum of dS over pairs with |dt| >= thr, th2 the same for thr2 (TM 1 and 4: two or
-//         three time buckets),
+//         three time buckets; one comparison per pair with TimePick's limits),
 // plus, for tiles spanning more buckets, per-lane runs along the lane's keys (which come in
 // increasing order): a lane adds its run sum to the LDS histogram only when its own bucket
 // changes (PG 2 position, TM 2 and 3 time).  LDS float atomics cost a few cycles per active
@@ -425,6 +426,7 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, in
                                               int u0, int g, int lane, const TimeSel tb,
                                               uint32_t ti, int64_t ti64) {
     TileSums ts{0.0f, 0.0f, 0.0f, 0.0f};
+    const TimePick pick(tb, ti);
     int pcur = -1, tcur = -1;  // per-lane runs of the many-bucket modes
     float pacc = 0.0f, tacc = 0.0f;
     auto prun = [&](int b, float ds) {
@@ -455,17 +457,20 @@ __device__ __forceinline__ TileSums grad_sums(const f32x16& dp, SmemB<D>& sm, in
                 ts.sum += ds;
                 if (GP && PG == 1) ts.mp = fmaf(ds, sm.rp[buf][u].bucket, ts.mp);
                 if (GP && PG == 2) prun((int)sm.rp[buf][u].bucket, ds);
-                if (GT && (TM == 1 || TM == 4)) {
-                    const uint32_t d = absdiff_u32(ti, tk4[c]);
-                    ts.th += d >= tb.thr ? ds : 0.0f;
-                    if (TM == 4) ts.th2 += d >= tb.thr2 ? ds : 0.0f;
+                if (GT && (TM == 1 || TM == 4)) {  // sums over te < l (see TimePick)
+                    ts.th += tk4[c] < pick.l1 ? ds : 0.0f;
+                    if (TM == 4) ts.th2 += tk4[c] < pick.l2 ? ds : 0.0f;
                 }
-                if (GT && TM == 2) trun(bucket_of(absdiff_u32(ti, tk4[c])), ds);
+                if (GT && TM == 2) trun(bucket_of(absdiff_sad(ti, tk4[c])), ds);
                 if (GT && TM == 3) trun(bucket_of(absdiff_sat(ti64, sm.tk64[buf][jj + c])), ds);
             }
         }
     if (GP && PG == 2 && pcur >= 0) atomicAdd(&sm.hbp[pcur], pacc);
     if (GT && (TM == 2 || TM == 3) && tcur >= 0) atomicAdd(&sm.hbt[tcur][lane & 31], tacc);
+    if (GT && (TM == 1 || TM == 4) && !tb.later) {  // te < l counted the pairs below thr
+        ts.th = ts.sum - ts.th;
+        ts.th2 = ts.sum - ts.th2;
+    }
     return ts;
 }
 
@@ -549,7 +554,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         if (i < nh) lim = imax(i, nc - 1);
         else { lim = nh - 1; dg = i; }
     }
-    uint32_t ti = 0;
+    uint32_t ti = 0, timax_rel = 0;
     int64_t ti64 = 0, timin = 0, timax = 0;
     bool wave_qfit = true;
     if (RT) {
@@ -558,6 +563,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         ti = rel_time_u32(ti64, tbase);
         timin = wave_min64(row_ok ? ti64 : INT64_MAX);
         timax = wave_max64(row_ok ? ti64 : INT64_MIN);
+        timax_rel = rel_time_u32(timax, tbase);  // used only when every row time fits
     }
     f32x16 dqt[D / 32];
 #pragma unroll
@@ -650,8 +656,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                st = bias_span(timin - sm.tkmax[buf][kh], timax - sm.tkmin[buf][kh]);
-                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb);
+                const int64_t dlo = timin - sm.tkmax[buf][kh];  // row minus key
+                st = bias_span(dlo, timax - sm.tkmin[buf][kh]);
+                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb, dlo >= 0, timax_rel);
             } else tb.set_const(bpos);
             if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);
             else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);

@@ -60,7 +60,7 @@ template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, int buf, int u0,
                                          int g, float alpha2, const TimeSel tb, uint32_t ti,
                                          int64_t ti64) {
-    const TimePick pick(tb);
+    const TimePick pick(tb, ti);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -71,9 +71,9 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, i
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = pick.get<TM>(ti, tq[c]);
+                float b = pick.get<TM>(tq[c]);
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
-                if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(ti, tq[c]))];
+                if (TM == 2) b += sm.wt[bucket_class(absdiff_sad(ti, tq[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
                 s[kb][e] = silu_scaled(fmaf(alpha2, s[kb][e], b));
             }
@@ -114,12 +114,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
     const FwdItem wu = p.items[blockIdx.x];
-    const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
-    const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
-    const int64_t tok0 = si.start;
+    const int n = wu.n, nc = wu.nc, nh = wu.nh, r0 = wu.row0, h = wu.head;
+    const int64_t tok0 = wu.start;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * p.ld_in + h * D;
-    const CacheSeq cs = CACHED ? p.cache[wu.seq] : CacheSeq{0, 0};
+    const CacheSeq cs = CACHED ? CacheSeq{wu.cstart, wu.cn} : CacheSeq{0, 0};
     const int64_t ktok0 = CACHED ? cs.start : tok0;
     const int64_t ld = CACHED ? p.ld_cache : p.ld_in;  // key / value token stride
     const bf16* __restrict__ kg = static_cast<const bf16*>(CACHED ? p.kc : p.k) + ktok0 * ld + h * D;
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         if (row_ok) qf[ks] = load_bf16x8(qg + (int64_t)i * ld + 16 * ks + 8 * g);
         else qf[ks] = bf16x8{};
     }
-    uint32_t ti = 0;
+    uint32_t ti = 0, timax_rel = 0;
     int64_t ti64 = 0, timin = 0, timax = 0;
     bool wave_qfit = true;
     if (RT) {
@@ -211,6 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         ti = rel_time_u32(ti64, tbase);
         timin = wave_min64(row_ok ? ti64 : INT64_MAX);
         timax = wave_max64(row_ok ? ti64 : INT64_MIN);
+        timax_rel = rel_time_u32(timax, tbase);  // used only when every row time fits
     }
 
     f32x16 o[D / 32];
@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                const BiasSpan st = bias_span(timin - sm.tkmax[buf], timax - sm.tkmin[buf]);
-                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb);
+                const int64_t dlo = timin - sm.tkmax[buf];
+                const BiasSpan st = bias_span(dlo, timax - sm.tkmin[buf]);
+                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb, dlo >= 0, timax_rel);
             } else tb.set_const(bpos);
             if (pm) epilogue_tm<D, 1>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);
             else epilogue_tm<D, 0>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);

@@ -54,6 +54,17 @@ HSTU_HD int bucket_of_class(int cls) { return bucket_of(class_representative(cls
 __device__ __forceinline__ uint32_t absdiff_u32(uint32_t a, uint32_t b) {
     return a > b ? a - b : b - a;
 }
+// The same in one instruction (v_sad_u32 computes |a - b| + c); as inline assembly it constrains
+// register allocation, so kernels at the register limit use absdiff_u32.
+__device__ __forceinline__ uint32_t absdiff_sad(uint32_t a, uint32_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t r;
+    asm("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+#else
+    return a > b ? a - b : b - a;
+#endif
+}
 
 // |a - b| for 64-bit timestamps, saturated to 32 bits (exact for bucketing, see bucket_of).
 __device__ __forceinline__ uint32_t absdiff_sat(int64_t a, int64_t b) {
@@ -129,45 +140,92 @@ HSTU_HD BiasSpan bias_span(int64_t lo, int64_t hi) {
     return r;
 }
 
+// A wavefront-uniform float kept in a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
 // Scalar part of a tile's bias plus the time-bias selection of modes 1 and 4 (see BiasSpan);
 // set() returns the time mode: 0 one bucket, 1 two buckets, 4 three buckets, 2 / 3 per-element
 // class lookup with 32-bit / 64-bit times.
+//
+// Modes 1 and 4 only arise when the time differences of the tile have one sign (bias_span
+// gives per-element mode otherwise), so |t_lane - t_elem| >= thr is a one-sided comparison of
+// the element's time with a per-lane limit: `later` = every lane's time >= every element's.
+// lane_tmax (the largest lane time, 32-bit relative) guards the limit t_lane + thr against
+// overflow in the other case (such tiles fall back to per-element mode).
 struct TimeSel {
     float b0, b1, b2;
     uint32_t thr, thr2;
+    bool later;
     __device__ __forceinline__ void set_const(float b) {
         b0 = b1 = b2 = b;
         thr = thr2 = 0xffffffffu;
+        later = true;
     }
-    __device__ __forceinline__ int set(const BiasSpan& st, bool fit, float bpos, const float* wtb) {
+    __device__ __forceinline__ int set(const BiasSpan& st, bool fit, float bpos, const float* wtb,
+                                       bool lane_later, uint32_t lane_tmax) {
         if (st.kind == 0) { set_const(bpos + wtb[st.b_lo]); return 0; }
         set_const(bpos);
         if (!fit) return 3;
         if (st.kind == 2) return 2;
-        b0 = bpos + wtb[st.b_lo];
-        b1 = bpos + wtb[st.b_lo + 1];
-        b2 = bpos + wtb[st.b_hi];
+        if (!lane_later &&
+            (uint64_t)lane_tmax + (st.kind == 1 ? st.thr : st.thr2) > 0xffffffffull)
+            return 2;
+        b0 = uniform(bpos + wtb[st.b_lo]);
+        b1 = uniform(bpos + wtb[st.b_lo + 1]);
+        b2 = uniform(bpos + wtb[st.b_hi]);
         thr = st.thr;
         thr2 = st.thr2;
+        later = lane_later;
         return st.kind == 1 ? 1 : 4;
     }
 };
 
-// The per-element selector of a TimeSel, built once per tile.  The third bucket is reached by
-// adding e2 = b2 - b1 (within one rounding of b2): a nested select among three values is turned
-// by the compiler into an indexed load from a scratch copy of them.
+// The per-element selector of a TimeSel for one lane's time tl, built once per tile:
+//   mode 1: bias = te < l1 ? x1 : y1;  mode 4: that plus (te < l2 ? x2 : y2).
+// With later, |tl - te| >= thr <=> te <= tl - thr <=> te < tl - thr + 1 (0 when tl < thr);
+// otherwise |tl - te| >= thr <=> te >= tl + thr, the same comparison with the values swapped.
+// The third bucket is reached by adding e2 = b2 - b1 (within one rounding of b2): a nested
+// select among three values is turned by the compiler into an indexed load from scratch.
 struct TimePick {
+    float b0, x1, y1, x2, y2;
+    uint32_t l1, l2;
+    __device__ __forceinline__ TimePick(const TimeSel& t, uint32_t tl) : b0(t.b0) {
+        const float e2 = t.b2 - t.b1;
+        if (t.later) {
+            l1 = tl >= t.thr ? tl - t.thr + 1u : 0u;
+            l2 = tl >= t.thr2 ? tl - t.thr2 + 1u : 0u;
+        } else {
+            l1 = tl + t.thr;   // no overflow in modes 1 and 4 (see TimeSel::set)
+            l2 = tl + t.thr2;
+        }
+        x1 = uniform(t.later ? t.b1 : t.b0);
+        y1 = uniform(t.later ? t.b0 : t.b1);
+        x2 = uniform(t.later ? e2 : 0.0f);
+        y2 = uniform(t.later ? 0.0f : e2);
+    }
+    template <int TM>
+    __device__ __forceinline__ float get(uint32_t te) const {
+        if (TM == 1) return te < l1 ? x1 : y1;
+        if (TM == 4) return (te < l1 ? x1 : y1) + (te < l2 ? x2 : y2);
+        return b0;
+    }
+};
+
+// The same selection from |tl - te| itself (one more instruction per element, but no per-lane
+// limits to keep: for kernels short of registers).
+struct TimePickAbs {
     float b0, b1, e2;
     uint32_t thr, thr2;
-    __device__ __forceinline__ explicit TimePick(const TimeSel& t)
-        : b0(t.b0), b1(t.b1), e2(t.b2 - t.b1), thr(t.thr), thr2(t.thr2) {}
+    __device__ __forceinline__ explicit TimePickAbs(const TimeSel& t)
+        : b0(t.b0), b1(t.b1), e2(uniform(t.b2 - t.b1)), thr(t.thr), thr2(t.thr2) {}
     template <int TM>
-    __device__ __forceinline__ float get(uint32_t ti, uint32_t tj) const {
-        if (TM == 1) return absdiff_u32(ti, tj) >= thr ? b1 : b0;
+    __device__ __forceinline__ float get(uint32_t tl, uint32_t te) const {
+        if (TM == 1) return absdiff_u32(tl, te) >= thr ? b1 : b0;
         if (TM == 4) {
-            const uint32_t d = absdiff_u32(ti, tj);
-            const float lo = d >= thr ? b1 : b0;
-            return lo + (d >= thr2 ? e2 : 0.0f);
+            const uint32_t d = absdiff_u32(tl, te);
+            return (d >= thr ? b1 : b0) + (d >= thr2 ? e2 : 0.0f);
         }
         return b0;
     }

@@ -43,9 +43,14 @@ struct WorkUnit {
 
 // A forward work item: key tiles [t0, t1) of the list key_tiles_for_rows() gives for one row
 // block.  part < 0: the item covers the whole list and writes the output rows itself; otherwise
-// it writes its fp32 partial sums to partial slot `part`, and a FixItem adds the slots up.
+// it writes its fp32 partial sums to partial slot `part`, and a FixItem adds the slots up.  The
+// item carries its sequence's SeqInfo (and the cached history's CacheSeq for candidate scoring)
+// so that a workgroup needs one 64-byte load, not two dependent ones, before it can start.
 struct FwdItem {
-    int32_t seq, head, row0, cost, t0, t1, part, pad;
+    int32_t seq, head, row0, cost, t0, t1, part, pad0;
+    int32_t start, n, nc, nh;  // SeqInfo of seq
+    int32_t cstart, cn;        // CacheSeq of seq (candidate scoring)
+    int32_t pad1, pad2;
 };
 // A row block whose key tiles were split over items with slots [part0, part0 + nparts).
 struct FixItem {

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 #include <cmath>
 #include <cstring>
 #include <initializer_list>
@@ -110,8 +111,53 @@ void sort_longest_first(std::vector<WorkUnit>& u) {
 // items.  (Below twice the average, the fix-up pass and the pieces' extra prologues cost more
 // than the shorter critical path saves.)
 // Because the output is a plain sum over keys (no softmax normalisation), the pieces' fp32
-// partial outputs just add up; a fix-up pass sums them.  Items are ordered longest first.
+// partial outputs just add up; a fix-up pass sums them.
+//
+// Launch order.  Workgroups are dispatched to the 8 XCDs round robin (workgroup i to XCD i % 8),
+// and each XCD has its own L2.  All items of one (sequence, head) read the same K and V, so they
+// are given indices of one residue mod 8, consecutively within it: they run on one XCD at about
+// the same time and all but the first find K and V in that XCD's L2.  Groups are taken longest
+// item first and each goes to the residue with the fewest items so far (greedy list scheduling
+// by group); within a group, longest first.
 constexpr int kMinSplit = 4;
+constexpr int kXcds = 8;
+
+void order_for_xcds(std::vector<FwdItem>& items) {
+    std::stable_sort(items.begin(), items.end(), [](const FwdItem& a, const FwdItem& b) {
+        return a.cost > b.cost;
+    });
+    // groups in order of their longest item
+    std::vector<std::vector<FwdItem>> groups;
+    std::vector<std::pair<int64_t, int>> index;  // (key, group) for lookup
+    for (const FwdItem& it : items) {
+        const int64_t key = (int64_t(it.seq) << 20) | it.head;
+        auto found = std::lower_bound(index.begin(), index.end(), std::make_pair(key, -1));
+        if (found != index.end() && found->first == key) {
+            groups[found->second].push_back(it);
+        } else {
+            index.insert(found, std::make_pair(key, (int)groups.size()));
+            groups.push_back({it});
+        }
+    }
+    std::vector<std::vector<FwdItem>> queues(kXcds);
+    for (const auto& grp : groups) {
+        int best = 0;
+        for (int r = 1; r < kXcds; ++r)
+            if (queues[r].size() < queues[best].size()) best = r;
+        queues[best].insert(queues[best].end(), grp.begin(), grp.end());
+    }
+    items.clear();
+    for (size_t k = 0;; ++k) {
+        bool any = false;
+        for (int r = 0; r < kXcds; ++r)
+            if (k < queues[r].size()) {
+                items.push_back(queues[r][k]);
+                any = true;
+            }
+        if (!any) break;
+    }
+}
+
 void build_fwd_items(hstu_plan_t* plan, int compute_units) {
     int64_t total = 0;
     for (const WorkUnit& u : plan->fwd) total += u.cost;
@@ -120,20 +166,25 @@ void build_fwd_items(hstu_plan_t* plan, int compute_units) {
     plan->items.clear();
     plan->fix.clear();
     plan->parts = 0;
+    auto item = [&](const WorkUnit& u, int cost, int t0, int t1, int part) {
+        const SeqInfo& si = plan->seqs[u.seq];
+        const CacheSeq cs = plan->cache.empty() ? CacheSeq{0, 0} : plan->cache[u.seq];
+        return FwdItem{u.seq, u.head, u.row0, cost, t0, t1, part, 0,
+                       si.start, si.n, si.nc, si.nh, cs.start, cs.n, 0, 0};
+    };
     for (const WorkUnit& u : plan->fwd) {
         if (u.cost <= cap) {
-            plan->items.push_back(FwdItem{u.seq, u.head, u.row0, u.cost, 0, u.cost, -1, 0});
+            plan->items.push_back(item(u, u.cost, 0, u.cost, -1));
             continue;
         }
         const int k = (u.cost + cap - 1) / cap;
         plan->fix.push_back(FixItem{u.seq, u.head, u.row0, plan->parts, k, 0, 0, 0});
         for (int c = 0; c < k; ++c) {
             const int t0 = (int)((int64_t)c * u.cost / k), t1 = (int)((int64_t)(c + 1) * u.cost / k);
-            plan->items.push_back(FwdItem{u.seq, u.head, u.row0, t1 - t0, t0, t1, plan->parts++, 0});
+            plan->items.push_back(item(u, t1 - t0, t0, t1, plan->parts++));
         }
     }
-    std::stable_sort(plan->items.begin(), plan->items.end(),
-                     [](const FwdItem& a, const FwdItem& b) { return a.cost > b.cost; });
+    order_for_xcds(plan->items);
 }
 
 size_t part_bytes(const hstu_plan_t* plan) {

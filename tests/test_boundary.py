@@ -158,7 +158,16 @@ def test_forward_items_split_long_row_blocks(name):
     blocks = hj.hstu_plan_units(plan, 0)
     items = hj.hstu_plan_units(plan, 2)
     assert info["fwd_items"] == len(items)
-    assert np.all(np.diff(items[:, 3]) <= 0)                              # longest first
+    # launch order: the items of one (sequence, head) share an index residue mod 8 (one XCD),
+    # at least for every group that lies in the first half of the list (queues only run
+    # unevenly at the tail)
+    pos = {}
+    for k, it in enumerate(items):
+        pos.setdefault((int(it[0]), int(it[1])), []).append(k)
+    for ks in pos.values():
+        if max(ks) < len(items) // 2:
+            assert len({k % 8 for k in ks}) == 1, ks
+            assert all(items[a][3] >= items[b][3] for a, b in zip(ks, ks[1:]))  # longest first
     cap = max(4, 2 * -(-int(blocks[:, 3].sum()) // 512))                   # host-only: 256 CUs
     cost = {tuple(b[:3]): int(b[3]) for b in blocks}
     by_block = {}
