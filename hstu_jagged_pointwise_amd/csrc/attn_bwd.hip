@@ -522,7 +522,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
     const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lr = lane & 31;
-    const int wave = (tid >> 6) & 3, kh = tid >> 8;  // row group, key half
+    const int wave = uniform_i((tid >> 6) & 3), kh = uniform_i(tid >> 8);  // row group, key half
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = si.start, ld = p.ld_in;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * ld + h * D;
@@ -561,8 +561,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         ti64 = row_ok ? p.ts[tok0 + i] : tbase;
         wave_qfit = __all(rel_time_fits(ti64, tbase));
         ti = rel_time_u32(ti64, tbase);
-        timin = wave_min64(row_ok ? ti64 : INT64_MAX);
-        timax = wave_max64(row_ok ? ti64 : INT64_MIN);
+        timin = uniform64(wave_min64(row_ok ? ti64 : INT64_MAX));
+        timax = uniform64(wave_max64(row_ok ? ti64 : INT64_MIN));
         timax_rel = rel_time_u32(timax, tbase);  // used only when every row time fits
     }
     f32x16 dqt[D / 32];
@@ -656,9 +656,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                const int64_t dlo = timin - sm.tkmax[buf][kh];  // row minus key
-                st = bias_span(dlo, timax - sm.tkmin[buf][kh]);
-                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb, dlo >= 0, timax_rel);
+                const int64_t dlo = timin - uniform64(sm.tkmax[buf][kh]);  // row minus key
+                st = bias_span(dlo, timax - uniform64(sm.tkmin[buf][kh]));
+                tm = tb.set(st, wave_qfit && uniform_i(sm.fits[buf]), bpos, sm.wtb, dlo >= 0, timax_rel);
             } else tb.set_const(bpos);
             if (pm) epilogue_b_tm<D, 1>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);
             else epilogue_b_tm<D, 0>(tm, s, dp, sm, buf, k0, u0, g, alpha2, tb, ti, ti64);

@@ -114,7 +114,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
     const FwdItem wu = p.items[blockIdx.x];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, lr = lane & 31;
+    const int tid = threadIdx.x, wave = uniform_i(tid >> 6), lane = tid & 63, g = lane >> 5,
+              lr = lane & 31;
     const int n = wu.n, nc = wu.nc, nh = wu.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = wu.start;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * p.ld_in + h * D;
@@ -208,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         ti64 = row_ok ? p.ts[tok0 + i] : tbase;
         wave_qfit = __all(rel_time_fits(ti64, tbase));
         ti = rel_time_u32(ti64, tbase);
-        timin = wave_min64(row_ok ? ti64 : INT64_MAX);
-        timax = wave_max64(row_ok ? ti64 : INT64_MIN);
+        timin = uniform64(wave_min64(row_ok ? ti64 : INT64_MAX));
+        timax = uniform64(wave_max64(row_ok ? ti64 : INT64_MIN));
         timax_rel = rel_time_u32(timax, tbase);  // used only when every row time fits
     }
 
@@ -250,9 +251,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                const int64_t dlo = timin - sm.tkmax[buf];
-                const BiasSpan st = bias_span(dlo, timax - sm.tkmin[buf]);
-                tm = tb.set(st, wave_qfit && sm.fits[buf], bpos, sm.wtb, dlo >= 0, timax_rel);
+                const int64_t dlo = timin - uniform64(sm.tkmax[buf]);
+                const BiasSpan st = bias_span(dlo, timax - uniform64(sm.tkmin[buf]));
+                tm = tb.set(st, wave_qfit && uniform_i(sm.fits[buf]), bpos, sm.wtb, dlo >= 0, timax_rel);
             } else tb.set_const(bpos);
             if (pm) epilogue_tm<D, 1>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);
             else epilogue_tm<D, 0>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);

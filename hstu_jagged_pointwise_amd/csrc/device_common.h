@@ -140,6 +140,16 @@ HSTU_HD BiasSpan bias_span(int64_t lo, int64_t hi) {
     return r;
 }
 
+// Wavefront-uniform values (read from LDS, hence in vector registers) moved to scalar registers,
+// so that the per-tile decisions built on them run on the scalar unit.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // A wavefront-uniform float kept in a scalar register.
 __device__ __forceinline__ float uniform(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
