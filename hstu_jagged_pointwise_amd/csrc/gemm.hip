@@ -119,38 +119,69 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
             for (int nb = 0; nb < 2; ++nb)
                 b[nb] = BT ? rowop.read(sm.b[buf], 2 * wn + nb, ks)
                            : trop.read(sm.b[buf], ks, 2 * wn + nb);
+            // Stored results come out transposed (C^T = B^T A^T: a lane holds one row of C and
+            // 4 consecutive columns per entry group, for vector stores); atomic results keep C's
+            // layout (consecutive lanes on consecutive columns: coalesced atomics).
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(a[mb], b[nb], acc[mb][nb]);
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = EPI == kEpiAtomicF32 ? mfma32(a[mb], b[nb], acc[mb][nb])
+                                                       : mfma32(b[nb], a[mb], acc[mb][nb]);
         }
     }
 
-    // lane holds C[64 wm + 32 mb + 8 r + 4 gq + c][64 wn + 32 nb + lr]
+    if constexpr (EPI == kEpiAtomicF32) {
+        // lane holds C[64 wm + 32 mb + 8 r + 4 gq + c][64 wn + 32 nb + lr]
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int64_t m = m0 + 64 * wm + 32 * mb + 8 * r + 4 * gq + c;
-                    const int64_t n = n0 + 64 * wn + 32 * nb + lr;
-                    if (m >= g.M) continue;
-                    const float x = acc[mb][nb][4 * r + c];
+                    for (int c = 0; c < 4; ++c) {
+                        const int64_t m = m0 + 64 * wm + 32 * mb + 8 * r + 4 * gq + c;
+                        const int64_t n = n0 + 64 * wn + 32 * nb + lr;
+                        if (m < g.M)
+                            unsafeAtomicAdd(static_cast<float*>(g.c) + m * g.ldc + n,
+                                            acc[mb][nb][4 * r + c]);
+                    }
+    } else {
+        // lane holds C[64 wm + 32 mb + lr][64 wn + 32 nb + 8 r + 4 gq + c], c = 0..3
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int64_t m = m0 + 64 * wm + 32 * mb + lr;
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t n = n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq;
+                    const f32x4 x = {acc[mb][nb][4 * r], acc[mb][nb][4 * r + 1],
+                                     acc[mb][nb][4 * r + 2], acc[mb][nb][4 * r + 3]};
                     if constexpr (EPI == kEpiSilu) {
-                        static_cast<bf16*>(g.c)[m * g.ldc + n] = (bf16)silu_f(x);
-                        if (g.c2) static_cast<bf16*>(g.c2)[m * g.ldc + n] = (bf16)x;
+                        bf16x4 y, z;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            y[c] = (bf16)silu_f(x[c]);
+                            z[c] = (bf16)x[c];
+                        }
+                        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
+                        if (g.c2) *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c2) + m * g.ldc + n) = z;
                     } else if constexpr (EPI == kEpiResidual) {
-                        static_cast<bf16*>(g.c)[m * g.ldc + n] =
-                            (bf16)(x + (float)static_cast<const bf16*>(g.r)[m * g.ldr + n]);
-                    } else if constexpr (EPI == kEpiStoreF32) {
-                        static_cast<float*>(g.c)[m * g.ldc + n] = x;
+                        const bf16x4 rv =
+                            *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.r) + m * g.ldr + n);
+                        bf16x4 y;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) y[c] = (bf16)(x[c] + (float)rv[c]);
+                        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
                     } else {
-                        unsafeAtomicAdd(static_cast<float*>(g.c) + m * g.ldc + n, x);
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + m * g.ldc + n) = x;
                     }
                 }
+        }
+    }
 }
 
 template <bool AT, bool BT>
