@@ -21,6 +21,7 @@ namespace hstu {
 namespace {
 
 constexpr int kGT = 256;               // threads
+constexpr int kXcds = 8;
 constexpr int kGM = 128, kGN = 128, kGK = 64;
 constexpr int kGTile = kGM * kGK;      // elements of one operand stage (either form)
 
@@ -60,9 +61,16 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
     __shared__ __attribute__((aligned(16))) GemmSmem sm;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 5, lr = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kGM;
-    const int n0 = blockIdx.x * kGN;
-    const int64_t kbeg = (int64_t)blockIdx.z * g.kchunk;
+    // Workgroup -> tile, XCD-aware: workgroups are dispatched to the 8 XCDs round robin, so
+    // workgroup id runs on XCD id % 8.  All tiles that share one A block (same row tile and K
+    // range) form a group; a group's tiles take consecutive slots of one XCD, so the A block is
+    // fetched into that XCD's L2 once and reused there.  Slots past the last group exit.
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int group = (slot / g.ntiles) * kXcds + xcd;
+    if (group >= g.mtiles * g.splits) return;  // uniform: whole workgroup
+    const int64_t m0 = (int64_t)(group % g.mtiles) * kGM;
+    const int n0 = (slot % g.ntiles) * kGN;
+    const int64_t kbeg = (int64_t)(group / g.mtiles) * g.kchunk;
     const int64_t kend = min(g.K, kbeg + g.kchunk);
     if (kbeg >= kend) return;  // uniform: whole workgroup
     const int nk = (int)((kend - kbeg + kGK - 1) / kGK);
@@ -219,7 +227,13 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     if (splits > 65535) return hipErrorInvalidValue;
     GemmArgs a = g;
     a.kchunk = kchunk;
-    dim3 grid(g.N / kGN, (unsigned)((g.M + kGM - 1) / kGM), (unsigned)splits);
+    a.mtiles = (int32_t)((g.M + kGM - 1) / kGM);
+    a.ntiles = g.N / kGN;
+    a.splits = (int32_t)splits;
+    const int64_t groups = (int64_t)a.mtiles * a.splits;
+    const int64_t blocks = (groups + kXcds - 1) / kXcds * kXcds * a.ntiles;
+    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks);
     if (!g.at && !g.bt) return launch_t<false, false>(a, grid, s);
     if (!g.at && g.bt) return launch_t<false, true>(a, grid, s);
     if (g.at && !g.bt) return launch_t<true, false>(a, grid, s);

@@ -100,6 +100,7 @@ struct GemmArgs {
     bool at;
     bool bt;            // at && bt is not supported
     int32_t epilogue;
+    int32_t mtiles, ntiles, splits;  // set by launch_gemm
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 
