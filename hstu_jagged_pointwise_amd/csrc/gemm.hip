@@ -3,8 +3,8 @@
 // gradients dW1 = X^T dH, dX = dH W1^T + dY, dW2 = G^T dY and dG = dY W2^T).
 //
 // C (M x N) = epilogue(op(A) op(B)) in bf16 with fp32 accumulation on v_mfma_f32_32x32x16_bf16.
-// Each workgroup (4 wavefronts, 64 x 64 outputs each) computes a 128 x 128 tile over a range of
-// K, 64 at a time.  Operand tiles go from memory straight into LDS with buffer loads that write
+// Each workgroup (4 wavefronts, 64 x 64 outputs each) computes 128 x 128 tiles over a range of
+// K, 64 at a time; workgroups are persistent (two per compute unit) and run sequences of tiles.  Operand tiles go from memory straight into LDS with buffer loads that write
 // LDS (no register staging), double buffered, in the XOR-swizzled tile layout of the attention
 // kernels:
 //   * an operand whose rows are the MFMA's row index and whose columns are K (A row-major,
@@ -14,6 +14,8 @@
 // K-major operands may have any K (rows past the end read as zero), so the token dimension of
 // the weight gradients can be the reduction dimension and can be split over blockIdx.z; those
 // launches add their fp32 partial results atomically into an output the caller has cleared.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -54,141 +56,173 @@ struct GemmSmem {
 
 __device__ __forceinline__ float silu_f(float x) { return x * fast_sigmoid(x); }
 
+// One output tile: rows [m0, m0 + 128), columns [n0, n0 + 128), K range [kbeg, kend).
+struct GemmTile {
+    int64_t m0, kbeg, kend;
+    int n0, nk;
+};
+
+// Tile number -> tile, XCD-aware.  Workgroups are dispatched to the 8 XCDs round robin
+// (workgroup w runs on XCD w % 8), and the persistent workgroup w takes tile numbers w, w + G,
+// ... (G, the grid, a multiple of 8), so all its tiles have numbers of one residue mod 8.  The
+// numbering puts all tiles that share one A block (same row tile and K range: a "group") on
+// consecutive numbers of one residue, i.e. on one XCD at about the same time: the A block is
+// fetched into that XCD's L2 once.  Numbers past the last group are skipped.
+__device__ __forceinline__ bool gemm_tile(const GemmArgs& g, int id, GemmTile& t) {
+    const int xcd = id % kXcds, slot = id / kXcds;
+    const int group = (slot / g.ntiles) * kXcds + xcd;
+    if (group >= g.mtiles * g.splits) return false;
+    t.m0 = (int64_t)(group % g.mtiles) * kGM;
+    t.n0 = (slot % g.ntiles) * kGN;
+    t.kbeg = (int64_t)(group / g.mtiles) * g.kchunk;
+    t.kend = min(g.K, t.kbeg + g.kchunk);
+    t.nk = (int)((t.kend - t.kbeg + kGK - 1) / kGK);
+    return t.kbeg < t.kend;
+}
+
 // AT: A is given as A^T (K x M, row stride lda); else A is M x K.  BT: B is given as B^T (N x K,
 // row stride ldb); else B is K x N.
+//
+// Persistent: each workgroup runs a sequence of tiles and keeps one K step in flight across tile
+// boundaries (the first step of the next tile loads while the current tile's last step and its
+// epilogue run), so a tile's first load does not stall the matrix units.
 template <bool AT, bool BT, int EPI>
 __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
     __shared__ __attribute__((aligned(16))) GemmSmem sm;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 5, lr = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
-    // Workgroup -> tile, XCD-aware: workgroups are dispatched to the 8 XCDs round robin, so
-    // workgroup id runs on XCD id % 8.  All tiles that share one A block (same row tile and K
-    // range) form a group; a group's tiles take consecutive slots of one XCD, so the A block is
-    // fetched into that XCD's L2 once and reused there.  Slots past the last group exit.
-    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
-    const int group = (slot / g.ntiles) * kXcds + xcd;
-    if (group >= g.mtiles * g.splits) return;  // uniform: whole workgroup
-    const int64_t m0 = (int64_t)(group % g.mtiles) * kGM;
-    const int n0 = (slot % g.ntiles) * kGN;
-    const int64_t kbeg = (int64_t)(group / g.mtiles) * g.kchunk;
-    const int64_t kend = min(g.K, kbeg + g.kchunk);
-    if (kbeg >= kend) return;  // uniform: whole workgroup
-    const int nk = (int)((kend - kbeg + kGK - 1) / kGK);
     const bf16* A = static_cast<const bf16*>(g.a);
     const bf16* B = static_cast<const bf16*>(g.b);
-
-    // A operand source
-    buffer_rsrc ars, brs;
-    if constexpr (AT) ars = rows_rsrc(A + kbeg * g.lda + m0, (int)(kend - kbeg), g.lda, kGM);
-    else ars = rows_rsrc(A + m0 * g.lda, (int)min<int64_t>(g.M - m0, kGM), g.lda, (int)g.K);
-    if constexpr (BT) brs = rows_rsrc(B + (int64_t)n0 * g.ldb, kGN, g.ldb, (int)g.K);
-    else brs = rows_rsrc(B + kbeg * g.ldb + n0, (int)(kend - kbeg), g.ldb, kGN);
     const TileDma<AT ? 128 : 64, kGT> adma(tid, g.lda);
     const TileDma<BT ? 64 : 128, kGT> bdma(tid, g.ldb);
 
-    auto issue = [&](int t, int buf) {
-        const int kk = t * kGK;  // relative to kbeg
+    // starts the copy of K step st of tile t into buffer buf
+    auto issue = [&](const GemmTile& t, int st, int buf) {
+        const int64_t kk = (int64_t)st * kGK;  // relative to kbeg
+        const int krows = (int)(t.kend - t.kbeg);
         if constexpr (AT) {
-            adma.issue(ars, sm.a[buf], (int)((int64_t)kk * g.lda * 2));
+            const buffer_rsrc rs = rows_rsrc(A + t.kbeg * g.lda + t.m0, krows, g.lda, kGM);
+            adma.issue(rs, sm.a[buf], (int)(kk * g.lda * 2));
         } else {
-            adma.issue(ars, sm.a[buf], (int)((kbeg + kk) * 2));
-            adma.issue(ars, sm.a[buf] + 64 * kGK, (int)((kbeg + kk + 64 * g.lda) * 2));
+            const buffer_rsrc rs = rows_rsrc(A + t.m0 * g.lda, (int)min<int64_t>(g.M - t.m0, kGM), g.lda, (int)g.K);
+            adma.issue(rs, sm.a[buf], (int)((t.kbeg + kk) * 2));
+            adma.issue(rs, sm.a[buf] + 64 * kGK, (int)((t.kbeg + kk + 64 * g.lda) * 2));
         }
         if constexpr (BT) {
-            bdma.issue(brs, sm.b[buf], (int)((kbeg + kk) * 2));
-            bdma.issue(brs, sm.b[buf] + 64 * kGK, (int)((kbeg + kk + 64 * g.ldb) * 2));
+            const buffer_rsrc rs = rows_rsrc(B + (int64_t)t.n0 * g.ldb, kGN, g.ldb, (int)g.K);
+            bdma.issue(rs, sm.b[buf], (int)((t.kbeg + kk) * 2));
+            bdma.issue(rs, sm.b[buf] + 64 * kGK, (int)((t.kbeg + kk + 64 * g.ldb) * 2));
         } else {
-            bdma.issue(brs, sm.b[buf], (int)((int64_t)kk * g.ldb * 2));
+            const buffer_rsrc rs = rows_rsrc(B + t.kbeg * g.ldb + t.n0, krows, g.ldb, kGN);
+            bdma.issue(rs, sm.b[buf], (int)(kk * g.ldb * 2));
         }
+    };
+    // next tile of this workgroup at or after number id (id advanced past it), if any
+    const int total = (int)gridDim.x * g.rounds;
+    auto next_tile = [&](int& id, GemmTile& t) {
+        for (; id < total; id += gridDim.x)
+            if (gemm_tile(g, id, t)) { id += gridDim.x; return true; }
+        return false;
     };
 
     const RowOperand<64> rowop(lane);
     const TrOperandNat<128> trop(lane);
-    f32x16 acc[2][2];
+    int id = blockIdx.x;
+    GemmTile cur, nxt;
+    if (!next_tile(id, cur)) return;  // uniform: whole workgroup
+    bool more = next_tile(id, nxt);
+    issue(cur, 0, 0);
+    int buf = 0;
+    for (;;) {
+        f32x16 acc[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
-
-    issue(0, 0);
-    for (int t = 0; t < nk; ++t) {
-        const int buf = t & 1;
-        wait_tile_dma();
-        __syncthreads();
-        if (t + 1 < nk) issue(t + 1, buf ^ 1);
+            for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+        for (int t = 0; t < cur.nk; ++t) {
+            wait_tile_dma();
+            __syncthreads();
+            if (t + 1 < cur.nk) issue(cur, t + 1, buf ^ 1);
+            else if (more) issue(nxt, 0, buf ^ 1);
 #pragma unroll
-        for (int ks = 0; ks < kGK / 16; ++ks) {
-            bf16x8 a[2], b[2];
+            for (int ks = 0; ks < kGK / 16; ++ks) {
+                bf16x8 a[2], b[2];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                a[mb] = AT ? trop.read(sm.a[buf], ks, 2 * wm + mb)
-                           : rowop.read(sm.a[buf], 2 * wm + mb, ks);
+                for (int mb = 0; mb < 2; ++mb)
+                    a[mb] = AT ? trop.read(sm.a[buf], ks, 2 * wm + mb)
+                               : rowop.read(sm.a[buf], 2 * wm + mb, ks);
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-                b[nb] = BT ? rowop.read(sm.b[buf], 2 * wn + nb, ks)
-                           : trop.read(sm.b[buf], ks, 2 * wn + nb);
-            // Stored results come out transposed (C^T = B^T A^T: a lane holds one row of C and
-            // 4 consecutive columns per entry group, for vector stores); atomic results keep C's
-            // layout (consecutive lanes on consecutive columns: coalesced atomics).
+                for (int nb = 0; nb < 2; ++nb)
+                    b[nb] = BT ? rowop.read(sm.b[buf], 2 * wn + nb, ks)
+                               : trop.read(sm.b[buf], ks, 2 * wn + nb);
+                // Stored results come out transposed (C^T = B^T A^T: a lane holds one row of C
+                // and 4 consecutive columns per entry group, for vector stores); atomic results
+                // keep C's layout (consecutive lanes on consecutive columns: coalesced atomics).
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        acc[mb][nb] = EPI == kEpiAtomicF32 ? mfma32(a[mb], b[nb], acc[mb][nb])
+                                                           : mfma32(b[nb], a[mb], acc[mb][nb]);
+            }
+            buf ^= 1;
+        }
+        const int64_t m0 = cur.m0;
+        const int n0 = cur.n0;
+        if constexpr (EPI == kEpiAtomicF32) {
+            // lane holds C[64 wm + 32 mb + 8 r + 4 gq + c][64 wn + 32 nb + lr]
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
-                    acc[mb][nb] = EPI == kEpiAtomicF32 ? mfma32(a[mb], b[nb], acc[mb][nb])
-                                                       : mfma32(b[nb], a[mb], acc[mb][nb]);
-        }
-    }
-
-    if constexpr (EPI == kEpiAtomicF32) {
-        // lane holds C[64 wm + 32 mb + 8 r + 4 gq + c][64 wn + 32 nb + lr]
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int64_t m = m0 + 64 * wm + 32 * mb + 8 * r + 4 * gq + c;
-                        const int64_t n = n0 + 64 * wn + 32 * nb + lr;
-                        if (m < g.M)
-                            unsafeAtomicAdd(static_cast<float*>(g.c) + m * g.ldc + n,
-                                            acc[mb][nb][4 * r + c]);
-                    }
-    } else {
-        // lane holds C[64 wm + 32 mb + lr][64 wn + 32 nb + 8 r + 4 gq + c], c = 0..3
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int64_t m = m0 + 64 * wm + 32 * mb + lr;
-            if (m >= g.M) continue;
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t n = n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq;
-                    const f32x4 x = {acc[mb][nb][4 * r], acc[mb][nb][4 * r + 1],
-                                     acc[mb][nb][4 * r + 2], acc[mb][nb][4 * r + 3]};
-                    if constexpr (EPI == kEpiSilu) {
-                        bf16x4 y, z;
+                    for (int r = 0; r < 4; ++r)
 #pragma unroll
                         for (int c = 0; c < 4; ++c) {
-                            y[c] = (bf16)silu_f(x[c]);
-                            z[c] = (bf16)x[c];
+                            const int64_t m = m0 + 64 * wm + 32 * mb + 8 * r + 4 * gq + c;
+                            const int64_t n = n0 + 64 * wn + 32 * nb + lr;
+                            if (m < g.M)
+                                unsafeAtomicAdd(static_cast<float*>(g.c) + m * g.ldc + n,
+                                                acc[mb][nb][4 * r + c]);
                         }
-                        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
-                        if (g.c2) *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c2) + m * g.ldc + n) = z;
-                    } else if constexpr (EPI == kEpiResidual) {
-                        const bf16x4 rv =
-                            *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.r) + m * g.ldr + n);
-                        bf16x4 y;
+        } else {
+            // lane holds C[64 wm + 32 mb + lr][64 wn + 32 nb + 8 r + 4 gq + c], c = 0..3
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) y[c] = (bf16)(x[c] + (float)rv[c]);
-                        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
-                    } else {
-                        *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + m * g.ldc + n) = x;
+            for (int mb = 0; mb < 2; ++mb) {
+                const int64_t m = m0 + 64 * wm + 32 * mb + lr;
+                if (m >= g.M) continue;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int64_t n = n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq;
+                        const f32x4 x = {acc[mb][nb][4 * r], acc[mb][nb][4 * r + 1],
+                                         acc[mb][nb][4 * r + 2], acc[mb][nb][4 * r + 3]};
+                        if constexpr (EPI == kEpiSilu) {
+                            bf16x4 y, z;
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                y[c] = (bf16)silu_f(x[c]);
+                                z[c] = (bf16)x[c];
+                            }
+                            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
+                            if (g.c2) *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c2) + m * g.ldc + n) = z;
+                        } else if constexpr (EPI == kEpiResidual) {
+                            const bf16x4 rv = *reinterpret_cast<const bf16x4*>(
+                                static_cast<const bf16*>(g.r) + m * g.ldr + n);
+                            bf16x4 y;
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) y[c] = (bf16)(x[c] + (float)rv[c]);
+                            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
+                        } else {
+                            *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + m * g.ldc + n) = x;
+                        }
                     }
-                }
+            }
         }
+        if (!more) break;
+        cur = nxt;
+        more = next_tile(id, nxt);
     }
 }
 
@@ -231,9 +265,15 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     a.ntiles = g.N / kGN;
     a.splits = (int32_t)splits;
     const int64_t groups = (int64_t)a.mtiles * a.splits;
-    const int64_t blocks = (groups + kXcds - 1) / kXcds * kXcds * a.ntiles;
-    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-    dim3 grid((unsigned)blocks);
+    const int64_t numbers = (groups + kXcds - 1) / kXcds * kXcds * a.ntiles;  // tile numbers
+    if (numbers >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    // persistent grid: two workgroups per compute unit (a multiple of 8), each taking every
+    // grid-th tile number
+    const int64_t slots = 2 * (int64_t)(g.compute_units > 0 ? g.compute_units : 256);
+    const int64_t gsize = std::min<int64_t>((numbers + kXcds - 1) / kXcds * kXcds,
+                                            (slots + kXcds - 1) / kXcds * kXcds);
+    a.rounds = (int32_t)((numbers + gsize - 1) / gsize);
+    dim3 grid((unsigned)gsize);
     if (!g.at && !g.bt) return launch_t<false, false>(a, grid, s);
     if (!g.at && g.bt) return launch_t<false, true>(a, grid, s);
     if (g.at && !g.bt) return launch_t<true, false>(a, grid, s);

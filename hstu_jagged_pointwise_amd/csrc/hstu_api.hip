@@ -572,8 +572,9 @@ hstu_status_t layer_checks(const hstu_plan_t* plan, const hstu_attn_args_t* args
     return HSTU_OK;
 }
 
-hstu::GemmArgs gemm_args(const void* a, int64_t lda, bool at, const void* b, int64_t ldb, bool bt,
-                         int64_t M, int32_t N, int64_t K, void* c, int64_t ldc, int32_t epi) {
+hstu::GemmArgs gemm_args(const hstu_plan_t* plan, const void* a, int64_t lda, bool at,
+                         const void* b, int64_t ldb, bool bt, int64_t M, int32_t N, int64_t K,
+                         void* c, int64_t ldc, int32_t epi) {
     hstu::GemmArgs g{};
     g.a = a;
     g.lda = lda;
@@ -587,6 +588,7 @@ hstu::GemmArgs gemm_args(const void* a, int64_t lda, bool at, const void* b, int
     g.c = c;
     g.ldc = ldc;
     g.epilogue = epi;
+    g.compute_units = plan->compute_units;
     return g;
 }
 
@@ -619,7 +621,7 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     char* a = z + align_up(size_t(T) * 4 * hd * 2, 256);
     // Z = SiLU(X W1): columns [U | V | Q | K]
     hipError_t e = hstu::launch_gemm(
-        gemm_args(x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z, 4 * hd, hstu::kEpiSilu), s);
+        gemm_args(plan, x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z, 4 * hd, hstu::kEpiSilu), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     hstu::AttnParams p = base_params(plan, args);
     const int64_t ldz = 4 * int64_t(hd);
@@ -635,7 +637,7 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     e = hstu::launch_ln_gate_bf16(a, z, ldz, a, T, hd, ln_eps, s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     // Y = G W2 + X
-    hstu::GemmArgs g = gemm_args(a, hd, false, w2, d_model, false, T, d_model, hd, y, d_model,
+    hstu::GemmArgs g = gemm_args(plan, a, hd, false, w2, d_model, false, T, d_model, hd, y, d_model,
                                  hstu::kEpiResidual);
     g.r = x;
     g.ldr = d_model;
@@ -682,7 +684,7 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     const int64_t ldz = 4 * int64_t(hd);
 
     // recompute H = X W1 and Z = SiLU(H), columns [U | V | Q | K]
-    hstu::GemmArgs ga = gemm_args(x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z,
+    hstu::GemmArgs ga = gemm_args(plan, x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z,
                                   ldz, hstu::kEpiSilu);
     ga.c2 = hpre;
     e = hstu::launch_gemm(ga, s);
@@ -699,14 +701,14 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     if (e == hipSuccess) e = hstu::launch_attn_fwd_bf16(p, s);
     // dG = dY W2^T (fp32)
     if (e == hipSuccess)
-        e = hstu::launch_gemm(gemm_args(dy, d_model, false, w2, d_model, true, T, hd, d_model, dg,
+        e = hstu::launch_gemm(gemm_args(plan, dy, d_model, false, w2, d_model, true, T, hd, d_model, dg,
                                         hd, hstu::kEpiStoreF32), s);
     // G, dA and the U-slot gradient of H
     if (e == hipSuccess)
         e = hstu::launch_ln_gate_bwd_bf16(a, z, hpre, ldz, dg, g, da, dh, ldz, T, hd, ln_eps, s);
     // dW2 = G^T dY, split over tokens
     if (e == hipSuccess) {
-        hstu::GemmArgs gw = gemm_args(g, hd, true, dy, d_model, false, hd, d_model, T, dw2,
+        hstu::GemmArgs gw = gemm_args(plan, g, hd, true, dy, d_model, false, hd, d_model, T, dw2,
                                       d_model, hstu::kEpiAtomicF32);
         gw.kchunk = token_chunk(plan, T, hd, d_model);
         e = hstu::launch_gemm(gw, s);
@@ -733,14 +735,14 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         e = hstu::launch_silu_bwd_bf16(dh + size_t(hd) * 2, hpre + size_t(hd) * 2, ldz, T, 3 * hd, s);
     // dW1 = X^T dH, split over tokens
     if (e == hipSuccess) {
-        hstu::GemmArgs gw = gemm_args(x, d_model, true, dh, ldz, false, d_model, 4 * hd, T, dw1,
+        hstu::GemmArgs gw = gemm_args(plan, x, d_model, true, dh, ldz, false, d_model, 4 * hd, T, dw1,
                                       ldz, hstu::kEpiAtomicF32);
         gw.kchunk = token_chunk(plan, T, d_model, 4 * hd);
         e = hstu::launch_gemm(gw, s);
     }
     // dX = dH W1^T + dY
     if (e == hipSuccess) {
-        hstu::GemmArgs gx = gemm_args(dh, ldz, false, w1, ldz, true, T, d_model, ldz, dx, d_model,
+        hstu::GemmArgs gx = gemm_args(plan, dh, ldz, false, w1, ldz, true, T, d_model, ldz, dx, d_model,
                                       hstu::kEpiResidual);
         gx.r = dy;
         gx.ldr = d_model;

@@ -100,7 +100,9 @@ struct GemmArgs {
     bool at;
     bool bt;            // at && bt is not supported
     int32_t epilogue;
+    int32_t compute_units;           // for the persistent grid (0: 256)
     int32_t mtiles, ntiles, splits;  // set by launch_gemm
+    int32_t rounds;                  // set by launch_gemm: tile numbers per workgroup
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 
