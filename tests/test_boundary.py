@@ -90,6 +90,52 @@ def test_plan_validation_codes():
     assert status_of(c, a, OFF, None, host) == 2
 
 
+def test_cached_plan_validation_and_units():
+    c = hj.hstu_plan_create_cached
+    host = hj.HSTU_PLAN_HOST_ONLY
+    cand = np.array([0, 4, 4, 10])            # 3 users, 4 + 0 + 6 candidates
+    cache = np.array([0, 7, 9, 9])            # 7 + 2 + 0 cached tokens
+    a = args(total_tokens=10, max_seqlen=11)
+    assert status_of(c, a, cand, cache, host) == 0
+    assert status_of(c, args(total_tokens=10, max_seqlen=10), cand, cache, host) == 3  # 7 + 4 > N
+    assert status_of(c, args(total_tokens=11, max_seqlen=11), cand, cache, host) == 3  # [B] != T
+    assert status_of(c, a, cand, np.array([0, 7, 5, 9]), host) == 3                    # decreasing
+    assert status_of(c, args(total_tokens=10, max_seqlen=11, dtype=hj.HSTU_F32), cand, cache,
+                     host) == 4                                                        # bf16 only
+    plan = c(a, cand, cache, host)
+    info = hj.hstu_plan_info(plan)
+    assert info["visible_pairs"] == 2 * (4 * (7 + 1) + 6 * (0 + 1))  # (cached + self) per row, head
+    items = hj.hstu_plan_units(plan, 2)
+    # one item per (user with candidates, head), covering the user's cache tiles
+    got = sorted((int(r[0]), int(r[1]), int(r[3])) for r in items)
+    assert got == [(0, 0, 1), (0, 1, 1), (2, 0, 0), (2, 1, 0)]
+    lib = _lib()
+    P = ctypes.c_void_p
+    # a cached plan serves only the cached forward, and the cached forward only a cached plan
+    assert lib.hstu_attn_fwd(P(plan.handle), ctypes.byref(a), P(16), P(16), P(16), None, 0.0,
+                             P(16), None, 0, None) == 8
+    assert lib.hstu_attn_fwd_cached(P(plan.handle), ctypes.byref(a), *([P(16)] * 6), P(16), None,
+                                    0, None) == 8                      # host-only plan
+    reg = hj.hstu_plan_create(args(), OFF, None, host)
+    assert lib.hstu_attn_fwd_cached(P(reg.handle), ctypes.byref(args()), *([P(16)] * 6), P(16),
+                                    None, 0, None) == 2
+    plan.close()
+    reg.close()
+
+
+def test_jagged_select_argument_checks():
+    lib = _lib()
+    P = ctypes.c_void_p
+    f = lib.hstu_jagged_select
+    assert f(2, P(16), 10, P(16), 0, None, 64, P(16), P(16), None) == 0    # nothing to copy
+    assert f(2, P(16), 10, P(16), 4, None, 12, P(16), P(16), None) == 5    # row not 8-byte
+    assert f(2, P(16), 10, P(16), 4, None, 64, P(20), P(16), None) == 5    # misaligned
+    assert f(2, None, 10, P(16), 4, None, 64, P(16), P(16), None) == 1
+    assert f(0, P(16), 10, P(16), 4, None, 64, P(16), P(16), None) == 2    # rows but no sequences
+    assert f(-1, P(16), 10, P(16), 4, None, 64, P(16), P(16), None) == 2
+    assert f(2, P(16), 10, P(16), 4, None, 0, P(16), P(16), None) == 2
+
+
 def test_calls_on_host_only_plan_and_mismatched_sizes():
     plan = hj.hstu_plan_create(args(), OFF, None, hj.HSTU_PLAN_HOST_ONLY)
     lib = _lib()
