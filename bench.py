@@ -5,7 +5,8 @@ One step = the whole path for one batch of the long-sequence forward+backward wo
 lengths uniform in [1024, 8192], 8 heads of width 128, 8 context tokens and 64 candidates per
 sequence, position + time relative bias, bf16 inputs with fp32 accumulation): build the work-list
 plan on the host and upload it, attention forward, then the dK/dV and dQ + bias-gradient
-backward passes.  Inputs are resident in HBM before timing starts.
+backward passes (the dK/dV pass stores dS, bf16, for the dQ pass to read back).  Inputs are
+resident in HBM before timing starts.
 
 FLOPs are counted on visible (unmasked) pairs only: 4d per pair per head forward, 10d backward.
 
@@ -169,6 +170,11 @@ def bench_headline(args, torch, hj, runner, w):
     drt = torch.empty((H, 128), dtype=torch.float32, device=out.device)
     timer = Timer(torch)
     plan_host_s = []
+    # stored dS: the same size for every step's plan of this batch
+    p0 = runner.plan_for(w, base_args)
+    ws = torch.empty(max(hj.hstu_workspace_bytes(p0, hj.OP_BWD), 16), dtype=torch.uint8,
+                     device=out.device)
+    p0.close()
 
     def step(record):
         t0 = time.perf_counter()
@@ -179,10 +185,12 @@ def bench_headline(args, torch, hj, runner, w):
             hj.hstu_attn_fwd(plan, base_args, dev["q"], dev["k"], dev["v"], out)
 
         def dkdv():
-            hj.hstu_attn_bwd_dkdv(plan, base_args, dev["q"], dev["k"], dev["v"], dev["dout"], dk, dv)
+            hj.hstu_attn_bwd_dkdv(plan, base_args, dev["q"], dev["k"], dev["v"], dev["dout"], dk, dv,
+                                  ws=ws)
 
         def dqp():
-            hj.hstu_attn_bwd_dq(plan, base_args, dev["q"], dev["k"], dev["v"], dev["dout"], dq, drp, drt)
+            hj.hstu_attn_bwd_dq(plan, base_args, dev["q"], dev["k"], dev["v"], dev["dout"], dq, drp, drt,
+                                ws=ws)
 
         if record:
             timer.record("fwd", fwd)

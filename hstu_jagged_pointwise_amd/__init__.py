@@ -87,9 +87,9 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_attn_fwd.restype = I32
     lib.hstu_attn_bwd.argtypes = [P, argp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_bwd.restype = I32
-    lib.hstu_attn_bwd_dkdv.argtypes = [P, argp, P, P, P, P, P, P, P]
+    lib.hstu_attn_bwd_dkdv.argtypes = [P, argp, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_bwd_dkdv.restype = I32
-    lib.hstu_attn_bwd_dq.argtypes = [P, argp, P, P, P, P, P, P, P, P]
+    lib.hstu_attn_bwd_dq.argtypes = [P, argp, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_bwd_dq.restype = I32
     lib.hstu_layer_fwd.argtypes = [P, argp, I32, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
     lib.hstu_layer_fwd.restype = I32
@@ -244,17 +244,24 @@ def hstu_attn_bwd(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, dk, dv, dra
         _stream(stream)))
 
 
-def hstu_attn_bwd_dkdv(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dk, dv, stream=None) -> None:
+def hstu_attn_bwd_dkdv(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dk, dv, ws=None,
+                       stream=None) -> None:
+    """dK, dV; with ws (hstu_workspace_bytes(plan, OP_BWD) bytes) also stores dS there for
+    hstu_attn_bwd_dq."""
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load_library().hstu_attn_bwd_dkdv(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-        _ptr(dk), _ptr(dv), _stream(stream)))
+        _ptr(dk), _ptr(dv), _ptr(ws), nbytes, _stream(stream)))
 
 
 def hstu_attn_bwd_dq(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, drab_pos=None,
-                     drab_ts=None, stream=None) -> None:
+                     drab_ts=None, ws=None, stream=None) -> None:
+    """dQ and the bias-table gradients; with ws, reads the dS that hstu_attn_bwd_dkdv stored in
+    the same ws, else recomputes S and dP."""
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load_library().hstu_attn_bwd_dq(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-        _ptr(dq), _ptr(drab_pos), _ptr(drab_ts), _stream(stream)))
+        _ptr(dq), _ptr(drab_pos), _ptr(drab_ts), _ptr(ws), nbytes, _stream(stream)))
 
 
 def hstu_layer_fwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, y,

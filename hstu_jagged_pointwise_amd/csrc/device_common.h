@@ -432,6 +432,23 @@ struct TrOperand {
     }
 };
 
+// The same transposed read for one fixed 32-column block mb of the tile (an MFMA B operand
+// B[k][n] = T[16 st + key(k)][32 mb + n] has the same per-lane layout as the A operand above).
+template <int D>
+struct TrBlock {
+    int off[2];
+    __device__ __forceinline__ TrBlock(int lane, int mb) {
+        const int s = lane & 15, q = (lane >> 4) & 1, rr = 4 * (lane >> 5) + (s >> 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) off[h] = tile_off<D>(rr + 8 * h, 32 * mb + 16 * q + 4 * (s & 3));
+    }
+    __device__ __forceinline__ bf16x8 read(const bf16* tile, int st) const {
+        const bf16x4 lo = lds_read_tr4(tile + 16 * st * D + off[0]);
+        const bf16x4 hi = lds_read_tr4(tile + 16 * st * D + off[1]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
 // Per-lane element offsets of an MFMA A operand read along tile rows: lane (lr = l % 32, g = l / 32)
 // takes row 32 blk + lr, columns 16 ks + 8g .. + 7.  Add 32 * blk * D for row block blk.
 template <int D>
@@ -461,6 +478,53 @@ __device__ __forceinline__ buffer_rsrc rows_rsrc(const bf16* base, int n, int64_
 #endif
 }
 
+// Copies into LDS issued from inline assembly: the compiler then does not know that LDS is
+// being written behind its back, so it neither waits for these copies before later LDS reads nor
+// counts them -- the caller waits for each copy itself (wait_vmcnt / wait_vmcnt_upto, then a
+// barrier) before anything reads its destination.  Used where several tiles stay in flight;
+// with the builtin, every LDS read would wait for all copies.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource words over `bytes` bytes at base (loads past the end return zeros).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)((a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// LDS byte address of a pointer into __shared__ memory (the low half of its generic address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
+// Lane l copies 16 bytes at byte offset voff to LDS address lds + 16 l.
+__device__ __forceinline__ void copy16_lds_asm(i32x4 rs, uint32_t lds, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+#else
+    (void)rs;
+    (void)lds;
+    (void)voff;
+#endif
+}
+
+// Lane l copies the dword at byte offset voff to LDS address lds + 4 l.
+__device__ __forceinline__ void copy4_lds_asm(i32x4 rs, uint32_t lds, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+#else
+    (void)rs;
+    (void)lds;
+    (void)voff;
+#endif
+}
+
 // Copies tile rows [r0, r0 + 64) of one slice from memory straight into an LDS tile (buffer
 // loads with the LDS-write option, 16 bytes per lane): instruction u of wavefront w fills the
 // 1 KB block u * W + w of the tile (W wavefronts; blocks past the tile's D / 8 are skipped), lane
@@ -484,6 +548,13 @@ struct TileDma {
             off[u] = (int)(((int64_t)row * ld + 8 * c) * 2);
         }
     }
+    // The same copy issued from inline assembly (see copy16_lds_asm).
+    __device__ __forceinline__ void issue_asm(i32x4 rs, bf16* tile, int row_bytes) const {
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            if (C % W == 0 || u * W + wave < C)
+                copy16_lds_asm(rs, lds_addr(tile + (u * W + wave) * 512), off[u] + row_bytes);
+    }
     // row_bytes = r0 * ld * 2
     __device__ __forceinline__ void issue(buffer_rsrc rs, bf16* tile, int row_bytes) const {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -500,7 +571,58 @@ struct TileDma {
     }
 };
 
+// 8-byte buffer store of 4 bf16 at byte offset voff + soff (soff wavefront-uniform); stores past
+// the resource's size are dropped.
+__device__ __forceinline__ void store_bf16x4(bf16x4 v, buffer_rsrc rs, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), rs, voff, soff, 0);
+#else
+    (void)v;
+    (void)rs;
+    (void)voff;
+    (void)soff;
+#endif
+}
+
 __device__ __forceinline__ void wait_tile_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits until at most N of this wavefront's vector memory loads are outstanding (they complete in
+// issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wavefront's LDS operations, then
+// s_barrier, without the vector-memory wait that __syncthreads() implies (copies into LDS that
+// are still in flight stay in flight; each wavefront waits for its own with wait_vmcnt first).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// wait_vmcnt with a wavefront-uniform count (counts above 15 wait for all).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    switch (n) {
+        case 15: wait_vmcnt<15>(); break;
+        case 14: wait_vmcnt<14>(); break;
+        case 13: wait_vmcnt<13>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 11: wait_vmcnt<11>(); break;
+        case 10: wait_vmcnt<10>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
 
 // Scheduling hint for a block of N MFMAs, each fed by one LDS read: issue LA reads first, then
 // alternate one MFMA and one read, so each read has LA matrix instructions to land.

@@ -36,6 +36,10 @@ struct hstu_plan {
     int32_t compute_units = 256;
     bool cached = false;         // candidate scoring against cached history
     std::vector<CacheSeq> cache;
+    // stored-dS backward (bf16, head_dim 64 / 128): per-sequence element offsets of the dense
+    // npad x npad blocks of every head, and their total
+    std::vector<int64_t> ds_off;
+    int64_t ds_elems = 0;
     void* dbuf = nullptr;
     const SeqInfo* d_seqs = nullptr;
     const WorkUnit* d_fwd = nullptr;
@@ -43,6 +47,7 @@ struct hstu_plan {
     const FwdItem* d_items = nullptr;
     const FixItem* d_fix = nullptr;
     const CacheSeq* d_cache = nullptr;
+    const int64_t* d_ds_off = nullptr;
 };
 
 namespace {
@@ -191,6 +196,29 @@ size_t part_bytes(const hstu_plan_t* plan) {
     return align_up(size_t(plan->parts) * plan->fwd_rows * plan->shape.head_dim * 4, 256);
 }
 
+// Stored dS of the bf16 backward (0 when the plan does not use it).
+size_t ds_bytes(const hstu_plan_t* plan) { return align_up(size_t(plan->ds_elems) * 2, 256); }
+
+// The stored-dS layout: a dense npad x npad bf16 block per (sequence, head), npad = n rounded up
+// to 128, addressed with 32-bit byte offsets within a block.  Head dims 64 and 128 only (the dQ
+// kernel keeps two 16 KB dS tiles where the query rows of the recomputing kernel go).
+void plan_ds_layout(hstu_plan_t* plan) {
+    plan->ds_off.clear();
+    plan->ds_elems = 0;
+    const hstu_attn_args_t& a = plan->shape;
+    if (plan->cached || a.dtype != HSTU_BF16 || a.head_dim < 64) return;
+    int64_t total = 0;
+    std::vector<int64_t> off(plan->seqs.size());
+    for (size_t b = 0; b < plan->seqs.size(); ++b) {
+        const int64_t npad = (int64_t(plan->seqs[b].n) + 127) / 128 * 128;
+        if (npad * npad * 2 >= (int64_t(1) << 31)) return;
+        off[b] = total;
+        total += int64_t(a.num_heads) * npad * npad;
+    }
+    plan->ds_off = std::move(off);
+    plan->ds_elems = total;
+}
+
 hstu::AttnParams base_params(const hstu_plan_t* plan, const hstu_attn_args_t* a) {
     hstu::AttnParams p{};
     p.seqs = plan->d_seqs;
@@ -231,24 +259,28 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
     }
     plan->compute_units = compute_units;
     if (plan->shape.dtype == HSTU_BF16) build_fwd_items(plan, compute_units);
+    plan_ds_layout(plan);
 
     if (!host_only) {
-        const size_t sizes[6] = {sizeof(SeqInfo) * plan->seqs.size(),
-                                 sizeof(WorkUnit) * plan->fwd.size(),
-                                 sizeof(WorkUnit) * plan->bwd.size(),
-                                 sizeof(FwdItem) * plan->items.size(),
-                                 sizeof(FixItem) * plan->fix.size(),
-                                 sizeof(CacheSeq) * plan->cache.size()};
-        const void* srcs[6] = {plan->seqs.data(), plan->fwd.data(), plan->bwd.data(),
-                               plan->items.data(), plan->fix.data(), plan->cache.data()};
-        size_t offs[6], total = 0;
-        for (int i = 0; i < 6; ++i) {
+        constexpr int kArrays = 7;
+        const size_t sizes[kArrays] = {sizeof(SeqInfo) * plan->seqs.size(),
+                                       sizeof(WorkUnit) * plan->fwd.size(),
+                                       sizeof(WorkUnit) * plan->bwd.size(),
+                                       sizeof(FwdItem) * plan->items.size(),
+                                       sizeof(FixItem) * plan->fix.size(),
+                                       sizeof(CacheSeq) * plan->cache.size(),
+                                       sizeof(int64_t) * plan->ds_off.size()};
+        const void* srcs[kArrays] = {plan->seqs.data(), plan->fwd.data(), plan->bwd.data(),
+                                     plan->items.data(), plan->fix.data(), plan->cache.data(),
+                                     plan->ds_off.data()};
+        size_t offs[kArrays], total = 0;
+        for (int i = 0; i < kArrays; ++i) {
             offs[i] = total;
             total += align_up(sizes[i], 16);
         }
         total = std::max<size_t>(total, 16);
         std::vector<char> host(total);
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < kArrays; ++i)
             if (sizes[i]) std::memcpy(host.data() + offs[i], srcs[i], sizes[i]);
         if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
             delete plan;
@@ -266,6 +298,7 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
         plan->d_items = reinterpret_cast<const FwdItem*>(base + offs[3]);
         plan->d_fix = reinterpret_cast<const FixItem*>(base + offs[4]);
         plan->d_cache = reinterpret_cast<const CacheSeq*>(base + offs[5]);
+        plan->d_ds_off = reinterpret_cast<const int64_t*>(base + offs[6]);
         plan->on_device = true;
     }
     *out = plan;
@@ -412,6 +445,7 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
     switch (op) {
         case 0: return part_bytes(plan);
         case 1: return align_up(thd * elem_size(a.dtype), 256) + part_bytes(plan);
+        case 2: return ds_bytes(plan);
         case 3: {
             (void)d_model;  // Z and A depend on H*d only
             return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256) + part_bytes(plan);
@@ -421,7 +455,7 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
             (void)d_model;
             // Z, H (pre-activation), dH: T x 4Hd bf16; A, G, dA: T x Hd bf16; dG: T x Hd fp32
             return 3 * align_up(4 * thd * 2, 256) + 3 * align_up(thd * 2, 256) +
-                   align_up(thd * 4, 256) + part_bytes(plan);
+                   align_up(thd * 4, 256) + std::max(part_bytes(plan), ds_bytes(plan));
         }
         default: return 0;
     }
@@ -498,13 +532,28 @@ hstu_status_t bwd_params(const hstu_plan_t* plan, const hstu_attn_args_t* args, 
 
 extern "C" {
 
+// The stored-dS workspace of a backward call: NULL when the plan has none or the caller passed
+// none (the dQ pass then recomputes S and dP).
+hstu_status_t ds_workspace(const hstu_plan_t* plan, void* ws, size_t ws_bytes, void** ds) {
+    *ds = nullptr;
+    const size_t need = hstu_workspace_bytes(plan, 2, 0);
+    if (need == 0 || !ws) return HSTU_OK;
+    if (ws_bytes < need) return HSTU_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(ws)) return HSTU_ERR_MISALIGNED;
+    *ds = ws;
+    return HSTU_OK;
+}
+
 hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                                  const void* q, const void* k, const void* v, const void* dout,
-                                 void* dk, void* dv, void* stream) {
+                                 void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
     hstu::AttnParams p;
     hstu_status_t st = bwd_params(plan, args, q, k, v, dout, {dk, dv}, &p);
     if (st != HSTU_OK) return st;
     if (args->total_tokens == 0) return HSTU_OK;
+    st = ds_workspace(plan, ws, ws_bytes, &p.ds);
+    if (st != HSTU_OK) return st;
+    p.ds_off = p.ds ? plan->d_ds_off : nullptr;
     p.units = plan->d_bwd;
     p.num_units = (int32_t)plan->bwd.size();
     p.dk = dk;
@@ -516,12 +565,18 @@ hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t
 
 hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                                const void* q, const void* k, const void* v, const void* dout,
-                               void* dq, float* drab_pos, float* drab_ts, void* stream) {
+                               void* dq, float* drab_pos, float* drab_ts, void* ws,
+                               size_t ws_bytes, void* stream) {
     hstu::AttnParams p;
     hstu_status_t st = bwd_params(plan, args, q, k, v, dout, {dq}, &p);
     if (st != HSTU_OK) return st;
     if ((drab_pos && !aligned16(drab_pos)) || (drab_ts && !aligned16(drab_ts)))
         return HSTU_ERR_MISALIGNED;
+    if (args->total_tokens != 0) {
+        st = ds_workspace(plan, ws, ws_bytes, &p.ds);
+        if (st != HSTU_OK) return st;
+        p.ds_off = p.ds ? plan->d_ds_off : nullptr;
+    }
     p.dq = dq;
     p.drab_pos = args->rab_pos ? drab_pos : nullptr;
     p.drab_ts = args->rab_ts ? drab_ts : nullptr;
@@ -540,14 +595,14 @@ hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
                             const void* k, const void* v, const void* dout, void* dq, void* dk,
                             void* dv, float* drab_pos, float* drab_ts, void* ws, size_t ws_bytes,
                             void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     hstu::AttnParams p;
     hstu_status_t st = bwd_params(plan, args, q, k, v, dout, {dq, dk, dv}, &p);
     if (st != HSTU_OK) return st;
-    st = hstu_attn_bwd_dkdv(plan, args, q, k, v, dout, dk, dv, stream);
+    if (args->total_tokens != 0 && hstu_workspace_bytes(plan, 2, 0) > 0 && !ws)
+        return HSTU_ERR_NULL_ARG;
+    st = hstu_attn_bwd_dkdv(plan, args, q, k, v, dout, dk, dv, ws, ws_bytes, stream);
     if (st != HSTU_OK) return st;
-    return hstu_attn_bwd_dq(plan, args, q, k, v, dout, dq, drab_pos, drab_ts, stream);
+    return hstu_attn_bwd_dq(plan, args, q, k, v, dout, dq, drab_pos, drab_ts, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
@@ -680,7 +735,9 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     char* g = a + narrow;
     char* da = g + narrow;
     float* dg = reinterpret_cast<float*>(da + narrow);
-    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(dg) + align_up(size_t(T) * hd * 4, 256));
+    // the forward's partial slots, later the backward's stored dS
+    char* tail = reinterpret_cast<char*>(dg) + align_up(size_t(T) * hd * 4, 256);
+    float* part = reinterpret_cast<float*>(tail);
     const int64_t ldz = 4 * int64_t(hd);
 
     // recompute H = X W1 and Z = SiLU(H), columns [U | V | Q | K]
@@ -721,6 +778,10 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         p.dk = dh + size_t(3 * hd) * 2;
         p.units = plan->d_bwd;
         p.num_units = (int32_t)plan->bwd.size();
+        if (plan->ds_elems > 0) {
+            p.ds = tail;
+            p.ds_off = plan->d_ds_off;
+        }
         e = hstu::launch_attn_bwd_dkdv_bf16(p, s);
     }
     if (e == hipSuccess) {

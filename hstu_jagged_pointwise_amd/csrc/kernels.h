@@ -46,6 +46,12 @@ struct AttnParams {
     const void* vc;
     const int64_t* ts_cache;
     int64_t ld_cache;
+    // bf16 backward with stored dS (head_dim 64 and 128): when ds is set, the dK/dV pass also
+    // writes dS * N of every pair it visits to ds, and the dQ pass reads it back instead of
+    // recomputing S and dP.  Sequence b, head h owns the dense npad x npad block (npad = n rounded
+    // up to 128) at ds + ds_off[b] + h npad^2, row = key, column = query.
+    void* ds;
+    const int64_t* ds_off;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s);

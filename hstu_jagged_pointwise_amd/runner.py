@@ -6,7 +6,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_fwd, hstu_attn_fwd_cached,
+from . import (HSTU_BF16, HSTU_F32, hstu_attn_bwd, hstu_attn_bwd_dkdv, hstu_attn_bwd_dq,
+               hstu_attn_fwd, hstu_attn_fwd_cached,
                hstu_layer_bwd, hstu_layer_fwd, hstu_plan_create, hstu_plan_create_cached,
                make_args)
 
@@ -69,7 +70,10 @@ def attn_fwd(batch: dict, dev: dict, plan=None, args=None, u=None, ln_eps: float
     return out
 
 
-def attn_bwd(batch: dict, dev: dict, plan=None, args=None, stream=None) -> dict:
+def attn_bwd(batch: dict, dev: dict, plan=None, args=None, stream=None, split: bool = False,
+             ws=None) -> dict:
+    """hstu_attn_bwd (with workspace ws, allocated when None), or with split=True its two halves
+    hstu_attn_bwd_dkdv and hstu_attn_bwd_dq, which recompute S and dP in the dQ pass."""
     import torch
     args = args_for(batch, dev) if args is None else args
     plan = plan_for(batch, args) if plan is None else plan
@@ -80,8 +84,14 @@ def attn_bwd(batch: dict, dev: dict, plan=None, args=None, stream=None) -> dict:
         g["drab_pos"] = torch.empty((H, 128), dtype=torch.float32, device=dev_device(dev))
     if dev.get("rab_ts") is not None:
         g["drab_ts"] = torch.empty((H, 128), dtype=torch.float32, device=dev_device(dev))
-    hstu_attn_bwd(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], g["dq"], g["dk"],
-                  g["dv"], g["drab_pos"], g["drab_ts"], stream=stream)
+    if split:
+        hstu_attn_bwd_dkdv(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], g["dk"], g["dv"],
+                           stream=stream)
+        hstu_attn_bwd_dq(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], g["dq"],
+                         g["drab_pos"], g["drab_ts"], stream=stream)
+    else:
+        hstu_attn_bwd(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], g["dq"], g["dk"],
+                      g["dv"], g["drab_pos"], g["drab_ts"], ws=ws, stream=stream)
     return g
 
 

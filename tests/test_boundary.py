@@ -157,11 +157,25 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
                               *([P(16)] * 6), 1 << 30, None) == 2
     assert lib.hstu_layer_bwd(P(plan.handle), ctypes.byref(a), 512, *([P(16)] * 4), 1e-5,
                               *([P(16)] * 6), 1 << 30, None) == 8   # host-only plan
-    # layer backward: Z, H and dH (T x 4Hd bf16), A, G, dA (T x Hd bf16), dG (T x Hd fp32)
+    # attention backward: the stored dS, one 128 x 128 bf16 block per (sequence, head) here
+    ds = 3 * 2 * 128 * 128 * 2
+    assert hj.hstu_workspace_bytes(plan, hj.OP_BWD) == ds
+    # layer backward: Z, H and dH (T x 4Hd bf16), A, G, dA (T x Hd bf16), dG (T x Hd fp32),
+    # then the stored dS (no partial slots here)
     hd = 2 * 64
-    want = 3 * (30 * 4 * hd * 2) + 3 * (30 * hd * 2) + 30 * hd * 4
+    want = 3 * (30 * 4 * hd * 2) + 3 * (30 * hd * 2) + 30 * hd * 4 + ds
     assert hj.hstu_workspace_bytes(plan, hj.OP_LAYER_BWD, 512) == want
     plan.close()
+    # no stored dS for fp32 or head_dim 32; npad rounds each length up to 128
+    for kw in (dict(dtype=hj.HSTU_F32), dict(head_dim=32)):
+        p2 = hj.hstu_plan_create(args(**kw), OFF, None, hj.HSTU_PLAN_HOST_ONLY)
+        assert hj.hstu_workspace_bytes(p2, hj.OP_BWD) == 0, kw
+        p2.close()
+    off = np.array([0, 128, 257, 257])
+    p3 = hj.hstu_plan_create(args(total_tokens=257, max_seqlen=200, head_dim=128), off, None,
+                             hj.HSTU_PLAN_HOST_ONLY)
+    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == 2 * (128 * 128 + 256 * 256) * 2
+    p3.close()
 
 
 def _plan(batch, dtype="bf16"):

@@ -435,6 +435,46 @@ def test_bwd_edges(d, mask, dtype):
     _bwd_check(w, dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", [0, 2, 3, 4])
+def test_bwd_recompute_path(d, mask):
+    """hstu_attn_bwd_dkdv + hstu_attn_bwd_dq: the dQ pass recomputes S and dP (no stored dS)."""
+    nc, nt = MASKS[mask]
+    w = hs.make_inputs(EDGE_LENGTHS, 2, d, dtype="bf16", seed=200 + d + mask, rab=True,
+                       num_contexts=nc, num_targets=nt, max_seqlen=300, backward=True)
+    say(f"bwd recompute path d={d} nc={nc} nt={nt}")
+    dev = runner.to_device(w)
+    g = runner.attn_bwd(w, dev, split=True)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(w)
+    for name in ("dq", "dk", "dv", "drab_pos", "drab_ts"):
+        check(name, host(g[name]), ref[name], "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_stored_ds_ignores_stale_workspace(d):
+    """The stored-dS path reads only the dS entries its own dK/dV pass wrote (or masks them):
+    a workspace filled with NaN beforehand changes nothing."""
+    w = hs.make_inputs([300, 64, 1, 129, 200], 2, d, dtype="bf16", seed=31 + d, rab=True,
+                       num_contexts=3, num_targets=9, max_seqlen=300, backward=True)
+    dev = runner.to_device(w)
+    plan = runner.plan_for(w, runner.args_for(w, dev))
+    need = hj.hstu_workspace_bytes(plan, hj.OP_BWD)
+    assert need > 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    say(f"bwd stored dS over a NaN-filled workspace d={d}")
+    g = runner.attn_bwd(w, dev, plan=plan, ws=ws)
+    g2 = runner.attn_bwd(w, dev, plan=plan, split=True)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(w)
+    for name in ("dq", "dk", "dv", "drab_pos", "drab_ts"):
+        assert torch.isfinite(g[name]).all(), name
+        check(name, host(g[name]), ref[name], "bf16")
+    # dK and dV come from the same kernel code either way
+    for name in ("dk", "dv"):
+        assert torch.equal(g[name], g2[name]), name
+
+
 def test_bwd_no_bias_and_determinism():
     w = hs.make_inputs([300, 64, 1], 2, 64, dtype="bf16", seed=4, rab=False, num_targets=7,
                        backward=True)
