@@ -193,7 +193,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) { dvt[db] = f32x16{}; dkt[db] = f32x16{}; }
 
-    const buffer_rsrc qrs = rows_rsrc(qg, n, ld, D), drs = rows_rsrc(dog, n, p.ld_out, D);
+    // query-tile copies from inline assembly (see the forward kernel): explicit waits only
+    const i32x4 qrs = rows_words(qg, n, ld, D), drs = rows_words(dog, n, p.ld_out, D);
     const TileDma<D, kThreads> qdma(tid, ld), ddma(tid, p.ld_out);
     const RowOperand<D> rowop(lane);
     const TrOperand<D> trop(lane);
@@ -211,12 +212,12 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     // starts the copy of a query tile's Q and dO rows into buffer buf and loads its timestamps
     auto load_tile = [&](int buf, int tile) {
         const int i0 = tile * kTile;
-        qdma.issue(qrs, sm.q[buf], (int)((int64_t)i0 * ld * 2));
-        ddma.issue(drs, sm.dout[buf], (int)((int64_t)i0 * p.ld_out * 2));
-        if (RT && tid < kTile) {
+        if (RT && tid < kTile) {  // first: see the forward kernel's load_tile
             const int i = i0 + tid;
             tqr = i < n ? p.ts[tok0 + i] : tbase;
         }
+        qdma.issue_asm(qrs, sm.q[buf], (int)((int64_t)i0 * ld * 2));
+        ddma.issue_asm(drs, sm.dout[buf], (int)((int64_t)i0 * p.ld_out * 2));
     };
     // the tile's small tables: query times and their range, position bias by (i - j)
     auto store_tile = [&](int buf, int tile) {
@@ -584,21 +585,23 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
     for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
     Run run_p_lo, run_p_hi, run_t_lo, run_t_mid, run_t_hi;  // bias-gradient running sums
 
-    const buffer_rsrc krs = rows_rsrc(kg, n, ld, D), vrs = rows_rsrc(vg, n, ld, D);
+    // key-tile copies from inline assembly (see the forward kernel): explicit waits only
+    const i32x4 krs = rows_words(kg, n, ld, D), vrs = rows_words(vg, n, ld, D);
     const TileDma<D, kThreads> dma(tid, ld);
     const RowOperand<D> rowop(lane);
     const TrOperand<D> trop(lane);
     int64_t tkr = 0;
-    // starts the copy of a key tile's K and V rows into buffer buf and loads its timestamps
+    // loads a key tile's timestamps (first: see the forward kernel's load_tile) and starts the
+    // copy of its K and V rows into buffer buf
     auto load_tile = [&](int buf, int tile) {
         const int j0 = tile * kTile;
         const int row_bytes = (int)((int64_t)j0 * ld * 2);
-        dma.issue(krs, sm.k[buf], row_bytes);
-        dma.issue(vrs, sm.v[buf], row_bytes);
         if (RT && tid < kTile) {
             const int jj = j0 + tid;
             tkr = jj < n ? p.ts[tok0 + jj] : tbase;
         }
+        dma.issue_asm(krs, sm.k[buf], row_bytes);
+        dma.issue_asm(vrs, sm.v[buf], row_bytes);
     };
     // the tile's small tables: key times and their range, position bias and bucket by (i - j)
     auto store_tile = [&](int buf, int tile) {

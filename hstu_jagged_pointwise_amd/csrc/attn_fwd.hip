@@ -134,22 +134,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const int tbeg = wu.t0, ntiles = wu.t1 - wu.t0;  // this item's part of the tile list
     auto tile_at = [&](int t) { return CACHED ? tbeg + t : kl.tile(tbeg + t); };
 
-    const buffer_rsrc krs = rows_rsrc(kg, nk, ld, D), vrs = rows_rsrc(vg, nk, ld, D);
+    // The tile copies are issued from inline assembly (TileDma::issue_asm): with the builtin the
+    // compiler would wait for the next tile's copy before every LDS read of the current tile.
+    // Each iteration waits for its copy explicitly (wait_tile_dma, then the barrier).
+    const i32x4 krs = rows_words(kg, nk, ld, D), vrs = rows_words(vg, nk, ld, D);
     const TileDma<D, kThreads> dma(tid, ld);
     const RowOperand<D> kop(lane);
     const TrOperand<D> vop(lane);
     int64_t tkr = 0;
 
-    // starts the copy of a tile's K and V rows into buffer buf and loads its timestamps
+    // loads a tile's timestamps and starts the copy of its K and V rows into buffer buf (the
+    // timestamp load goes first: the compiler's wait for its register then finds no copy in
+    // flight)
     auto load_tile = [&](int buf, int tile) {
         const int j0 = tile * kBN;
         const int row_bytes = (int)((int64_t)j0 * ld * 2);
-        dma.issue(krs, sm.k[buf], row_bytes);
-        dma.issue(vrs, sm.v[buf], row_bytes);
         if (RT && tid < kBN) {
             const int j = j0 + tid;
             tkr = j < nk ? tsk[j] : tbase;
         }
+        dma.issue_asm(krs, sm.k[buf], row_bytes);
+        dma.issue_asm(vrs, sm.v[buf], row_bytes);
     };
 
     // the tile's small tables: key times and their range, position bias by (i - j)

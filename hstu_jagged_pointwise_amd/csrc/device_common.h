@@ -496,6 +496,11 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, int64_t bytes) {
     return r;
 }
 
+// rsrc_words over rows [0, n) of a bf16 slice with row stride ld (elements), as rows_rsrc.
+__device__ __forceinline__ i32x4 rows_words(const bf16* base, int n, int64_t ld, int width) {
+    return rsrc_words(base, n > 0 ? ((int64_t)(n - 1) * ld + width) * 2 : 0);
+}
+
 // LDS byte address of a pointer into __shared__ memory (the low half of its generic address).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)reinterpret_cast<uintptr_t>(p));
@@ -585,7 +590,14 @@ __device__ __forceinline__ void store_bf16x4(bf16x4 v, buffer_rsrc rs, int voff,
 #endif
 }
 
-__device__ __forceinline__ void wait_tile_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits for all of this wavefront's vector memory operations.  Written with the builtin (not
+// inline assembly) so that the compiler's own wait tracking sees it: otherwise it still counts
+// loads issued before this point as outstanding and waits for them again inside the next loop,
+// where that wait would also cover copies into LDS issued since.
+__device__ __forceinline__ void wait_tile_dma() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15
+    asm volatile("" ::: "memory");
+}
 
 // Waits until at most N of this wavefront's vector memory loads are outstanding (they complete in
 // issue order).

@@ -27,7 +27,7 @@ struct hstu_plan {
     int32_t fwd_rows = 0;      // query rows per forward / dQ work unit
     int32_t bwd_keys = 0;      // keys per dK/dV work unit
     int64_t pairs = 0;
-    int64_t fwd_tiles = 0;
+    int64_t fwd_tiles = -1;    // computed on first hstu_plan_info (-1: not yet)
     std::vector<SeqInfo> seqs;
     std::vector<WorkUnit> fwd, bwd;
     std::vector<FwdItem> items;  // bf16 forward launch (fwd, the longest split by key tiles)
@@ -366,14 +366,6 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
         for (int r0 = 0; r0 < s.n; r0 += plan->fwd_rows) {
             int rhi = std::min(r0 + plan->fwd_rows, s.n);
             hstu::KeyTiles kt = hstu::key_tiles_for_rows(r0, rhi, s.nc, s.nh);
-            int64_t wave_tiles = 0;
-            for (int t = 0; t < kt.count(); ++t) {
-                int j0 = kt.tile(t) * hstu::kKeyTile;
-                for (int w0 = r0; w0 < rhi; w0 += hstu::kWaveRows)
-                    wave_tiles += hstu::classify_row_tile(w0, std::min(w0 + hstu::kWaveRows, rhi),
-                                                          j0, s.n, s.nc, s.nh) != hstu::kEmpty;
-            }
-            plan->fwd_tiles += wave_tiles * H;
             for (int h = 0; h < H; ++h) plan->fwd.push_back(WorkUnit{b, h, r0, kt.count()});
         }
         // dK/dV: key blocks
@@ -396,12 +388,30 @@ void hstu_plan_destroy(hstu_plan_t* plan) {
     delete plan;
 }
 
+// (32-row, 64-key) tiles the forward computes: every wavefront's non-empty tiles of every row
+// block, all heads.  Only reported, so counted on request rather than while planning.
+int64_t count_fwd_tiles(const hstu_plan_t* plan) {
+    int64_t total = 0;
+    for (const SeqInfo& s : plan->seqs)
+        for (int r0 = 0; r0 < s.n; r0 += plan->fwd_rows) {
+            const int rhi = std::min(r0 + plan->fwd_rows, s.n);
+            const hstu::KeyTiles kt = hstu::key_tiles_for_rows(r0, rhi, s.nc, s.nh);
+            for (int t = 0; t < kt.count(); ++t) {
+                const int j0 = kt.tile(t) * hstu::kKeyTile;
+                for (int w0 = r0; w0 < rhi; w0 += hstu::kWaveRows)
+                    total += hstu::classify_row_tile(w0, std::min(w0 + hstu::kWaveRows, rhi), j0,
+                                                     s.n, s.nc, s.nh) != hstu::kEmpty;
+            }
+        }
+    return total * plan->shape.num_heads;
+}
+
 hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info) {
     if (!plan || !info) return HSTU_ERR_NULL_ARG;
     info->visible_pairs = plan->pairs;
     info->fwd_units = (int64_t)plan->fwd.size();
     info->bwd_units = (int64_t)plan->bwd.size();
-    info->fwd_tiles = plan->fwd_tiles;
+    info->fwd_tiles = plan->fwd_tiles >= 0 ? plan->fwd_tiles : count_fwd_tiles(plan);
     info->fwd_row_block = plan->fwd_rows;
     info->bwd_key_block = plan->bwd_keys;
     info->fwd_items = plan->shape.dtype == HSTU_BF16 ? (int64_t)plan->items.size()
@@ -838,6 +848,7 @@ hstu_status_t hstu_plan_create_cached(const hstu_attn_args_t* args, const int64_
     plan->cached = true;
     plan->fwd_rows = 4 * hstu::kWaveRows;
     plan->bwd_keys = 0;
+    plan->fwd_tiles = 0;  // counted here: every key tile of the cache is visible
     const int H = args->num_heads;
     plan->seqs.resize(B);
     plan->cache.resize(B);
