@@ -42,8 +42,7 @@ KERNEL_SOURCES = {
     "bwd_dq": "hstu_jagged_pointwise_amd/csrc/attn_bwd.hip",
 }
 # Algorithmic MFMA work per visible pair per head, in units of d: forward S and P.V; the dK/dV
-# pass S, dP, dV, dK; the dQ pass counts only dQ (its recomputed S and dP are counted once, in
-# the dK/dV pass).
+# pass S, dP, dV, dK (it also stores dS); the dQ pass dS.K from the stored dS.
 FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
 
 
@@ -72,7 +71,7 @@ def measured_traffic(kernel):
 
 
 KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128", "bwd_dkdv": "bwd_dkdv_kernel<128",
-                "bwd_dq": "bwd_dq_kernel<128"}
+                "bwd_dq": "bwd_dq_stored_kernel<128"}
 
 
 def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRAFFIC_FILE):

@@ -294,6 +294,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
             else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
             if (kind == kPartial) mask_queries(s, dp, g, iq0, lo, hi);
+            bf16x8 pb[2], db8[2];
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
                 float tp[8], td[8];
@@ -302,17 +303,27 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                     tp[x] = s[8 * sl + x];
                     td[x] = dp[8 * sl + x];
                 }
-                const bf16x8 pb = pack8(tp), db8 = pack8(td);
+                pb[sl] = pack8(tp);
+                db8[sl] = pack8(td);
+            }
+            if constexpr (DS) {
+                // stored before the dV / dK products, so that the writes complete while those run
+                // (the tile-end wait counts stores too); entries 8sl .. 8sl + 3 are queries
+                // 16sl + 4g + c, then + 8
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    store_bf16x4(__builtin_shufflevector(db8[sl], db8[sl], 0, 1, 2, 3), dsrs, ds_voff + 32 * sl, i0 * 2);
+                    store_bf16x4(__builtin_shufflevector(db8[sl], db8[sl], 4, 5, 6, 7), dsrs, ds_voff + 32 * sl + 16, i0 * 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qh + sl, db), pb, dvt[db]);
-                    dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qh + sl, db), db8, dkt[db]);
+                    dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qh + sl, db), pb[sl], dvt[db]);
+                    dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qh + sl, db), db8[sl], dkt[db]);
                 }
-                if constexpr (DS) {  // entries 8sl .. 8sl + 3 are queries 16sl + 4g + c, then + 8
-                    store_bf16x4(__builtin_shufflevector(db8, db8, 0, 1, 2, 3), dsrs, ds_voff + 32 * sl, i0 * 2);
-                    store_bf16x4(__builtin_shufflevector(db8, db8, 4, 5, 6, 7), dsrs, ds_voff + 32 * sl + 16, i0 * 2);
-                }
-            }
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tfirst + t + 1);
         wait_tile_dma();
