@@ -173,13 +173,16 @@ def bench_headline(args, torch, hj, runner, w):
     p0 = runner.plan_for(w, base_args)
     ws = torch.empty(max(hj.hstu_workspace_bytes(p0, hj.OP_BWD), 16), dtype=torch.uint8,
                      device=out.device)
+    info = hj.hstu_plan_info(p0)
     p0.close()
 
-    def step(record):
+    def build():
         t0 = time.perf_counter()
         plan = runner.plan_for(w, base_args)
         plan_host_s.append(time.perf_counter() - t0)
+        return plan
 
+    def launch(plan, record):
         def fwd():
             hj.hstu_attn_fwd(plan, base_args, dev["q"], dev["k"], dev["v"], out)
 
@@ -197,26 +200,27 @@ def bench_headline(args, torch, hj, runner, w):
             timer.record("bwd_dq", dqp)
         else:
             fwd(); dkdv(); dqp()
-        return plan
 
-    plan = None
     for _ in range(args.warmup):
-        if plan is not None:
-            torch.cuda.current_stream().synchronize()
-            plan.close()
-        plan = step(False)
-    torch.cuda.synchronize()
-    info = hj.hstu_plan_info(plan)
-    plan_host_s.clear()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        # the previous step's plan is freed once the stream has finished with it
+        plan = build()
+        launch(plan, False)
         torch.cuda.current_stream().synchronize()
         plan.close()
-        plan = step(True)
+    torch.cuda.synchronize()
+    plan_host_s.clear()
+    t0 = time.perf_counter()
+    # Every step builds its own plan on the host.  A step's plan is built while the previous
+    # step's kernels run (as a data loader prepares the next batch); its upload is a synchronous
+    # copy on the default stream, so it lands after those kernels and before the step's own.
+    plan = build()
+    for k in range(args.steps):
+        launch(plan, True)
+        nxt = build() if k + 1 < args.steps else None
+        torch.cuda.current_stream().synchronize()  # the plan is freed once its kernels are done
+        plan.close()
+        plan = nxt
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    plan.close()
     assert torch.isfinite(out.float()).all() and torch.isfinite(dq.float()).all()
 
     pairs = info["visible_pairs"]
