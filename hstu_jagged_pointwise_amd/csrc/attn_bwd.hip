@@ -73,6 +73,10 @@ struct SmemA {
     int64_t tq64[2][kTile];
     int64_t tqmin[2][2], tqmax[2][2];  // time range of the real queries of each 32-query half
     int fits[2];
+    // bias-table gradient sums of the unit (stored-dS pass only), by bucket; time sums by
+    // (bucket, lane % 32) so that per-lane additions rarely share an address
+    float hbp[kNumBuckets];
+    float hbt[kNumBuckets][32];
     alignas(16) bf16 q[2][kTile * D];    // swizzled tiles (tile_off)
     bf16 dout[2][kTile * D];
     bf16 kb[kBlk * D];                   // the unit's keys and values, swizzled like the tiles
@@ -134,6 +138,116 @@ __device__ __forceinline__ void mask_queries(f32x16& s, f32x16& dp, int g, int i
     }
 }
 
+// Bias-table gradient sums of one (wavefront, tile) of the dK/dV pass: d8 holds dS * N (as
+// stored, bf16; element e = 8 sl + x in d8[sl][x]) of the queries i = iq0 + (8r + 4g + c) for
+// this lane's key j (zero where not visible).  The tile's
+// pairs fall in the buckets the forward bias decisions found (sp: position, st / tm: time):
+//   one bucket: the wavefront's sum of dS goes to it;
+//   two or three adjacent buckets: per lane, the sums over pairs at or past each threshold are
+//     kept too (one comparison per pair and threshold), and the splits go to the buckets;
+//   more: each pair's bucket is computed and per-lane runs along the lane's queries (whose
+//     buckets change rarely) are added to the histogram when the bucket changes.
+// Wavefront sums go through a DPP reduction and one single-lane LDS atomic per bucket.
+template <int D, bool GP, bool GT, int PG, int TM>
+__device__ __forceinline__ void grads_a_t(const bf16x8 (&d8)[2], SmemA<D>& sm, int buf, int q0,
+                                          int iq0, int j, int g, int lane, const BiasSpan& sp,
+                                          bool pneg, const BiasSpan& st, uint32_t thr,
+                                          uint32_t thr2, uint32_t tj, int64_t tj64) {
+    float sum = 0.0f, thp = 0.0f, tht = 0.0f, tht2 = 0.0f;
+    // position: i - j = base + 8r + c, of one sign over the tile when PG < 2 (pneg: every
+    // i - j <= 0); lanes and queries outside the tile's visible pairs carry dS = 0
+    const int base = iq0 + 4 * g - j;
+    int pcur = -1, tcur = -1;
+    float pacc = 0.0f, tacc = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int ii = q0 + 8 * r + 4 * g;
+        u32x4 tq4;
+        if (TM == 1 || TM == 2 || TM == 4) tq4 = *reinterpret_cast<const u32x4*>(&sm.tq[buf][ii]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int e = 4 * r + c;
+            const float ds = (float)d8[e >> 3][e & 7];
+            const int d = base + 8 * r + c;  // i - j
+            sum += ds;
+            if (PG == 1) thp += (uint32_t)(pneg ? -d : d) >= sp.thr ? ds : 0.0f;
+            if (PG == 2) {
+                const int b = bucket_of((uint32_t)(d < 0 ? -d : d));
+                if (b != pcur) {
+                    if (pcur >= 0) atomicAdd(&sm.hbp[pcur], pacc);
+                    pcur = b;
+                    pacc = 0.0f;
+                }
+                pacc += ds;
+            }
+            if (TM == 1 || TM == 4) {
+                const uint32_t dt = absdiff_u32(tj, tq4[c]);
+                tht += dt >= thr ? ds : 0.0f;
+                if (TM == 4) tht2 += dt >= thr2 ? ds : 0.0f;
+            }
+            if (TM == 2 || TM == 3) {
+                const int b = TM == 2 ? bucket_of(absdiff_u32(tj, tq4[c]))
+                                      : bucket_of(absdiff_sat(tj64, sm.tq64[buf][ii + c]));
+                if (b != tcur) {
+                    if (tcur >= 0) atomicAdd(&sm.hbt[tcur][lane & 31], tacc);
+                    tcur = b;
+                    tacc = 0.0f;
+                }
+                tacc += ds;
+            }
+        }
+    }
+    if (PG == 2 && pcur >= 0) atomicAdd(&sm.hbp[pcur], pacc);
+    if ((TM == 2 || TM == 3) && tcur >= 0) atomicAdd(&sm.hbt[tcur][lane & 31], tacc);
+    constexpr bool pfew = GP && PG < 2, tfew = GT && (TM == 0 || TM == 1 || TM == 4);
+    if constexpr (pfew || tfew) {
+        const float tot = wave_sum_dpp(sum);
+        const float tp = PG == 1 ? wave_sum_dpp(thp) : 0.0f;
+        const float t1 = TM == 1 || TM == 4 ? wave_sum_dpp(tht) : 0.0f;
+        const float t2 = TM == 4 ? wave_sum_dpp(tht2) : 0.0f;
+        if (lane == 0) {
+            if (pfew) {
+                atomicAdd(&sm.hbp[sp.b_lo], tot - tp);
+                if (PG == 1) atomicAdd(&sm.hbp[sp.b_hi], tp);
+            }
+            if (tfew) {
+                atomicAdd(&sm.hbt[st.b_lo][0], tot - t1);
+                if (TM == 1) atomicAdd(&sm.hbt[st.b_hi][0], t1);
+                if (TM == 4) {
+                    atomicAdd(&sm.hbt[st.b_lo + 1][0], t1 - t2);
+                    atomicAdd(&sm.hbt[st.b_hi][0], t2);
+                }
+            }
+        }
+    }
+}
+
+template <int D, bool GP, bool GT, int PG>
+__device__ __forceinline__ void grads_a_pg(int tm, const bf16x8 (&d8)[2], SmemA<D>& sm, int buf,
+                                           int q0, int iq0, int j, int g, int lane,
+                                           const BiasSpan& sp, bool pneg, const BiasSpan& st,
+                                           uint32_t thr, uint32_t thr2, uint32_t tj, int64_t tj64) {
+    switch (GT ? tm : 0) {
+        case 0: grads_a_t<D, GP, GT, PG, 0>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
+        case 1: grads_a_t<D, GP, GT, PG, 1>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
+        case 4: grads_a_t<D, GP, GT, PG, 4>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
+        case 2: grads_a_t<D, GP, GT, PG, 2>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
+        default: grads_a_t<D, GP, GT, PG, 3>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
+    }
+}
+
+template <int D, bool GP, bool GT>
+__device__ __forceinline__ void grads_a(const bf16x8 (&d8)[2], SmemA<D>& sm, int buf, int q0,
+                                        int iq0, int j, int g, int lane, const BiasSpan& sp,
+                                        bool pneg, const BiasSpan& st, int tm, uint32_t thr,
+                                        uint32_t thr2, uint32_t tj, int64_t tj64) {
+    const int pg = !GP ? -1 : sp.kind == 0 ? 0 : sp.kind == 1 ? 1 : 2;
+    if (pg == 0) grads_a_pg<D, GP, GT, 0>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
+    else if (pg == 1) grads_a_pg<D, GP, GT, 1>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
+    else if (pg == 2) grads_a_pg<D, GP, GT, 2>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
+    else grads_a_pg<D, GP, GT, 3>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
+}
+
 template <int D, bool RP, bool RT, bool DS>
 __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams p) {
     constexpr int kThreads = kThreadsA;  // the helpers below stride over the whole workgroup
@@ -159,9 +273,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
         for (int e = tid; e < kNumBuckets; e += kThreads)
             sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
     }
-    const int64_t tbase = RT ? p.ts[tok0] : 0;
-
-    const int khi = imin(k0 + kBlk, n);
+        if constexpr (DS && (RP || RT)) {
+        for (int e = tid; e < kNumBuckets; e += kThreads) sm.hbp[e] = 0.0f;
+        for (int e = tid; e < kNumBuckets * 32; e += kThreads) (&sm.hbt[0][0])[e] = 0.0f;
+    }
+    const int64_t tbase = RT ? p.ts[tok0] : 0;  const int khi = imin(k0 + kBlk, n);
     int qlo, qhi;
     rows_for_keys(k0, khi, n, nc, nh, &qlo, &qhi);
     const int tfirst = qlo / kTile, ntiles = cdiv(qhi, kTile) - tfirst;
@@ -279,8 +395,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             float bpos = 0.0f;
             int pm = 0;
             const int ihi = imin(iq0 + kWaveRows, n) - 1;
+            BiasSpan sp{0, 0, 0, 0, 0}, st{0, 0, 0, 0, 0};
             if (RP) {
-                const BiasSpan sp = bias_span((int64_t)iq0 - (wk1 - 1), (int64_t)ihi - wk0);
+                sp = bias_span((int64_t)iq0 - (wk1 - 1), (int64_t)ihi - wk0);
                 if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
@@ -288,7 +405,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             int tm = 0;
             if (RT) {
                 // TimePickAbs compares |t_key - t_query| itself: no sign or overflow condition
-                const BiasSpan st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
+                st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
                 tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb, true, 0u);
             } else tb.set_const(bpos);
             if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
@@ -324,6 +441,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                     dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qh + sl, db), pb[sl], dvt[db]);
                     dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qh + sl, db), db8[sl], dkt[db]);
                 }
+            // from the stored values, after the products are issued (their vector work overlaps
+            // the matrix instructions, and S and dP in fp32 are no longer held)
+            if constexpr (DS && (RP || RT))
+                grads_a<D, RP, RT>(db8, sm, buf, q0, iq0, j, g, lane, sp, ihi - wk0 <= 0, st, tm,
+                                   tb.thr, tb.thr2, tj, tj64);
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tfirst + t + 1);
         wait_tile_dma();
@@ -368,6 +490,18 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 *reinterpret_cast<bf16x4*>(dvg + 32 * db + 8 * r + 4 * g) = wv;
                 *reinterpret_cast<bf16x4*>(dkg + 32 * db + 8 * r + 4 * g) = wk;
             }
+    }
+    if constexpr (DS && (RP || RT)) {  // the unit's bias-table gradient sums: one global atomic
+        __syncthreads();                // per non-zero bucket
+        for (int b = tid; b < kNumBuckets; b += kThreads) {
+            if (RP && p.gpos && sm.hbp[b] != 0.0f) atomicAdd(&p.gpos[h * kNumBuckets + b], sm.hbp[b] * p.inv_n);
+            if (RT && p.gts) {
+                float v = 0.0f;
+#pragma unroll 8
+                for (int l = 0; l < 32; ++l) v += sm.hbt[b][(l + b) & 31];
+                if (v != 0.0f) atomicAdd(&p.gts[h * kNumBuckets + b], v * p.inv_n);
+            }
+        }
     }
 }
 
@@ -1238,12 +1372,9 @@ template <int D, bool RP, bool RT>
 hipError_t launch_dq_t(const AttnParams& p, hipStream_t s) {
     const bool gp = RP && p.drab_pos, gt = RT && p.drab_ts;
     const dim3 grid(p.num_units), block(kThreadsA);
-    if (p.ds) {  // stored dS: the bias tables matter only for their gradients
+    if (p.ds) {  // stored dS: the dK/dV pass has summed the bias-table gradients
         if constexpr (D >= 64) {
-            if (gp && gt) hipLaunchKernelGGL((bwd_dq_stored_kernel<D, true, true>), grid, block, 0, s, p);
-            else if (gp) hipLaunchKernelGGL((bwd_dq_stored_kernel<D, true, false>), grid, block, 0, s, p);
-            else if (gt) hipLaunchKernelGGL((bwd_dq_stored_kernel<D, false, true>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((bwd_dq_stored_kernel<D, false, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((bwd_dq_stored_kernel<D, false, false>), grid, block, 0, s, p);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;

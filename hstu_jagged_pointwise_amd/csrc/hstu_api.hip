@@ -199,6 +199,12 @@ size_t part_bytes(const hstu_plan_t* plan) {
 // Stored dS of the bf16 backward (0 when the plan does not use it).
 size_t ds_bytes(const hstu_plan_t* plan) { return align_up(size_t(plan->ds_elems) * 2, 256); }
 
+// The bias-table gradients the stored-dS dK/dV pass sums for the dQ pass to hand out: two
+// [H][128] fp32 tables after the stored dS.
+size_t grad_bytes(const hstu_plan_t* plan) {
+    return plan->ds_elems > 0 ? align_up(size_t(2) * plan->shape.num_heads * hstu::kNumBuckets * 4, 256) : 0;
+}
+
 // The stored-dS layout: a dense npad x npad bf16 block per (sequence, head), npad = n rounded up
 // to 128, addressed with 32-bit byte offsets within a block.  Head dims 64 and 128 only (the dQ
 // kernel keeps two 16 KB dS tiles where the query rows of the recomputing kernel go).
@@ -455,7 +461,7 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
     switch (op) {
         case 0: return part_bytes(plan);
         case 1: return align_up(thd * elem_size(a.dtype), 256) + part_bytes(plan);
-        case 2: return ds_bytes(plan);
+        case 2: return ds_bytes(plan) + grad_bytes(plan);
         case 3: {
             (void)d_model;  // Z and A depend on H*d only
             return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256) + part_bytes(plan);
@@ -569,6 +575,13 @@ hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t
     p.dk = dk;
     p.dv = dv;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.ds) {  // this pass sums the bias-table gradients into the workspace
+        float* grads = reinterpret_cast<float*>(static_cast<char*>(ws) + ds_bytes(plan));
+        const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
+        p.gpos = args->rab_pos ? grads : nullptr;
+        p.gts = args->rab_ts ? grads + nb : nullptr;
+        if (hstu::launch_zero_f32(grads, 2 * nb, s) != hipSuccess) return HSTU_ERR_HIP;
+    }
     return hip_status(args->dtype == HSTU_BF16 ? hstu::launch_attn_bwd_dkdv_bf16(p, s)
                                                : hstu::launch_attn_bwd_dkdv_f32(p, s));
 }
@@ -593,8 +606,17 @@ hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
     hipError_t e = hipSuccess;
-    if (p.drab_pos) e = hstu::launch_zero_f32(p.drab_pos, nb, s);
-    if (e == hipSuccess && p.drab_ts) e = hstu::launch_zero_f32(p.drab_ts, nb, s);
+    if (p.ds) {  // the dK/dV pass summed the bias-table gradients into the workspace
+        const float* grads =
+            reinterpret_cast<const float*>(static_cast<const char*>(ws) + ds_bytes(plan));
+        if (p.drab_pos)
+            e = hipMemcpyAsync(p.drab_pos, grads, nb * 4, hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && p.drab_ts)
+            e = hipMemcpyAsync(p.drab_ts, grads + nb, nb * 4, hipMemcpyDeviceToDevice, s);
+    } else {
+        if (p.drab_pos) e = hstu::launch_zero_f32(p.drab_pos, nb, s);
+        if (e == hipSuccess && p.drab_ts) e = hstu::launch_zero_f32(p.drab_ts, nb, s);
+    }
     if (e != hipSuccess) return HSTU_ERR_HIP;
     if (args->total_tokens == 0) return HSTU_OK;
     return hip_status(args->dtype == HSTU_BF16 ? hstu::launch_attn_bwd_dq_bf16(p, s)
@@ -788,9 +810,11 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         p.dk = dh + size_t(3 * hd) * 2;
         p.units = plan->d_bwd;
         p.num_units = (int32_t)plan->bwd.size();
-        if (plan->ds_elems > 0) {
+        if (plan->ds_elems > 0) {  // the dK/dV pass then sums the bias-table gradients
             p.ds = tail;
             p.ds_off = plan->d_ds_off;
+            p.gpos = drab_pos;
+            p.gts = drab_ts;
         }
         e = hstu::launch_attn_bwd_dkdv_bf16(p, s);
     }

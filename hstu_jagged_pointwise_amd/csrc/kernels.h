@@ -52,6 +52,10 @@ struct AttnParams {
     // up to 128) at ds + ds_off[b] + h npad^2, row = key, column = query.
     void* ds;
     const int64_t* ds_off;
+    // With ds, the dK/dV pass also sums the bias-table gradients ([H][128] fp32, already zeroed,
+    // either may be NULL) and the dQ pass does not.
+    float* gpos;
+    float* gts;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s);

@@ -135,7 +135,8 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
  * include 512 * head_dim bytes per partial slot of split row blocks (0 when the plan splits
  * none).  Op 2, and op 4 when larger than the partial slots, is the stored dS of the bf16
  * backward with head_dim 64 or 128: 2 * H * npad^2 bytes per sequence, npad = its length rounded
- * up to 128 (0 for fp32, head_dim 32, or a sequence longer than 32640). */
+ * up to 128 (0 for fp32, head_dim 32, or a sequence longer than 32640); op 2 adds 2 * H * 128
+ * fp32 (rounded up to 256 bytes) for the bias-table gradients that pass sums. */
 size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
 
 /* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.
@@ -150,8 +151,9 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
  * the pointers and the matching tables are non-NULL, drab_pos / drab_ts ([H][128] fp32,
  * overwritten).  Bias gradients are summed with fp32 atomics, so their low bits depend on
  * scheduling.  ws must hold hstu_workspace_bytes(plan, 2, 0) bytes (it may be NULL when that is
- * 0): the dK/dV pass stores dS there (bf16, dS * max_seqlen) for every pair it visits, and the dQ
- * pass reads it back instead of recomputing S and dP.  Same as hstu_attn_bwd_dkdv followed by
+ * 0): the dK/dV pass stores dS there (bf16, dS * max_seqlen) for every pair it visits and sums
+ * the bias-table gradients from it (fp32, before rounding), and the dQ pass reads dS back instead
+ * of recomputing S and dP and copies the gradients out.  Same as hstu_attn_bwd_dkdv followed by
  * hstu_attn_bwd_dq with the same ws. */
 hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                             const void* q, const void* k, const void* v, const void* dout,
@@ -160,8 +162,9 @@ hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
 
 /* The two halves of hstu_attn_bwd.  _dkdv writes dk and dv; _dq writes dq and the bias gradients
  * as hstu_attn_bwd does.  With ws (at least hstu_workspace_bytes(plan, 2, 0) bytes, else
- * HSTU_ERR_WORKSPACE_TOO_SMALL) _dkdv stores dS into it and _dq reads it: call _dq after _dkdv
- * on the same stream (or after it has finished), with the same plan, inputs and ws.  With ws
+ * HSTU_ERR_WORKSPACE_TOO_SMALL) _dkdv stores dS and the bias-table gradients into it and _dq
+ * reads them: call _dq after _dkdv on the same stream (or after it has finished), with the same
+ * plan, args, inputs and ws.  With ws
  * NULL (or a plan whose op 2 needs 0 bytes) nothing is stored and _dq recomputes S and dP; the
  * two calls then only read the inputs and may run on different streams at once. */
 hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t* args,

@@ -157,9 +157,11 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
                               *([P(16)] * 6), 1 << 30, None) == 2
     assert lib.hstu_layer_bwd(P(plan.handle), ctypes.byref(a), 512, *([P(16)] * 4), 1e-5,
                               *([P(16)] * 6), 1 << 30, None) == 8   # host-only plan
-    # attention backward: the stored dS, one 128 x 128 bf16 block per (sequence, head) here
+    # attention backward: the stored dS, one 128 x 128 bf16 block per (sequence, head) here, then
+    # the two [H][128] fp32 bias-gradient tables the dK/dV pass sums (rounded up to 256 bytes)
     ds = 3 * 2 * 128 * 128 * 2
-    assert hj.hstu_workspace_bytes(plan, hj.OP_BWD) == ds
+    grads = 2 * 2 * 128 * 4
+    assert hj.hstu_workspace_bytes(plan, hj.OP_BWD) == ds + grads
     # layer backward: Z, H and dH (T x 4Hd bf16), A, G, dA (T x Hd bf16), dG (T x Hd fp32),
     # then the stored dS (no partial slots here)
     hd = 2 * 64
@@ -174,7 +176,7 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
     off = np.array([0, 128, 257, 257])
     p3 = hj.hstu_plan_create(args(total_tokens=257, max_seqlen=200, head_dim=128), off, None,
                              hj.HSTU_PLAN_HOST_ONLY)
-    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == 2 * (128 * 128 + 256 * 256) * 2
+    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == 2 * (128 * 128 + 256 * 256) * 2 + 2 * 2 * 128 * 4
     p3.close()
 
 
