@@ -77,6 +77,7 @@ struct SmemA {
     // (bucket, lane % 32) so that per-lane additions rarely share an address
     float hbp[kNumBuckets];
     float hbt[kNumBuckets][32];
+    int64_t kt64[kBlk];                  // the unit's key times (read by the 64-bit time mode)
     alignas(16) bf16 q[2][kTile * D];    // swizzled tiles (tile_off)
     bf16 dout[2][kTile * D];
     bf16 kb[kBlk * D];                   // the unit's keys and values, swizzled like the tiles
@@ -92,7 +93,7 @@ struct SmemA {
 template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>& sm, int buf,
                                            int q0, int u0, int g, float alpha2, const TimeSel tb,
-                                           uint32_t tj, int64_t tj64) {
+                                           uint32_t tj, int kl) {
     const TimePickAbs pick(tb);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -105,7 +106,7 @@ __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>
             float b = pick.get<TM>(tj, tq4[c]);
             if (PM == 1) b += sm.rp[buf][u0 + 8 * r + c];
             if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
-            if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(tj64, sm.tq64[buf][ii + c]))];
+            if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(sm.kt64[kl], sm.tq64[buf][ii + c]))];
             const Grad gr = silu_grad(fmaf(alpha2, s[e], b), dp[e]);
             s[e] = gr.p;
             dp[e] = gr.ds;
@@ -116,13 +117,13 @@ __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>
 template <int D, int PM>
 __device__ __forceinline__ void epilogue_a_tm(int tm, f32x16& s, f32x16& dp, const SmemA<D>& sm,
                                               int buf, int q0, int u0, int g, float alpha2,
-                                              const TimeSel tb, uint32_t tj, int64_t tj64) {
+                                              const TimeSel tb, uint32_t tj, int kl) {
     switch (tm) {
-        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
-        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
-        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
-        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
-        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64); break;
+        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
     }
 }
 
@@ -152,7 +153,7 @@ template <int D, bool GP, bool GT, int PG, int TM>
 __device__ __forceinline__ void grads_a_t(const bf16x8 (&d8)[2], SmemA<D>& sm, int buf, int q0,
                                           int iq0, int j, int g, int lane, const BiasSpan& sp,
                                           bool pneg, const BiasSpan& st, uint32_t thr,
-                                          uint32_t thr2, uint32_t tj, int64_t tj64) {
+                                          uint32_t thr2, uint32_t tj, int kl) {
     float sum = 0.0f, thp = 0.0f, tht = 0.0f, tht2 = 0.0f;
     // position: i - j = base + 8r + c, of one sign over the tile when PG < 2 (pneg: every
     // i - j <= 0); lanes and queries outside the tile's visible pairs carry dS = 0
@@ -187,7 +188,7 @@ __device__ __forceinline__ void grads_a_t(const bf16x8 (&d8)[2], SmemA<D>& sm, i
             }
             if (TM == 2 || TM == 3) {
                 const int b = TM == 2 ? bucket_of(absdiff_u32(tj, tq4[c]))
-                                      : bucket_of(absdiff_sat(tj64, sm.tq64[buf][ii + c]));
+                                      : bucket_of(absdiff_sat(sm.kt64[kl], sm.tq64[buf][ii + c]));
                 if (b != tcur) {
                     if (tcur >= 0) atomicAdd(&sm.hbt[tcur][lane & 31], tacc);
                     tcur = b;
@@ -226,13 +227,13 @@ template <int D, bool GP, bool GT, int PG>
 __device__ __forceinline__ void grads_a_pg(int tm, const bf16x8 (&d8)[2], SmemA<D>& sm, int buf,
                                            int q0, int iq0, int j, int g, int lane,
                                            const BiasSpan& sp, bool pneg, const BiasSpan& st,
-                                           uint32_t thr, uint32_t thr2, uint32_t tj, int64_t tj64) {
+                                           uint32_t thr, uint32_t thr2, uint32_t tj, int kl) {
     switch (GT ? tm : 0) {
-        case 0: grads_a_t<D, GP, GT, PG, 0>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
-        case 1: grads_a_t<D, GP, GT, PG, 1>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
-        case 4: grads_a_t<D, GP, GT, PG, 4>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
-        case 2: grads_a_t<D, GP, GT, PG, 2>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
-        default: grads_a_t<D, GP, GT, PG, 3>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64); break;
+        case 0: grads_a_t<D, GP, GT, PG, 0>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl); break;
+        case 1: grads_a_t<D, GP, GT, PG, 1>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl); break;
+        case 4: grads_a_t<D, GP, GT, PG, 4>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl); break;
+        case 2: grads_a_t<D, GP, GT, PG, 2>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl); break;
+        default: grads_a_t<D, GP, GT, PG, 3>(d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl); break;
     }
 }
 
@@ -240,12 +241,12 @@ template <int D, bool GP, bool GT>
 __device__ __forceinline__ void grads_a(const bf16x8 (&d8)[2], SmemA<D>& sm, int buf, int q0,
                                         int iq0, int j, int g, int lane, const BiasSpan& sp,
                                         bool pneg, const BiasSpan& st, int tm, uint32_t thr,
-                                        uint32_t thr2, uint32_t tj, int64_t tj64) {
+                                        uint32_t thr2, uint32_t tj, int kl) {
     const int pg = !GP ? -1 : sp.kind == 0 ? 0 : sp.kind == 1 ? 1 : 2;
-    if (pg == 0) grads_a_pg<D, GP, GT, 0>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
-    else if (pg == 1) grads_a_pg<D, GP, GT, 1>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
-    else if (pg == 2) grads_a_pg<D, GP, GT, 2>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
-    else grads_a_pg<D, GP, GT, 3>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, tj64);
+    if (pg == 0) grads_a_pg<D, GP, GT, 0>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl);
+    else if (pg == 1) grads_a_pg<D, GP, GT, 1>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl);
+    else if (pg == 2) grads_a_pg<D, GP, GT, 2>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl);
+    else grads_a_pg<D, GP, GT, 3>(tm, d8, sm, buf, q0, iq0, j, g, lane, sp, pneg, st, thr, thr2, tj, kl);
 }
 
 template <int D, bool RP, bool RT, bool DS>
@@ -301,8 +302,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
         tj64 = key_ok ? p.ts[tok0 + j] : tbase;
         wave_kfit = __all(rel_time_fits(tj64, tbase));
         tj = rel_time_u32(tj64, tbase);
-        tjmin = wave_min64(key_ok ? tj64 : INT64_MAX);
-        tjmax = wave_max64(key_ok ? tj64 : INT64_MIN);
+        tjmin = uniform64(wave_min64(key_ok ? tj64 : INT64_MAX));
+        tjmax = uniform64(wave_max64(key_ok ? tj64 : INT64_MIN));
+        if (qh == 0) sm.kt64[kWaveRows * wave + lr] = tj64;  // read after the first barrier
     }
 
     f32x16 dvt[D / 32], dkt[D / 32];
@@ -395,9 +397,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             float bpos = 0.0f;
             int pm = 0;
             const int ihi = imin(iq0 + kWaveRows, n) - 1;
-            BiasSpan sp{0, 0, 0, 0, 0}, st{0, 0, 0, 0, 0};
             if (RP) {
-                sp = bias_span((int64_t)iq0 - (wk1 - 1), (int64_t)ihi - wk0);
+                const BiasSpan sp = bias_span((int64_t)iq0 - (wk1 - 1), (int64_t)ihi - wk0);
                 if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
@@ -405,11 +406,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             int tm = 0;
             if (RT) {
                 // TimePickAbs compares |t_key - t_query| itself: no sign or overflow condition
-                st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
+                const BiasSpan st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
                 tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb, true, 0u);
             } else tb.set_const(bpos);
-            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
-            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, tj64);
+            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
+            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
             if (kind == kPartial) mask_queries(s, dp, g, iq0, lo, hi);
             bf16x8 pb[2], db8[2];
 #pragma unroll
@@ -443,9 +444,26 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 }
             // from the stored values, after the products are issued (their vector work overlaps
             // the matrix instructions, and S and dP in fp32 are no longer held)
-            if constexpr (DS && (RP || RT))
-                grads_a<D, RP, RT>(db8, sm, buf, q0, iq0, j, g, lane, sp, ihi - wk0 <= 0, st, tm,
-                                   tb.thr, tb.thr2, tj, tj64);
+            if constexpr (DS && (RP || RT)) {
+                // The tile's bucket spans are derived again from their inputs rather than held
+                // across the epilogue and the products, where registers are short (the empty
+                // assembly statements keep the compiler from reusing the first results).
+                int ia = iq0;
+                asm volatile("" : "+v"(ia));
+                asm volatile("" ::: "memory");
+                const int ib = imin(ia + kWaveRows, n) - 1;
+                BiasSpan gsp{0, 0, 0, 0, 0}, gst{0, 0, 0, 0, 0};
+                int gtm = 0;
+                if (RP) gsp = bias_span((int64_t)ia - (wk1 - 1), (int64_t)ib - wk0);
+                if (RT) {
+                    gst = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
+                    // the mode TimeSel::set picks (no overflow condition here)
+                    gtm = gst.kind == 0 ? 0 : !(wave_kfit && sm.fits[buf]) ? 3
+                        : gst.kind == 2 ? 2 : gst.kind == 1 ? 1 : 4;
+                }
+                grads_a<D, RP, RT>(db8, sm, buf, q0, ia, j, g, lane, gsp, ib - wk0 <= 0, gst, gtm,
+                                   gst.thr, gst.thr2, tj, kWaveRows * wave + lr);
+            }
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tfirst + t + 1);
         wait_tile_dma();
