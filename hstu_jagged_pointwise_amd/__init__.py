@@ -246,8 +246,8 @@ def hstu_attn_bwd(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, dk, dv, dra
 
 def hstu_attn_bwd_dkdv(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dk, dv, ws=None,
                        stream=None) -> None:
-    """dK, dV; with ws (hstu_workspace_bytes(plan, OP_BWD) bytes) also stores dS there for
-    hstu_attn_bwd_dq."""
+    """dK, dV; with ws (hstu_workspace_bytes(plan, OP_BWD) bytes) also stores dS and the
+    bias-table gradients there for hstu_attn_bwd_dq."""
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load_library().hstu_attn_bwd_dkdv(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
@@ -256,8 +256,8 @@ def hstu_attn_bwd_dkdv(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dk, dv, ws
 
 def hstu_attn_bwd_dq(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, drab_pos=None,
                      drab_ts=None, ws=None, stream=None) -> None:
-    """dQ and the bias-table gradients; with ws, reads the dS that hstu_attn_bwd_dkdv stored in
-    the same ws, else recomputes S and dP."""
+    """dQ and the bias-table gradients; with ws, reads the dS and copies out the gradients that
+    hstu_attn_bwd_dkdv left in the same ws, else recomputes S and dP and sums the gradients."""
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     _check(load_library().hstu_attn_bwd_dq(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),

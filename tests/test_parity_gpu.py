@@ -452,6 +452,47 @@ def test_bwd_recompute_path(d, mask):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("which", ["none", "pos", "ts"])
+def test_bwd_bias_subsets_stored_ds(d, which):
+    """Stored-dS backward with each subset of the bias tables: the dK/dV pass sums only the
+    gradients of the tables present (position only, time only, none)."""
+    w = hs.make_inputs([300, 64, 1, 129, 200], 3, d, dtype="bf16", seed=51 + d, rab=True,
+                       num_contexts=2, num_targets=8, max_seqlen=300, backward=True)
+    if which in ("none", "ts"):
+        w["rab_pos"] = None
+    if which in ("none", "pos"):
+        w["rab_ts"] = None
+    say(f"bwd stored dS bias subset {which} d={d}")
+    _bwd_check(w, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_split_calls_share_workspace(d):
+    """hstu_attn_bwd_dkdv then hstu_attn_bwd_dq on one workspace (the bench's calls): the dK/dV
+    pass leaves dS and the bias-table gradients there and the dQ pass hands the gradients out;
+    a dQ call that asks for one table only gets that one."""
+    w = hs.make_inputs([500, 64, 129, 200], 2, d, dtype="bf16", seed=61 + d, rab=True,
+                       num_contexts=3, num_targets=9, max_seqlen=500, backward=True)
+    dev = runner.to_device(w)
+    args = runner.args_for(w, dev)
+    plan = runner.plan_for(w, args)
+    ws = torch.empty(hj.hstu_workspace_bytes(plan, hj.OP_BWD), dtype=torch.uint8, device="cuda:0")
+    dq, dk, dv = (runner.empty_like_thd(w, dev) for _ in range(3))
+    drp = torch.full((2, 128), float("nan"), dtype=torch.float32, device="cuda:0")
+    drt = torch.full((2, 128), float("nan"), dtype=torch.float32, device="cuda:0")
+    say(f"bwd split calls on one workspace d={d}")
+    hj.hstu_attn_bwd_dkdv(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], dk, dv, ws=ws)
+    hj.hstu_attn_bwd_dq(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], dq, drp, None,
+                        ws=ws)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(w)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv), ("drab_pos", drp)):
+        check(name, host(got), ref[name], "bf16")
+    assert torch.isnan(drt).all()  # not asked for: left alone
+    plan.close()
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_bwd_stored_ds_ignores_stale_workspace(d):
     """The stored-dS path reads only the dS entries its own dK/dV pass wrote (or masks them):
     a workspace filled with NaN beforehand changes nothing."""
