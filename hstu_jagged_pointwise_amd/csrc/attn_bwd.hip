@@ -94,7 +94,7 @@ template <int D, int PM, int TM>
 __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>& sm, int buf,
                                            int q0, int u0, int g, float alpha2, const TimeSel tb,
                                            uint32_t tj, int kl) {
-    const TimePickAbs pick(tb);
+    const TimePick pick(tb, tj);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int ii = q0 + 8 * r + 4 * g;
@@ -103,7 +103,7 @@ __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int e = 4 * r + c;
-            float b = pick.get<TM>(tj, tq4[c]);
+            float b = pick.get<TM>(tq4[c]);
             if (PM == 1) b += sm.rp[buf][u0 + 8 * r + c];
             if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
             if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(sm.kt64[kl], sm.tq64[buf][ii + c]))];
@@ -297,6 +297,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     }
     uint32_t tj = 0;
     int64_t tj64 = 0, tjmin = 0, tjmax = 0;
+    uint32_t tjmax_rel = 0;
     bool wave_kfit = true;
     if (RT) {
         tj64 = key_ok ? p.ts[tok0 + j] : tbase;
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
         tj = rel_time_u32(tj64, tbase);
         tjmin = uniform64(wave_min64(key_ok ? tj64 : INT64_MAX));
         tjmax = uniform64(wave_max64(key_ok ? tj64 : INT64_MIN));
+        tjmax_rel = rel_time_u32(tjmax, tbase);  // used only when every key time fits
         if (qh == 0) sm.kt64[kWaveRows * wave + lr] = tj64;  // read after the first barrier
     }
 
@@ -405,9 +407,12 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             TimeSel tb;
             int tm = 0;
             if (RT) {
-                // TimePickAbs compares |t_key - t_query| itself: no sign or overflow condition
-                const BiasSpan st = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
-                tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb, true, 0u);
+                // key minus query: in the two- and three-bucket modes all differences of the tile
+                // have one sign, and each pair takes one comparison of the query time with a
+                // per-lane limit (TimePick)
+                const int64_t dlo = tjmin - sm.tqmax[buf][qh];
+                const BiasSpan st = bias_span(dlo, tjmax - sm.tqmin[buf][qh]);
+                tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb, dlo >= 0, tjmax_rel);
             } else tb.set_const(bpos);
             if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
             else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
