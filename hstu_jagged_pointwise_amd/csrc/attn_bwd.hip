@@ -941,36 +941,24 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
 }
 
 // ---------------------------------------------------------------------------------------------
-// pass B with stored dS: dQ = sum_j dS_ij k_j and the bias-table gradients
+// pass B with stored dS: dQ = sum_j dS_ij k_j
 // ---------------------------------------------------------------------------------------------
-// The dK/dV pass has written dS * N for every pair it visits (AttnParams::ds, rows = keys), so
-// per key tile this pass only copies the K rows and the 64 x 128 dS block of its rows into LDS
-// and runs dQ^T += K^T dS^T.  With so little arithmetic per tile the copies set the pace: a ring
-// of kStages tiles keeps kStages - 1 of them in flight.  The key tiles' timestamps are copied
-// into LDS one tile ahead of their K and dS rows, so that wavefront 0 can derive the next tile's
-// time tables right after the barrier that opens a tile.
+// The dK/dV pass has written dS * N for every pair it visits (AttnParams::ds, rows = keys) and
+// summed the bias-table gradients, so per key tile this pass only copies the K rows and the
+// 64 x 128 dS block of its rows into LDS and runs dQ^T += K^T dS^T.  With so little arithmetic
+// per tile the copies set the pace: a ring of kStages tiles keeps kStages - 1 of them in flight.
 
 constexpr int kStages = 4;
 
 template <int D>
 struct SmemC {
-    float wtb[kNumBuckets];              // time bias by bucket (only the time-bucket split reads it)
-    ToepEntry rp[2][kToep + 1];          // position bucket by (i - j) (the bias field is unused)
-    uint32_t tk[2][kTile];
-    int64_t tk64[2][kTile];
-    int64_t tkmin[2][2], tkmax[2][2];
-    int fits[2];
-    int64_t tsraw[kStages][kTile];       // the key tiles' timestamps as copied
-    float hbp[kNumBuckets];
-    float hbt[kNumBuckets][32];
     alignas(16) bf16 k[kStages][kTile * D];   // swizzled tiles (tile_off)
     bf16 ds[kStages][kTile * kBlk];           // dS^T rows j0 .. j0 + 63, the unit's 128 columns
 };
 
-template <int D, bool GP, bool GT>
+template <int D>
 __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnParams p) {
     constexpr int kThreads = kThreadsA;
-    constexpr bool RP = GP, RT = GT;  // only the gradients need the bias structure
     __shared__ __attribute__((aligned(16))) SmemC<D> sm;
     static_assert(sizeof(SmemC<D>) <= 160 * 1024, "LDS");
 
@@ -978,17 +966,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lr = lane & 31;
     const int wave = uniform_i((tid >> 6) & 3), kh = uniform_i(tid >> 8);  // row group, key half
-    const bool wave0 = uniform_i(tid >> 6) == 0;
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = si.start, ld = p.ld_in;
     const bf16* __restrict__ kg = static_cast<const bf16*>(p.k) + tok0 * ld + h * D;
-
-    if (RT)
-        for (int e = tid; e < kNumBuckets; e += kThreads)
-            sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
-    for (int e = tid; e < kNumBuckets; e += kThreads) sm.hbp[e] = 0.0f;
-    for (int e = tid; e < kNumBuckets * 32; e += kThreads) (&sm.hbt[0][0])[e] = 0.0f;
-    const int64_t tbase = RT ? p.ts[tok0] : 0;
 
     const int rhi = imin(r0 + kBlk, n);
     const KeyTiles ktl = key_tiles_for_rows(r0, rhi, nc, nh);
@@ -1001,101 +981,37 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
         if (i < nh) lim = imax(i, nc - 1);
         else { lim = nh - 1; dg = i; }
     }
-    uint32_t ti = 0, timax_rel = 0;
-    int64_t ti64 = 0, timin = 0, timax = 0;
-    bool wave_qfit = true;
-    if (RT) {
-        ti64 = row_ok ? p.ts[tok0 + i] : tbase;
-        wave_qfit = __all(rel_time_fits(ti64, tbase));
-        ti = rel_time_u32(ti64, tbase);
-        timin = uniform64(wave_min64(row_ok ? ti64 : INT64_MAX));
-        timax = uniform64(wave_max64(row_ok ? ti64 : INT64_MIN));
-        timax_rel = rel_time_u32(timax, tbase);
-    }
     f32x16 dqt[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
-    Run run_p_lo, run_p_hi, run_t_lo, run_t_mid, run_t_hi;
 
     const int npad = (n + kBlk - 1) & ~(kBlk - 1);
     const bf16* dsb = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq] + (int64_t)h * npad * npad + r0;
-    // byte sizes as rows_rsrc computes them (rows past the end, and times past n, read as zero)
+    // byte sizes as rows_rsrc computes them (rows past the end read as zero)
     const i32x4 krs = rsrc_words(kg, n > 0 ? ((int64_t)(n - 1) * ld + D) * 2 : 0);
     const i32x4 dsrs = rsrc_words(dsb, ((int64_t)(npad - 1) * npad + kBlk) * 2);
-    const i32x4 tsrs = rsrc_words(RT ? p.ts + tok0 : nullptr, RT ? (int64_t)n * 8 : 0);
     const TileDma<D, kThreads> kdma(tid, ld);
     const TileDma<kBlk, kThreads> dsdma(tid, npad);
     const TrOperand<D> trop(lane);
     const TrBlock<kBlk> dsop(lane, wave);
 
-    // The copies of list entry t form a group: K and dS rows of entry t, then (wavefront 0) the
-    // timestamps of entry t + 1 in two 256-byte pieces.  Groups are issued in order, so waiting
-    // for group t also covers the timestamps that derive(t + 1) reads.
+    // The copies of list entry t form a group (its K and dS rows); groups are issued in order.
     constexpr int kPerTile = TileDma<D, kThreads>::N + TileDma<kBlk, kThreads>::N;
-    auto issue_ts = [&](int t) {
-        if (RT && wave0) {
-            const int off = ktl.tile(t) * kTile * 8 + 4 * lane;
-            const uint32_t dst = lds_addr(sm.tsraw[t % kStages]);
-            copy4_lds_asm(tsrs, dst, off);
-            copy4_lds_asm(tsrs, dst + 256, off + 256);
-        }
-    };
     auto issue_group = [&](int t) {
         const int j0 = ktl.tile(t) * kTile;
         kdma.issue_asm(krs, sm.k[t % kStages], (int)((int64_t)j0 * ld * 2));
         dsdma.issue_asm(dsrs, sm.ds[t % kStages], j0 * npad * 2);
-        if (t + 1 < ntiles) issue_ts(t + 1);
     };
     // waits for this thread's copies of group t, with groups t + 1 .. t + k still in flight
-    auto wait_group = [&](int t) {
-        const int k = imin(kStages - 2, ntiles - 1 - t);
-        int later = k * kPerTile;
-        if (RT && wave0) later += 2 * (k - (k > 0 && t + k == ntiles - 1 ? 1 : 0));
-        wait_vmcnt_upto(later);
-    };
-    // time and position tables of list entry t into slot t & 1
-    auto derive = [&](int t) {
-        const int j0 = ktl.tile(t) * kTile, sl = t & 1;
-        if (RT && wave0) {
-            const bool real = j0 + lane < n;
-            const int64_t tkr = real ? sm.tsraw[t % kStages][lane] : tbase;
-            sm.tk64[sl][lane] = tkr;
-            sm.tk[sl][lane] = rel_time_u32(tkr, tbase);
-            const TimeRange tr = wave_time_range(tkr, real, tbase);
-            if (lane == 0) {
-                sm.fits[sl] = tr.fit ? 1 : 0;
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    sm.tkmin[sl][hf] = tr.lo[hf];
-                    sm.tkmax[sl][hf] = tr.hi[hf];
-                }
-            }
-        }
-        if (RP)
-            for (int u = tid; u < kToep; u += kThreads) {
-                const int delta = (r0 - j0) + (kBlk - 1) - u;
-                const int bk = bucket_of((uint32_t)(delta < 0 ? -delta : delta));
-                sm.rp[sl][u] = ToepEntry{0.0f, (float)bk};
-            }
-    };
+    auto wait_group = [&](int t) { wait_vmcnt_upto(imin(kStages - 2, ntiles - 1 - t) * kPerTile); };
 
-    // prologue: the timestamps of entry 0, then the first kStages - 1 groups
-    if (ntiles > 0) issue_ts(0);
     for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_group(t);
-    if (ntiles > 0) {
-        wait_group(0);
-        lds_barrier();
-        derive(0);
-    }
 
     const int k0 = kWaveRows * kh;
-    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1) + k0;
-
     for (int t = 0; t < ntiles; ++t) {
-        const int st = t % kStages, sl2 = t & 1, j0 = ktl.tile(t) * kTile, jk0 = j0 + k0;
+        const int st = t % kStages, jk0 = ktl.tile(t) * kTile + k0;
         wait_group(t);    // this thread's copies of entry t have landed
-        lds_barrier();    // everyone's, and entry t's tables; entry t - 1 is done with
-        if (t + 1 < ntiles) derive(t + 1);
+        lds_barrier();    // everyone's; entry t - 1 is done with
         if (t + kStages - 1 < ntiles) issue_group(t + kStages - 1);
         const int kind = wlo < rhi && jk0 < n ? classify_row_tile(wlo, whi, jk0, n, nc, nh, kWaveRows)
                                               : kEmpty;
@@ -1103,11 +1019,10 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
         bf16x8 b8[2];  // dS (times N) of keys jk0 + 16sl + key(k) for this lane's row
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) b8[sl] = dsop.read(sm.ds[st], 2 * kh + sl);
-        f32x16 dp;
-        if (GP || GT || kind == kPartial)
+        if (kind == kPartial) {  // entries the dK/dV pass did not write for this row
+            f32x16 dp;
 #pragma unroll
             for (int x = 0; x < 16; ++x) dp[x] = (float)b8[x >> 3][x & 7];
-        if (kind == kPartial) {
             mask_keys_b(dp, g, jk0, lim, dg);
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
@@ -1115,44 +1030,6 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
 #pragma unroll
                 for (int x = 0; x < 8; ++x) td[x] = dp[8 * sl + x];
                 b8[sl] = pack8(td);
-            }
-        }
-        if (GP || GT) {
-            BiasSpan sp{0, 0, 0, 0, 0}, stt{0, 0, 0, 0, 0};
-            int pm = 0;
-            if (RP) {
-                const int jhi = imin(jk0 + kWaveRows, n) - 1;
-                sp = bias_span((int64_t)wlo - jhi, (int64_t)(whi - 1) - jk0);
-                pm = sp.kind != 0;
-            }
-            (void)pm;
-            TimeSel tb;
-            int tm = 0;
-            if (RT) {
-                const int64_t dlo = timin - uniform64(sm.tkmax[sl2][kh]);  // row minus key
-                stt = bias_span(dlo, timax - uniform64(sm.tkmin[sl2][kh]));
-                tm = tb.set(stt, wave_qfit && uniform_i(sm.fits[sl2]), 0.0f, sm.wtb, dlo >= 0, timax_rel);
-            } else tb.set_const(0.0f);
-            const int pg = !GP ? 0 : (sp.kind == 0 ? 0 : (sp.kind == 1 ? 1 : 2));
-            TileSums ts;
-            if (pg == 0) ts = grad_sums_tm<D, 0, GP, GT>(tm, dp, sm, sl2, k0, u0, g, lane, tb, ti, ti64);
-            else if (pg == 1) ts = grad_sums_tm<D, 1, GP, GT>(tm, dp, sm, sl2, k0, u0, g, lane, tb, ti, ti64);
-            else ts = grad_sums_tm<D, 2, GP, GT>(tm, dp, sm, sl2, k0, u0, g, lane, tb, ti, ti64);
-            if (GP && pg == 0) run_p_lo.add(sm.hbp, sp.b_lo, ts.sum, lane);
-            if (GP && pg == 1) {
-                const float hi_part = ts.mp - (float)sp.b_lo * ts.sum;
-                run_p_lo.add(sm.hbp, sp.b_lo, ts.sum - hi_part, lane);
-                run_p_hi.add(sm.hbp, sp.b_hi, hi_part, lane);
-            }
-            if (GT && tm == 0) run_t_lo.add(&sm.hbt[0][0], stt.b_lo, ts.sum, lane, 32);
-            if (GT && tm == 1) {
-                run_t_lo.add(&sm.hbt[0][0], stt.b_lo, ts.sum - ts.th, lane, 32);
-                run_t_hi.add(&sm.hbt[0][0], stt.b_hi, ts.th, lane, 32);
-            }
-            if (GT && tm == 4) {
-                run_t_lo.add(&sm.hbt[0][0], stt.b_lo, ts.sum - ts.th, lane, 32);
-                run_t_mid.add(&sm.hbt[0][0], stt.b_lo + 1, ts.th - ts.th2, lane, 32);
-                run_t_hi.add(&sm.hbt[0][0], stt.b_hi, ts.th2, lane, 32);
             }
         }
 #pragma unroll
@@ -1194,24 +1071,6 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
                 for (int c = 0; c < 4; ++c) w[c] = (bf16)(dqt[db][4 * r + c] * sq);
                 *reinterpret_cast<bf16x4*>(dqg + 32 * db + 8 * r + 4 * g) = w;
             }
-    }
-    if (GP || GT) {
-        if (GP) { run_p_lo.add(sm.hbp, -2, 0.0f, lane); run_p_hi.add(sm.hbp, -2, 0.0f, lane); }  // flush
-        if (GT) {
-            run_t_lo.add(&sm.hbt[0][0], -2, 0.0f, lane, 32);
-            run_t_mid.add(&sm.hbt[0][0], -2, 0.0f, lane, 32);
-            run_t_hi.add(&sm.hbt[0][0], -2, 0.0f, lane, 32);
-        }
-        __syncthreads();
-        for (int b = tid; b < kNumBuckets; b += kThreads) {
-            if (GP && sm.hbp[b] != 0.0f) atomicAdd(&p.drab_pos[h * kNumBuckets + b], sm.hbp[b] * p.inv_n);
-            if (GT) {
-                float v = 0.0f;
-#pragma unroll 8
-                for (int l = 0; l < 32; ++l) v += sm.hbt[b][(l + b) & 31];
-                if (v != 0.0f) atomicAdd(&p.drab_ts[h * kNumBuckets + b], v * p.inv_n);
-            }
-        }
     }
 }
 
@@ -1397,7 +1256,7 @@ hipError_t launch_dq_t(const AttnParams& p, hipStream_t s) {
     const dim3 grid(p.num_units), block(kThreadsA);
     if (p.ds) {  // stored dS: the dK/dV pass has summed the bias-table gradients
         if constexpr (D >= 64) {
-            hipLaunchKernelGGL((bwd_dq_stored_kernel<D, false, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((bwd_dq_stored_kernel<D>), grid, block, 0, s, p);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;

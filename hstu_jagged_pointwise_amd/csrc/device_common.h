@@ -518,18 +518,6 @@ __device__ __forceinline__ void copy16_lds_asm(i32x4 rs, uint32_t lds, int voff)
 #endif
 }
 
-// Lane l copies the dword at byte offset voff to LDS address lds + 4 l.
-__device__ __forceinline__ void copy4_lds_asm(i32x4 rs, uint32_t lds, int voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
-#else
-    (void)rs;
-    (void)lds;
-    (void)voff;
-#endif
-}
-
 // Copies tile rows [r0, r0 + 64) of one slice from memory straight into an LDS tile (buffer
 // loads with the LDS-write option, 16 bytes per lane): instruction u of wavefront w fills the
 // 1 KB block u * W + w of the tile (W wavefronts; blocks past the tile's D / 8 are skipped), lane
