@@ -12,14 +12,17 @@
 //     keys 32 (w % 4) .. + 31 and the query half 32 (w / 4) .. + 31 of each visited 64-query tile
 //     (two wavefronts per SIMD; the two halves' dK, dV partial sums are added through LDS at the
 //     end).  The unit's K and V rows stay in LDS and are read as MFMA B operands, which keeps a
-//     wavefront within the 256 registers that two wavefronts per SIMD allow.  S = Q K^T and dP = dO V^T put one key per lane, which is the B-operand layout for
-//     dV^T += dO^T P and dK^T += Q^T dS; the Q and dO tiles are read along their rows for the A
-//     operands of the first two products and with transposing LDS reads for the last two.
+//     wavefront within the 256 registers that two wavefronts per SIMD allow.  S = Q K^T and
+//     dP = dO V^T put one key per lane, which is the B-operand layout for dV^T += dO^T P and
+//     dK^T += Q^T dS; the Q and dO tiles are read along their rows for the A operands of the
+//     first two products and with transposing LDS reads for the last two.  With a workspace,
+//     pass A also writes dS (bf16) for pass B and sums the bias-table gradients from it.
 //   pass B (query-stationary): unit = (sequence, head, 128 rows) like the forward, 8 wavefronts:
 //     wavefront w owns rows 32 (w % 4) .. + 31 and the key half 32 (w / 4) .. + 31 of each
 //     64-key tile; S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T (K^T read transposed from the K
 //     tile), and the bias-table gradients.  The unit's Q and dO rows stay in LDS (B operands),
 //     two wavefronts per SIMD; the key halves' dQ partial sums are added through LDS at the end.
+//     With the stored dS, pass B only reads dS and K (bwd_dq_stored_kernel).
 // Tiles are copied from memory straight into LDS by buffer loads, double-buffered, as in the
 // forward.
 // Bias-gradient sums: when all pairs of a (wavefront, tile) fall into one bucket -- the common
