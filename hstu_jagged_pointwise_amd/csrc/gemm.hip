@@ -96,25 +96,28 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
     const TileDma<AT ? 128 : 64, kGT> adma(tid, g.lda);
     const TileDma<BT ? 64 : 128, kGT> bdma(tid, g.ldb);
 
-    // starts the copy of K step st of tile t into buffer buf
+    // starts the copy of K step st of tile t into buffer buf.  The copies are issued from inline
+    // assembly: with the copy builtin the compiler waits for every copy in flight before the
+    // step's LDS reads, i.e. for the next step's copy; each step waits for its own copy
+    // explicitly (wait_tile_dma, then the barrier).
     auto issue = [&](const GemmTile& t, int st, int buf) {
         const int64_t kk = (int64_t)st * kGK;  // relative to kbeg
         const int krows = (int)(t.kend - t.kbeg);
         if constexpr (AT) {
-            const buffer_rsrc rs = rows_rsrc(A + t.kbeg * g.lda + t.m0, krows, g.lda, kGM);
-            adma.issue(rs, sm.a[buf], (int)(kk * g.lda * 2));
+            const i32x4 rs = rows_words(A + t.kbeg * g.lda + t.m0, krows, g.lda, kGM);
+            adma.issue_asm(rs, sm.a[buf], (int)(kk * g.lda * 2));
         } else {
-            const buffer_rsrc rs = rows_rsrc(A + t.m0 * g.lda, (int)min<int64_t>(g.M - t.m0, kGM), g.lda, (int)g.K);
-            adma.issue(rs, sm.a[buf], (int)((t.kbeg + kk) * 2));
-            adma.issue(rs, sm.a[buf] + 64 * kGK, (int)((t.kbeg + kk + 64 * g.lda) * 2));
+            const i32x4 rs = rows_words(A + t.m0 * g.lda, (int)min<int64_t>(g.M - t.m0, kGM), g.lda, (int)g.K);
+            adma.issue_asm(rs, sm.a[buf], (int)((t.kbeg + kk) * 2));
+            adma.issue_asm(rs, sm.a[buf] + 64 * kGK, (int)((t.kbeg + kk + 64 * g.lda) * 2));
         }
         if constexpr (BT) {
-            const buffer_rsrc rs = rows_rsrc(B + (int64_t)t.n0 * g.ldb, kGN, g.ldb, (int)g.K);
-            bdma.issue(rs, sm.b[buf], (int)((t.kbeg + kk) * 2));
-            bdma.issue(rs, sm.b[buf] + 64 * kGK, (int)((t.kbeg + kk + 64 * g.ldb) * 2));
+            const i32x4 rs = rows_words(B + (int64_t)t.n0 * g.ldb, kGN, g.ldb, (int)g.K);
+            bdma.issue_asm(rs, sm.b[buf], (int)((t.kbeg + kk) * 2));
+            bdma.issue_asm(rs, sm.b[buf] + 64 * kGK, (int)((t.kbeg + kk + 64 * g.ldb) * 2));
         } else {
-            const buffer_rsrc rs = rows_rsrc(B + t.kbeg * g.ldb + t.n0, krows, g.ldb, kGN);
-            bdma.issue(rs, sm.b[buf], (int)(kk * g.ldb * 2));
+            const i32x4 rs = rows_words(B + t.kbeg * g.ldb + t.n0, krows, g.ldb, kGN);
+            bdma.issue_asm(rs, sm.b[buf], (int)(kk * g.ldb * 2));
         }
     };
     // next tile of this workgroup at or after number id (id advanced past it), if any
