@@ -194,6 +194,16 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
             for (int mb = 0; mb < 2; ++mb) {
                 const int64_t m = m0 + 64 * wm + 32 * mb + lr;
                 if (m >= g.M) continue;
+                // the residual row's values, all loaded before any store (the compiler may not
+                // move a load of r above a store to c, which it cannot prove apart)
+                bf16x4 res[2][4];
+                if constexpr (EPI == kEpiResidual)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            res[nb][r] = *reinterpret_cast<const bf16x4*>(
+                                static_cast<const bf16*>(g.r) + m * g.ldr + n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -211,8 +221,7 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
                             *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
                             if (g.c2) *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c2) + m * g.ldc + n) = z;
                         } else if constexpr (EPI == kEpiResidual) {
-                            const bf16x4 rv = *reinterpret_cast<const bf16x4*>(
-                                static_cast<const bf16*>(g.r) + m * g.ldr + n);
+                            const bf16x4 rv = res[nb][r];
                             bf16x4 y;
 #pragma unroll
                             for (int c = 0; c < 4; ++c) y[c] = (bf16)(x[c] + (float)rv[c]);
