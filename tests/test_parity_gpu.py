@@ -369,6 +369,27 @@ def test_layer_bwd_small():
     _layer_bwd_check(w)
 
 
+def test_layer_bwd_without_bias_gradient_outputs():
+    """Bias tables present but their gradients not asked for (NULL outputs): the dK/dV pass still
+    sums them in LDS and writes nothing; dX, dW1, dW2 are unchanged."""
+    w = hs.make_inputs([17, 130, 1, 64], 4, 128, dtype="bf16", seed=41, rab=True,
+                       num_contexts=4, num_targets=16, layer_dim=512, backward=True)
+    dev = runner.to_device(w)
+    args = runner.args_for(w, dev)
+    plan = runner.plan_for(w, args)
+    T, D, Hd = w["total_tokens"], w["layer_dim"], w["heads"] * w["d"]
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device="cuda:0")
+    dw1 = torch.empty((D, 4 * Hd), dtype=torch.float32, device="cuda:0")
+    dw2 = torch.empty((Hd, D), dtype=torch.float32, device="cuda:0")
+    say("layer backward without bias-gradient outputs")
+    hj.hstu_layer_bwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], dev["dy"], dx, dw1, dw2)
+    torch.cuda.synchronize()
+    ref = oracle.layer_bwd(w)
+    for name, got in (("dx", dx), ("dw1", dw1), ("dw2", dw2)):
+        check(name, host(got), ref[name], "bf16")
+    plan.close()
+
+
 @pytest.mark.parametrize("heads,d,D", [(2, 64, 128), (4, 32, 256), (1, 128, 384)])
 def test_layer_bwd_shapes(heads, d, D):
     # weights scaled so that the attention, LayerNorm and gate terms carry the gradients
