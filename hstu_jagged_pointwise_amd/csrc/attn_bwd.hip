@@ -306,8 +306,12 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
         tj64 = key_ok ? p.ts[tok0 + j] : tbase;
         wave_kfit = __all(rel_time_fits(tj64, tbase));
         tj = rel_time_u32(tj64, tbase);
-        tjmin = uniform64(wave_min64(key_ok ? tj64 : INT64_MAX));
-        tjmax = uniform64(wave_max64(key_ok ? tj64 : INT64_MIN));
+        {
+            int64_t lo, hi;
+            wave_time_minmax(tj64, key_ok, tbase, lo, hi);
+            tjmin = uniform64(lo);
+            tjmax = uniform64(hi);
+        }
         tjmax_rel = rel_time_u32(tjmax, tbase);  // used only when every key time fits
         if (qh == 0) sm.kt64[kWaveRows * wave + lr] = tj64;  // read after the first barrier
     }
@@ -747,8 +751,12 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         ti64 = row_ok ? p.ts[tok0 + i] : tbase;
         wave_qfit = __all(rel_time_fits(ti64, tbase));
         ti = rel_time_u32(ti64, tbase);
-        timin = uniform64(wave_min64(row_ok ? ti64 : INT64_MAX));
-        timax = uniform64(wave_max64(row_ok ? ti64 : INT64_MIN));
+        {
+            int64_t lo, hi;
+            wave_time_minmax(ti64, row_ok, tbase, lo, hi);
+            timin = uniform64(lo);
+            timax = uniform64(hi);
+        }
         timax_rel = rel_time_u32(timax, tbase);  // used only when every row time fits
     }
     f32x16 dqt[D / 32];

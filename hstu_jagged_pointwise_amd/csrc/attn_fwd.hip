@@ -214,8 +214,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         ti64 = row_ok ? p.ts[tok0 + i] : tbase;
         wave_qfit = __all(rel_time_fits(ti64, tbase));
         ti = rel_time_u32(ti64, tbase);
-        timin = uniform64(wave_min64(row_ok ? ti64 : INT64_MAX));
-        timax = uniform64(wave_max64(row_ok ? ti64 : INT64_MIN));
+        {
+            int64_t lo, hi;
+            wave_time_minmax(ti64, row_ok, tbase, lo, hi);
+            timin = uniform64(lo);
+            timax = uniform64(hi);
+        }
         timax_rel = rel_time_u32(timax, tbase);  // used only when every row time fits
     }
 

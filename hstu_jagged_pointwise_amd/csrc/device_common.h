@@ -354,6 +354,16 @@ __device__ __forceinline__ TimeRange wave_time_range(int64_t t, bool real, int64
     return r;
 }
 
+// Minimum and maximum of the real lanes' times over the whole wavefront (through
+// wave_time_range: DPP on 32-bit relative times when they fit, instead of 64-bit shuffles).  A
+// wavefront without real lanes gets an empty range (min > max).
+__device__ __forceinline__ void wave_time_minmax(int64_t t, bool real, int64_t base, int64_t& mn,
+                                                 int64_t& mx) {
+    const TimeRange r = wave_time_range(t, real, base);
+    mn = r.lo[0] < r.lo[1] ? r.lo[0] : r.lo[1];
+    mx = r.hi[0] > r.hi[1] ? r.hi[0] : r.hi[1];
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
     bf16x8 r;
 #pragma unroll
