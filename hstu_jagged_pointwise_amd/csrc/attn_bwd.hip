@@ -32,6 +32,8 @@
 // histogram entry goes to the global table with one atomic add.
 // Scores are carried as -log2(e) S (folded into alpha and the staged bias tables), as in the
 // forward, so sigmoid costs one exp2 and one rcp.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -1249,6 +1251,20 @@ __global__ void zero_f32_kernel(float* p, int64_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
+// Up to four buffers cleared by one launch: blockIdx.y picks the buffer, each block-thread
+// strides over it.
+struct ZeroList {
+    float* p[4];
+    int64_t n[4];
+};
+__global__ void zero_f32_list_kernel(const ZeroList z) {
+    float* p = z.p[blockIdx.y];
+    const int64_t n = z.n[blockIdx.y];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
 template <int D, bool RP, bool RT>
 hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
     if constexpr (D >= 64)
@@ -1332,6 +1348,24 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int threads = 256;
     hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + threads - 1) / threads)), dim3(threads), 0, s, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32_list(float* const* ptrs, const int64_t* counts, int k, hipStream_t s) {
+    ZeroList z{};
+    int m = 0;
+    int64_t most = 0;
+    for (int i = 0; i < k && i < 4; ++i)
+        if (ptrs[i] && counts[i] > 0) {
+            z.p[m] = ptrs[i];
+            z.n[m] = counts[i];
+            most = std::max(most, counts[i]);
+            ++m;
+        }
+    if (m == 0) return hipSuccess;
+    const int threads = 256;
+    const int64_t blocks = std::min<int64_t>((most + threads - 1) / threads, 1024);
+    hipLaunchKernelGGL(zero_f32_list_kernel, dim3((unsigned)blocks, (unsigned)m), dim3(threads), 0, s, z);
     return hipGetLastError();
 }
 

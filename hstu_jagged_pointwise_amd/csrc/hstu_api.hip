@@ -753,10 +753,9 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     drab_pos = args->rab_pos ? drab_pos : nullptr;
     drab_ts = args->rab_ts ? drab_ts : nullptr;
     const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
-    hipError_t e = hstu::launch_zero_f32(dw1, int64_t(d_model) * 4 * hd, s);
-    if (e == hipSuccess) e = hstu::launch_zero_f32(dw2, int64_t(hd) * d_model, s);
-    if (e == hipSuccess && drab_pos) e = hstu::launch_zero_f32(drab_pos, nb, s);
-    if (e == hipSuccess && drab_ts) e = hstu::launch_zero_f32(drab_ts, nb, s);
+    float* const outs[4] = {dw1, dw2, drab_pos, drab_ts};
+    const int64_t counts[4] = {int64_t(d_model) * 4 * hd, int64_t(hd) * d_model, nb, nb};
+    hipError_t e = hstu::launch_zero_f32_list(outs, counts, 4, s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     if (T == 0) return HSTU_OK;
     const size_t wide = align_up(size_t(T) * 4 * hd * 2, 256), narrow = align_up(size_t(T) * hd * 2, 256);

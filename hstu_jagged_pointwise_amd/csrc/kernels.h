@@ -67,6 +67,8 @@ hipError_t launch_attn_bwd_dq_bf16(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_bwd_dkdv_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_attn_bwd_dq_f32(const AttnParams& p, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// Clears up to four fp32 buffers (NULL entries or zero counts are skipped) with one launch.
+hipError_t launch_zero_f32_list(float* const* ptrs, const int64_t* counts, int k, hipStream_t s);
 
 // LayerNorm over `width` features of each row of a (bf16), times gate u (token stride ldu),
 // written to out (dense, may alias a).
