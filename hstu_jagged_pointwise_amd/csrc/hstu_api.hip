@@ -127,14 +127,15 @@ void sort_longest_first(std::vector<WorkUnit>& u) {
 constexpr int kMinSplit = 4;
 constexpr int kXcds = 8;
 
-void order_for_xcds(std::vector<FwdItem>& items) {
-    std::stable_sort(items.begin(), items.end(), [](const FwdItem& a, const FwdItem& b) {
+template <class Item>
+void order_for_xcds(std::vector<Item>& items) {
+    std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
         return a.cost > b.cost;
     });
     // groups in order of their longest item
-    std::vector<std::vector<FwdItem>> groups;
+    std::vector<std::vector<Item>> groups;
     std::vector<std::pair<int64_t, int>> index;  // (key, group) for lookup
-    for (const FwdItem& it : items) {
+    for (const Item& it : items) {
         const int64_t key = (int64_t(it.seq) << 20) | it.head;
         auto found = std::lower_bound(index.begin(), index.end(), std::make_pair(key, -1));
         if (found != index.end() && found->first == key) {
@@ -144,7 +145,7 @@ void order_for_xcds(std::vector<FwdItem>& items) {
             groups.push_back({it});
         }
     }
-    std::vector<std::vector<FwdItem>> queues(kXcds);
+    std::vector<std::vector<Item>> queues(kXcds);
     for (const auto& grp : groups) {
         int best = 0;
         for (int r = 1; r < kXcds; ++r)
@@ -383,7 +384,9 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
             for (int h = 0; h < H; ++h) plan->bwd.push_back(WorkUnit{b, h, k0, cost});
         }
     }
-    sort_longest_first(plan->fwd);
+    // row blocks in the XCD launch order (the dQ pass reads each (sequence, head)'s K rows from
+    // one L2); key blocks longest first (their costs differ widely and the longest bound the pass)
+    order_for_xcds(plan->fwd);
     sort_longest_first(plan->bwd);
     return finish_plan(plan, flags, out);
 }

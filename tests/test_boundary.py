@@ -190,7 +190,7 @@ def _plan(batch, dtype="bf16"):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_plan_covers_every_block_once_longest_first(dtype):
+def test_plan_covers_every_block_once_in_launch_order(dtype):
     w = hs.make_workload("longtail_fwd")
     plan = _plan(w, dtype)
     info = hj.hstu_plan_info(plan)
@@ -201,7 +201,16 @@ def test_plan_covers_every_block_once_longest_first(dtype):
     assert rows == (128 if dtype == "bf16" else 64)
     for op, block in ((0, rows), (1, info["bwd_key_block"])):
         u = hj.hstu_plan_units(plan, op)
-        assert np.all(np.diff(u[:, 3]) <= 0)                 # longest first
+        if op == 1:
+            assert np.all(np.diff(u[:, 3]) <= 0)             # key blocks: longest first
+        else:  # row blocks: one (sequence, head) per index residue mod 8, longest first in it
+            pos = {}
+            for k, x in enumerate(u):
+                pos.setdefault((int(x[0]), int(x[1])), []).append(k)
+            for ks in pos.values():
+                if max(ks) < len(u) // 2:
+                    assert len({k % 8 for k in ks}) == 1, ks
+                assert all(u[a][3] >= u[b][3] for a, b in zip(ks, ks[1:]))
         got = sorted(map(tuple, u[:, :3].tolist()))
         want = sorted((b, h, r) for b, n in enumerate(w["lengths"]) for h in range(H)
                       for r in range(0, int(n), block))
