@@ -36,10 +36,13 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "long_fwdbwd"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# What a kernel's HBM traffic depends on: its source, the shared device helpers and the plan
+# code that fixes the launch order (the L2 hits across work units).
+_CSRC = "hstu_jagged_pointwise_amd/csrc/"
 KERNEL_SOURCES = {
-    "fwd": "hstu_jagged_pointwise_amd/csrc/attn_fwd.hip",
-    "bwd_dkdv": "hstu_jagged_pointwise_amd/csrc/attn_bwd.hip",
-    "bwd_dq": "hstu_jagged_pointwise_amd/csrc/attn_bwd.hip",
+    "fwd": (_CSRC + "attn_fwd.hip", _CSRC + "device_common.h", _CSRC + "hstu_api.hip"),
+    "bwd_dkdv": (_CSRC + "attn_bwd.hip", _CSRC + "device_common.h", _CSRC + "hstu_api.hip"),
+    "bwd_dq": (_CSRC + "attn_bwd.hip", _CSRC + "device_common.h", _CSRC + "hstu_api.hip"),
 }
 # Algorithmic MFMA work per visible pair per head, in units of d: forward S and P.V; the dK/dV
 # pass S, dP, dV, dK (it also stores dS); the dQ pass dS.K from the stored dS.
@@ -53,14 +56,17 @@ def describe(w):
             f"position+time bias {'yes' if w.get('rab_pos') is not None else 'no'}")
 
 
-def sha256(path):
-    with open(os.path.join(ROOT, path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sha256(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if the kernel source is
-    unchanged since they were taken; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if the kernel source, the
+    device helpers and the plan code are unchanged since they were taken; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE)).get(kernel)
     except (OSError, ValueError):
