@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -193,6 +194,21 @@ void build_fwd_items(hstu_plan_t* plan, int compute_units) {
     order_for_xcds(plan->items);
 }
 
+// The stream plan uploads go through, one per device, created on first use: non-blocking, so an
+// upload neither waits for nor is ordered after the caller's queued kernels (the plan's buffer is
+// new, nothing queued can touch it).
+hipStream_t upload_stream(int device) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static hipStream_t streams[kMaxDevices] = {};
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[device] &&
+        hipStreamCreateWithFlags(&streams[device], hipStreamNonBlocking) != hipSuccess)
+        streams[device] = nullptr;
+    return streams[device];
+}
+
 size_t part_bytes(const hstu_plan_t* plan) {
     return align_up(size_t(plan->parts) * plan->fwd_rows * plan->shape.head_dim * 4, 256);
 }
@@ -293,7 +309,10 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
             delete plan;
             return HSTU_ERR_HIP;
         }
-        if (hipMemcpy(plan->dbuf, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
+        hipStream_t up = upload_stream(plan->device);
+        if (!up ||
+            hipMemcpyAsync(plan->dbuf, host.data(), total, hipMemcpyHostToDevice, up) != hipSuccess ||
+            hipStreamSynchronize(up) != hipSuccess) {
             (void)hipFree(plan->dbuf);
             delete plan;
             return HSTU_ERR_HIP;

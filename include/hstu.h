@@ -102,13 +102,18 @@ typedef struct {
  * even assignment of irregular work to cores).  seq_offsets_host: host [B+1] int64 start offsets
  * (KeyedJaggedTensor offsets, page 1 section 3.1.2) with [0] = 0 and [B] = T.
  * num_targets_host: host [B] int32 candidates per sequence, or NULL for none.  Work items are
- * (sequence, head, row block) ordered by decreasing cost, so the hardware dispatcher assigns the
- * longest first.  For bf16, a row block costing more than the average load of a workgroup slot
+ * (sequence, head, row block) and (sequence, head, key block).  Key blocks are ordered by
+ * decreasing cost, so the hardware dispatcher assigns the longest first; row blocks (and forward
+ * items) are dealt to the 8 XCDs' dispatch residues one (sequence, head) at a time, longest group
+ * first, so that the blocks sharing K and V run on one XCD and read them from its L2.  For bf16, a row block costing more than the average load of a workgroup slot
  * (two per compute unit of the current device, 256 units for a host-only plan) runs as several
  * forward items over disjoint key tiles whose fp32 partial outputs are summed afterwards (exact
  * up to fp32 summation order: there is no softmax normalisation).  Unless flags has
- * HSTU_PLAN_HOST_ONLY, the lists are copied synchronously into one device buffer owned by the
- * plan, on the current device.  *out receives the plan, or NULL on error.  The caller frees it
+ * HSTU_PLAN_HOST_ONLY, the lists are copied into one device buffer owned by the plan, on the
+ * current device, through a non-blocking stream the library keeps per device: the call returns
+ * once the copy is complete and does not wait for work queued on other streams (a plan for the
+ * next batch can be built while the current batch's kernels run).  *out receives the plan, or
+ * NULL on error.  The caller frees it
  * with hstu_plan_destroy. */
 hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* seq_offsets_host,
                                const int32_t* num_targets_host, uint32_t flags,
