@@ -218,9 +218,9 @@ def bench_headline(args, torch, hj, runner, w):
         plan.close()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    # Every step builds its own plan on the host.  A step's plan is built while the previous
-    # step's kernels run (as a data loader prepares the next batch); its upload is a synchronous
-    # copy on the default stream, so it lands after those kernels and before the step's own.
+    # Every step builds its own plan on the host.  A step's plan is built, and uploaded through
+    # the library's own stream, while the previous step's kernels run (as a data loader prepares
+    # the next batch); the previous plan is freed once its kernels are done.
     plan = build()
     for k in range(args.steps):
         launch(plan, True)
