@@ -193,6 +193,28 @@ def test_longtail_workload_full():
     check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
 
 
+def test_plan_built_while_kernels_run():
+    # a plan created and used while another plan's launches are still queued: its upload does not
+    # wait for them, and its lists are complete before its own kernels read them
+    say("plan created behind queued long-tail forwards, then the ranking forward")
+    w1, w2 = hs.make_workload("longtail_fwd"), hs.make_workload("ranking_fwd")
+    dev1, dev2 = runner.to_device(w1), runner.to_device(w2)
+    a1 = runner.args_for(w1, dev1)
+    p1 = runner.plan_for(w1, a1)
+    out1 = runner.empty_like_thd(w1, dev1)
+    for _ in range(40):
+        hj.hstu_attn_fwd(p1, a1, dev1["q"], dev1["k"], dev1["v"], out1)
+    a2 = runner.args_for(w2, dev2)
+    p2 = runner.plan_for(w2, a2)
+    out2 = runner.empty_like_thd(w2, dev2)
+    hj.hstu_attn_fwd(p2, a2, dev2["q"], dev2["k"], dev2["v"], out2)
+    torch.cuda.synchronize()
+    check("O ranking", host(out2), oracle.attn_fwd(w2), "bf16")
+    check("O long-tail", host(out1), oracle.attn_fwd(w1), "bf16")
+    p1.close()
+    p2.close()
+
+
 # ---- full layer -----------------------------------------------------------------------------
 
 def _layer_check(w):
