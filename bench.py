@@ -220,15 +220,17 @@ def bench_headline(args, torch, hj, runner, w):
     t0 = time.perf_counter()
     # Every step builds its own plan on the host.  A step's plan is built, and uploaded through
     # the library's own stream, while the previous step's kernels run (as a data loader prepares
-    # the next batch); the previous plan is freed once its kernels are done.
-    plan = build()
+    # the next batch).  A plan is destroyed after the next step is queued: its buffer goes back in
+    # the order of this (default) stream, after the kernels that read it.
+    plan, prev = build(), None
     for k in range(args.steps):
         launch(plan, True)
         nxt = build() if k + 1 < args.steps else None
-        torch.cuda.current_stream().synchronize()  # the plan is freed once its kernels are done
-        plan.close()
-        plan = nxt
+        if prev is not None:
+            prev.close()
+        prev, plan = plan, nxt
     torch.cuda.synchronize()
+    prev.close()
     wall = time.perf_counter() - t0
     assert torch.isfinite(out.float()).all() and torch.isfinite(dq.float()).all()
 

@@ -42,6 +42,7 @@ struct hstu_plan {
     std::vector<int64_t> ds_off;
     int64_t ds_elems = 0;
     void* dbuf = nullptr;
+    bool pooled = false;  // dbuf from the device's stream-ordered pool (else hipMalloc)
     const SeqInfo* d_seqs = nullptr;
     const WorkUnit* d_fwd = nullptr;
     const WorkUnit* d_bwd = nullptr;
@@ -209,6 +210,15 @@ hipStream_t upload_stream(int device) {
     return streams[device];
 }
 
+// Pool memory goes back in the order of the default stream (after the work queued there and on
+// the streams that synchronize with it); hipMalloc memory with hipFree, which waits for the device.
+void release_device_lists(hstu_plan_t* plan) {
+    if (!plan->dbuf) return;
+    if (plan->pooled) (void)hipFreeAsync(plan->dbuf, nullptr);
+    else (void)hipFree(plan->dbuf);
+    plan->dbuf = nullptr;
+}
+
 size_t part_bytes(const hstu_plan_t* plan) {
     return align_up(size_t(plan->parts) * plan->fwd_rows * plan->shape.head_dim * 4, 256);
 }
@@ -305,15 +315,25 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
         std::vector<char> host(total);
         for (int i = 0; i < kArrays; ++i)
             if (sizes[i]) std::memcpy(host.data() + offs[i], srcs[i], sizes[i]);
-        if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
+        hipStream_t up = upload_stream(plan->device);
+        if (!up) {
             delete plan;
             return HSTU_ERR_HIP;
         }
-        hipStream_t up = upload_stream(plan->device);
-        if (!up ||
-            hipMemcpyAsync(plan->dbuf, host.data(), total, hipMemcpyHostToDevice, up) != hipSuccess ||
+        // stream-ordered allocation where the device supports it, so that freeing a plan need
+        // not synchronize the device
+        plan->pooled = hipMallocAsync(&plan->dbuf, total, up) == hipSuccess;
+        if (!plan->pooled) {
+            (void)hipGetLastError();
+            plan->dbuf = nullptr;
+            if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
+                delete plan;
+                return HSTU_ERR_HIP;
+            }
+        }
+        if (hipMemcpyAsync(plan->dbuf, host.data(), total, hipMemcpyHostToDevice, up) != hipSuccess ||
             hipStreamSynchronize(up) != hipSuccess) {
-            (void)hipFree(plan->dbuf);
+            release_device_lists(plan);
             delete plan;
             return HSTU_ERR_HIP;
         }
@@ -412,7 +432,7 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
 
 void hstu_plan_destroy(hstu_plan_t* plan) {
     if (!plan) return;
-    if (plan->dbuf) (void)hipFree(plan->dbuf);
+    release_device_lists(plan);
     delete plan;
 }
 

@@ -119,8 +119,12 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* seq_
                                const int32_t* num_targets_host, uint32_t flags,
                                hstu_plan_t** out);
 
-/* Frees the plan and its device buffer (waits for nothing: the caller must not destroy a plan
- * that queued work still uses).  NULL is ignored. */
+/* Frees the plan and its device buffer.  Where the device has a stream-ordered memory pool the
+ * buffer comes from it and goes back in the order of the default (null) stream: after the work
+ * queued there and on the blocking streams that synchronize with it, without waiting on the host.
+ * Otherwise it is released with hipFree, which waits for the device.  Work queued on non-blocking
+ * streams is not waited for: the caller must not destroy a plan such work still uses.  NULL is
+ * ignored. */
 void hstu_plan_destroy(hstu_plan_t* plan);
 
 /* Fills *info. */
