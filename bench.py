@@ -119,30 +119,35 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRAF
     print(json.dumps(rec))
 
 
-def cpu_baseline(w_full, budget_pairs=60_000_000):
-    """The oracle (fp64 loops, OpenMP) on a bounded sample of the workload: the first sequence,
-    with as many heads as fit the pair budget (heads are independent)."""
+def cpu_baseline(w_full, budget_pairs=250_000_000):
+    """The oracle (fp64 loops, OpenMP over (sequence, head) units) on a bounded sample of the
+    workload: its first sequences, all heads, as many as fit the pair budget (at least the
+    first).  `cores` is the number of threads that had work: one unit per thread at most."""
     import oracle
     off = w_full["seq_offsets"]
-    d = w_full["d"]
-    per_head = oracle.count_pairs(off[:2], w_full["num_contexts"], w_full["num_targets"][:1])
-    hs_ = int(max(1, min(w_full["heads"], budget_pairs // max(per_head, 1))))
-    e = int(off[1])
+    d, H = w_full["d"], w_full["heads"]
+    nb, pairs = 0, 0
+    for b in range(w_full["batch"]):
+        p = H * oracle.count_pairs(off[b:b + 2] - off[b], w_full["num_contexts"],
+                                   w_full["num_targets"][b:b + 1])
+        if nb > 0 and pairs + p > budget_pairs:
+            break
+        nb, pairs = nb + 1, pairs + p
+    e = int(off[nb])
     w = dict(w_full)
-    w.update(batch=1, heads=hs_, seq_offsets=off[:2].copy(), num_targets=w_full["num_targets"][:1],
-             total_tokens=e, timestamps=w_full["timestamps"][:e],
-             rab_pos=w_full["rab_pos"][:hs_], rab_ts=w_full["rab_ts"][:hs_])
+    w.update(batch=nb, seq_offsets=off[:nb + 1].copy(), num_targets=w_full["num_targets"][:nb],
+             total_tokens=e, timestamps=w_full["timestamps"][:e])
     for key in ("q", "k", "v", "dout"):
-        w[key] = np.ascontiguousarray(w_full[key][:e, :hs_])
-    pairs = per_head * hs_
+        w[key] = np.ascontiguousarray(w_full[key][:e])
     t0 = time.perf_counter()
     oracle.attn_fwd(w)
     oracle.attn_bwd(w)
     dt = time.perf_counter() - t0
     flops = pairs * 14 * d
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": min(oracle.num_threads(), nb * H), "threads_available": oracle.num_threads(),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"forward+backward of sequence 0 ({e} tokens) on heads 0..{hs_ - 1}: "
+            "sample": f"forward+backward of the first {nb} sequence(s) ({e} tokens), all {H} heads: "
                       f"{pairs} visible pairs of the same workload, fp64"}
 
 
@@ -193,6 +198,10 @@ def bench_headline(args, torch, hj, runner, w):
         plan_host_s.append(time.perf_counter() - t0)
 
     def launch(plan, record):
+        if record:
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+
         def fwd():
             hj.hstu_attn_fwd(plan, base_args, dev["q"], dev["k"], dev["v"], out)
 
@@ -208,6 +217,9 @@ def bench_headline(args, torch, hj, runner, w):
             timer.record("fwd", fwd)
             timer.record("bwd_dkdv", dkdv)
             timer.record("bwd_dq", dqp)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev1.record()
+            timer.marks.setdefault("step", []).append((ev0, ev1))
         else:
             fwd(); dkdv(); dqp()
 
@@ -220,17 +232,19 @@ def bench_headline(args, torch, hj, runner, w):
     t0 = time.perf_counter()
     # Every step builds its own plan on the host.  A step's plan is built, and uploaded through
     # the library's own stream, while the previous step's kernels run (as a data loader prepares
-    # the next batch).  A plan is destroyed after the next step is queued: its buffer goes back in
-    # the order of this (default) stream, after the kernels that read it.
+    # the next batch).  A plan is destroyed after the next step is queued, in the order of the
+    # stream its kernels run on (hstu_plan_destroy_on): its buffer goes back after them, and the
+    # host does not wait.
+    stream = torch.cuda.current_stream()
     plan, prev = build(), None
     for k in range(args.steps):
         launch(plan, True)
         nxt = build() if k + 1 < args.steps else None
         if prev is not None:
-            prev.close()
+            prev.close(stream)
         prev, plan = plan, nxt
     torch.cuda.synchronize()
-    prev.close()
+    prev.close(stream)
     wall = time.perf_counter() - t0
     assert torch.isfinite(out.float()).all() and torch.isfinite(dq.float()).all()
 
@@ -239,20 +253,71 @@ def bench_headline(args, torch, hj, runner, w):
     ms_step = wall * 1e3 / args.steps
     kern = {name: float(np.mean(timer.ms(name))) for name in ("fwd", "bwd_dkdv", "bwd_dq")}
     gpu_ms = sum(kern.values())
+    step_ms = timer.ms("step")
     return dict(info=info, pairs=pairs, flops=flops, ms_step=ms_step, kern=kern, gpu_ms=gpu_ms,
-                plan_ms=1e3 * float(np.median(plan_host_s)), tokens=T)
+                plan_ms=1e3 * float(np.median(plan_host_s)), tokens=T, step_ms=step_ms)
 
 
-def roofline(kern, pairs, d):
+def algorithmic_bytes(name, T, H, d, s=2):
+    """HBM bytes a kernel must move by the survey's definition: the forward reads q, k, v and
+    writes o (4 T H d s); the backward reads q, k, v, dO and writes dq, dk, dv (7 T H d s), split
+    between the passes as dK/dV: q, k, v, dO in, dk, dv out (6 T H d s) and dQ: k in, dq out
+    (2 T H d s).  The stored dS (2 bytes per visible pair, written by dK/dV and read by dQ) is not
+    algorithmic; it is reported as a separate overhead."""
+    return {"fwd": 4, "bwd_dkdv": 6, "bwd_dq": 2}[name] * T * H * d * s
+
+
+def roofline(kern, pairs, T, H, d, peaks=None):
     name = max(kern, key=kern.get)
     flops = pairs * FLOPS_PER_PAIR_D[name] * d
     achieved = flops / (kern[name] * 1e-3) / 1e12
     traffic = measured_traffic(name)
-    return {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
-            "algorithmic_flops_per_launch": flops,
-            "per_unit": f"{FLOPS_PER_PAIR_D[name]}*d flops per visible pair per head"}
+    alg = algorithmic_bytes(name, T, H, d)
+    ds_bytes = 2 * pairs if name in ("bwd_dkdv", "bwd_dq") else 0
+    r = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 2),
+         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+         "traffic": traffic,
+         "algorithmic_flops_per_launch": flops,
+         "per_unit": f"{FLOPS_PER_PAIR_D[name]}*d flops per visible pair per head",
+         "algorithmic_bytes": alg,
+         "stored_ds_overhead_bytes": ds_bytes,
+         "traffic_over_algorithmic": round(traffic / alg, 2) if traffic else None}
+    if peaks and peaks.get("bf16_gemm_tflops"):
+        r["frac_of_measured_gemm_peak"] = round(achieved / peaks["bf16_gemm_tflops"], 4)
+    return r
+
+
+def measure_peaks(torch):
+    """Attainable rates measured on this GPU in the same run: a 1 GiB device-to-device copy
+    (bytes read + written per second) and a bf16 8192^3 matrix product through torch (the
+    vendor BLAS), as empirical ceilings next to the published peaks."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    timer = Timer(torch)
+    for _ in range(3):
+        b.copy_(a)
+    for _ in range(10):
+        timer.record("copy", lambda: b.copy_(a))
+    torch.cuda.synchronize()
+    copy_ms = float(np.median(timer.ms("copy")))
+    del a, b
+    n = 8192
+    x = torch.randn((n, n), device="cuda:0").to(torch.bfloat16)
+    y = torch.randn((n, n), device="cuda:0").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y)
+    for _ in range(10):
+        timer.record("gemm", lambda: torch.matmul(x, y))
+    torch.cuda.synchronize()
+    gemm_ms = float(np.median(timer.ms("gemm")))
+    return {"copy_GBps": round(2 * (1 << 30) / copy_ms / 1e6, 1),
+            "bf16_gemm_tflops": round(2 * n ** 3 / gemm_ms / 1e9, 1),
+            "how": "1 GiB device copy (read + write bytes); torch.matmul bf16 8192^3; medians of 10"}
+
+
+def pctl(ms):
+    return {"median": round(float(np.median(ms)), 4), "p10": round(float(np.percentile(ms, 10)), 4),
+            "p90": round(float(np.percentile(ms, 90)), 4)}
 
 
 def bench_forward(torch, hj, runner, name, iters=20, cold=False):
@@ -275,7 +340,8 @@ def bench_forward(torch, hj, runner, name, iters=20, cold=False):
         out = runner.empty_like_thd(w, dev)
         call = lambda: hj.hstu_attn_fwd(plan, a, dev["q"], dev["k"], dev["v"], out)
         flops = info["visible_pairs"] * 4 * d
-        nbytes = T * H * d * 2 * 4 + (T * 8 if w.get("timestamps") is not None else 0)
+        esize = 4 if w["dtype"] == "fp32" else 2
+        nbytes = T * H * d * esize * 4 + (T * 8 if w.get("timestamps") is not None else 0)
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0") if cold else None
     for _ in range(5):
         call()
@@ -394,6 +460,152 @@ def bench_layer_bwd(torch, hj, runner, iters=20):
             "flops_counted": "dG, dW2, dW1, dX products and 10d per visible pair per head"}
 
 
+ONLY = ("long_fwdbwd", "tiny_fp32", "ranking_fwd", "longtail_fwd", "layer_fwd", "layer_bwd",
+        "cached_scoring", "stochastic_length")
+
+
+def profile_md(folder, out):
+    """Markdown summary of one profiled bench run (no GPU use).
+
+    `folder` holds the rocprofv3 outputs of one workload, each pass in its own subfolder as the
+    profile commands written into the summary produce them: trace/ (--kernel-trace --stats),
+    fetch/ and write/ (--pmc FETCH_SIZE, --pmc WRITE_SIZE), copyf/ and copyw/ (the same counters
+    on `bench.py --copy-calibration`), sq/ and sq2/ (issue counters), and bench.json, the JSON
+    line the traced run printed.  Missing passes are left out of the summary."""
+    import csv
+    import glob
+
+    def rows(sub, suffix):
+        paths = sorted(glob.glob(os.path.join(folder, sub, f"*{suffix}")))
+        return list(csv.DictReader(open(paths[0]))) if paths else []
+
+    def short(name):
+        return name.replace("hstu::(anonymous namespace)::", "").replace("(hstu::AttnParams)", "") \
+                   .replace("(hstu::GemmArgs)", "").replace("void ", "")
+
+    bench = {}
+    bj = os.path.join(folder, "bench.json")
+    if os.path.exists(bj):
+        lines = [x for x in open(bj) if x.startswith("{")]
+        bench = json.loads(lines[-1]) if lines else {}
+    only = bench.get("only", HEADLINE)
+    flags = f"--only {only} --steps 5 --warmup 2"
+    L = [f"# Kernel profile: {only}", ""]
+    if bench.get("config"):
+        L += [f"Workload: {bench['config'].get('workload', '')}", ""]
+    L += ["Commands (from the repository root on the GPU host; R = the repository root):", "", "```",
+          "cd /tmp && export TMPDIR=/tmp",
+          f"rocprofv3 --kernel-trace --stats -f csv -d P/trace -o trace -- python3 $R/bench.py {flags} > P/bench.json",
+          f"rocprofv3 --pmc FETCH_SIZE -f csv -d P/fetch -o fetch -- python3 $R/bench.py {flags}",
+          f"rocprofv3 --pmc WRITE_SIZE -f csv -d P/write -o write -- python3 $R/bench.py {flags}",
+          "rocprofv3 --pmc FETCH_SIZE -f csv -d P/copyf -o copyf -- python3 $R/bench.py --copy-calibration",
+          "rocprofv3 --pmc WRITE_SIZE -f csv -d P/copyw -o copyw -- python3 $R/bench.py --copy-calibration",
+          f"rocprofv3 --pmc {' '.join(SQ1)} -f csv -d P/sq -o sq -- python3 $R/bench.py {flags}",
+          f"rocprofv3 --pmc {' '.join(SQ2)} -f csv -d P/sq2 -o sq2 -- python3 $R/bench.py {flags}",
+          "python3 $R/bench.py --profile-md P profiles/<this file>",
+          "```", ""]
+    trace = rows("trace", "_kernel_trace.csv")
+    per = {}
+    for r in trace:
+        per.setdefault(r["Kernel_Name"], []).append(r)
+    order = sorted(per, key=lambda k: -sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in per[k]))
+    if trace:
+        total = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace)
+        L += ["## Kernel trace", "",
+              "| kernel | dispatches | average (us) | min (us) | max (us) | share | VGPR | AGPR | SGPR | LDS (B) | scratch (B/lane) |",
+              "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for k in order[:12]:
+            ds = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in per[k]]
+            r0 = per[k][0]
+            L.append(f"| `{short(k)[:100]}` | {len(ds)} | {np.mean(ds) / 1e3:.1f} | {min(ds) / 1e3:.1f} | "
+                     f"{max(ds) / 1e3:.1f} | {100 * sum(ds) / total:.1f}% | {r0['VGPR_Count']} | "
+                     f"{r0['Accum_VGPR_Count']} | {r0['SGPR_Count']} | {r0['LDS_Block_Size']} | {r0['Scratch_Size']} |")
+        L.append("")
+    if bench:
+        keep = {k: bench[k] for k in ("kernel_ms", "ms_per_step", "value", "roofline", "warm", "cold")
+                if k in bench}
+        L += ["Live HIP-event figures printed by the same traced run:", "", "```",
+              json.dumps(keep, indent=1)[:3000], "```", ""]
+
+    def counters(sub):
+        out = {}
+        for r in rows(sub, "_counter_collection.csv"):
+            out.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    fetch, write = counters("fetch"), counters("write")
+    copyf, copyw = counters("copyf"), counters("copyw")
+    if fetch and write and copyf and copyw:
+        def scale(c, name):
+            v = [x for k, d in c.items() if "copyBuffer" in k for x in d.get(name, [])]
+            return (1 << 30) / (1024.0 * float(np.median(v)))
+        fs, ws = scale(copyf, "FETCH_SIZE"), scale(copyw, "WRITE_SIZE")
+        L += ["## HBM traffic per dispatch", "",
+              f"FETCH_SIZE and WRITE_SIZE (KiB) scaled by a 1 GiB device copy profiled the same way: "
+              f"{1024 * fs:.0f} bytes per KiB read, {1024 * ws:.0f} per KiB written.", "",
+              "| kernel | dispatches | HBM read (MB) | HBM write (MB) |", "|---|---|---|---|"]
+        for k in order[:8]:
+            if k in fetch and k in write:
+                L.append(f"| `{short(k)[:100]}` | {len(fetch[k]['FETCH_SIZE'])} | "
+                         f"{1024 * fs * np.mean(fetch[k]['FETCH_SIZE']) / 1e6:.2f} | "
+                         f"{1024 * ws * np.mean(write[k]['WRITE_SIZE']) / 1e6:.2f} |")
+        L.append("")
+    sq = counters("sq")
+    for k, d in counters("sq2").items():
+        sq.setdefault(k, {}).update(d)
+    if sq:
+        names = [k for k in order[:4] if k in sq]
+        L += ["## Issue counters per dispatch", "",
+              "| counter | " + " | ".join(f"`{short(k)[:40]}`" for k in names) + " |",
+              "|---|" + "---|" * len(names)]
+        for c in SQ1 + SQ2:
+            L.append(f"| {c} | " + " | ".join(f"{np.mean(sq[k].get(c, [0])):.3g}" for k in names) + " |")
+        def ratio(k, a, b):
+            x, y = np.mean(sq[k].get(a, [0])), np.mean(sq[k].get(b, [0]))
+            return f"{x / y:.2f}" if y else "-"
+        for a, b in (("SQ_INSTS_VALU", "SQ_INSTS_MFMA"), ("SQ_INSTS_SALU", "SQ_INSTS_MFMA"),
+                     ("SQ_INSTS_LDS", "SQ_INSTS_MFMA"), ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES")):
+            L.append(f"| {a} / {b} | " + " | ".join(ratio(k, a, b) for k in names) + " |")
+        L.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(L) + "\n")
+    print(out)
+
+
+SQ1 = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+       "SQ_INSTS_LDS", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT"]
+SQ2 = ["SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_INST_LEVEL_VMEM", "SQ_ACTIVE_INST_VALU",
+       "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU", "SQ_BUSY_CU_CYCLES"]
+
+
+def run_only(args, torch, hj, runner, hs):
+    """One workload alone (for profiling it on its own): prints its figures as one JSON line."""
+    name = args.only
+    if name == "long_fwdbwd":
+        w = hs.make_workload(HEADLINE)
+        r = bench_headline(args, torch, hj, runner, w)
+        res = {"kernel_ms": {k: round(v, 4) for k, v in r["kern"].items()},
+               "ms_per_step": round(r["ms_step"], 4),
+               "value": round(r["flops"] / (r["ms_step"] * 1e-3) / 1e12, 2),
+               "step_event_ms": pctl(r["step_ms"]),
+               "roofline": roofline(r["kern"], r["pairs"], w["total_tokens"], w["heads"], w["d"]),
+               "config": {"workload": describe(w)}}
+    elif name == "layer_bwd":
+        res = bench_layer_bwd(torch, hj, runner, iters=args.steps)
+    elif name == "cached_scoring":
+        res = bench_cached(torch, hj, runner, iters=args.steps)
+    elif name == "stochastic_length":
+        res = bench_select(torch, hj, iters=args.steps)
+    else:
+        res = {"warm": bench_forward(torch, hj, runner, name, iters=args.steps)}
+        if args.cold:
+            res["cold"] = bench_forward(torch, hj, runner, name, iters=args.steps, cold=True)
+        w = hs.make_workload(name)
+        res["config"] = {"workload": describe(w)}
+    res["only"] = name
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,15 +613,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--only", choices=ONLY,
+                    help="run one workload alone (its figures only; for profiling it on its own)")
+    ap.add_argument("--cold", action="store_true", help="with --only: also time cold-cache calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                          "COPY_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE / WRITE_SIZE counter files into the per-kernel "
                          "HBM traffic record (no GPU use)")
+    ap.add_argument("--profile-md", nargs=2, metavar=("FOLDER", "OUT"),
+                    help="summarize the rocprofv3 outputs of one profiled workload as markdown "
+                         "(no GPU use)")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.profile_md:
+        profile_md(*args.profile_md)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only; this implementation has no multi-GPU path "
@@ -431,12 +652,17 @@ def main():
     import hstu_synth as hs
     from hstu_jagged_pointwise_amd import runner
     hj.load_library()
+    if args.only:
+        run_only(args, torch, hj, runner, hs)
+        return
 
     w = hs.make_workload(HEADLINE)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     r = bench_headline(args, torch, hj, runner, w)
-    d = w["d"]
+    peaks = None if args.no_extra else measure_peaks(torch)
+    T, H, d = w["total_tokens"], w["heads"], w["d"]
     value = r["flops"] / (r["ms_step"] * 1e-3) / 1e12
+    step = pctl(r["step_ms"])
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -455,17 +681,27 @@ def main():
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(r["tokens"] / (r["ms_step"] * 1e-3), 1),
+        # GPU time of each step (HIP events around its three launches); the wall-clock
+        # ms_per_step above also holds the gaps between steps
+        "step_event_ms": step,
+        "step_event_tflops": {k: round(r["flops"] / (v * 1e-3) / 1e12, 2) for k, v in step.items()},
         "visible_pairs": r["pairs"],
         "flops_per_step": r["flops"],
+        "bytes_per_step": {"forward": algorithmic_bytes("fwd", T, H, d),
+                           "backward": 7 * T * H * d * 2,
+                           "stored_ds_overhead": 2 * 2 * r["pairs"]},
         "kernel_ms": {k: round(v, 4) for k, v in r["kern"].items()},
         "kernel_sum_ms": round(r["gpu_ms"], 4),
         "kernel_only_tflops": round(r["flops"] / (r["gpu_ms"] * 1e-3) / 1e12, 2),
         "plan_host_ms": round(r["plan_ms"], 4),
-        "roofline": roofline(r["kern"], r["pairs"], d),
+        "roofline": roofline(r["kern"], r["pairs"], T, H, d, peaks),
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
+    if peaks:
+        result["pct_of_measured_gemm_peak"] = round(100 * value / peaks["bf16_gemm_tflops"], 2)
     if not args.no_extra:
-        extra = {}
+        extra = {"tiny_fp32": {"warm": bench_forward(torch, hj, runner, "tiny_fp32")}}
         for name in ("ranking_fwd", "longtail_fwd", "layer_fwd"):
             extra[name] = {"warm": bench_forward(torch, hj, runner, name)}
         extra["longtail_fwd"]["cold"] = bench_forward(torch, hj, runner, "longtail_fwd", cold=True)

@@ -50,10 +50,13 @@ class HstuPlanInfo(ctypes.Structure):
         ("bwd_key_block", ctypes.c_int64),
         ("fwd_items", ctypes.c_int64),
         ("fwd_split_blocks", ctypes.c_int64),
+        ("bwd_stored_ds", ctypes.c_int64),
+        ("bwd_ds_bytes", ctypes.c_int64),
     ]
 
 
-EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_info",
+EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_destroy_on",
+           "hstu_plan_info",
            "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_bwd",
            "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd", "hstu_layer_bwd",
            "hstu_plan_create_cached", "hstu_attn_fwd_cached", "hstu_jagged_select"]
@@ -77,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_plan_create.restype = I32
     lib.hstu_plan_destroy.argtypes = [P]
     lib.hstu_plan_destroy.restype = None
+    lib.hstu_plan_destroy_on.argtypes = [P, P]
+    lib.hstu_plan_destroy_on.restype = None
     lib.hstu_plan_info.argtypes = [P, ctypes.POINTER(HstuPlanInfo)]
     lib.hstu_plan_info.restype = I32
     lib.hstu_plan_units.argtypes = [P, I32, P, I64, ctypes.POINTER(I64)]
@@ -150,15 +155,21 @@ def make_args(*, dtype: int, batch: int, num_heads: int, head_dim: int, total_to
 
 
 class Plan:
-    """Owns a hstu_plan_t*; freed with hstu_plan_destroy."""
+    """Owns a hstu_plan_t*.  close() (or garbage collection) frees it with hstu_plan_destroy, which
+    waits for the device; close(stream) frees it in the order of that stream instead
+    (hstu_plan_destroy_on), after the calls already queued there."""
 
     def __init__(self, handle: int, args: HstuAttnArgs):
         self.handle = handle
         self.args = args
 
-    def close(self) -> None:
+    def close(self, stream=None) -> None:
         if self.handle:
-            load_library().hstu_plan_destroy(ctypes.c_void_p(self.handle))
+            lib = load_library()
+            if stream is None:
+                lib.hstu_plan_destroy(ctypes.c_void_p(self.handle))
+            else:
+                lib.hstu_plan_destroy_on(ctypes.c_void_p(self.handle), _stream(stream))
             self.handle = 0
 
     def __del__(self):
@@ -196,6 +207,16 @@ def hstu_plan_destroy(plan: Plan) -> None:
     plan.close()
 
 
+def hstu_plan_destroy_on(plan: Plan, stream=None) -> None:
+    """Frees the plan in the order of `stream` (torch's current stream when None)."""
+    plan.close(torch_current_stream() if stream is None else stream)
+
+
+def torch_current_stream():
+    import torch
+    return torch.cuda.current_stream()
+
+
 def hstu_plan_info(plan: Plan) -> dict:
     info = HstuPlanInfo()
     _check(load_library().hstu_plan_info(ctypes.c_void_p(plan.handle), ctypes.byref(info)))
@@ -219,17 +240,29 @@ def hstu_workspace_bytes(plan: Plan, op: int, d_model: int = 0) -> int:
                                                    int(d_model)))
 
 
-def _workspace(plan: Plan, op: int, d_model: int, ws, device):
+def _workspace(plan: Plan, op: int, d_model: int, ws, device, stream=None):
+    """The caller's workspace, or a temporary one from torch's allocator.  A temporary is
+    allocated on torch's current stream; when the call is queued on another stream it is marked
+    as used there, so torch does not hand the memory out again before that stream's work ends."""
     need = hstu_workspace_bytes(plan, op, d_model)
     if ws is None and need > 0:
         import torch
         ws = torch.empty(need, dtype=torch.uint8, device=device)
+        if stream is not None:
+            ws.record_stream(_torch_stream(stream, device))
     return ws, (ws.numel() * ws.element_size() if ws is not None else 0)
+
+
+def _torch_stream(stream, device):
+    import torch
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def hstu_attn_fwd(plan: Plan, args: HstuAttnArgs, q, k, v, out, u=None, ln_eps: float = 1e-5,
                   ws=None, stream=None) -> None:
-    ws, nbytes = _workspace(plan, OP_FWD_GATED if u is not None else OP_FWD, 0, ws, q.device)
+    ws, nbytes = _workspace(plan, OP_FWD_GATED if u is not None else OP_FWD, 0, ws, q.device, stream)
     _check(load_library().hstu_attn_fwd(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(u),
         float(ln_eps), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
@@ -237,7 +270,7 @@ def hstu_attn_fwd(plan: Plan, args: HstuAttnArgs, q, k, v, out, u=None, ln_eps: 
 
 def hstu_attn_bwd(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, dk, dv, drab_pos=None,
                   drab_ts=None, ws=None, stream=None) -> None:
-    ws, nbytes = _workspace(plan, OP_BWD, 0, ws, q.device)
+    ws, nbytes = _workspace(plan, OP_BWD, 0, ws, q.device, stream)
     _check(load_library().hstu_attn_bwd(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drab_pos), _ptr(drab_ts), _ptr(ws), nbytes,
@@ -266,7 +299,7 @@ def hstu_attn_bwd_dq(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, drab_pos
 
 def hstu_layer_fwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, y,
                    ln_eps: float = 1e-5, ws=None, stream=None) -> None:
-    ws, nbytes = _workspace(plan, OP_LAYER, d_model, ws, x.device)
+    ws, nbytes = _workspace(plan, OP_LAYER, d_model, ws, x.device, stream)
     _check(load_library().hstu_layer_fwd(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), int(d_model), _ptr(x), _ptr(w1),
         _ptr(w2), float(ln_eps), _ptr(y), _ptr(ws), nbytes, _stream(stream)))
@@ -275,7 +308,7 @@ def hstu_layer_fwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, y,
 def hstu_layer_bwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, dy, dx, dw1, dw2,
                    drab_pos=None, drab_ts=None, ln_eps: float = 1e-5, ws=None,
                    stream=None) -> None:
-    ws, nbytes = _workspace(plan, OP_LAYER_BWD, d_model, ws, x.device)
+    ws, nbytes = _workspace(plan, OP_LAYER_BWD, d_model, ws, x.device, stream)
     _check(load_library().hstu_layer_bwd(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), int(d_model), _ptr(x), _ptr(w1),
         _ptr(w2), _ptr(dy), float(ln_eps), _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(drab_pos),
@@ -284,7 +317,7 @@ def hstu_layer_bwd(plan: Plan, args: HstuAttnArgs, d_model: int, x, w1, w2, dy, 
 
 def hstu_attn_fwd_cached(plan: Plan, args: HstuAttnArgs, q, k, v, k_cache, v_cache,
                          cache_timestamps, out, ws=None, stream=None) -> None:
-    ws, nbytes = _workspace(plan, OP_CACHED, 0, ws, q.device)
+    ws, nbytes = _workspace(plan, OP_CACHED, 0, ws, q.device, stream)
     _check(load_library().hstu_attn_fwd_cached(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v),
         _ptr(k_cache), _ptr(v_cache), _ptr(cache_timestamps), _ptr(out), _ptr(ws), nbytes,

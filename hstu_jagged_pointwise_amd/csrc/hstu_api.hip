@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <utility>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
@@ -134,25 +135,35 @@ void order_for_xcds(std::vector<Item>& items) {
     std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
         return a.cost > b.cost;
     });
-    // groups in order of their longest item
-    std::vector<std::vector<Item>> groups;
-    std::vector<std::pair<int64_t, int>> index;  // (key, group) for lookup
-    for (const Item& it : items) {
-        const int64_t key = (int64_t(it.seq) << 20) | it.head;
-        auto found = std::lower_bound(index.begin(), index.end(), std::make_pair(key, -1));
-        if (found != index.end() && found->first == key) {
-            groups[found->second].push_back(it);
-        } else {
-            index.insert(found, std::make_pair(key, (int)groups.size()));
-            groups.push_back({it});
-        }
+    // groups: runs of a stable sort by (sequence, head) of the positions in cost order, so each
+    // group keeps its members longest first and starts at its longest item's position
+    const size_t n = items.size();
+    std::vector<size_t> pos(n);
+    for (size_t i = 0; i < n; ++i) pos[i] = i;
+    std::stable_sort(pos.begin(), pos.end(), [&](size_t a, size_t b) {
+        const Item& x = items[a];
+        const Item& y = items[b];
+        return x.seq != y.seq ? x.seq < y.seq : x.head < y.head;
+    });
+    std::vector<std::pair<size_t, size_t>> runs;  // [begin, end) in pos
+    for (size_t i = 0; i < n;) {
+        size_t e = i + 1;
+        while (e < n && items[pos[e]].seq == items[pos[i]].seq && items[pos[e]].head == items[pos[i]].head)
+            ++e;
+        runs.emplace_back(i, e);
+        i = e;
     }
+    // groups in order of their longest item
+    std::sort(runs.begin(), runs.end(), [&](const std::pair<size_t, size_t>& a,
+                                            const std::pair<size_t, size_t>& b) {
+        return pos[a.first] < pos[b.first];
+    });
     std::vector<std::vector<Item>> queues(kXcds);
-    for (const auto& grp : groups) {
+    for (const auto& run : runs) {
         int best = 0;
         for (int r = 1; r < kXcds; ++r)
             if (queues[r].size() < queues[best].size()) best = r;
-        queues[best].insert(queues[best].end(), grp.begin(), grp.end());
+        for (size_t i = run.first; i < run.second; ++i) queues[best].push_back(items[pos[i]]);
     }
     items.clear();
     for (size_t k = 0;; ++k) {
@@ -210,13 +221,31 @@ hipStream_t upload_stream(int device) {
     return streams[device];
 }
 
-// Pool memory goes back in the order of the default stream (after the work queued there and on
-// the streams that synchronize with it); hipMalloc memory with hipFree, which waits for the device.
-void release_device_lists(hstu_plan_t* plan) {
+// Returns the plan's device buffer: pool memory in the order of `stream` (after the work queued
+// there), hipMalloc memory with hipFree, which waits for the device.
+void release_device_lists(hstu_plan_t* plan, hipStream_t stream) {
     if (!plan->dbuf) return;
-    if (plan->pooled) (void)hipFreeAsync(plan->dbuf, nullptr);
+    if (plan->pooled) (void)hipFreeAsync(plan->dbuf, stream);
     else (void)hipFree(plan->dbuf);
     plan->dbuf = nullptr;
+}
+
+// HSTU_DEBUG_SYNC=1 in the environment: every kernel launch of the entry points is followed by a
+// synchronisation of its stream and an error check, so a fault is reported by the call that
+// caused it (as HSTU_ERR_HIP) instead of at a later synchronisation.
+bool debug_sync() {
+    static const bool on = [] {
+        const char* v = std::getenv("HSTU_DEBUG_SYNC");
+        return v && v[0] && !(v[0] == '0' && v[1] == 0);
+    }();
+    return on;
+}
+
+hipError_t checked(hipError_t e, hipStream_t s) {
+    if (e != hipSuccess || !debug_sync()) return e;
+    e = hipStreamSynchronize(s);
+    const hipError_t last = hipGetLastError();
+    return e != hipSuccess ? e : last;
 }
 
 size_t part_bytes(const hstu_plan_t* plan) {
@@ -333,7 +362,7 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
         }
         if (hipMemcpyAsync(plan->dbuf, host.data(), total, hipMemcpyHostToDevice, up) != hipSuccess ||
             hipStreamSynchronize(up) != hipSuccess) {
-            release_device_lists(plan);
+            release_device_lists(plan, up);
             delete plan;
             return HSTU_ERR_HIP;
         }
@@ -432,7 +461,21 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
 
 void hstu_plan_destroy(hstu_plan_t* plan) {
     if (!plan) return;
-    release_device_lists(plan);
+    if (plan->dbuf) {
+        // wait for every stream of the plan's device, then free
+        int cur = -1;
+        const bool other = hipGetDevice(&cur) == hipSuccess && cur != plan->device;
+        if (other) (void)hipSetDevice(plan->device);
+        (void)hipDeviceSynchronize();
+        release_device_lists(plan, nullptr);
+        if (other) (void)hipSetDevice(cur);
+    }
+    delete plan;
+}
+
+void hstu_plan_destroy_on(hstu_plan_t* plan, void* stream) {
+    if (!plan) return;
+    release_device_lists(plan, static_cast<hipStream_t>(stream));
     delete plan;
 }
 
@@ -465,6 +508,8 @@ hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info) {
     info->fwd_items = plan->shape.dtype == HSTU_BF16 ? (int64_t)plan->items.size()
                                                      : (int64_t)plan->fwd.size();
     info->fwd_split_blocks = (int64_t)plan->fix.size();
+    info->bwd_stored_ds = plan->ds_elems > 0 ? 1 : 0;
+    info->bwd_ds_bytes = (int64_t)ds_bytes(plan);
     return HSTU_OK;
 }
 
@@ -546,15 +591,15 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
     // partial slots follow the gated path's attention buffer in ws
     const size_t gated_bytes = u ? align_up(size_t(args->total_tokens) * p.ld_out * elem_size(args->dtype), 256) : 0;
     p.part = plan->parts ? reinterpret_cast<float*>(static_cast<char*>(ws) + gated_bytes) : nullptr;
-    hipError_t e = args->dtype == HSTU_BF16 ? hstu::launch_attn_fwd_bf16(p, s)
-                                            : hstu::launch_attn_fwd_f32(p, s);
+    hipError_t e = args->dtype == HSTU_BF16 ? checked(hstu::launch_attn_fwd_bf16(p, s), s)
+                                            : checked(hstu::launch_attn_fwd_f32(p, s), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     if (u) {
         int64_t ldu = args->qkv_token_stride ? args->qkv_token_stride : p.ld_out;
         int32_t width = (int32_t)p.ld_out;
         e = args->dtype == HSTU_BF16
-                ? hstu::launch_ln_gate_bf16(ws, u, ldu, out, args->total_tokens, width, ln_eps, s)
-                : hstu::launch_ln_gate_f32(ws, u, ldu, out, args->total_tokens, width, ln_eps, s);
+                ? checked(hstu::launch_ln_gate_bf16(ws, u, ldu, out, args->total_tokens, width, ln_eps, s), s)
+                : checked(hstu::launch_ln_gate_f32(ws, u, ldu, out, args->total_tokens, width, ln_eps, s), s);
     }
     return hip_status(e);
 }
@@ -586,10 +631,6 @@ hstu_status_t bwd_params(const hstu_plan_t* plan, const hstu_attn_args_t* args, 
     return HSTU_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
 // The stored-dS workspace of a backward call: NULL when the plan has none or the caller passed
 // none (the dQ pass then recomputes S and dP).
 hstu_status_t ds_workspace(const hstu_plan_t* plan, void* ws, size_t ws_bytes, void** ds) {
@@ -601,6 +642,10 @@ hstu_status_t ds_workspace(const hstu_plan_t* plan, void* ws, size_t ws_bytes, v
     *ds = ws;
     return HSTU_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                                  const void* q, const void* k, const void* v, const void* dout,
@@ -622,10 +667,10 @@ hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t
         const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
         p.gpos = args->rab_pos ? grads : nullptr;
         p.gts = args->rab_ts ? grads + nb : nullptr;
-        if (hstu::launch_zero_f32(grads, 2 * nb, s) != hipSuccess) return HSTU_ERR_HIP;
+        if (checked(hstu::launch_zero_f32(grads, 2 * nb, s), s) != hipSuccess) return HSTU_ERR_HIP;
     }
-    return hip_status(args->dtype == HSTU_BF16 ? hstu::launch_attn_bwd_dkdv_bf16(p, s)
-                                               : hstu::launch_attn_bwd_dkdv_f32(p, s));
+    return hip_status(args->dtype == HSTU_BF16 ? checked(hstu::launch_attn_bwd_dkdv_bf16(p, s), s)
+                                               : checked(hstu::launch_attn_bwd_dkdv_f32(p, s), s));
 }
 
 hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* args,
@@ -656,13 +701,13 @@ hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* 
         if (e == hipSuccess && p.drab_ts)
             e = hipMemcpyAsync(p.drab_ts, grads + nb, nb * 4, hipMemcpyDeviceToDevice, s);
     } else {
-        if (p.drab_pos) e = hstu::launch_zero_f32(p.drab_pos, nb, s);
-        if (e == hipSuccess && p.drab_ts) e = hstu::launch_zero_f32(p.drab_ts, nb, s);
+        if (p.drab_pos) e = checked(hstu::launch_zero_f32(p.drab_pos, nb, s), s);
+        if (e == hipSuccess && p.drab_ts) e = checked(hstu::launch_zero_f32(p.drab_ts, nb, s), s);
     }
     if (e != hipSuccess) return HSTU_ERR_HIP;
     if (args->total_tokens == 0) return HSTU_OK;
-    return hip_status(args->dtype == HSTU_BF16 ? hstu::launch_attn_bwd_dq_bf16(p, s)
-                                               : hstu::launch_attn_bwd_dq_f32(p, s));
+    return hip_status(args->dtype == HSTU_BF16 ? checked(hstu::launch_attn_bwd_dq_bf16(p, s), s)
+                                               : checked(hstu::launch_attn_bwd_dq_f32(p, s), s));
 }
 
 hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args, const void* q,
@@ -749,8 +794,8 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     char* z = static_cast<char*>(ws);
     char* a = z + align_up(size_t(T) * 4 * hd * 2, 256);
     // Z = SiLU(X W1): columns [U | V | Q | K]
-    hipError_t e = hstu::launch_gemm(
-        gemm_args(plan, x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z, 4 * hd, hstu::kEpiSilu), s);
+    hipError_t e = checked(hstu::launch_gemm(
+        gemm_args(plan, x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z, 4 * hd, hstu::kEpiSilu), s), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     hstu::AttnParams p = base_params(plan, args);
     const int64_t ldz = 4 * int64_t(hd);
@@ -760,17 +805,17 @@ hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     p.q = z + size_t(2 * hd) * 2;
     p.k = z + size_t(3 * hd) * 2;
     p.out = a;
-    e = hstu::launch_attn_fwd_bf16(p, s);
+    e = checked(hstu::launch_attn_fwd_bf16(p, s), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     // G = LayerNorm(A) * U, in place over A
-    e = hstu::launch_ln_gate_bf16(a, z, ldz, a, T, hd, ln_eps, s);
+    e = checked(hstu::launch_ln_gate_bf16(a, z, ldz, a, T, hd, ln_eps, s), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     // Y = G W2 + X
     hstu::GemmArgs g = gemm_args(plan, a, hd, false, w2, d_model, false, T, d_model, hd, y, d_model,
                                  hstu::kEpiResidual);
     g.r = x;
     g.ldr = d_model;
-    return hip_status(hstu::launch_gemm(g, s));
+    return hip_status(checked(hstu::launch_gemm(g, s), s));
 }
 
 hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
@@ -797,7 +842,7 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
     float* const outs[4] = {dw1, dw2, drab_pos, drab_ts};
     const int64_t counts[4] = {int64_t(d_model) * 4 * hd, int64_t(hd) * d_model, nb, nb};
-    hipError_t e = hstu::launch_zero_f32_list(outs, counts, 4, s);
+    hipError_t e = checked(hstu::launch_zero_f32_list(outs, counts, 4, s), s);
     if (e != hipSuccess) return HSTU_ERR_HIP;
     if (T == 0) return HSTU_OK;
     const size_t wide = align_up(size_t(T) * 4 * hd * 2, 256), narrow = align_up(size_t(T) * hd * 2, 256);
@@ -817,7 +862,7 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     hstu::GemmArgs ga = gemm_args(plan, x, d_model, false, w1, 4 * hd, false, T, 4 * hd, d_model, z,
                                   ldz, hstu::kEpiSilu);
     ga.c2 = hpre;
-    e = hstu::launch_gemm(ga, s);
+    e = checked(hstu::launch_gemm(ga, s), s);
     // recompute A = attention(Q, K, V)
     hstu::AttnParams p = base_params(plan, args);
     p.ld_in = ldz;
@@ -828,20 +873,20 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
     p.k = z + size_t(3 * hd) * 2;
     p.out = a;
     p.part = plan->parts ? part : nullptr;
-    if (e == hipSuccess) e = hstu::launch_attn_fwd_bf16(p, s);
+    if (e == hipSuccess) e = checked(hstu::launch_attn_fwd_bf16(p, s), s);
     // dG = dY W2^T (fp32)
     if (e == hipSuccess)
-        e = hstu::launch_gemm(gemm_args(plan, dy, d_model, false, w2, d_model, true, T, hd, d_model, dg,
-                                        hd, hstu::kEpiStoreF32), s);
+        e = checked(hstu::launch_gemm(gemm_args(plan, dy, d_model, false, w2, d_model, true, T, hd, d_model, dg,
+                                        hd, hstu::kEpiStoreF32), s), s);
     // G, dA and the U-slot gradient of H
     if (e == hipSuccess)
-        e = hstu::launch_ln_gate_bwd_bf16(a, z, hpre, ldz, dg, g, da, dh, ldz, T, hd, ln_eps, s);
+        e = checked(hstu::launch_ln_gate_bwd_bf16(a, z, hpre, ldz, dg, g, da, dh, ldz, T, hd, ln_eps, s), s);
     // dW2 = G^T dY, split over tokens
     if (e == hipSuccess) {
         hstu::GemmArgs gw = gemm_args(plan, g, hd, true, dy, d_model, false, hd, d_model, T, dw2,
                                       d_model, hstu::kEpiAtomicF32);
         gw.kchunk = token_chunk(plan, T, hd, d_model);
-        e = hstu::launch_gemm(gw, s);
+        e = checked(hstu::launch_gemm(gw, s), s);
     }
     // attention backward with dout = dA: dV, dQ, dK into their slots of dH
     if (e == hipSuccess) {
@@ -857,24 +902,24 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
             p.gpos = drab_pos;
             p.gts = drab_ts;
         }
-        e = hstu::launch_attn_bwd_dkdv_bf16(p, s);
+        e = checked(hstu::launch_attn_bwd_dkdv_bf16(p, s), s);
     }
     if (e == hipSuccess) {
         p.units = plan->d_fwd;
         p.num_units = (int32_t)plan->fwd.size();
         p.drab_pos = drab_pos;
         p.drab_ts = drab_ts;
-        e = hstu::launch_attn_bwd_dq_bf16(p, s);
+        e = checked(hstu::launch_attn_bwd_dq_bf16(p, s), s);
     }
     // dH = dZ * SiLU'(H) on the V, Q, K slots (the U slot is already done)
     if (e == hipSuccess)
-        e = hstu::launch_silu_bwd_bf16(dh + size_t(hd) * 2, hpre + size_t(hd) * 2, ldz, T, 3 * hd, s);
+        e = checked(hstu::launch_silu_bwd_bf16(dh + size_t(hd) * 2, hpre + size_t(hd) * 2, ldz, T, 3 * hd, s), s);
     // dW1 = X^T dH, split over tokens
     if (e == hipSuccess) {
         hstu::GemmArgs gw = gemm_args(plan, x, d_model, true, dh, ldz, false, d_model, 4 * hd, T, dw1,
                                       ldz, hstu::kEpiAtomicF32);
         gw.kchunk = token_chunk(plan, T, d_model, 4 * hd);
-        e = hstu::launch_gemm(gw, s);
+        e = checked(hstu::launch_gemm(gw, s), s);
     }
     // dX = dH W1^T + dY
     if (e == hipSuccess) {
@@ -882,7 +927,7 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
                                       hstu::kEpiResidual);
         gx.r = dy;
         gx.ldr = d_model;
-        e = hstu::launch_gemm(gx, s);
+        e = checked(hstu::launch_gemm(gx, s), s);
     }
     return hip_status(e);
 }
@@ -973,7 +1018,8 @@ hstu_status_t hstu_attn_fwd_cached(const hstu_plan_t* plan, const hstu_attn_args
     p.vc = v_cache;
     p.ts_cache = args->rab_ts ? cache_timestamps : nullptr;
     p.ld_cache = int64_t(args->num_heads) * args->head_dim;
-    return hip_status(hstu::launch_attn_fwd_bf16(p, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(checked(hstu::launch_attn_fwd_bf16(p, s), s));
 }
 
 hstu_status_t hstu_jagged_select(int32_t batch, const int64_t* src_offsets, int64_t src_rows,
@@ -988,9 +1034,10 @@ hstu_status_t hstu_jagged_select(int32_t batch, const int64_t* src_offsets, int6
     for (const void* ptr : {(const void*)src_offsets, (const void*)dst_offsets,
                             (const void*)keep_start, src, (const void*)dst})
         if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 7) != 0) return HSTU_ERR_MISALIGNED;
-    return hip_status(hstu::launch_jagged_select(batch, src_offsets, src_rows, dst_offsets, dst_rows,
-                                                 keep_start, row_bytes, src, dst,
-                                                 static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return hip_status(checked(hstu::launch_jagged_select(batch, src_offsets, src_rows, dst_offsets,
+                                                         dst_rows, keep_start, row_bytes, src, dst, s),
+                              s));
 }
 
 }  // extern "C"

@@ -46,6 +46,14 @@ def plan_for(batch: dict, args, flags: int = 0):
     return hstu_plan_create(args, batch["seq_offsets"], batch.get("num_targets"), flags)
 
 
+def _release(plan, own: bool, stream) -> None:
+    """A plan made for one call is freed in the order of the call's stream (after its kernels),
+    without waiting on the host."""
+    if own:
+        import torch
+        plan.close(torch.cuda.current_stream() if stream is None else stream)
+
+
 def empty_like_thd(batch: dict, dev: dict):
     import torch
     T, H, d = batch["total_tokens"], batch["heads"], batch["d"]
@@ -63,10 +71,12 @@ def dev_device(dev: dict):
 def attn_fwd(batch: dict, dev: dict, plan=None, args=None, u=None, ln_eps: float = 1e-5,
              out=None, stream=None):
     args = args_for(batch, dev) if args is None else args
-    plan = plan_for(batch, args) if plan is None else plan
+    own = plan is None
+    plan = plan_for(batch, args) if own else plan
     out = empty_like_thd(batch, dev) if out is None else out
     hstu_attn_fwd(plan, args, dev["q"], dev["k"], dev["v"], out, u=u, ln_eps=ln_eps,
                   stream=stream)
+    _release(plan, own, stream)
     return out
 
 
@@ -76,7 +86,8 @@ def attn_bwd(batch: dict, dev: dict, plan=None, args=None, stream=None, split: b
     hstu_attn_bwd_dkdv and hstu_attn_bwd_dq, which recompute S and dP in the dQ pass."""
     import torch
     args = args_for(batch, dev) if args is None else args
-    plan = plan_for(batch, args) if plan is None else plan
+    own = plan is None
+    plan = plan_for(batch, args) if own else plan
     g = dict(dq=empty_like_thd(batch, dev), dk=empty_like_thd(batch, dev),
              dv=empty_like_thd(batch, dev), drab_pos=None, drab_ts=None)
     H = batch["heads"]
@@ -92,6 +103,7 @@ def attn_bwd(batch: dict, dev: dict, plan=None, args=None, stream=None, split: b
     else:
         hstu_attn_bwd(plan, args, dev["q"], dev["k"], dev["v"], dev["dout"], g["dq"], g["dk"],
                       g["dv"], g["drab_pos"], g["drab_ts"], ws=ws, stream=stream)
+    _release(plan, own, stream)
     return g
 
 
@@ -99,10 +111,12 @@ def layer_fwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5
               stream=None):
     import torch
     args = args_for(batch, dev) if args is None else args
-    plan = plan_for(batch, args) if plan is None else plan
+    own = plan is None
+    plan = plan_for(batch, args) if own else plan
     T, D = batch["total_tokens"], batch["layer_dim"]
     y = torch.empty((T, D), dtype=torch.bfloat16, device=dev_device(dev)) if y is None else y
     hstu_layer_fwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], y, ln_eps=ln_eps, stream=stream)
+    _release(plan, own, stream)
     return y
 
 
@@ -111,7 +125,8 @@ def layer_bwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5
     """Gradients of sum(dy * Y) for the layer: dx (bf16), dw1, dw2 and bias tables (fp32)."""
     import torch
     args = args_for(batch, dev) if args is None else args
-    plan = plan_for(batch, args) if plan is None else plan
+    own = plan is None
+    plan = plan_for(batch, args) if own else plan
     T, D, H = batch["total_tokens"], batch["layer_dim"], batch["heads"]
     Hd = H * batch["d"]
     device = dev_device(dev)
@@ -125,15 +140,18 @@ def layer_bwd(batch: dict, dev: dict, plan=None, args=None, ln_eps: float = 1e-5
         g["drab_ts"] = torch.empty((H, 128), dtype=torch.float32, device=device)
     hstu_layer_bwd(plan, args, D, dev["x"], dev["w1"], dev["w2"], dev["dy"], g["dx"], g["dw1"],
                    g["dw2"], g["drab_pos"], g["drab_ts"], ln_eps=ln_eps, ws=ws, stream=stream)
+    _release(plan, own, stream)
     return g
 
 
 def attn_fwd_cached(batch: dict, dev: dict, plan=None, args=None, out=None, stream=None):
     """Candidate rows scored against the cached history of each user."""
     args = args_for(batch, dev) if args is None else args
-    if plan is None:
+    own = plan is None
+    if own:
         plan = hstu_plan_create_cached(args, batch["cand_offsets"], batch["cache_offsets"])
     out = empty_like_thd(batch, dev) if out is None else out
     hstu_attn_fwd_cached(plan, args, dev["q"], dev["k"], dev["v"], dev.get("k_cache"),
                          dev.get("v_cache"), dev.get("cache_timestamps"), out, stream=stream)
+    _release(plan, own, stream)
     return out

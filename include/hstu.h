@@ -94,6 +94,9 @@ typedef struct {
     int64_t bwd_key_block;     /* keys per dK/dV work item */
     int64_t fwd_items;         /* items of the forward launch (bf16: row blocks, long ones split) */
     int64_t fwd_split_blocks;  /* row blocks whose key tiles are split over several items */
+    int64_t bwd_stored_ds;     /* 1: given a workspace, the backward stores dS and the dQ pass reads
+                                  it back; 0: the dQ pass recomputes S and dP (fp32, head_dim 32) */
+    int64_t bwd_ds_bytes;      /* bytes of stored dS in the op 2 workspace (0 when not stored) */
 } hstu_plan_info_t;
 
 #define HSTU_PLAN_HOST_ONLY 1u /* plan_create flag: plan on the host only (inspection, tests) */
@@ -119,13 +122,18 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* seq_
                                const int32_t* num_targets_host, uint32_t flags,
                                hstu_plan_t** out);
 
-/* Frees the plan and its device buffer.  Where the device has a stream-ordered memory pool the
- * buffer comes from it and goes back in the order of the default (null) stream: after the work
- * queued there and on the blocking streams that synchronize with it, without waiting on the host.
- * Otherwise it is released with hipFree, which waits for the device.  Work queued on non-blocking
- * streams is not waited for: the caller must not destroy a plan such work still uses.  NULL is
- * ignored. */
+/* Frees the plan and its device buffer.  Waits for all work queued on the plan's device (on
+ * every stream) first, so it is safe whatever stream used the plan, at the cost of a device
+ * synchronisation; hstu_plan_destroy_on frees without waiting.  NULL is ignored. */
 void hstu_plan_destroy(hstu_plan_t* plan);
+
+/* Frees the plan without waiting on the host: its device buffer goes back to the device's
+ * stream-ordered pool in the order of `stream` (a hipStream_t of the plan's device; NULL = the
+ * default stream), i.e. after the work already queued there.  Every call that used the plan must
+ * be queued on `stream` already, or on a stream that `stream` waits for (an event); calls on
+ * other streams must be joined into `stream` first.  Where the device has no stream-ordered pool
+ * the buffer is released with hipFree, which waits for the device.  NULL is ignored. */
+void hstu_plan_destroy_on(hstu_plan_t* plan, void* stream);
 
 /* Fills *info. */
 hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info);
@@ -156,20 +164,26 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
                             const void* q, const void* k, const void* v, const void* u,
                             float ln_eps, void* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Attention backward: given dout = dL/dO, writes dq, dk, dv (dense THD, args->dtype) and, when
- * the pointers and the matching tables are non-NULL, drab_pos / drab_ts ([H][128] fp32,
- * overwritten).  Bias gradients are summed with fp32 atomics, so their low bits depend on
- * scheduling.  ws must hold hstu_workspace_bytes(plan, 2, 0) bytes (it may be NULL when that is
- * 0): the dK/dV pass stores dS there (bf16, dS * max_seqlen) for every pair it visits and sums
- * the bias-table gradients from it (fp32, before rounding), and the dQ pass reads dS back instead
- * of recomputing S and dP and copies the gradients out.  Same as hstu_attn_bwd_dkdv followed by
- * hstu_attn_bwd_dq with the same ws. */
+/* Attention backward (page 1 section 2.1.2, HSTU spatial aggregation, equation (2), through the
+ * chain rule; the pages give no backward of their own).  With S, sigma = sigmoid(S) and
+ * P = SiLU(S) / N on visible pairs as in hstu_attn_fwd, and dO = dout:
+ *     dV_j = sum_i P_ij dO_i,      dP_ij = dO_i . v_j,     dS_ij = dP_ij sigma (1 + S (1 - sigma)) / N,
+ *     dQ_i = alpha sum_j dS_ij k_j,    dK_j = alpha sum_i dS_ij q_i,
+ *     d rab_pos[h, b] = sum of dS_ij over pairs with bucket(|i - j|) = b (and d rab_ts likewise
+ *     over bucket(|t_i - t_j|)).
+ * Writes dq, dk, dv (dense THD, args->dtype) and, when the pointers and the matching tables are
+ * non-NULL, drab_pos / drab_ts ([H][128] fp32, overwritten).  Bias gradients are summed with fp32
+ * atomics, so their low bits depend on scheduling.  ws must hold hstu_workspace_bytes(plan, 2, 0)
+ * bytes (it may be NULL when that is 0): the dK/dV pass stores dS there (bf16, dS * max_seqlen)
+ * for every pair it visits and sums the bias-table gradients from it (fp32, before rounding),
+ * and the dQ pass reads dS back instead of recomputing S and dP and copies the gradients out.
+ * Same as hstu_attn_bwd_dkdv followed by hstu_attn_bwd_dq with the same ws. */
 hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                             const void* q, const void* k, const void* v, const void* dout,
                             void* dq, void* dk, void* dv, float* drab_pos, float* drab_ts,
                             void* ws, size_t ws_bytes, void* stream);
 
-/* The two halves of hstu_attn_bwd.  _dkdv writes dk and dv; _dq writes dq and the bias gradients
+/* The two halves of hstu_attn_bwd (the same passage and formulas).  _dkdv writes dk and dv; _dq writes dq and the bias gradients
  * as hstu_attn_bwd does.  With ws (at least hstu_workspace_bytes(plan, 2, 0) bytes, else
  * HSTU_ERR_WORKSPACE_TOO_SMALL) _dkdv stores dS and the bias-table gradients into it and _dq
  * reads them: call _dq after _dkdv on the same stream (or after it has finished), with the same
@@ -184,9 +198,13 @@ hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* 
                                void* dq, float* drab_pos, float* drab_ts, void* ws,
                                size_t ws_bytes, void* stream);
 
-/* Full HSTU layer forward, bf16 only.  x: (T, d_model) dense; w1: (d_model, 4*H*d) row-major;
- * w2: (H*d, d_model) row-major; y: (T, d_model).  args->qkv_token_stride is ignored (Q, K, V, U
- * are produced internally).  ws must hold hstu_workspace_bytes(plan, 3, d_model). */
+/* Full HSTU layer forward (page 1 section 2.1.2, HSTU layer: equation (1) pointwise projection
+ * Z = SiLU(X W1) split into U, V, Q, K; equation (2) spatial aggregation A = attention(Q, K, V)
+ * as in hstu_attn_fwd; equation (3) pointwise transformation Y = (LayerNorm(A) * U) W2 + X, with
+ * the residual connection the section describes between layers), bf16 only.  x: (T, d_model)
+ * dense; w1: (d_model, 4*H*d) row-major; w2: (H*d, d_model) row-major; y: (T, d_model).
+ * args->qkv_token_stride is ignored (Q, K, V, U are produced internally).  ws must hold
+ * hstu_workspace_bytes(plan, 3, d_model). */
 hstu_status_t hstu_layer_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                              int32_t d_model, const void* x, const void* w1, const void* w2,
                              float ln_eps, void* y, void* ws, size_t ws_bytes, void* stream);
@@ -232,7 +250,9 @@ hstu_status_t hstu_plan_create_cached(const hstu_attn_args_t* args, const int64_
                                       const int64_t* cache_off, uint32_t flags,
                                       hstu_plan_t** plan);
 
-/* q, k, v: candidate THD tensors (token stride args->qkv_token_stride or H*d); k_cache, v_cache:
+/* Candidate scoring of the rows hstu_plan_create_cached describes (page 1 section 2.1.2, ranking:
+ * candidates see the whole history and themselves; page 2, HSTU acceleration operator: KV cache).
+ * q, k, v: candidate THD tensors (token stride args->qkv_token_stride or H*d); k_cache, v_cache:
  * dense THD cache (cache_off[B] rows); cache_timestamps: [cache_off[B]] int64, needed when
  * args->rab_ts is set; out: dense THD (T, H, d).  ws must hold hstu_workspace_bytes(plan, 5, 0)
  * bytes (partial sums of long caches split over several workgroups; 0 when nothing is split). */

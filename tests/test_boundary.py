@@ -36,10 +36,57 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = _lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(names) == sorted(hj.EXPORTS)
+
+
+def _declaration_comments():
+    """Each declared function with the comment block that precedes its declaration (a comment
+    shared by several consecutive declarations counts for each of them)."""
+    text = open(HEADER).read()
+    out = {}
+    last = ""
+    pos = 0
+    for m in re.finditer(r"/\*.*?\*/|\b(hstu_[a-z_]+)\s*\(", text, flags=re.S):
+        if m.group(0).startswith("/*"):
+            # a comment directly before a declaration (only whitespace or other declarations
+            # between) describes it
+            last = m.group(0)
+        elif m.group(1) and m.group(1) not in out:
+            line_start = text.rfind("\n", 0, m.start()) + 1
+            if not text[line_start:m.start()].strip().startswith(("typedef", "#")):
+                out[m.group(1)] = last
+        pos = m.end()
+    return out
+
+
+# The entry points that compute something the pages define, and the passage each must cite.
+CITED = {
+    "hstu_plan_create": "page 2",             # greedy even assignment of work to cores
+    "hstu_plan_create_cached": "page 2",      # KV-cache support of the operator
+    "hstu_attn_fwd": "equation (2)",
+    "hstu_attn_fwd_cached": "page 1 section 2.1.2",
+    "hstu_attn_bwd": "equation (2)",
+    "hstu_attn_bwd_dkdv": "hstu_attn_bwd",    # "the same passage and formulas"
+    "hstu_attn_bwd_dq": "hstu_attn_bwd",
+    "hstu_layer_fwd": "equation (3)",
+    "hstu_layer_bwd": "equations (1)-(3)",
+    "hstu_jagged_select": "page 1 section 2.1.3",
+}
+
+
+def test_header_cites_the_passage_of_each_operation():
+    comments = _declaration_comments()
+    assert set(comments) == set(declared_functions())
+    for name, needle in CITED.items():
+        c = re.sub(r"\s+", " ", comments[name])
+        assert needle in c, (name, needle, c[:200])
+    # the forward's own comment refers to the formula block at the top of the header, which
+    # cites equation (2) of page 1 section 2.1.2
+    top = open(HEADER).read().split("*/")[0]
+    assert "equation (2)" in top and "page 1 section 2.1.2" in top
 
 
 def test_status_strings():

@@ -610,3 +610,93 @@ def test_long_workload_full_sampled():
     dp, dt = host(g["drab_pos"]), host(g["drab_ts"])
     np.testing.assert_allclose(dp.sum(axis=1), dt.sum(axis=1),
                                rtol=2e-2, atol=2e-2 * np.abs(dp).max())
+
+
+def _longest_sequence(w_full):
+    """The longest sequence of a workload as a batch of its own (same max_seqlen, contexts,
+    candidates, bias tables and inputs)."""
+    off = w_full["seq_offsets"]
+    b = int(np.argmax(np.diff(off)))
+    s, e = int(off[b]), int(off[b + 1])
+    w = dict(w_full)
+    w.update(batch=1, seq_offsets=np.array([0, e - s], np.int64), lengths=np.array([e - s]),
+             num_targets=w_full["num_targets"][b:b + 1].copy(), total_tokens=e - s,
+             timestamps=w_full["timestamps"][s:e].copy())
+    for key in ("q", "k", "v", "dout"):
+        w[key] = np.ascontiguousarray(w_full[key][s:e])
+    return w
+
+
+def test_long_workload_longest_sequence_full_compare():
+    """The long-sequence workload's longest sequence (7983 tokens, 8 contexts, 64 candidates, all
+    8 heads) alone, forward and stored-dS backward, compared element by element with the oracle:
+    O, dQ, dK, dV and both bias-table gradients.  Its position distances reach bucket 51 and its
+    key blocks far from the diagonal take the one-, two- and three-bucket gradient sums over
+    spans of thousands of tokens."""
+    w = _longest_sequence(hs.make_workload("long_fwdbwd"))
+    assert w["total_tokens"] == 7983 and w["heads"] == 8
+    dev = runner.to_device(w)
+    args = runner.args_for(w, dev)
+    plan = runner.plan_for(w, args)
+    info = hj.hstu_plan_info(plan)
+    assert info["bwd_stored_ds"] == 1 and info["bwd_ds_bytes"] > 0
+    say("long_fwdbwd longest sequence: forward + stored-dS backward, all heads")
+    out = runner.attn_fwd(w, dev, plan=plan, args=args)
+    g = runner.attn_bwd(w, dev, plan=plan, args=args)
+    torch.cuda.synchronize()
+    say("long_fwdbwd longest sequence: oracle")
+    check("O", host(out), oracle.attn_fwd(w), "bf16")
+    ref = oracle.attn_bwd(w)
+    # the far position buckets are really exercised
+    assert np.all(np.abs(ref["drab_pos"][:, 41:52]) > 0)
+    for name in ("dq", "dk", "dv", "drab_pos", "drab_ts"):
+        check(name, host(g[name]), ref[name], "bf16")
+    plan.close()
+
+
+def test_plan_freed_in_stream_order_while_kernels_queued():
+    """A plan destroyed right after its launches (in the order of the launch stream) and a second
+    plan created and launched at once, reusing the freed memory: both outputs are right.  Once
+    on the default stream and once on a non-blocking stream."""
+    wa = hs.make_inputs([900, 40, 333], 4, 128, dtype="bf16", seed=61, rab=True, num_targets=16)
+    wb = hs.make_inputs([77, 1200, 5, 260], 4, 128, dtype="bf16", seed=62, rab=True,
+                        num_contexts=3, num_targets=9)
+    for label, stream in (("default", None), ("non-blocking", torch.cuda.Stream())):
+        say(f"plan destroyed in {label} stream order, next plan launched at once")
+        outs = []
+        for w in (wa, wb):
+            dev = runner.to_device(w)
+            torch.cuda.synchronize()
+            args = runner.args_for(w, dev)
+            plan = runner.plan_for(w, args)
+            out = runner.empty_like_thd(w, dev)
+            hj.hstu_attn_fwd(plan, args, dev["q"], dev["k"], dev["v"], out, stream=stream)
+            plan.close(stream if stream is not None else torch.cuda.current_stream())
+            outs.append(out)
+        torch.cuda.synchronize()
+        for w, out in zip((wa, wb), outs):
+            check("O", host(out), oracle.attn_fwd(w), "bf16")
+
+
+def test_runner_temporary_plans_on_side_stream():
+    """The convenience layer's per-call plans and workspaces on a non-blocking stream: freed in
+    that stream's order, so back-to-back calls leave both results intact."""
+    w1 = hs.make_inputs([500, 64, 129], 2, 64, dtype="bf16", seed=71, rab=True, num_targets=8,
+                        backward=True)
+    w2 = hs.make_inputs([300, 700], 2, 64, dtype="bf16", seed=72, rab=True, num_contexts=2,
+                        num_targets=5, backward=True)
+    side = torch.cuda.Stream()
+    d1, d2 = runner.to_device(w1), runner.to_device(w2)
+    torch.cuda.synchronize()
+    say("runner calls with temporary plans on a side stream")
+    with torch.cuda.stream(side):
+        o1 = runner.attn_fwd(w1, d1, stream=side)
+        g1 = runner.attn_bwd(w1, d1, stream=side)
+        o2 = runner.attn_fwd(w2, d2, stream=side)
+        g2 = runner.attn_bwd(w2, d2, stream=side)
+    side.synchronize()
+    for w, o, g in ((w1, o1, g1), (w2, o2, g2)):
+        check("O", host(o), oracle.attn_fwd(w), "bf16")
+        ref = oracle.attn_bwd(w)
+        for name in ("dq", "dk", "dv", "drab_pos", "drab_ts"):
+            check(name, host(g[name]), ref[name], "bf16")
