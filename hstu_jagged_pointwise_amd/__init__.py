@@ -57,7 +57,8 @@ class HstuPlanInfo(ctypes.Structure):
 
 EXPORTS = ["hstu_status_str", "hstu_plan_create", "hstu_plan_destroy", "hstu_plan_destroy_on",
            "hstu_plan_info",
-           "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_bwd",
+           "hstu_plan_units", "hstu_workspace_bytes", "hstu_attn_fwd", "hstu_attn_fwd_noalloc",
+           "hstu_attn_bwd",
            "hstu_attn_bwd_dkdv", "hstu_attn_bwd_dq", "hstu_layer_fwd", "hstu_layer_bwd",
            "hstu_plan_create_cached", "hstu_attn_fwd_cached", "hstu_jagged_select"]
 
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.hstu_workspace_bytes.restype = ctypes.c_size_t
     lib.hstu_attn_fwd.argtypes = [P, argp, P, P, P, P, ctypes.c_float, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_fwd.restype = I32
+    lib.hstu_attn_fwd_noalloc.argtypes = [P, argp, P, P, P, P, ctypes.c_float, P, P]
+    lib.hstu_attn_fwd_noalloc.restype = I32
     lib.hstu_attn_bwd.argtypes = [P, argp, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.hstu_attn_bwd.restype = I32
     lib.hstu_attn_bwd_dkdv.argtypes = [P, argp, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -266,6 +269,15 @@ def hstu_attn_fwd(plan: Plan, args: HstuAttnArgs, q, k, v, out, u=None, ln_eps: 
     _check(load_library().hstu_attn_fwd(
         ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(u),
         float(ln_eps), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def hstu_attn_fwd_noalloc(plan: Plan, args: HstuAttnArgs, q, k, v, out, u=None,
+                          ln_eps: float = 1e-5, stream=None) -> None:
+    """hstu_attn_fwd with its scratch in the library's static per-device array: allocates
+    nothing (not even a temporary workspace)."""
+    _check(load_library().hstu_attn_fwd_noalloc(
+        ctypes.c_void_p(plan.handle), ctypes.byref(args), _ptr(q), _ptr(k), _ptr(v), _ptr(u),
+        float(ln_eps), _ptr(out), _stream(stream)))
 
 
 def hstu_attn_bwd(plan: Plan, args: HstuAttnArgs, q, k, v, dout, dq, dk, dv, drab_pos=None,

@@ -380,6 +380,33 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
     return HSTU_OK;
 }
 
+// Scratch memory of hstu_attn_fwd_noalloc: a static device array, so that the call needs no
+// allocation.  Each device holds its own copy (from the first call on it until the process ends);
+// host code reaches a device's copy only through the address hipGetSymbolAddress returns for it,
+// kept per device.  Calls that overlap on one device share the array and race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The scratch array's address on the current device (looked up once per device).
+hstu_status_t scratch_address(void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HSTU_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return HSTU_ERR_HIP;
+        }
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,6 +424,8 @@ const char* hstu_status_str(hstu_status_t s) {
         case HSTU_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than hstu_workspace_bytes()";
         case HSTU_ERR_HIP: return "a HIP runtime call failed";
         case HSTU_ERR_NO_DEVICE_PLAN: return "plan was created host-only";
+        case HSTU_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the library's static "
+                                           "buffer holds (hstu_attn_fwd_noalloc: 64 MiB)";
     }
     return "unknown status";
 }
@@ -602,6 +631,27 @@ hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* arg
                 : checked(hstu::launch_ln_gate_f32(ws, u, ldu, out, args->total_tokens, width, ln_eps, s), s);
     }
     return hip_status(e);
+}
+
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                                    const void* q, const void* k, const void* v, const void* u,
+                                    float ln_eps, void* out, void* stream) {
+    hstu_status_t st = check_call(plan, args);
+    if (st != HSTU_OK) return st;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HSTU_ERR_HIP;
+    if (dev != plan->device) return HSTU_ERR_BAD_SHAPE;
+    const size_t need = hstu_workspace_bytes(plan, u ? 1 : 0, 0);
+    if (need > kScratchBytes) return HSTU_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (need > 0 && args->total_tokens > 0) {
+        st = scratch_address(&ws);
+        if (st != HSTU_OK) return st;
+    }
+    // the same launches as hstu_attn_fwd, with the workspace in the static array: the partial
+    // slots and the gated path's attention buffer are written in full before they are read, so
+    // nothing left there by an earlier call is seen
+    return hstu_attn_fwd(plan, args, q, k, v, u, ln_eps, out, ws, ws ? kScratchBytes : 0, stream);
 }
 
 }  // extern "C"

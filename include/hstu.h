@@ -60,7 +60,8 @@ typedef enum {
     HSTU_ERR_MISALIGNED = 5,           /* pointer or stride alignment */
     HSTU_ERR_WORKSPACE_TOO_SMALL = 6,  /* ws_bytes < hstu_workspace_bytes() */
     HSTU_ERR_HIP = 7,                  /* a HIP runtime call failed */
-    HSTU_ERR_NO_DEVICE_PLAN = 8        /* plan was created host-only and cannot be launched */
+    HSTU_ERR_NO_DEVICE_PLAN = 8,       /* plan was created host-only and cannot be launched */
+    HSTU_ERR_SCRATCH_LIMIT = 9         /* needs more than the static scratch of _noalloc calls */
 } hstu_status_t;
 
 typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype_t;
@@ -163,6 +164,21 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
 hstu_status_t hstu_attn_fwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                             const void* q, const void* k, const void* v, const void* u,
                             float ln_eps, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* hstu_attn_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation and arguments,
+ * without ws.  The scratch it needs (hstu_workspace_bytes(plan, u ? 1 : 0, 0): the partial sums
+ * of split row blocks, and the attention output before the LayerNorm when u is given) lives in
+ * a static 64 MiB device array of the library, one per device, held from the first call on that
+ * device until the process ends; the call allocates nothing and returns HSTU_ERR_SCRATCH_LIMIT
+ * when the plan needs more.  The current device must be the plan's (HSTU_ERR_BAD_SHAPE
+ * otherwise).  All such calls on one device share the array: calls that may overlap in time on
+ * one device (different streams, or hosts threads without ordering) race; calls queued on one
+ * stream do not.  Nothing from an earlier call is read (the scratch is written before it is
+ * read). */
+hstu_status_t hstu_attn_fwd_noalloc(const hstu_plan_t* plan, const hstu_attn_args_t* args,
+                                    const void* q, const void* k, const void* v, const void* u,
+                                    float ln_eps, void* out, void* stream);
 
 /* Attention backward (page 1 section 2.1.2, HSTU spatial aggregation, equation (2), through the
  * chain rule; the pages give no backward of their own).  With S, sigma = sigmoid(S) and

@@ -36,7 +36,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = _lib()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert sorted(names) == sorted(hj.EXPORTS)
@@ -68,6 +68,7 @@ CITED = {
     "hstu_plan_create_cached": "page 2",      # KV-cache support of the operator
     "hstu_attn_fwd": "equation (2)",
     "hstu_attn_fwd_cached": "page 1 section 2.1.2",
+    "hstu_attn_fwd_noalloc": "cannot allocate",  # names the callers it is for
     "hstu_attn_bwd": "equation (2)",
     "hstu_attn_bwd_dkdv": "hstu_attn_bwd",    # "the same passage and formulas"
     "hstu_attn_bwd_dq": "hstu_attn_bwd",
@@ -90,7 +91,7 @@ def test_header_cites_the_passage_of_each_operation():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert hj.hstu_status_str(s) and hj.hstu_status_str(s) != "unknown status"
     assert hj.hstu_status_str(99) == "unknown status"
 

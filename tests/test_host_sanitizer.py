@@ -1,11 +1,12 @@
 """The library's host code (argument checks, plan building, work-list readback) run under
 AddressSanitizer and UndefinedBehaviorSanitizer on the CPU.
 
-hstu_api.hip is compiled for the host only with both sanitizers and linked into a small driver
-(sanitize_plan_driver.cpp) whose kernel launchers are stubs that abort: host-only plans never
-launch.  The driver builds plans for the five workload shapes, a ranking batch of thousands of
-users, and randomized jagged batches with edge lengths, contexts and candidates beyond the
-sequence length, then reads back every work list.  Any sanitizer report fails the test."""
+hstu_api.hip is compiled with both sanitizers on its host code (its device part, a static
+scratch array, is built as usual) and linked into a small driver (sanitize_plan_driver.cpp) whose
+kernel launchers are stubs that abort: host-only plans never launch.  The driver builds plans for
+the five workload shapes, a ranking batch of thousands of users, and randomized jagged batches
+with edge lengths, contexts and candidates beyond the sequence length, then reads back every
+work list.  Any sanitizer report fails the test."""
 import os
 import subprocess
 
@@ -19,8 +20,8 @@ CSRC = os.path.join(ROOT, "hstu_jagged_pointwise_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Each -fsanitize= follows -Xarch_host: the sanitizers apply to host code only.
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
-CFLAGS = ["-x", "hip", "--cuda-host-only", "-O1", "-g", "-std=c++17", "-fno-omit-frame-pointer",
-          "-I", os.path.join(ROOT, "include"), "-I", CSRC] + SAN
+CFLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
+          "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"), "-I", CSRC] + SAN
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +35,8 @@ def driver(tmp_path_factory):
         subprocess.run([HIPCC, *CFLAGS, "-c", src, "-o", obj], check=True, capture_output=True)
         objs.append(obj)
     exe = str(d / "drv")
-    subprocess.run([HIPCC, *SAN, *objs, "-o", exe], check=True, capture_output=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", *SAN, *objs, "-o", exe], check=True,
+                   capture_output=True)
     return exe
 
 
