@@ -327,16 +327,20 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     const TileDma<D, kThreads> qdma(tid, ld), ddma(tid, p.ld_out);
     const RowOperand<D> rowop(lane);
     const TrOperand<D> trop(lane);
-    // stored dS: this lane's key row of the (sequence, head) block, its 4 queries 4g .. 4g + 3
-    // of each group of 8 (byte offset); the tile's first query goes into the scalar offset
+    // stored dS: the unit's chunks (geometry.h), one 128-key x 64-query block per tile; this
+    // lane's key row, its 4 queries 4g .. 4g + 3 of each group of 8 (byte offset); the tile's
+    // chunk goes into the scalar offset
     const bf16* dsb = nullptr;
-    int ds_voff = 0, dsn = 0;
+    int ds_voff = 0;
+    int64_t ds_size = 0;
     if constexpr (DS) {
-        dsn = (n + kBlk - 1) & ~(kBlk - 1);
-        dsb = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq] + (int64_t)h * dsn * dsn;
-        ds_voff = (j * dsn + kWaveRows * qh + 4 * g) * 2;
+        const int kb = k0 / kBlk, nch = ds_chunks(kb, n, nc, nh);
+        dsb = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq] +
+              (int64_t)kDsChunk * ((int64_t)p.heads * ds_chunks_before(kb, n, nc, nh) + (int64_t)h * nch);
+        ds_voff = ((j - k0) * kTile + kWaveRows * qh + 4 * g) * 2;
+        ds_size = (int64_t)nch * kDsChunk * 2;
     }
-    const buffer_rsrc dsrs = rows_rsrc(dsb, dsn, dsn, dsn);
+    const buffer_rsrc dsrs = bytes_rsrc(dsb, ds_size);
     int64_t tqr = 0;
     // starts the copy of a query tile's Q and dO rows into buffer buf and loads its timestamps
     auto load_tile = [&](int buf, int tile) {
@@ -444,8 +448,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 // 16sl + 4g + c, then + 8
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl) {
-                    store_bf16x4(__builtin_shufflevector(db8[sl], db8[sl], 0, 1, 2, 3), dsrs, ds_voff + 32 * sl, i0 * 2);
-                    store_bf16x4(__builtin_shufflevector(db8[sl], db8[sl], 4, 5, 6, 7), dsrs, ds_voff + 32 * sl + 16, i0 * 2);
+                    store_bf16x4(__builtin_shufflevector(db8[sl], db8[sl], 0, 1, 2, 3), dsrs, ds_voff + 32 * sl, t * kDsChunk * 2);
+                    store_bf16x4(__builtin_shufflevector(db8[sl], db8[sl], 4, 5, 6, 7), dsrs, ds_voff + 32 * sl + 16, t * kDsChunk * 2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -963,6 +967,34 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
 
 constexpr int kStages = 4;
 
+// Copies the 64 x 128 dS block of one key tile and the unit's 128 query rows into an LDS tile
+// laid out like a 128-column operand tile (TileDma<kBlk>): its columns 0..63 are the 64-query
+// chunk of the unit's first query tile and 64..127 the next chunk (two consecutive chunks of the
+// tile's key block, geometry.h); the tile's 64 keys are rows 64 * (key tile & 1) .. + 63 of
+// both chunks (row_bytes adds that offset).
+struct DsPairDma {
+    static constexpr int C = kBlk / 8;  // 16-byte chunks per LDS row
+    static constexpr int W = kThreadsA / 64;
+    static constexpr int N = C / W;
+    int off[N];
+    int wave;
+    __device__ __forceinline__ explicit DsPairDma(int tid) {
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+#pragma unroll
+        for (int u = 0; u < N; ++u) {
+            const int pos = (u * W + wave) * 64 + lane;
+            const int row = pos / C, c = (pos % C) ^ tile_swz<kBlk>(row);
+            off[u] = ((c >> 3) * kDsChunk + row * kTile + 8 * (c & 7)) * 2;
+        }
+    }
+    __device__ __forceinline__ void issue_asm(i32x4 rs, bf16* tile, int row_bytes) const {
+#pragma unroll
+        for (int u = 0; u < N; ++u)
+            copy16_lds_asm(rs, lds_addr(tile + (u * W + wave) * 512), off[u] + row_bytes);
+    }
+};
+
 template <int D>
 struct SmemC {
     alignas(16) bf16 k[kStages][kTile * D];   // swizzled tiles (tile_off)
@@ -998,22 +1030,24 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
 
-    const int npad = (n + kBlk - 1) & ~(kBlk - 1);
-    const bf16* dsb = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq] + (int64_t)h * npad * npad + r0;
-    // byte sizes as rows_rsrc computes them (rows past the end read as zero)
+    const bf16* dss = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq];  // the sequence's chunks
+    // byte size as rows_rsrc computes it (rows past the end read as zero)
     const i32x4 krs = rsrc_words(kg, n > 0 ? ((int64_t)(n - 1) * ld + D) * 2 : 0);
-    const i32x4 dsrs = rsrc_words(dsb, ((int64_t)(npad - 1) * npad + kBlk) * 2);
     const TileDma<D, kThreads> kdma(tid, ld);
-    const TileDma<kBlk, kThreads> dsdma(tid, npad);
+    const DsPairDma dsdma(tid);
     const TrOperand<D> trop(lane);
     const TrBlock<kBlk> dsop(lane, wave);
 
     // The copies of list entry t form a group (its K and dS rows); groups are issued in order.
-    constexpr int kPerTile = TileDma<D, kThreads>::N + TileDma<kBlk, kThreads>::N;
+    constexpr int kPerTile = TileDma<D, kThreads>::N + DsPairDma::N;
+    // the unit's two query tiles are two consecutive chunks of the key tile's block
     auto issue_group = [&](int t) {
-        const int j0 = ktl.tile(t) * kTile;
+        const int kt = ktl.tile(t), kb = kt >> 1, j0 = kt * kTile;
         kdma.issue_asm(krs, sm.k[t % kStages], (int)((int64_t)j0 * ld * 2));
-        dsdma.issue_asm(dsrs, sm.ds[t % kStages], j0 * npad * 2);
+        const bf16* pair = dss + (int64_t)kDsChunk *
+            ((int64_t)p.heads * ds_chunks_before(kb, n, nc, nh) + (int64_t)h * ds_chunks(kb, n, nc, nh) +
+             (r0 / kTile - ds_first_qtile(kb, nc)));
+        dsdma.issue_asm(rsrc_words(pair, 2 * kDsChunk * 2), sm.ds[t % kStages], (kt & 1) * kTile * kTile * 2);
     };
     // waits for this thread's copies of group t, with groups t + 1 .. t + k still in flight
     auto wait_group = [&](int t) { wait_vmcnt_upto(imin(kStages - 2, ntiles - 1 - t) * kPerTile); };

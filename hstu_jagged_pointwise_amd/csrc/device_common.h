@@ -488,6 +488,18 @@ __device__ __forceinline__ buffer_rsrc rows_rsrc(const bf16* base, int n, int64_
 #endif
 }
 
+// Buffer resource over `bytes` bytes at base (raw addressing; accesses past the end are dropped
+// or read zero).
+__device__ __forceinline__ buffer_rsrc bytes_rsrc(const bf16* base, int64_t bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), (short)0, (int)bytes, 0x00020000);
+#else
+    (void)base;
+    (void)bytes;
+    return buffer_rsrc{};
+#endif
+}
+
 // Copies into LDS issued from inline assembly: the compiler then does not know that LDS is
 // being written behind its back, so it neither waits for these copies before later LDS reads nor
 // counts them -- the caller waits for each copy itself (wait_vmcnt / wait_vmcnt_upto, then a

@@ -118,6 +118,36 @@ HSTU_HD void rows_for_keys(int klo, int khi, int n, int nc, int nh, int* qlo, in
     *qhi = klo < nh ? n : imin(khi, n);
 }
 
+// Stored-dS layout of one sequence (bf16 backward).  Key block kb (keys [128 kb, 128 kb + 128))
+// owns chunks of kDsChunk elements, one per 64-query tile from ds_first_qtile() on: chunk c holds
+// dS of the block's 128 keys (rows) and queries [64 (q0 + c), + 64) (columns), q0 the first
+// tile.  The chunks cover the 128-row-aligned range of the queries that see the block (the rows
+// rows_for_keys() gives, rounded out to 128), so every 128-row block that visits one of the
+// block's key tiles finds its two query tiles as two consecutive chunks.  A sequence's blocks
+// are stored in order, each block's heads one after another: head h of block kb starts at
+//   kDsChunk * (H * ds_chunks_before(kb) + h * ds_chunks(kb))
+// elements from the sequence's start.
+constexpr int kDsChunk = 128 * 64;
+
+HSTU_HD int ds_first_qtile(int kb, int nc) { return 128 * kb < nc ? 0 : 2 * kb; }
+
+// Chunks of key block kb (the sequence has nc contexts and nh non-candidates, nc <= nh).
+HSTU_HD int ds_chunks(int kb, int n, int nc, int nh) {
+    const int klo = 128 * kb;
+    if (klo < nc) return 2 * cdiv(n, 128);               // every query sees a context key
+    if (klo < nh) return 2 * cdiv(n, 128) - 2 * kb;      // history keys: queries from klo on
+    return 2;                                            // candidates: only themselves
+}
+
+// Chunks of key blocks 0 .. kb - 1, in closed form: blocks below ceil(nc / 128) hold the whole
+// query range, blocks below ceil(nh / 128) the range from their own first key, the rest 2.
+HSTU_HD int64_t ds_chunks_before(int kb, int n, int nc, int nh) {
+    const int64_t cn = 2 * cdiv(n, 128);
+    const int64_t k1 = imin(kb, cdiv(nc, 128)), k2 = imin(kb, cdiv(nh, 128));
+    const int64_t m2 = k2 - k1;                          // blocks k1 .. k2 - 1
+    return k1 * cn + m2 * cn - m2 * (k1 + k2 - 1) + 2 * (int64_t)(kb - k2);
+}
+
 // Classification of the block queries [i0, i0 + rows) x keys [klo, khi) (khi <= n).
 HSTU_HD int classify_key_tile(int klo, int khi, int i0, int n, int nc, int nh,
                               int rows = kQueryTile) {

@@ -38,8 +38,8 @@ struct hstu_plan {
     int32_t compute_units = 256;
     bool cached = false;         // candidate scoring against cached history
     std::vector<CacheSeq> cache;
-    // stored-dS backward (bf16, head_dim 64 / 128): per-sequence element offsets of the dense
-    // npad x npad blocks of every head, and their total
+    // stored-dS backward (bf16, head_dim 64 / 128): per-sequence element offsets of the chunked
+    // layout (geometry.h), and their total
     std::vector<int64_t> ds_off;
     int64_t ds_elems = 0;
     void* dbuf = nullptr;
@@ -261,9 +261,10 @@ size_t grad_bytes(const hstu_plan_t* plan) {
     return plan->ds_elems > 0 ? align_up(size_t(2) * plan->shape.num_heads * hstu::kNumBuckets * 4, 256) : 0;
 }
 
-// The stored-dS layout: a dense npad x npad bf16 block per (sequence, head), npad = n rounded up
-// to 128, addressed with 32-bit byte offsets within a block.  Head dims 64 and 128 only (the dQ
-// kernel keeps two 16 KB dS tiles where the query rows of the recomputing kernel go).
+// The stored-dS layout (geometry.h): per sequence, its 128-key blocks in order, each holding one
+// 128 x 64 bf16 chunk per 64-query tile its visible queries span, heads one after another; the
+// sequence's first element offset goes to the device.  Head dims 64 and 128 only (the dQ kernel
+// keeps its dS tiles where the query rows of the recomputing kernel go).
 void plan_ds_layout(hstu_plan_t* plan) {
     plan->ds_off.clear();
     plan->ds_elems = 0;
@@ -272,10 +273,12 @@ void plan_ds_layout(hstu_plan_t* plan) {
     int64_t total = 0;
     std::vector<int64_t> off(plan->seqs.size());
     for (size_t b = 0; b < plan->seqs.size(); ++b) {
-        const int64_t npad = (int64_t(plan->seqs[b].n) + 127) / 128 * 128;
-        if (npad * npad * 2 >= (int64_t(1) << 31)) return;
+        const SeqInfo& si = plan->seqs[b];
+        // a key block's chunks are addressed with 32-bit byte offsets (sequences up to ~8M tokens)
+        if (int64_t(2) * hstu::cdiv(si.n, 128) * hstu::kDsChunk * 2 >= (int64_t(1) << 31)) return;
         off[b] = total;
-        total += int64_t(a.num_heads) * npad * npad;
+        total += int64_t(hstu::kDsChunk) * a.num_heads *
+                 hstu::ds_chunks_before(hstu::cdiv(si.n, 128), si.n, si.nc, si.nh);
     }
     plan->ds_off = std::move(off);
     plan->ds_elems = total;

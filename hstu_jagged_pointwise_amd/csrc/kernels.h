@@ -48,8 +48,8 @@ struct AttnParams {
     int64_t ld_cache;
     // bf16 backward with stored dS (head_dim 64 and 128): when ds is set, the dK/dV pass also
     // writes dS * N of every pair it visits to ds, and the dQ pass reads it back instead of
-    // recomputing S and dP.  Sequence b, head h owns the dense npad x npad block (npad = n rounded
-    // up to 128) at ds + ds_off[b] + h npad^2, row = key, column = query.
+    // recomputing S and dP.  Sequence b's chunks (geometry.h: one 128 x 64 block per key block
+    // and query tile, row = key, column = query) start at ds + ds_off[b].
     void* ds;
     const int64_t* ds_off;
     // With ds, the dK/dV pass also sums the bias-table gradients ([H][128] fp32, already zeroed,

@@ -96,7 +96,8 @@ typedef struct {
     int64_t fwd_items;         /* items of the forward launch (bf16: row blocks, long ones split) */
     int64_t fwd_split_blocks;  /* row blocks whose key tiles are split over several items */
     int64_t bwd_stored_ds;     /* 1: given a workspace, the backward stores dS and the dQ pass reads
-                                  it back; 0: the dQ pass recomputes S and dP (fp32, head_dim 32) */
+                                  it back; 0: the dQ pass recomputes S and dP (fp32, head_dim 32,
+                                  or a sequence of 8M tokens or more) */
     int64_t bwd_ds_bytes;      /* bytes of stored dS in the op 2 workspace (0 when not stored) */
 } hstu_plan_info_t;
 
@@ -152,9 +153,11 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
  * is the model width; it does not change the result at present).  The forward ops, and op 4,
  * include 512 * head_dim bytes per partial slot of split row blocks (0 when the plan splits
  * none).  Op 2, and op 4 when larger than the partial slots, is the stored dS of the bf16
- * backward with head_dim 64 or 128: 2 * H * npad^2 bytes per sequence, npad = its length rounded
- * up to 128 (0 for fp32, head_dim 32, or a sequence longer than 32640); op 2 adds 2 * H * 128
- * fp32 (rounded up to 256 bytes) for the bias-table gradients that pass sums. */
+ * backward with head_dim 64 or 128: per sequence and head, each 128-key block holds one
+ * 128 x 64 bf16 chunk per 64-query tile of the queries that see it (their range rounded out to
+ * 128), about 2 bytes per visible pair plus the blocks on the diagonal (0 for fp32, head_dim 32,
+ * or a sequence of 8M tokens or more); op 2 adds 2 * H * 128 fp32 (rounded up to 256 bytes) for
+ * the bias-table gradients that pass sums. */
 size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
 
 /* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.

@@ -17,4 +17,9 @@ void shim_rows_for_keys(int klo, int khi, int n, int nc, int nh, int* out2) {
 int shim_classify_key(int klo, int khi, int i0, int n, int nc, int nh, int rows) {
     return hstu::classify_key_tile(klo, khi, i0, n, nc, nh, rows);
 }
+int shim_ds_first_qtile(int kb, int nc) { return hstu::ds_first_qtile(kb, nc); }
+int shim_ds_chunks(int kb, int n, int nc, int nh) { return hstu::ds_chunks(kb, n, nc, nh); }
+long long shim_ds_chunks_before(int kb, int n, int nc, int nh) {
+    return (long long)hstu::ds_chunks_before(kb, n, nc, nh);
+}
 }

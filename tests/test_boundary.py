@@ -205,8 +205,9 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
                               *([P(16)] * 6), 1 << 30, None) == 2
     assert lib.hstu_layer_bwd(P(plan.handle), ctypes.byref(a), 512, *([P(16)] * 4), 1e-5,
                               *([P(16)] * 6), 1 << 30, None) == 8   # host-only plan
-    # attention backward: the stored dS, one 128 x 128 bf16 block per (sequence, head) here, then
-    # the two [H][128] fp32 bias-gradient tables the dK/dV pass sums (rounded up to 256 bytes)
+    # attention backward: the stored dS, here two 128 x 64 bf16 chunks per (sequence, head) (one
+    # key block, contexts: both query tiles), then the two [H][128] fp32 bias-gradient tables the
+    # dK/dV pass sums (rounded up to 256 bytes)
     ds = 3 * 2 * 128 * 128 * 2
     grads = 2 * 2 * 128 * 4
     assert hj.hstu_workspace_bytes(plan, hj.OP_BWD) == ds + grads
@@ -224,7 +225,10 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
     off = np.array([0, 128, 257, 257])
     p3 = hj.hstu_plan_create(args(total_tokens=257, max_seqlen=200, head_dim=128), off, None,
                              hj.HSTU_PLAN_HOST_ONLY)
-    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == 2 * (128 * 128 + 256 * 256) * 2 + 2 * 2 * 128 * 4
+    # chunks of 128 keys x 64 queries: the 128-token sequence's block (a context block) spans its
+    # 2 query tiles; the 129-token sequence's first block (contexts) all 4, its second block the
+    # query tiles from its own first key on, 2; two heads
+    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == 2 * (2 + 4 + 2) * 128 * 64 * 2 + 2 * 2 * 128 * 4
     p3.close()
 
 
@@ -400,3 +404,46 @@ def test_tile_geometry_matches_mask(shim):
                             assert not sub.any(), (n, c, t, i0, w0, rows)
                         if kind == 2:
                             assert sub.shape[0] == rows and sub.all(), (n, c, t, i0, w0, rows)
+
+
+def test_stored_ds_chunks_cover_every_visit(shim):
+    """The stored-dS layout: each 128-key block's chunks (64-query tiles) cover every query that
+    sees one of its keys, every 64-query tile the dK/dV pass writes for it, and the two query
+    tiles of every 128-row block the dQ pass reads for it; the closed-form chunk count before a
+    block equals the sum of the blocks' counts.  Checked against the oracle's mask."""
+    shim.shim_ds_chunks_before.restype = ctypes.c_longlong
+    rng = np.random.default_rng(3)
+    cases = [(n, c, t) for n in (1, 2, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 390)
+             for c in (0, 1, 70, 130, 300) for t in (0, 1, 16, 64, 130, 500)]
+    cases += [tuple(int(x) for x in (rng.integers(1, 700), rng.integers(0, 300), rng.integers(0, 300)))
+              for _ in range(40)]
+    for n, c, t in cases:
+        nc_, nh_ = ctypes.c_int(), ctypes.c_int()
+        shim.shim_split(n, c, t, ctypes.byref(nc_), ctypes.byref(nh_))
+        nc, nh = nc_.value, nh_.value
+        m = brute.role_mask(n, c, t, n)
+        nblk = (n + 127) // 128
+        total = 0
+        for kb in range(nblk):
+            assert shim.shim_ds_chunks_before(kb, n, nc, nh) == total, (n, c, t, kb)
+            q0 = shim.shim_ds_first_qtile(kb, nc)
+            nch = shim.shim_ds_chunks(kb, n, nc, nh)
+            total += nch
+            k0, khi = 128 * kb, min(128 * kb + 128, n)
+            q = (ctypes.c_int * 2)()
+            shim.shim_rows_for_keys(k0, khi, n, nc, nh, q)
+            qlo, qhi = q[0], q[1]
+            # the definition: the 128-aligned range of the rows that see the block
+            assert 64 * q0 == qlo and 64 * nch == -(-qhi // 128) * 128 - qlo, (n, c, t, kb)
+            rows = np.nonzero(m[:, k0:khi].any(axis=1))[0]
+            assert rows.min() // 64 >= q0 and rows.max() // 64 < q0 + nch
+            # the dK/dV pass writes query tiles qlo / 64 .. ceil(qhi / 64) - 1
+            assert -(-qhi // 64) <= q0 + nch
+            # the dQ pass: a 128-row block reading a key tile of this block reads its two tiles
+            for r0 in range(0, n, 128):
+                rhi = min(r0 + 128, n)
+                main, first, nd = _call3(shim.shim_key_tiles, r0, rhi, nc, nh)
+                for tile in list(range(main)) + list(range(first, first + nd)):
+                    if tile // 2 == kb:
+                        assert r0 // 64 >= q0 and r0 // 64 + 2 <= q0 + nch, (n, c, t, r0, tile)
+        assert shim.shim_ds_chunks_before(nblk, n, nc, nh) == total

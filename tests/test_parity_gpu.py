@@ -700,3 +700,28 @@ def test_runner_temporary_plans_on_side_stream():
         ref = oracle.attn_bwd(w)
         for name in ("dq", "dk", "dv", "drab_pos", "drab_ts"):
             check(name, host(g[name]), ref[name], "bf16")
+
+
+def test_bwd_stored_ds_sequence_beyond_32k():
+    """A 33000-token sequence takes the stored-dS path (chunked per key block, 64-bit chunk
+    offsets): sampled rows of dQ, dK, dV from the oracle, the bias-table gradients' totals."""
+    w = hs.make_inputs([33000, 70], 1, 64, dtype="bf16", seed=91, rab=True, num_contexts=2,
+                       num_targets=16, backward=True)
+    dev = runner.to_device(w)
+    args = runner.args_for(w, dev)
+    plan = runner.plan_for(w, args)
+    assert hj.hstu_plan_info(plan)["bwd_stored_ds"] == 1
+    say("bwd stored dS on a 33000-token sequence")
+    g = runner.attn_bwd(w, dev, plan=plan, args=args)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    toks = np.concatenate([[0, 1, 2, 100, 32767, 32768, 32769, 32983, 32984, 32999, 33000, 33069],
+                           rng.integers(0, 33070, 12)]).astype(np.int64)
+    heads = np.zeros(len(toks), np.int64)
+    ref = oracle.attn_bwd_rows(w, toks, heads)
+    for name in ("dq", "dk", "dv"):
+        check(f"{name} rows", host(g[name])[toks, 0], ref[name], "bf16")
+    # every bucket's gradient is a sum of dS, so both tables share one total per head
+    dp, dt = host(g["drab_pos"]), host(g["drab_ts"])
+    np.testing.assert_allclose(dp.sum(), dt.sum(), rtol=1e-3, atol=1e-3 * np.abs(dp).max())
+    plan.close()
