@@ -83,9 +83,9 @@ KERNEL_NAMES = {"fwd": "fwd_bf16_kernel<128", "bwd_dkdv": "bwd_dkdv_kernel<128",
 def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, out=TRAFFIC_FILE):
     """HBM bytes per launch of the headline kernels from rocprofv3 counter runs.
 
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) come from separate runs of
-    `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extra`; each is scaled by bytes / counter
-    for a plain 1 GiB device copy (`bench.py --copy-calibration`) profiled with the same counter.
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) come from separate rocprofv3 --pmc runs of
+    `bench.py --only long_fwdbwd --steps 5 --warmup 2`; each is scaled by bytes / counter for a
+    plain 1 GiB device copy (`bench.py --copy-calibration`) profiled with the same counter.
     """
     import csv
 
