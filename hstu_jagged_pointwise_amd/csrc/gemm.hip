@@ -31,20 +31,23 @@ constexpr int kGTile = kGM * kGK;      // elements of one operand stage (either 
 // c0 + lr of K rows 16 st + 8g + 0..7 from a 64 x D tile.  In each group of 16 lanes, lane s
 // supplies the address of row 8g + 4h + s / 4, columns 16 q + 4 (s % 4) .. + 3 (q = bit 4 of
 // the lane), so that after the transposing read lane i holds row 8g + 4h + e, column 16 q + i.
-template <int D>
+template <int D, int NB>
 struct TrOperandNat {
-    int off[D / 32][2];
-    __device__ __forceinline__ explicit TrOperandNat(int lane) {
+    // Offsets for the wavefront's own column blocks cb0 .. cb0 + NB - 1 (32 columns each), so
+    // that the reads index this array with constants only (an array indexed at run time is
+    // moved to LDS by the compiler, and every K step then waits for an extra LDS round trip).
+    int off[NB][2];
+    __device__ __forceinline__ TrOperandNat(int lane, int cb0) {
         const int s = lane & 15, q = (lane >> 4) & 1, g = lane >> 5;
 #pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb)
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                off[cb][h] = tile_off<D>(8 * g + 4 * h + (s >> 2), 32 * cb + 16 * q + 4 * (s & 3));
+                off[i][h] = tile_off<D>(8 * g + 4 * h + (s >> 2), 32 * ((cb0 + i) & (D / 32 - 1)) + 16 * q + 4 * (s & 3));
     }
-    __device__ __forceinline__ bf16x8 read(const bf16* tile, int st, int cb) const {
-        const bf16x4 lo = lds_read_tr4(tile + 16 * st * D + off[cb][0]);
-        const bf16x4 hi = lds_read_tr4(tile + 16 * st * D + off[cb][1]);
+    __device__ __forceinline__ bf16x8 read(const bf16* tile, int st, int i) const {
+        const bf16x4 lo = lds_read_tr4(tile + 16 * st * D + off[i][0]);
+        const bf16x4 hi = lds_read_tr4(tile + 16 * st * D + off[i][1]);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
 };
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
     };
 
     const RowOperand<64> rowop(lane);
-    const TrOperandNat<128> trop(lane);
+    const TrOperandNat<128, 2> tra(lane, 2 * wm), trb(lane, 2 * wn);
     int id = blockIdx.x;
     GemmTile cur, nxt;
     if (!next_tile(id, cur)) return;  // uniform: whole workgroup
@@ -145,19 +148,25 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
         for (int t = 0; t < cur.nk; ++t) {
             wait_tile_dma();
             __syncthreads();
+            // operand fragments of 16-wide K slices, two slices in registers at a time
+            bf16x8 a[2][2], b[2][2];
+            auto load = [&](int ks, int slot) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+                    a[slot][mb] = AT ? tra.read(sm.a[buf], ks, mb)
+                                     : rowop.read(sm.a[buf], 2 * wm + mb, ks);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    b[slot][nb] = BT ? rowop.read(sm.b[buf], 2 * wn + nb, ks)
+                                     : trb.read(sm.b[buf], ks, nb);
+            };
+            load(0, 0);
             if (t + 1 < cur.nk) issue(cur, t + 1, buf ^ 1);
             else if (more) issue(nxt, 0, buf ^ 1);
 #pragma unroll
             for (int ks = 0; ks < kGK / 16; ++ks) {
-                bf16x8 a[2], b[2];
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    a[mb] = AT ? trop.read(sm.a[buf], ks, 2 * wm + mb)
-                               : rowop.read(sm.a[buf], 2 * wm + mb, ks);
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    b[nb] = BT ? rowop.read(sm.b[buf], 2 * wn + nb, ks)
-                               : trop.read(sm.b[buf], ks, 2 * wn + nb);
+                if (ks + 1 < kGK / 16) load(ks + 1, (ks + 1) & 1);
+                const int sl = ks & 1;
                 // Stored results come out transposed (C^T = B^T A^T: a lane holds one row of C
                 // and 4 consecutive columns per entry group, for vector stores); atomic results
                 // keep C's layout (consecutive lanes on consecutive columns: coalesced atomics).
@@ -165,8 +174,8 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb)
-                        acc[mb][nb] = EPI == kEpiAtomicF32 ? mfma32(a[mb], b[nb], acc[mb][nb])
-                                                           : mfma32(b[nb], a[mb], acc[mb][nb]);
+                        acc[mb][nb] = EPI == kEpiAtomicF32 ? mfma32(a[sl][mb], b[sl][nb], acc[mb][nb])
+                                                           : mfma32(b[sl][nb], a[sl][mb], acc[mb][nb]);
             }
             buf ^= 1;
         }
