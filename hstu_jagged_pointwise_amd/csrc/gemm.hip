@@ -14,6 +14,8 @@
 // K-major operands may have any K (rows past the end read as zero), so the token dimension of
 // the weight gradients can be the reduction dimension and can be split over blockIdx.z; those
 // launches add their fp32 partial results atomically into an output the caller has cleared.
+// bf16 results leave through LDS (the operand buffer the last K step read) so that every store
+// instruction writes whole row segments.
 #include <algorithm>
 
 #include "device_common.h"
@@ -58,6 +60,14 @@ struct GemmSmem {
 };
 
 __device__ __forceinline__ float silu_f(float x) { return x * fast_sigmoid(x); }
+
+// Orders a wavefront's LDS accesses: its earlier LDS writes and reads complete before any later
+// one issues, and the compiler moves no LDS access across this point (lanes read what other lanes
+// of the same wavefront wrote).
+__device__ __forceinline__ void lds_wave_sync() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+}
 
 // One output tile: rows [m0, m0 + 128), columns [n0, n0 + 128), K range [kbeg, kend).
 struct GemmTile {
@@ -197,48 +207,82 @@ __global__ __launch_bounds__(kGT, 2) void gemm_kernel(const GemmArgs g) {
                                 unsafeAtomicAdd(static_cast<float*>(g.c) + m * g.ldc + n,
                                                 acc[mb][nb][4 * r + c]);
                         }
-        } else {
-            // lane holds C[64 wm + 32 mb + lr][64 wn + 32 nb + 8 r + 4 gq + c], c = 0..3
+        } else if constexpr (EPI == kEpiStoreF32) {
+            // lane holds C[64 wm + 32 mb + lr][64 wn + 32 nb + 8 r + 4 gq + c], c = 0..3: fp32
+            // results are stored from there, 16 bytes per lane (staged through LDS they were
+            // slower on the layer shapes)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
                 const int64_t m = m0 + 64 * wm + 32 * mb + lr;
                 if (m >= g.M) continue;
-                // the residual row's values, all loaded before any store (the compiler may not
-                // move a load of r above a store to c, which it cannot prove apart)
-                bf16x4 res[2][4];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + m * g.ldc + n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq) =
+                            f32x4{acc[mb][nb][4 * r], acc[mb][nb][4 * r + 1], acc[mb][nb][4 * r + 2], acc[mb][nb][4 * r + 3]};
+            }
+        } else {
+            // The wavefront's 64 x 64 results go out through LDS, 32 rows at a time in fp32, so
+            // that a store instruction writes 8 whole 128-byte row segments (from the MFMA
+            // layout a lane holds 4 columns of one row: 32 rows per store instruction).  The
+            // staging area is the operand buffer the last K step read, 8 KB per wavefront, free
+            // once every wavefront is past that step; the next tile's copies go to the other
+            // buffer until its first step's barrier.  16-byte chunks of a staged row are
+            // XOR-swizzled by the row's low 4 bits: conflict-free writes and reads.
+            __syncthreads();
+            float* const stage = reinterpret_cast<float*>(wave < 2 ? sm.a[buf ^ 1] : sm.b[buf ^ 1]) + (wave & 1) * 2048;
+            const int cp = lane & 7;  // read-back: 8 consecutive columns 8 cp .. 8 cp + 7 of a row
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int64_t mrow = m0 + 64 * wm + 32 * mb;  // first row of this half
+                const int n = n0 + 64 * wn + 8 * cp;
+                // the residual values first: the compiler may not move a load of r above a store
+                // to c, which it cannot prove apart
+                bf16x8 res[4];
                 if constexpr (EPI == kEpiResidual)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            res[nb][r] = *reinterpret_cast<const bf16x4*>(
-                                static_cast<const bf16*>(g.r) + m * g.ldr + n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq);
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t m = mrow + (lane >> 3) + 8 * i;
+                        if (m < g.M)
+                            res[i] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(g.r) + m * g.ldr + n);
+                    }
+                // lane holds C[mrow + lr][64 wn + 32 nb + 8 r + 4 gq + c], c = 0..3
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int64_t n = n0 + 64 * wn + 32 * nb + 8 * r + 4 * gq;
-                        const f32x4 x = {acc[mb][nb][4 * r], acc[mb][nb][4 * r + 1],
-                                         acc[mb][nb][4 * r + 2], acc[mb][nb][4 * r + 3]};
-                        if constexpr (EPI == kEpiSilu) {
-                            bf16x4 y, z;
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                y[c] = (bf16)silu_f(x[c]);
-                                z[c] = (bf16)x[c];
-                            }
-                            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
-                            if (g.c2) *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c2) + m * g.ldc + n) = z;
-                        } else if constexpr (EPI == kEpiResidual) {
-                            const bf16x4 rv = res[nb][r];
-                            bf16x4 y;
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) y[c] = (bf16)(x[c] + (float)rv[c]);
-                            *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
-                        } else {
-                            *reinterpret_cast<f32x4*>(static_cast<float*>(g.c) + m * g.ldc + n) = x;
-                        }
+                        const int chunk = 8 * nb + 2 * r + gq;
+                        *reinterpret_cast<f32x4*>(stage + lr * 64 + 4 * (chunk ^ (lr & 15))) =
+                            f32x4{acc[mb][nb][4 * r], acc[mb][nb][4 * r + 1], acc[mb][nb][4 * r + 2],
+                                  acc[mb][nb][4 * r + 3]};
                     }
+                lds_wave_sync();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = (lane >> 3) + 8 * i;
+                    const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + row * 64 + 4 * ((2 * cp) ^ (row & 15)));
+                    const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + row * 64 + 4 * ((2 * cp + 1) ^ (row & 15)));
+                    const int64_t m = mrow + row;
+                    if (m >= g.M) continue;
+                    const float x[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    if constexpr (EPI == kEpiSilu) {
+                        bf16x8 y, z;
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            y[c] = (bf16)silu_f(x[c]);
+                            z[c] = (bf16)x[c];
+                        }
+                        *reinterpret_cast<bf16x8*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
+                        if (g.c2) *reinterpret_cast<bf16x8*>(static_cast<bf16*>(g.c2) + m * g.ldc + n) = z;
+                    } else {
+                        bf16x8 y;
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) y[c] = (bf16)(x[c] + (float)res[i][c]);
+                        *reinterpret_cast<bf16x8*>(static_cast<bf16*>(g.c) + m * g.ldc + n) = y;
+                    }
+                }
+                lds_wave_sync();  // the next half overwrites what this one read
             }
         }
         if (!more) break;

@@ -820,10 +820,11 @@ hstu::GemmArgs gemm_args(const hstu_plan_t* plan, const void* a, int64_t lda, bo
 }
 
 // Tokens per workgroup for a weight gradient (M x N outputs summed over T tokens): enough
-// splits for about four workgroups per compute unit, at least 256 tokens each.
+// splits for about one tile per compute unit, at least 256 tokens each.  More splits add more
+// fp32 partial tiles atomically (four per compute unit took twice as long on the layer shapes).
 int64_t token_chunk(const hstu_plan_t* plan, int64_t T, int64_t M, int64_t N) {
     const int64_t tiles = (M / 128) * (N / 128);
-    const int64_t want = std::max<int64_t>(1, (4 * int64_t(plan->compute_units) + tiles - 1) / tiles);
+    const int64_t want = std::max<int64_t>(1, (int64_t(plan->compute_units) + tiles - 1) / tiles);
     int64_t chunk = (T + want - 1) / want;
     chunk = std::max<int64_t>(256, (chunk + 63) / 64 * 64);
     while ((T + chunk - 1) / chunk > 65535) chunk *= 2;
