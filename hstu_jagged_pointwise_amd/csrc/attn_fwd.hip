@@ -56,13 +56,15 @@ struct FwdSmem {
 //   TM 0: time bias absent or one bucket (inside tb.b0); 1: two buckets, tb.b1 where
 //      |dt| >= thr; 4: three buckets (tb.b2 where |dt| >= thr2); 2: per-element bucket class,
 //      32-bit relative times; 3: the same with 64-bit times.
-template <int D, int PM, int TM>
-__device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, int buf, int u0,
+// s[x] holds the 32-key block kb0 + x of the tile (x < NKB).
+template <int D, int PM, int TM, int NKB>
+__device__ __forceinline__ void epilogue(f32x16 (&s)[NKB], const FwdSmem<D>& sm, int buf, int u0,
                                          int g, float alpha2, const TimeSel tb, uint32_t ti,
-                                         int64_t ti64) {
+                                         int64_t ti64, int kb0) {
     const TimePick pick(tb, ti);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int x = 0; x < NKB; ++x) {
+        const int kb = kb0 + x;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jj = 32 * kb + 8 * r + 4 * g;  // first of this lane's 4 keys
@@ -75,22 +77,22 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[2], const FwdSmem<D>& sm, i
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_sad(ti, tq[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
-                s[kb][e] = silu_scaled(fmaf(alpha2, s[kb][e], b));
+                s[x][e] = silu_scaled(fmaf(alpha2, s[x][e], b));
             }
         }
     }
 }
 
-template <int D, int PM>
-__device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[2], const FwdSmem<D>& sm, int buf,
+template <int D, int PM, int NKB>
+__device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[NKB], const FwdSmem<D>& sm, int buf,
                                             int u0, int g, float alpha2, const TimeSel tb,
-                                            uint32_t ti, int64_t ti64) {
+                                            uint32_t ti, int64_t ti64, int kb0) {
     switch (tm) {
-        case 0: epilogue<D, PM, 0>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        case 1: epilogue<D, PM, 1>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        case 4: epilogue<D, PM, 4>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        case 2: epilogue<D, PM, 2>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
-        default: epilogue<D, PM, 3>(s, sm, buf, u0, g, alpha2, tb, ti, ti64); break;
+        case 0: epilogue<D, PM, 0, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
+        case 1: epilogue<D, PM, 1, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
+        case 4: epilogue<D, PM, 4, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
+        case 2: epilogue<D, PM, 2, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
+        default: epilogue<D, PM, 3, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
     }
 }
 
@@ -108,14 +110,21 @@ __device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int g, int j0, int lim
 // CACHED: candidate scoring.  The item's rows are candidates (positions nk + i, where nk is the
 // user's cached history length) and its key tiles run over the cache; every cached key is
 // visible (rows past the cache end read as zero, and zero V rows add nothing), and each row's
-// own key is added after the tiles by the item that holds the first tile.
+// own key is added after the tiles by the item that holds the first tile.  Items are 64
+// candidate rows, and the 4 wavefronts are 2 row groups x 2 key halves (wavefront w: rows
+// 32 (w % 2) .. + 31 of the item, keys 32 (w / 2) .. + 31 of each tile), so a short candidate
+// list keeps every wavefront busy; the key halves' partial outputs are added through LDS.
 template <int D, bool RP, bool RT, bool CACHED>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
+    constexpr bool KH = CACHED;                      // key halves (see above)
+    constexpr int kItemRows = KH ? 2 * kWaveRows : kRows;
+    constexpr int NKB = KH ? 1 : 2;                  // 32-key blocks per wavefront and tile
     const FwdItem wu = p.items[blockIdx.x];
     const int tid = threadIdx.x, wave = uniform_i(tid >> 6), lane = tid & 63, g = lane >> 5,
               lr = lane & 31;
+    const int rg = KH ? (wave & 1) : wave, kh = KH ? (wave >> 1) : 0;  // row group, key half
     const int n = wu.n, nc = wu.nc, nh = wu.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = wu.start;
     const bf16* __restrict__ qg = static_cast<const bf16*>(p.q) + tok0 * p.ld_in + h * D;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     const int64_t* __restrict__ tsk = (CACHED ? p.ts_cache : p.ts) + ktok0;
 
     const int64_t tbase = RT ? (nk > 0 ? tsk[0] : p.ts[tok0]) : 0;
-    const int rhi = imin(r0 + kRows, n);
+    const int rhi = imin(r0 + kItemRows, n);
     const KeyTiles kl = key_tiles_for_rows(r0, rhi, nc, nh);
     const int tbeg = wu.t0, ntiles = wu.t1 - wu.t0;  // this item's part of the tile list
     auto tile_at = [&](int t) { return CACHED ? tbeg + t : kl.tile(tbeg + t); };
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     }
 
     // this wavefront's rows and this lane's row
-    const int wlo = r0 + kWaveRows * wave, whi = imin(wlo + kWaveRows, rhi);
+    const int wlo = r0 + kWaveRows * rg, whi = imin(wlo + kWaveRows, rhi);
     const int i = wlo + lr;
     const bool row_ok = i < rhi;
     int lim = -1, dg = -1;  // visible keys: j <= lim or j == dg
@@ -233,27 +242,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     __syncthreads();
 
     // slot of (row i, key j0 + jj) in rp is u0 + jj - 4g; see store_tile
-    const int u0 = 4 * g - (kWaveRows * wave + lr) + (kRows - 1);
+    const int u0 = 4 * g - (kWaveRows * rg + lr) + (kRows - 1);
     const float alpha2 = -kLog2e * p.alpha;
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, j0 = tile_at(t) * kBN;
         if (t + 1 < ntiles) load_tile(buf ^ 1, tile_at(t + 1));
-        const int kind = wlo >= rhi ? kEmpty : CACHED ? kFull : classify_row_tile(wlo, whi, j0, n, nc, nh);
+        // this wavefront's keys of the tile: [jw, jw + 32 NKB)
+        const int jw = j0 + kWaveRows * kh;
+        const int kind = wlo >= rhi || jw >= nk ? kEmpty
+                         : CACHED ? kFull : classify_row_tile(wlo, whi, j0, n, nc, nh);
         if (kind != kEmpty) {
-            f32x16 s[2] = {f32x16{}, f32x16{}};
+            f32x16 s[NKB];
 #pragma unroll
-            for (int x = 0; x < 2 * (D / 16); ++x) {
-                const int ks = x >> 1, kb = x & 1;
-                s[kb] = mfma32(kop.read(sm.k[buf], kb, ks), qf[ks], s[kb]);
+            for (int x = 0; x < NKB; ++x) s[x] = f32x16{};
+#pragma unroll
+            for (int y = 0; y < NKB * (D / 16); ++y) {
+                const int ks = y / NKB, x = y % NKB;
+                s[x] = mfma32(kop.read(sm.k[buf], kh + x, ks), qf[ks], s[x]);
             }
-            sched_mfma_lds<2 * (D / 16), 4>();
+            sched_mfma_lds<NKB * (D / 16), 2 * NKB>();
             // bias mode of this (wavefront, tile): one bucket for the whole tile when possible
             float bpos = 0.0f;
             int pm = 0;
             if (RP) {
-                const int jhi = imin(j0 + kBN, nk) - 1;
-                const BiasSpan sp = bias_span((int64_t)wlo + rpos0 - jhi, (int64_t)(whi - 1 + rpos0) - j0);
+                const int jhi = imin(jw + kWaveRows * NKB, nk) - 1;
+                const BiasSpan sp = bias_span((int64_t)wlo + rpos0 - jhi, (int64_t)(whi - 1 + rpos0) - jw);
                 if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
                 else pm = 1;
             }
@@ -264,17 +278,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                 const BiasSpan st = bias_span(dlo, timax - uniform64(sm.tkmin[buf]));
                 tm = tb.set(st, wave_qfit && uniform_i(sm.fits[buf]), bpos, sm.wtb, dlo >= 0, timax_rel);
             } else tb.set_const(bpos);
-            if (pm) epilogue_tm<D, 1>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);
-            else epilogue_tm<D, 0>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64);
-            if (kind == kPartial) mask_keys(s, g, j0, lim, dg);
+            if (pm) epilogue_tm<D, 1, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
+            else epilogue_tm<D, 0, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
+            if constexpr (!KH)
+                if (kind == kPartial) mask_keys(s, g, j0, lim, dg);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int st = 0; st < 2 * NKB; ++st) {
                 float tmp[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) tmp[x] = s[st >> 1][8 * (st & 1) + x];
                 const bf16x8 pb = pack8(tmp);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vop.read(sm.v[buf], st, db), pb, o[db]);
+                for (int db = 0; db < D / 32; ++db) o[db] = mfma32(vop.read(sm.v[buf], 2 * kh + st, db), pb, o[db]);
             }
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tile_at(t + 1));
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         __syncthreads();
     }
 
-    if (CACHED && row_ok && wu.t0 == 0) {  // the row's own key and value
+    if (CACHED && row_ok && wu.t0 == 0 && kh == 0) {  // the row's own key and value
         const bf16* kr = static_cast<const bf16*>(p.k) + (tok0 + i) * p.ld_in + h * D;
         const bf16* vr = static_cast<const bf16*>(p.v) + (tok0 + i) * p.ld_in + h * D;
         float dot = 0.0f;
@@ -307,8 +322,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             }
     }
 
+    if constexpr (KH) {
+        // the second key half's partial outputs into the first's, through the (then idle) K
+        // tiles laid out [row group][db][element][lane]
+        static_assert(sizeof(sm.k) >= 2 * (D / 32) * 16 * 64 * sizeof(float), "reduction buffer");
+        float* mine = reinterpret_cast<float*>(&sm.k[0][0]) + (size_t)rg * (D / 32) * 16 * 64 + lane;
+        if (kh == 1)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[(db * 16 + e) * 64] = o[db][e];
+        __syncthreads();
+        if (kh == 0)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[db][e] += mine[(db * 16 + e) * 64];
+        if (kh != 0) return;
+    }
     if (row_ok && wu.part >= 0) {  // one piece of a split row block: fp32 partial sums
-        float* pg = p.part + ((size_t)wu.part * kRows + (i - r0)) * D;
+        float* pg = p.part + ((size_t)wu.part * kItemRows + (i - r0)) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -389,16 +422,16 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(const AttnParams p) {
     }
 }
 
-// Sums the partial slots of each split row block and writes its output rows (scaled like the
-// unsplit rows).  Workgroup (x, y) takes rows [y * kFixRows, + kFixRows) of split block x; each
-// thread owns 4 columns of one row.
+// Sums the partial slots of each split row block of ROWS rows and writes its output rows (scaled
+// like the unsplit rows).  Workgroup (x, y) takes rows [y * kFixRows, + kFixRows) of split block
+// x; each thread owns 4 columns of one row.
 constexpr int kFixRows = 4 * kThreads / 128;
-template <int D>
+template <int D, int ROWS>
 __global__ __launch_bounds__(kThreads) void fwd_fix_kernel(const AttnParams p) {
     constexpr int RPT = kThreads / (D / 4);  // rows per pass of the workgroup
     const FixItem f = p.fix[blockIdx.x];
     const SeqInfo si = p.seqs[f.seq];
-    const int rows = imin(kRows, si.n - f.row0);
+    const int rows = imin(ROWS, si.n - f.row0);
     const float oscale = -kLn2 * p.inv_n;
     const int c = 4 * (threadIdx.x % (D / 4));
 #pragma unroll
@@ -407,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void fwd_fix_kernel(const AttnParams p) {
         if (r >= rows || r >= (int)(blockIdx.y + 1) * kFixRows) continue;
         f32x4 acc = f32x4{};
         for (int k = 0; k < f.nparts; ++k)
-            acc += *reinterpret_cast<const f32x4*>(p.part + ((size_t)(f.part0 + k) * kRows + r) * D + c);
+            acc += *reinterpret_cast<const f32x4*>(p.part + ((size_t)(f.part0 + k) * ROWS + r) * D + c);
         bf16x4 w;
 #pragma unroll
         for (int x = 0; x < 4; ++x) w[x] = (bf16)(acc[x] * oscale);
@@ -424,7 +457,10 @@ hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
         hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, false>), dim3(p.num_items), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.num_fix == 0) return e;
-    hipLaunchKernelGGL((fwd_fix_kernel<D>), dim3(p.num_fix, kRows / kFixRows), dim3(kThreads), 0, s, p);
+    if (p.cache)  // candidate items: 64 rows (see fwd_bf16_kernel)
+        hipLaunchKernelGGL((fwd_fix_kernel<D, 2 * kWaveRows>), dim3(p.num_fix, 2 * kWaveRows / kFixRows), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_fix_kernel<D, kRows>), dim3(p.num_fix, kRows / kFixRows), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

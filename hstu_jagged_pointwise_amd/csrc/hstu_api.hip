@@ -1010,7 +1010,7 @@ hstu_status_t hstu_plan_create_cached(const hstu_attn_args_t* args, const int64_
     plan->shape.rab_pos = nullptr;
     plan->shape.rab_ts = nullptr;
     plan->cached = true;
-    plan->fwd_rows = 4 * hstu::kWaveRows;
+    plan->fwd_rows = 2 * hstu::kWaveRows;  // 64 candidates per item (fwd_bf16_kernel)
     plan->bwd_keys = 0;
     plan->fwd_tiles = 0;  // counted here: every key tile of the cache is visible
     const int H = args->num_heads;
