@@ -52,6 +52,7 @@ class HstuPlanInfo(ctypes.Structure):
         ("fwd_split_blocks", ctypes.c_int64),
         ("bwd_stored_ds", ctypes.c_int64),
         ("bwd_ds_bytes", ctypes.c_int64),
+        ("fwd_item_rows", ctypes.c_int64),
     ]
 
 

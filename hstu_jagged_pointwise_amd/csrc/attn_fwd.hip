@@ -96,29 +96,32 @@ __device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[NKB], const FwdS
     }
 }
 
-// Zero the entries of keys this lane's row does not see (partial tiles only).
-__device__ __forceinline__ void mask_keys(f32x16 (&s)[2], int g, int j0, int lim, int dg) {
+// Zero the entries of keys this lane's row does not see (partial tiles only); s[x] holds the
+// 32-key block kb0 + x of the tile.
+template <int NKB>
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[NKB], int g, int j0, int lim, int dg, int kb0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int x = 0; x < NKB; ++x)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int j = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-            s[kb][e] = (j <= lim || j == dg) ? s[kb][e] : 0.0f;
+            const int j = j0 + 32 * (kb0 + x) + 8 * (e >> 2) + 4 * g + (e & 3);
+            s[x][e] = (j <= lim || j == dg) ? s[x][e] : 0.0f;
         }
 }
 
 // CACHED: candidate scoring.  The item's rows are candidates (positions nk + i, where nk is the
 // user's cached history length) and its key tiles run over the cache; every cached key is
 // visible (rows past the cache end read as zero, and zero V rows add nothing), and each row's
-// own key is added after the tiles by the item that holds the first tile.  Items are 64
-// candidate rows, and the 4 wavefronts are 2 row groups x 2 key halves (wavefront w: rows
-// 32 (w % 2) .. + 31 of the item, keys 32 (w / 2) .. + 31 of each tile), so a short candidate
-// list keeps every wavefront busy; the key halves' partial outputs are added through LDS.
-template <int D, bool RP, bool RT, bool CACHED>
+// own key is added after the tiles by the item that holds the first tile.
+// KH: items of 64 rows, and the 4 wavefronts are 2 row groups x 2 key halves (wavefront w: rows
+// 32 (w % 2) .. + 31 of the item, keys 32 (w / 2) .. + 31 of each tile): half the work per
+// wavefront and tile for candidate lists and small batches, where the items do not fill the
+// GPU; the key halves' partial outputs are added through LDS.  Otherwise items of 128 rows, 4
+// row groups of 32 over whole tiles.
+template <int D, bool RP, bool RT, bool CACHED, bool KH>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
 
-    constexpr bool KH = CACHED;                      // key halves (see above)
     constexpr int kItemRows = KH ? 2 * kWaveRows : kRows;
     constexpr int NKB = KH ? 1 : 2;                  // 32-key blocks per wavefront and tile
     const FwdItem wu = p.items[blockIdx.x];
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
         // this wavefront's keys of the tile: [jw, jw + 32 NKB)
         const int jw = j0 + kWaveRows * kh;
         const int kind = wlo >= rhi || jw >= nk ? kEmpty
-                         : CACHED ? kFull : classify_row_tile(wlo, whi, j0, n, nc, nh);
+                         : CACHED ? kFull : classify_row_tile(wlo, whi, jw, n, nc, nh, kWaveRows * NKB);
         if (kind != kEmpty) {
             f32x16 s[NKB];
 #pragma unroll
@@ -280,8 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             } else tb.set_const(bpos);
             if (pm) epilogue_tm<D, 1, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
             else epilogue_tm<D, 0, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
-            if constexpr (!KH)
-                if (kind == kPartial) mask_keys(s, g, j0, lim, dg);
+            if (kind == kPartial) mask_keys<NKB>(s, g, j0, lim, dg, kh);
 #pragma unroll
             for (int st = 0; st < 2 * NKB; ++st) {
                 float tmp[8];
@@ -451,16 +453,20 @@ __global__ __launch_bounds__(kThreads) void fwd_fix_kernel(const AttnParams p) {
 
 template <int D, bool RP, bool RT>
 hipError_t launch_bf16_t(const AttnParams& p, hipStream_t s) {
+    const bool kh = p.item_rows == 2 * kWaveRows;  // else kRows (checked by the caller)
+    const dim3 grid(p.num_items), block(kThreads);
     if (p.cache)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, true>), dim3(p.num_items), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, true, true>), grid, block, 0, s, p);
+    else if (kh)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, false, true>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, false>), dim3(p.num_items), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, RP, RT, false, false>), grid, block, 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.num_fix == 0) return e;
-    if (p.cache)  // candidate items: 64 rows (see fwd_bf16_kernel)
-        hipLaunchKernelGGL((fwd_fix_kernel<D, 2 * kWaveRows>), dim3(p.num_fix, 2 * kWaveRows / kFixRows), dim3(kThreads), 0, s, p);
+    if (kh)
+        hipLaunchKernelGGL((fwd_fix_kernel<D, 2 * kWaveRows>), dim3(p.num_fix, 2 * kWaveRows / kFixRows), block, 0, s, p);
     else
-        hipLaunchKernelGGL((fwd_fix_kernel<D, kRows>), dim3(p.num_fix, kRows / kFixRows), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((fwd_fix_kernel<D, kRows>), dim3(p.num_fix, kRows / kFixRows), block, 0, s, p);
     return hipGetLastError();
 }
 
@@ -478,6 +484,8 @@ hipError_t launch_bf16_d(const AttnParams& p, hipStream_t s) {
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s) {
     if (p.num_items == 0) return hipSuccess;
     if (p.num_fix > 0 && p.part == nullptr) return hipErrorInvalidValue;
+    if (p.item_rows != kRows && p.item_rows != 2 * kWaveRows) return hipErrorInvalidValue;
+    if (p.cache && p.item_rows != 2 * kWaveRows) return hipErrorInvalidValue;
     switch (p.head_dim) {
         case 32: return launch_bf16_d<32>(p, s);
         case 64: return launch_bf16_d<64>(p, s);

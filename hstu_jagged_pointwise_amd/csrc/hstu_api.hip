@@ -32,8 +32,9 @@ struct hstu_plan {
     int64_t fwd_tiles = -1;    // computed on first hstu_plan_info (-1: not yet)
     std::vector<SeqInfo> seqs;
     std::vector<WorkUnit> fwd, bwd;
-    std::vector<FwdItem> items;  // bf16 forward launch (fwd, the longest split by key tiles)
+    std::vector<FwdItem> items;  // bf16 forward launch (row blocks, the longest split by key tiles)
     std::vector<FixItem> fix;
+    int32_t item_rows = 128;     // rows per forward item: 128, or 64 (key-half layout)
     int32_t parts = 0;           // partial slots the split items write
     int32_t compute_units = 256;
     bool cached = false;         // candidate scoring against cached history
@@ -177,10 +178,29 @@ void order_for_xcds(std::vector<Item>& items) {
     }
 }
 
+// Rows per item: the forward's items are the plan's 128-row blocks, unless those blocks fill at
+// most half of the workgroup slots (small batches) or the plan scores candidates: then 64-row
+// blocks, run in the key-half layout (two row groups x two key halves per workgroup), which
+// halves the work per wavefront and tile where the GPU would otherwise idle.
 void build_fwd_items(hstu_plan_t* plan, int compute_units) {
-    int64_t total = 0;
-    for (const WorkUnit& u : plan->fwd) total += u.cost;
     const int64_t slots = 2 * int64_t(compute_units);
+    std::vector<WorkUnit> half;  // 64-row blocks of the regular plan, when used
+    const std::vector<WorkUnit>* units = &plan->fwd;
+    plan->item_rows = plan->cached ? 2 * hstu::kWaveRows : 4 * hstu::kWaveRows;
+    if (!plan->cached && 2 * int64_t(plan->fwd.size()) <= slots) {
+        plan->item_rows = 2 * hstu::kWaveRows;
+        for (const WorkUnit& u : plan->fwd) {
+            const SeqInfo& si = plan->seqs[u.seq];
+            for (int r0 = u.row0; r0 < std::min(u.row0 + 4 * hstu::kWaveRows, si.n); r0 += 2 * hstu::kWaveRows) {
+                const hstu::KeyTiles kt =
+                    hstu::key_tiles_for_rows(r0, std::min(r0 + 2 * hstu::kWaveRows, si.n), si.nc, si.nh);
+                half.push_back(WorkUnit{u.seq, u.head, r0, kt.count()});
+            }
+        }
+        units = &half;
+    }
+    int64_t total = 0;
+    for (const WorkUnit& u : *units) total += u.cost;
     const int cap = (int)std::max<int64_t>(kMinSplit, 2 * ((total + slots - 1) / slots));
     plan->items.clear();
     plan->fix.clear();
@@ -191,7 +211,7 @@ void build_fwd_items(hstu_plan_t* plan, int compute_units) {
         return FwdItem{u.seq, u.head, u.row0, cost, t0, t1, part, 0,
                        si.start, si.n, si.nc, si.nh, cs.start, cs.n, 0, 0};
     };
-    for (const WorkUnit& u : plan->fwd) {
+    for (const WorkUnit& u : *units) {
         if (u.cost <= cap) {
             plan->items.push_back(item(u, u.cost, 0, u.cost, -1));
             continue;
@@ -249,7 +269,7 @@ hipError_t checked(hipError_t e, hipStream_t s) {
 }
 
 size_t part_bytes(const hstu_plan_t* plan) {
-    return align_up(size_t(plan->parts) * plan->fwd_rows * plan->shape.head_dim * 4, 256);
+    return align_up(size_t(plan->parts) * plan->item_rows * plan->shape.head_dim * 4, 256);
 }
 
 // Stored dS of the bf16 backward (0 when the plan does not use it).
@@ -293,6 +313,7 @@ hstu::AttnParams base_params(const hstu_plan_t* plan, const hstu_attn_args_t* a)
     p.num_items = (int32_t)plan->items.size();
     p.fix = plan->d_fix;
     p.num_fix = (int32_t)plan->fix.size();
+    p.item_rows = plan->item_rows;
     p.heads = a->num_heads;
     p.head_dim = a->head_dim;
     int64_t hd = int64_t(a->num_heads) * a->head_dim;
@@ -540,6 +561,7 @@ hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info) {
     info->fwd_items = plan->shape.dtype == HSTU_BF16 ? (int64_t)plan->items.size()
                                                      : (int64_t)plan->fwd.size();
     info->fwd_split_blocks = (int64_t)plan->fix.size();
+    info->fwd_item_rows = plan->shape.dtype == HSTU_BF16 ? plan->item_rows : plan->fwd_rows;
     info->bwd_stored_ds = plan->ds_elems > 0 ? 1 : 0;
     info->bwd_ds_bytes = (int64_t)ds_bytes(plan);
     return HSTU_OK;

@@ -16,7 +16,8 @@ struct AttnParams {
     int32_t num_items;
     const FixItem* fix;     // bf16 forward: split row blocks to sum
     int32_t num_fix;
-    float* part;            // bf16 forward: partial slots, [slot][128 rows][head_dim] fp32
+    int32_t item_rows;      // bf16 forward: rows per item, 128 or 64 (64: key-half layout)
+    float* part;            // bf16 forward: partial slots, [slot][item_rows][head_dim] fp32
     int32_t heads;
     int32_t head_dim;
     int64_t ld_in;    // token stride of q, k, v (elements)

@@ -91,7 +91,7 @@ typedef struct {
     int64_t fwd_units;         /* work items of the forward (and dQ) launch */
     int64_t bwd_units;         /* work items of the dK/dV launch */
     int64_t fwd_tiles;         /* (32-row, 64-key) tiles the forward computes, all units */
-    int64_t fwd_row_block;     /* query rows per forward work item */
+    int64_t fwd_row_block;     /* query rows per forward (and dQ) work unit */
     int64_t bwd_key_block;     /* keys per dK/dV work item */
     int64_t fwd_items;         /* items of the forward launch (bf16: row blocks, long ones split) */
     int64_t fwd_split_blocks;  /* row blocks whose key tiles are split over several items */
@@ -99,6 +99,9 @@ typedef struct {
                                   it back; 0: the dQ pass recomputes S and dP (fp32, head_dim 32,
                                   or a sequence of 8M tokens or more) */
     int64_t bwd_ds_bytes;      /* bytes of stored dS in the op 2 workspace (0 when not stored) */
+    int64_t fwd_item_rows;     /* rows per item of the forward launch: 128, or 64 for candidate
+                                  scoring and for batches whose 128-row blocks fill at most half
+                                  of the workgroup slots (2 per compute unit) */
 } hstu_plan_info_t;
 
 #define HSTU_PLAN_HOST_ONLY 1u /* plan_create flag: plan on the host only (inspection, tests) */

@@ -271,7 +271,7 @@ def test_plan_covers_every_block_once_in_launch_order(dtype):
 
 
 @pytest.mark.parametrize("name", ["longtail_fwd", "one_long", "long_fwdbwd"])
-def test_forward_items_split_long_row_blocks(name):
+def test_forward_items_split_long_row_blocks(name, shim):
     if name == "one_long":   # one long sequence among short ones: its last row blocks split
         w = hs.make_inputs([4000] + [60] * 50, 2, 64, dtype="bf16", seed=5, rab=True, num_targets=8)
     else:
@@ -280,6 +280,21 @@ def test_forward_items_split_long_row_blocks(name):
     info = hj.hstu_plan_info(plan)
     blocks = hj.hstu_plan_units(plan, 0)
     items = hj.hstu_plan_units(plan, 2)
+    # 128-row blocks, or 64-row ones when the 128-row blocks fill at most half of the 512
+    # workgroup slots of a host-only plan (256 compute units)
+    rows = 64 if 2 * len(blocks) <= 512 else 128
+    assert info["fwd_item_rows"] == rows
+    if rows == 64:
+        blocks = []
+        for b, n in enumerate(w["lengths"]):
+            nc_, nh_ = ctypes.c_int(), ctypes.c_int()
+            shim.shim_split(int(n), w["num_contexts"], int(w["num_targets"][b]), ctypes.byref(nc_),
+                            ctypes.byref(nh_))
+            nc, nh = nc_.value, nh_.value
+            for r0 in range(0, int(n), 64):
+                main, first, nd = _call3(shim.shim_key_tiles, r0, min(r0 + 64, int(n)), nc, nh)
+                blocks += [(b, h, r0, main + nd) for h in range(w["heads"])]
+        blocks = np.array(blocks, dtype=np.int64)
     assert info["fwd_items"] == len(items)
     # launch order: the items of one (sequence, head) share an index residue mod 8 (one XCD),
     # at least for every group that lies in the first half of the list (queues only run
@@ -313,7 +328,7 @@ def test_forward_items_split_long_row_blocks(name):
             assert cost[key] > cap
     assert info["fwd_split_blocks"] == split
     assert sorted(slots) == list(range(len(slots)))                        # slots used once
-    want_ws = -(-(len(slots) * 128 * w["d"] * 4) // 256) * 256
+    want_ws = -(-(len(slots) * rows * w["d"] * 4) // 256) * 256
     assert hj.hstu_workspace_bytes(plan, 0) == want_ws
     assert (split > 0) == (name == "one_long")
     plan.close()
@@ -357,34 +372,36 @@ def test_tile_geometry_matches_mask(shim):
         m = brute.role_mask(n, c, t, n)                      # oracle-side mask, (n, n)
         assert nh == n - min(t, n - min(c, n))
         ntile = (n + 63) // 64
-        # forward / dQ: 128-row units, 32-row wavefronts, 64-key tiles
-        for r0 in range(0, n, 128):
-            rhi = min(r0 + 128, n)
-            main, first, nd = _call3(shim.shim_key_tiles, r0, rhi, nc, nh)
-            listed = set(range(main)) | set(range(first, first + nd))
-            assert len(listed) == main + nd and max(listed) < ntile
-            for tile in range(ntile):
-                blk = m[r0:rhi, 64 * tile: 64 * tile + 64]
-                if tile not in listed:
-                    assert not blk.any(), (n, c, t, r0, tile)
-                for w0 in range(r0, rhi, 32):
-                    w1 = min(w0 + 32, rhi)
-                    sub = m[w0:w1, 64 * tile: 64 * tile + 64]
-                    kind = shim.shim_classify_row(w0, w1, 64 * tile, n, nc, nh, 64)
-                    if kind == 0:
-                        assert not sub.any(), (n, c, t, w0, tile)
-                    if kind == 2:  # no mask needed: every real row sees all 64 keys
-                        assert sub.shape[1] == 64 and sub.all(), (n, c, t, w0, tile)
-                    if sub.any():
-                        assert tile in listed
-                    for kh in range(2):  # the tile's 32-key halves
-                        j0 = 64 * tile + 32 * kh
-                        sub = m[w0:w1, j0:j0 + 32]
-                        kind = shim.shim_classify_row(w0, w1, j0, n, nc, nh, 32)
+        # forward / dQ: 128-row units (and the forward's 64-row items), 32-row wavefronts,
+        # 64-key tiles and their 32-key halves
+        for unit in (128, 64):
+            for r0 in range(0, n, unit):
+                rhi = min(r0 + unit, n)
+                main, first, nd = _call3(shim.shim_key_tiles, r0, rhi, nc, nh)
+                listed = set(range(main)) | set(range(first, first + nd))
+                assert len(listed) == main + nd and max(listed) < ntile
+                for tile in range(ntile):
+                    blk = m[r0:rhi, 64 * tile: 64 * tile + 64]
+                    if tile not in listed:
+                        assert not blk.any(), (n, c, t, r0, tile)
+                    for w0 in range(r0, rhi, 32):
+                        w1 = min(w0 + 32, rhi)
+                        sub = m[w0:w1, 64 * tile: 64 * tile + 64]
+                        kind = shim.shim_classify_row(w0, w1, 64 * tile, n, nc, nh, 64)
                         if kind == 0:
-                            assert not sub.any(), (n, c, t, w0, j0)
-                        if kind == 2:
-                            assert sub.shape[1] == 32 and sub.all(), (n, c, t, w0, j0)
+                            assert not sub.any(), (n, c, t, w0, tile)
+                        if kind == 2:  # no mask needed: every real row sees all 64 keys
+                            assert sub.shape[1] == 64 and sub.all(), (n, c, t, w0, tile)
+                        if sub.any():
+                            assert tile in listed
+                        for kh in range(2):  # the tile's 32-key halves
+                            j0 = 64 * tile + 32 * kh
+                            sub = m[w0:w1, j0:j0 + 32]
+                            kind = shim.shim_classify_row(w0, w1, j0, n, nc, nh, 32)
+                            if kind == 0:
+                                assert not sub.any(), (n, c, t, w0, j0)
+                            if kind == 2:
+                                assert sub.shape[1] == 32 and sub.all(), (n, c, t, w0, j0)
         # dK/dV: 128-key units, 32-key wavefronts, 64-query tiles
         for k0 in range(0, n, 128):
             khi = min(k0 + 128, n)
