@@ -146,7 +146,7 @@ hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info);
 /* Copies the work list of `op` (0 = forward / dQ, 1 = dK/dV) to host memory as int32 quadruples
  * {sequence, head, first row (or key), cost} in launch order; op 2 gives the bf16 forward items
  * as int32 octets {sequence, head, first row, cost, first tile, end tile, partial slot or -1, 0}
- * (tiles index the row block's list of visible key tiles).  Writes at most `cap` items and
+ * (row blocks of fwd_item_rows rows; tiles index the row block's list of visible key tiles).  Writes at most `cap` items and
  * returns the total count through *count. */
 hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* units, int64_t cap,
                               int64_t* count);
@@ -154,8 +154,8 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
 /* Scratch bytes a call needs: op 0 = hstu_attn_fwd without u, 1 = hstu_attn_fwd with u,
  * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd, 4 = hstu_layer_bwd, 5 = hstu_attn_fwd_cached (d_model
  * is the model width; it does not change the result at present).  The forward ops, and op 4,
- * include 512 * head_dim bytes per partial slot of split row blocks (0 when the plan splits
- * none).  Op 2, and op 4 when larger than the partial slots, is the stored dS of the bf16
+ * include 4 * head_dim bytes per row per partial slot of split row blocks (fwd_item_rows rows:
+ * 512 * head_dim bytes for 128-row items; 0 when the plan splits none).  Op 2, and op 4 when larger than the partial slots, is the stored dS of the bf16
  * backward with head_dim 64 or 128: per sequence and head, each 128-key block holds one
  * 128 x 64 bf16 chunk per 64-query tile of the queries that see it (their range rounded out to
  * 128), about 2 bytes per visible pair plus the blocks on the diagonal (0 for fp32, head_dim 32,
