@@ -63,6 +63,43 @@ __device__ __forceinline__ Grad silu_grad(float t, float dp) {
     return Grad{pv, dp * (fmaf(-xs, sg, xs) + sg)};
 }
 
+// The layer backward's pre-activations for one lane's part of a gradient row (C layout of D / 32
+// accumulators: columns 32 db + 8 r + 4 g + c), gate_delta bytes after each output element
+// (AttnParams).  Loaded before the unit's final reduction, so their latency overlaps it.
+template <int D>
+struct GateRow {
+    bf16x4 hv[D / 32][4];
+    __device__ __forceinline__ void load(const bf16* row, int g, int64_t gate_delta) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                hv[db][r] = *reinterpret_cast<const bf16x4*>(
+                    reinterpret_cast<const char*>(row + 32 * db + 8 * r + 4 * g) + gate_delta);
+    }
+};
+
+// One lane's part of a gradient row leaving the backward: scaled, and in the layer backward
+// (gate_delta != 0, gr loaded) multiplied by SiLU'(h).
+template <int D>
+__device__ __forceinline__ void store_grad_row(bf16* row, const f32x16 (&acc)[D / 32], int g,
+                                               float scale, int64_t gate_delta,
+                                               const GateRow<D>& gr) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bf16x4 w;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float x = acc[db][4 * r + c] * scale;
+                w[c] = (bf16)(gate_delta != 0 ? x * silu_deriv((float)gr.hv[db][r][c]) : x);
+            }
+            *reinterpret_cast<bf16x4*>(row + 32 * db + 8 * r + 4 * g) = w;
+        }
+}
+
+
 
 // ---------------------------------------------------------------------------------------------
 // pass A: dK, dV
@@ -506,26 +543,20 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 for (int e = 0; e < 16; ++e) acc[db][e] += mine[(db * 16 + e) * 64];
         __syncthreads();
     };
+    bf16* dvg = static_cast<bf16*>(p.dv) + (tok0 + j) * p.ld_grad + h * D;
+    bf16* dkg = static_cast<bf16*>(p.dk) + (tok0 + j) * p.ld_grad + h * D;
+    GateRow<D> gv, gk;
+    if (p.gate_delta != 0 && key_ok && qh == 0) {
+        gv.load(dvg, g, p.gate_delta);
+        gk.load(dkg, g, p.gate_delta);
+    }
     exchange(dvt);
     exchange(dkt);
 
     if (key_ok && qh == 0) {
-        bf16* dvg = static_cast<bf16*>(p.dv) + (tok0 + j) * p.ld_grad + h * D;
-        bf16* dkg = static_cast<bf16*>(p.dk) + (tok0 + j) * p.ld_grad + h * D;
         const float sv = -kLn2 * p.inv_n, sk = p.alpha * p.inv_n;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                bf16x4 wv, wk;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    wv[c] = (bf16)(dvt[db][4 * r + c] * sv);
-                    wk[c] = (bf16)(dkt[db][4 * r + c] * sk);
-                }
-                *reinterpret_cast<bf16x4*>(dvg + 32 * db + 8 * r + 4 * g) = wv;
-                *reinterpret_cast<bf16x4*>(dkg + 32 * db + 8 * r + 4 * g) = wk;
-            }
+        store_grad_row<D>(dvg, dvt, g, sv, p.gate_delta, gv);
+        store_grad_row<D>(dkg, dkt, g, sk, p.gate_delta, gk);
     }
     if constexpr (DS && (RP || RT)) {  // the unit's bias-table gradient sums: one global atomic
         __syncthreads();                // per non-zero bucket
@@ -904,6 +935,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
         __syncthreads();
     }
 
+    bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
+    GateRow<D> gq;
+    if (p.gate_delta != 0 && row_ok && kh == 0) gq.load(dqg, g, p.gate_delta);
     // add the second key half's partial dQ into the first's through the idle K and V tile
     // buffers (adjacent), laid out [row group][db][element][lane]
     static_assert(sizeof(sm.k) + sizeof(sm.v) >= 4 * (D / 32) * 16 * 64 * sizeof(float),
@@ -924,17 +958,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
     }
 
     if (row_ok && kh == 0) {
-        bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
         const float sq = p.alpha * p.inv_n;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                bf16x4 w;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (bf16)(dqt[db][4 * r + c] * sq);
-                *reinterpret_cast<bf16x4*>(dqg + 32 * db + 8 * r + 4 * g) = w;
-            }
+        store_grad_row<D>(dqg, dqt, g, sq, p.gate_delta, gq);
     }
     if (GP || GT) {
         if (GP) { run_p_lo.add(sm.hbp, -2, 0.0f, lane); run_p_hi.add(sm.hbp, -2, 0.0f, lane); }  // flush
@@ -1088,6 +1113,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     __syncthreads();  // every wavefront is done with the K ring (the last wait_group left no copy
                       // in flight)
 
+    bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
+    GateRow<D> gq;
+    if (p.gate_delta != 0 && row_ok && kh == 0) gq.load(dqg, g, p.gate_delta);
     // add the second key half's partial dQ into the first's through the K ring, laid out
     // [row group][db][element][lane]
     static_assert(sizeof(sm.k) >= 4 * (D / 32) * 16 * 64 * sizeof(float), "reduction buffer");
@@ -1107,17 +1135,8 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     }
 
     if (row_ok && kh == 0) {
-        bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
         const float sq = p.alpha * p.inv_n;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                bf16x4 w;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (bf16)(dqt[db][4 * r + c] * sq);
-                *reinterpret_cast<bf16x4*>(dqg + 32 * db + 8 * r + 4 * g) = w;
-            }
+        store_grad_row<D>(dqg, dqt, g, sq, p.gate_delta, gq);
     }
 }
 

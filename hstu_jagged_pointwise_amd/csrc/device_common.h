@@ -88,6 +88,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float fast_sigmoid(float x) {
     return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
+// d SiLU(h) / dh = s (1 + h (1 - s)), s = sigmoid(h)
+__device__ __forceinline__ float silu_deriv(float h) {
+    const float sg = fast_sigmoid(h);
+    return sg * (1.0f + h * (1.0f - sg));
+}
 
 // Scores are carried as t = -log2(e) * S, so sigmoid(S) = 1 / (1 + 2^t) and
 // SiLU(S) = -ln(2) * t * sigmoid(S): the caller folds -ln(2) into one final scale.

@@ -964,8 +964,10 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         gw.kchunk = token_chunk(plan, T, hd, d_model);
         e = checked(hstu::launch_gemm(gw, s), s);
     }
-    // attention backward with dout = dA: dV, dQ, dK into their slots of dH
+    // attention backward with dout = dA: dV, dQ, dK into their slots of dH, already multiplied
+    // by SiLU'(H) (the projection's SiLU; the U slot is done by the LayerNorm backward)
     if (e == hipSuccess) {
+        p.gate_delta = hpre - dh;
         p.dout = da;
         p.dv = dh + size_t(hd) * 2;
         p.dq = dh + size_t(2 * hd) * 2;
@@ -987,9 +989,6 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         p.drab_ts = drab_ts;
         e = checked(hstu::launch_attn_bwd_dq_bf16(p, s), s);
     }
-    // dH = dZ * SiLU'(H) on the V, Q, K slots (the U slot is already done)
-    if (e == hipSuccess)
-        e = checked(hstu::launch_silu_bwd_bf16(dh + size_t(hd) * 2, hpre + size_t(hd) * 2, ldz, T, 3 * hd, s), s);
     // dW1 = X^T dH, split over tokens
     if (e == hipSuccess) {
         hstu::GemmArgs gw = gemm_args(plan, x, d_model, true, dh, ldz, false, d_model, 4 * hd, T, dw1,

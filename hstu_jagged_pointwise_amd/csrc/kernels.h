@@ -57,6 +57,10 @@ struct AttnParams {
     // either may be NULL) and the dQ pass does not.
     float* gpos;
     float* gts;
+    // Layer backward: when nonzero, dQ, dK and dV leave multiplied by SiLU'(h), the derivative of
+    // the projection's SiLU at its pre-activation h (bf16), found gate_delta bytes after each
+    // output element (dQ, dK, dV are blocks of dH, and H has the same layout).
+    int64_t gate_delta;
 };
 
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, hipStream_t s);
@@ -85,9 +89,6 @@ hipError_t launch_ln_gate_f32(const void* a, const void* u, int64_t ldu, void* o
 hipError_t launch_ln_gate_bwd_bf16(const void* a, const void* u, const void* hu, int64_t ldz,
                                    const float* dg, void* g, void* da, void* dhu, int64_t lddh,
                                    int64_t rows, int32_t width, float eps, hipStream_t s);
-// In place dz *= SiLU'(h) over rows x width elements with token strides ld (both).
-hipError_t launch_silu_bwd_bf16(void* dz, const void* h, int64_t ld, int64_t rows, int32_t width,
-                                hipStream_t s);
 
 // C (M x N) = epilogue(op(A) op(B)), bf16 operands, fp32 accumulation.
 enum GemmEpilogue : int32_t {

@@ -8,9 +8,8 @@
 // ln_gate_bwd_kernel: one wavefront per token.  With xhat = (a - mean) * rstd and the incoming
 // gradient dg of g = xhat * u: du = dg * xhat, dxhat = dg * u and the LayerNorm backward
 // da = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)).  The same pass writes g (for
-// dW2 = G^T dY) and turns du into the gradient before the U projection's SiLU.
-//
-// silu_bwd_kernel: dz * SiLU'(h) in place, SiLU'(h) = s (1 + h (1 - s)), s = sigmoid(h).
+// dW2 = G^T dY) and turns du into the gradient before the U projection's SiLU (the V, Q and K
+// blocks get theirs in the attention backward's stores).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -98,10 +97,6 @@ __global__ __launch_bounds__(64 * kLnRowsPerBlock) void ln_gate_kernel(
     }
 }
 
-__device__ __forceinline__ float silu_grad(float h) {
-    const float sg = fast_sigmoid(h);
-    return sg * (1.0f + h * (1.0f - sg));
-}
 
 __global__ __launch_bounds__(64 * kLnRowsPerBlock) void ln_gate_bwd_kernel(
     const bf16* a, const bf16* __restrict__ u, const bf16* __restrict__ hu, int64_t ldz,
@@ -150,7 +145,7 @@ __global__ __launch_bounds__(64 * kLnRowsPerBlock) void ln_gate_bwd_kernel(
                 x[k][e] = xh;
                 gout[e] = xh * uu[e];
                 dx[k][e] = gg[e] * uu[e];
-                dh[e] = gg[e] * xh * silu_grad(hh[e]);
+                dh[e] = gg[e] * xh * silu_deriv(hh[e]);
                 s1 += dx[k][e];
                 s2 = fmaf(dx[k][e], xh, s2);
             }
@@ -169,22 +164,6 @@ __global__ __launch_bounds__(64 * kLnRowsPerBlock) void ln_gate_bwd_kernel(
             store8(da + row * width + c, o);
         }
     }
-}
-
-constexpr int kSiluThreads = 256;
-
-__global__ __launch_bounds__(kSiluThreads) void silu_bwd_kernel(bf16* dz, const bf16* __restrict__ h,
-                                                               int64_t ld, int64_t rows, int chunks) {
-    const int64_t i = (int64_t)blockIdx.x * kSiluThreads + threadIdx.x;
-    if (i >= rows * chunks) return;
-    const int64_t row = i / chunks;
-    const int c = 8 * (int)(i - row * chunks);
-    float zz[8], hh[8];
-    load8(dz + row * ld + c, zz);
-    load8(h + row * ld + c, hh);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zz[e] *= silu_grad(hh[e]);
-    store8(dz + row * ld + c, zz);
 }
 
 template <typename T>
@@ -224,16 +203,5 @@ hipError_t launch_ln_gate_bwd_bf16(const void* a, const void* u, const void* hu,
     return hipGetLastError();
 }
 
-hipError_t launch_silu_bwd_bf16(void* dz, const void* h, int64_t ld, int64_t rows, int32_t width,
-                                hipStream_t s) {
-    if (rows <= 0 || width <= 0) return hipSuccess;
-    if (width % 8 != 0) return hipErrorInvalidValue;
-    const int chunks = width / 8;
-    const int64_t n = rows * chunks;
-    hipLaunchKernelGGL(silu_bwd_kernel, dim3((unsigned)((n + kSiluThreads - 1) / kSiluThreads)),
-                       dim3(kSiluThreads), 0, s, static_cast<bf16*>(dz),
-                       static_cast<const bf16*>(h), ld, rows, chunks);
-    return hipGetLastError();
-}
 
 }  // namespace hstu

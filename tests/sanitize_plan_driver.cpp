@@ -39,7 +39,6 @@ HSTU_STUB(launch_ln_gate_f32, const void*, const void*, int64_t, void*, int64_t,
           hipStream_t)
 HSTU_STUB(launch_ln_gate_bwd_bf16, const void*, const void*, const void*, int64_t, const float*,
           void*, void*, void*, int64_t, int64_t, int32_t, float, hipStream_t)
-HSTU_STUB(launch_silu_bwd_bf16, void*, const void*, int64_t, int64_t, int32_t, hipStream_t)
 HSTU_STUB(launch_gemm, const GemmArgs&, hipStream_t)
 HSTU_STUB(launch_jagged_select, int32_t, const int64_t*, int64_t, const int64_t*, int64_t,
           const int64_t*, int64_t, const void*, void*, hipStream_t)
