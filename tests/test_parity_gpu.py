@@ -157,17 +157,21 @@ def test_fwd_gated_by_u(dtype):
 
 
 @pytest.mark.parametrize("gated", [False, True])
-def test_fwd_split_row_blocks(gated):
+@pytest.mark.parametrize("short", [40, 300])
+def test_fwd_split_row_blocks(gated, short):
     # one long sequence among short ones: its last row blocks run as several items whose fp32
-    # partial outputs a fix-up pass sums (the plan reports them)
-    w = hs.make_inputs([3000] + [60] * 40, 2, 64, dtype="bf16", seed=21, rab=True, num_contexts=2,
-                       num_targets=8)
+    # partial outputs a fix-up pass sums (the plan reports them); with 40 short sequences the
+    # items are 64-row blocks in the key-half layout, with 300 the 128-row blocks
+    w = hs.make_inputs([3000] + [60] * short, 2, 64, dtype="bf16", seed=21, rab=True,
+                       num_contexts=2, num_targets=8)
     dev = runner.to_device(w)
     a = runner.args_for(w, dev)
     plan = runner.plan_for(w, a)
-    assert hj.hstu_plan_info(plan)["fwd_split_blocks"] > 0
+    info = hj.hstu_plan_info(plan)
+    assert info["fwd_split_blocks"] > 0
+    assert info["fwd_item_rows"] == (64 if short == 40 else 128)
     plan.close()
-    say(f"fwd split row blocks gated={gated}")
+    say(f"fwd split row blocks gated={gated} short={short}")
     A = oracle.attn_fwd(w)
     if not gated:
         check("O", run_fwd(w), A, "bf16")
