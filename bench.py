@@ -512,12 +512,15 @@ def profile_md(folder, out):
     if trace:
         total = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace)
         L += ["## Kernel trace", "",
-              "| kernel | dispatches | average (us) | min (us) | max (us) | share | VGPR | AGPR | SGPR | LDS (B) | scratch (B/lane) |",
-              "|---|---|---|---|---|---|---|---|---|---|---|"]
+              "All dispatches of the traced run (warm-up steps included, so the average sits above the "
+              "median; the live figures below cover the timed steps only). Register and LDS columns as "
+              "rocprofv3 reports them.", "",
+              "| kernel | dispatches | average (us) | median (us) | min (us) | max (us) | share | VGPR | AGPR | SGPR | LDS (B) | scratch (B/lane) |",
+              "|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for k in order[:12]:
             ds = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in per[k]]
             r0 = per[k][0]
-            L.append(f"| `{short(k)[:100]}` | {len(ds)} | {np.mean(ds) / 1e3:.1f} | {min(ds) / 1e3:.1f} | "
+            L.append(f"| `{short(k)[:100]}` | {len(ds)} | {np.mean(ds) / 1e3:.1f} | {np.median(ds) / 1e3:.1f} | {min(ds) / 1e3:.1f} | "
                      f"{max(ds) / 1e3:.1f} | {100 * sum(ds) / total:.1f}% | {r0['VGPR_Count']} | "
                      f"{r0['Accum_VGPR_Count']} | {r0['SGPR_Count']} | {r0['LDS_Block_Size']} | {r0['Scratch_Size']} |")
         L.append("")
