@@ -310,9 +310,35 @@ def measure_peaks(torch):
         timer.record("gemm", lambda: torch.matmul(x, y))
     torch.cuda.synchronize()
     gemm_ms = float(np.median(timer.ms("gemm")))
+    del x, y
+    # the floor of the event timing itself: a one-element kernel, timed alone and back to back
+    z = torch.zeros(1, device="cuda:0")
+    tiny = lambda: z.add_(1.0)
+    for _ in range(10):
+        tiny()
+    for _ in range(20):
+        timer.record("tiny", tiny)
+    torch.cuda.synchronize()
     return {"copy_GBps": round(2 * (1 << 30) / copy_ms / 1e6, 1),
             "bf16_gemm_tflops": round(2 * n ** 3 / gemm_ms / 1e9, 1),
-            "how": "1 GiB device copy (read + write bytes); torch.matmul bf16 8192^3; medians of 10"}
+            "tiny_kernel_ms": round(float(np.median(timer.ms("tiny"))), 4),
+            "tiny_kernel_back_to_back_ms": round(back_to_back_ms(torch, tiny), 4),
+            "how": "1 GiB device copy (read + write bytes); torch.matmul bf16 8192^3; a one-element "
+                   "kernel timed like the forward workloads (alone, and 50 back to back); medians "
+                   "of 10 or 20"}
+
+
+def back_to_back_ms(torch, call, reps=50):
+    """Time per call of `reps` calls queued back to back between two events: what a call
+    occupies the GPU when the launches overlap (latency-bound workloads)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def pctl(ms):
@@ -353,9 +379,10 @@ def bench_forward(torch, hj, runner, name, iters=20, cold=False):
     torch.cuda.synchronize()
     ms = timer.ms("x")
     med = float(np.median(ms))
+    b2b = None if cold else round(back_to_back_ms(torch, call), 4)
     plan.close()
     return {"ms_median": round(med, 4), "ms_p10": round(float(np.percentile(ms, 10)), 4),
-            "ms_p90": round(float(np.percentile(ms, 90)), 4),
+            "ms_p90": round(float(np.percentile(ms, 90)), 4), "ms_back_to_back": b2b,
             "tflops": round(flops / med / 1e9, 2), "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
             "tokens_per_s": round(T / med * 1e3, 1), "algorithmic_GBps": round(nbytes / med / 1e6, 1),
             "pct_hbm_peak": round(100 * nbytes / med / 1e6 / PEAK_HBM_GBS, 2),
@@ -387,8 +414,9 @@ def bench_cached(torch, hj, runner, iters=20):
         timer.record("x", call)
     torch.cuda.synchronize()
     med = float(np.median(timer.ms("x")))
+    b2b = round(back_to_back_ms(torch, call), 4)
     plan.close()
-    return {"ms_median": round(med, 4), "tflops": round(flops / med / 1e9, 2),
+    return {"ms_median": round(med, 4), "ms_back_to_back": b2b, "tflops": round(flops / med / 1e9, 2),
             "pct_bf16_peak": round(100 * flops / med / 1e9 / PEAK_BF16_TFLOPS, 2),
             "candidates_per_s": round(T / med * 1e3, 1),
             "algorithmic_GBps": round(nbytes / med / 1e6, 1),
