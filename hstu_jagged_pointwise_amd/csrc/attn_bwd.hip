@@ -45,6 +45,7 @@ constexpr int kThreadsA = 512;          // pass A: 8 wavefronts
 constexpr int kBlk = 4 * kWaveRows;      // 128 keys (pass A) or rows (pass B) per unit
 constexpr int kTile = 64;                // queries (pass A) or keys (pass B) per tile
 constexpr int kToep = kBlk + kTile - 1;  // 191 distinct i - j per (unit, tile)
+constexpr int kReadAhead = 2;            // dK/dV pass: matrix instructions between a read and its use
 
 struct ToepEntry {
     float bias;     // -log2(e) * position bias
@@ -105,6 +106,56 @@ __device__ __forceinline__ void store_grad_row(bf16* row, const f32x16 (&acc)[D 
 // pass A: dK, dV
 // ---------------------------------------------------------------------------------------------
 
+// LDS operand reads by byte address.  In a 256-byte aligned tile (rows of 2D bytes, 16-byte
+// chunks XOR-swizzled within a row), the chunk index occupies address bits 4 .. 3 + log2(D / 8):
+// the row read at k-step ks is the ks = 0 address with bits 5.. flipped by ks, and the transposing
+// read of 32-column block mb is the mb = 0 address with bits 6.. flipped by mb.  One register per
+// lane and stream then addresses every k-step (one XOR each) instead of one register per k-step.
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_cchar*)p;
+}
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *(__attribute__((address_space(3))) const bf16x8*)(uintptr_t)a;
+#else
+    (void)a;
+    return bf16x8{};
+#endif
+}
+__device__ __forceinline__ bf16x4 lds_tr4_at(uint32_t a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_bit_cast(
+        bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)a));
+#else
+    (void)a;
+    return bf16x4{};
+#endif
+}
+// Byte offset in a tile of lane (lr = l % 32, g = l / 32)'s row read at ks = 0 (RowOperand).
+template <int D>
+__device__ __forceinline__ uint32_t row_read_off(int lane) {
+    return 2u * (uint32_t)tile_off<D>(lane & 31, 8 * (lane >> 5));
+}
+// Byte offsets in a tile of the lane's two transposing reads at mb = 0 (TrOperand).
+template <int D>
+__device__ __forceinline__ uint32_t tr_read_off(int lane, int h) {
+    const int s = lane & 15, q = (lane >> 4) & 1, rr = 4 * (lane >> 5) + (s >> 2);
+    return 2u * (uint32_t)tile_off<D>(rr + 8 * h, 16 * q + 4 * (s & 3));
+}
+// Issue order for the dK/dV pass's product blocks: N MFMAs, each fed by two LDS reads; the reads
+// run LA matrix instructions ahead.
+template <int N, int LA>
+__device__ __forceinline__ void sched_mfma_2lds() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < N - LA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
 template <int D>
 struct SmemA {
     float wt[kNumClasses];               // -log2(e) * time bias by class
@@ -120,9 +171,9 @@ struct SmemA {
     float hbp[kNumBuckets];
     float hbt[kNumBuckets][32];
     int64_t kt64[kBlk];                  // the unit's key times (read by the 64-bit time mode)
-    alignas(16) bf16 q[2][kTile * D];    // swizzled tiles (tile_off)
+    alignas(256) bf16 q[2][kTile * D];   // swizzled tiles (tile_off), 256-byte aligned (lds_b128)
     bf16 dout[2][kTile * D];
-    bf16 kb[kBlk * D];                   // the unit's keys and values, swizzled like the tiles
+    alignas(256) bf16 kb[kBlk * D];      // the unit's keys and values, swizzled like the tiles
     bf16 vb[kBlk * D];
 };
 
@@ -362,8 +413,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     // query-tile copies from inline assembly (see the forward kernel): explicit waits only
     const i32x4 qrs = rows_words(qg, n, ld, D), drs = rows_words(dog, n, p.ld_out, D);
     const TileDma<D, kThreads> qdma(tid, ld), ddma(tid, p.ld_out);
-    const RowOperand<D> rowop(lane);
-    const TrOperand<D> trop(lane);
+    // byte offsets of this lane's operand reads (lds_b128, lds_tr4_at)
+    const uint32_t roff = row_read_off<D>(lane) + (uint32_t)(qh * 64 * D);
+    const uint32_t kaddr = lds_u32(sm.kb) + row_read_off<D>(lane) + (uint32_t)(wave * 64 * D);
+    const uint32_t toff0 = tr_read_off<D>(lane, 0) + (uint32_t)(qh * 64 * D);
+    const uint32_t toff1 = tr_read_off<D>(lane, 1) + (uint32_t)(qh * 64 * D);
     // stored dS: the unit's chunks (geometry.h), one 128-key x 64-query block per tile; this
     // lane's key row, its 4 queries 4g .. 4g + 3 of each group of 8 (byte offset); the tile's
     // chunk goes into the scalar offset
@@ -441,11 +495,17 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                                               : kEmpty;
         if (kind != kEmpty) {
             f32x16 s = f32x16{}, dp = f32x16{};
+            // this lane's Q row (dO: + sizeof(sm.q)) and key row (V: + sizeof(sm.kb)) at ks = 0,
+            // opaque so that the per-ks addresses are formed here rather than held in registers
+            uint32_t qa = lds_u32(sm.q[buf]) + roff, ka = kaddr;
+            asm volatile("" : "+v"(qa), "+v"(ka));
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                s = mfma32(rowop.read(sm.q[buf], qh, ks), rowop.read(sm.kb, wave, ks), s);
-                dp = mfma32(rowop.read(sm.dout[buf], qh, ks), rowop.read(sm.vb, wave, ks), dp);
+                const uint32_t xq = qa ^ (uint32_t)(ks << 5), xk = ka ^ (uint32_t)(ks << 5);
+                s = mfma32(lds_b128(xq), lds_b128(xk), s);
+                dp = mfma32(lds_b128(xq + (uint32_t)sizeof(sm.q)), lds_b128(xk + (uint32_t)sizeof(sm.kb)), dp);
             }
+            sched_mfma_2lds<D / 8, kReadAhead>();
             float bpos = 0.0f;
             int pm = 0;
             const int ihi = imin(iq0 + kWaveRows, n) - 1;
@@ -490,13 +550,22 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            uint32_t ta0 = lds_u32(sm.q[buf]) + toff0, ta1 = lds_u32(sm.q[buf]) + toff1;
+            asm volatile("" : "+v"(ta0), "+v"(ta1));
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    dvt[db] = mfma32(trop.read(sm.dout[buf], 2 * qh + sl, db), pb[sl], dvt[db]);
-                    dkt[db] = mfma32(trop.read(sm.q[buf], 2 * qh + sl, db), db8[sl], dkt[db]);
+                    // Q tile at +0, dO tile at + sizeof(sm.q); 16 query rows per sl
+                    const uint32_t x0 = (ta0 ^ (uint32_t)(db << 6)) + (uint32_t)(sl * 32 * D);
+                    const uint32_t x1 = (ta1 ^ (uint32_t)(db << 6)) + (uint32_t)(sl * 32 * D);
+                    const uint32_t dq = (uint32_t)sizeof(sm.q);
+                    const bf16x4 d0 = lds_tr4_at(x0 + dq), d1 = lds_tr4_at(x1 + dq);
+                    const bf16x4 q0v = lds_tr4_at(x0), q1v = lds_tr4_at(x1);
+                    dvt[db] = mfma32(__builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7), pb[sl], dvt[db]);
+                    dkt[db] = mfma32(__builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7), db8[sl], dkt[db]);
                 }
+            sched_mfma_2lds<D / 8, kReadAhead>();
             // from the stored values, after the products are issued (their vector work overlaps
             // the matrix instructions, and S and dP in fp32 are no longer held)
             if constexpr (DS && (RP || RT)) {
