@@ -156,6 +156,45 @@ __device__ __forceinline__ void sched_mfma_2lds() {
     __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
 }
 
+// Bias modes of one (wavefront, query tile) of the dK/dV pass: decided once per tile for all eight
+// wavefronts by eight lanes of wavefront 0 (with the tile's tables) and read by each wavefront,
+// instead of every wavefront deriving them from the tile's ranges itself.
+struct TileModes {
+    int kind;                 // classify_key_tile
+    int pm;                   // position bias: 0 one bucket (folded into b0 .. b2), 1 per element
+    int tm;                   // time mode, as TimeSel::set
+    int later;                // TimeSel
+    float b0, b1, b2;
+    uint32_t thr, thr2;
+    int pkind, pb_lo, pb_hi;  // position span (bias-gradient sums)
+    uint32_t pthr;
+    int pneg;                 // every i - j of the tile <= 0
+    int tb_lo, tb_hi;         // time span (bias-gradient sums)
+};
+
+// TimeSel::set for one lane's own (wavefront, tile) into a TileModes record (no wavefront-uniform
+// values assumed).
+__device__ __forceinline__ int time_mode(const BiasSpan& st, bool fit, float bpos, const float* wtb,
+                                         bool later, uint32_t kmax_rel, TileModes& m) {
+    m.b0 = m.b1 = m.b2 = bpos;
+    m.thr = m.thr2 = 0xffffffffu;
+    m.later = 1;
+    if (st.kind == 0) {
+        m.b0 = m.b1 = m.b2 = bpos + wtb[st.b_lo];
+        return 0;
+    }
+    if (!fit) return 3;
+    if (st.kind == 2) return 2;
+    if (!later && (uint64_t)kmax_rel + (st.kind == 1 ? st.thr : st.thr2) > 0xffffffffull) return 2;
+    m.b0 = bpos + wtb[st.b_lo];
+    m.b1 = bpos + wtb[st.b_lo + 1];
+    m.b2 = bpos + wtb[st.b_hi];
+    m.thr = st.thr;
+    m.thr2 = st.thr2;
+    m.later = later ? 1 : 0;
+    return st.kind == 1 ? 1 : 4;
+}
+
 template <int D>
 struct SmemA {
     float wt[kNumClasses];               // -log2(e) * time bias by class
@@ -164,8 +203,10 @@ struct SmemA {
     float rp[2][kToep + 1];
     uint32_t tq[2][kTile];
     int64_t tq64[2][kTile];
-    int64_t tqmin[2][2], tqmax[2][2];  // time range of the real queries of each 32-query half
-    int fits[2];
+    TileModes modes[2][8];               // by tile buffer, 4 * query half + key group
+    int64_t kgmin[4], kgmax[4];          // key times of each key group: range, whether all fit
+    uint32_t kgmax_rel[4];               // in 32 bits relative to the sequence's first time
+    int kgfit[4];
     // bias-table gradient sums of the unit (stored-dS pass only), by bucket; time sums by
     // (bucket, lane % 32) so that per-lane additions rarely share an address
     float hbp[kNumBuckets];
@@ -404,6 +445,12 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
         }
         tjmax_rel = rel_time_u32(tjmax, tbase);  // used only when every key time fits
         if (qh == 0) sm.kt64[kWaveRows * wave + lr] = tj64;  // read after the first barrier
+        if (qh == 0 && lane == 0) {
+            sm.kgmin[wave] = tjmin;
+            sm.kgmax[wave] = tjmax;
+            sm.kgmax_rel[wave] = tjmax_rel;
+            sm.kgfit[wave] = wave_kfit ? 1 : 0;
+        }
     }
 
     f32x16 dvt[D / 32], dkt[D / 32];
@@ -443,21 +490,53 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
         qdma.issue_asm(qrs, sm.q[buf], (int)((int64_t)i0 * ld * 2));
         ddma.issue_asm(drs, sm.dout[buf], (int)((int64_t)i0 * p.ld_out * 2));
     };
-    // the tile's small tables: query times and their range, position bias by (i - j)
+    // the tile's small tables: query times, the bias modes of its eight (wavefront, tile) blocks,
+    // position bias by (i - j)
     auto store_tile = [&](int buf, int tile) {
         const int i0 = tile * kTile;
-        if (RT && tid < kTile) {  // exactly wavefront 0
-            const bool real = i0 + tid < n;
-            sm.tq64[buf][tid] = tqr;
-            sm.tq[buf][tid] = rel_time_u32(tqr, tbase);
-            const TimeRange tr = wave_time_range(tqr, real, tbase);
-            if (tid == 0) {
-                sm.fits[buf] = tr.fit ? 1 : 0;
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    sm.tqmin[buf][hf] = tr.lo[hf];
-                    sm.tqmax[buf][hf] = tr.hi[hf];
+        if (tid < kTile) {  // exactly wavefront 0
+            TimeRange tr{};
+            if (RT) {
+                const bool real = i0 + tid < n;
+                sm.tq64[buf][tid] = tqr;
+                sm.tq[buf][tid] = rel_time_u32(tqr, tbase);
+                tr = wave_time_range(tqr, real, tbase);
+            }
+            if (tid < 8) {  // lane 4 hq + w: key group w, query half hq
+                const int w = tid & 3, hq = tid >> 2;
+                const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
+                const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
+                TileModes m{};
+                m.kind = mk0 < khi && mq0 < n ? classify_key_tile(mk0, mk1, mq0, n, nc, nh, kWaveRows)
+                                              : kEmpty;
+                float bpos = 0.0f;
+                if (RP) {
+                    const BiasSpan sp = bias_span((int64_t)mq0 - (mk1 - 1), (int64_t)mq1 - mk0);
+                    m.pkind = sp.kind;
+                    m.pb_lo = sp.b_lo;
+                    m.pb_hi = sp.b_hi;
+                    m.pthr = sp.thr;
+                    m.pneg = mq1 - mk0 <= 0 ? 1 : 0;
+                    if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
+                    else m.pm = 1;
                 }
+                if (RT) {
+                    // key minus query: in the two- and three-bucket modes all differences of the
+                    // block have one sign, and each pair takes one comparison of the query time
+                    // with a per-lane limit (TimePick)
+                    const int64_t tlo = hq ? tr.lo[1] : tr.lo[0], thi = hq ? tr.hi[1] : tr.hi[0];
+                    const int64_t dlo = sm.kgmin[w] - thi;
+                    const BiasSpan st = bias_span(dlo, sm.kgmax[w] - tlo);
+                    m.tm = time_mode(st, sm.kgfit[w] && tr.fit, bpos, sm.wtb, dlo >= 0,
+                                     sm.kgmax_rel[w], m);
+                    m.tb_lo = st.b_lo;
+                    m.tb_hi = st.b_hi;
+                } else {
+                    m.b0 = m.b1 = m.b2 = bpos;
+                    m.thr = m.thr2 = 0xffffffffu;
+                    m.later = 1;
+                }
+                sm.modes[buf][tid] = m;
             }
         }
         if (RP)
@@ -487,12 +566,13 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     const int q0 = kWaveRows * qh;
     const int u0 = 4 * g - (kWaveRows * wave + lr) + (kBlk - 1) + q0;
     const float alpha2 = -kLog2e * p.alpha;
+    const int mslot = uniform_i(4 * qh + wave);
 
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, i0 = (tfirst + t) * kTile, iq0 = i0 + q0;
         if (t + 1 < ntiles) load_tile(buf ^ 1, tfirst + t + 1);
-        const int kind = wk0 < khi && iq0 < n ? classify_key_tile(wk0, wk1, iq0, n, nc, nh, kWaveRows)
-                                              : kEmpty;
+        const TileModes& md = sm.modes[buf][mslot];
+        const int kind = uniform_i(md.kind);
         if (kind != kEmpty) {
             f32x16 s = f32x16{}, dp = f32x16{};
             // this lane's Q row (dO: + sizeof(sm.q)) and key row (V: + sizeof(sm.kb)) at ks = 0,
@@ -506,24 +586,14 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 dp = mfma32(lds_b128(xq + (uint32_t)sizeof(sm.q)), lds_b128(xk + (uint32_t)sizeof(sm.kb)), dp);
             }
             sched_mfma_2lds<D / 8, kReadAhead>();
-            float bpos = 0.0f;
-            int pm = 0;
-            const int ihi = imin(iq0 + kWaveRows, n) - 1;
-            if (RP) {
-                const BiasSpan sp = bias_span((int64_t)iq0 - (wk1 - 1), (int64_t)ihi - wk0);
-                if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
-                else pm = 1;
-            }
+            const int pm = RP ? uniform_i(md.pm) : 0, tm = RT ? uniform_i(md.tm) : 0;
             TimeSel tb;
-            int tm = 0;
-            if (RT) {
-                // key minus query: in the two- and three-bucket modes all differences of the tile
-                // have one sign, and each pair takes one comparison of the query time with a
-                // per-lane limit (TimePick)
-                const int64_t dlo = tjmin - sm.tqmax[buf][qh];
-                const BiasSpan st = bias_span(dlo, tjmax - sm.tqmin[buf][qh]);
-                tm = tb.set(st, wave_kfit && sm.fits[buf], bpos, sm.wtb, dlo >= 0, tjmax_rel);
-            } else tb.set_const(bpos);
+            tb.b0 = md.b0;
+            tb.b1 = md.b1;
+            tb.b2 = md.b2;
+            tb.thr = md.thr;
+            tb.thr2 = md.thr2;
+            tb.later = md.later != 0;
             if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
             else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
             if (kind == kPartial) mask_queries(s, dp, g, iq0, lo, hi);
@@ -569,24 +639,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             // from the stored values, after the products are issued (their vector work overlaps
             // the matrix instructions, and S and dP in fp32 are no longer held)
             if constexpr (DS && (RP || RT)) {
-                // The tile's bucket spans are derived again from their inputs rather than held
-                // across the epilogue and the products, where registers are short (the empty
-                // assembly statements keep the compiler from reusing the first results).
-                int ia = iq0;
-                asm volatile("" : "+v"(ia));
-                asm volatile("" ::: "memory");
-                const int ib = imin(ia + kWaveRows, n) - 1;
-                BiasSpan gsp{0, 0, 0, 0, 0}, gst{0, 0, 0, 0, 0};
-                int gtm = 0;
-                if (RP) gsp = bias_span((int64_t)ia - (wk1 - 1), (int64_t)ib - wk0);
-                if (RT) {
-                    gst = bias_span(sm.tqmin[buf][qh] - tjmax, sm.tqmax[buf][qh] - tjmin);
-                    // the mode TimeSel::set picks (no overflow condition here)
-                    gtm = gst.kind == 0 ? 0 : !(wave_kfit && sm.fits[buf]) ? 3
-                        : gst.kind == 2 ? 2 : gst.kind == 1 ? 1 : 4;
-                }
-                grads_a<D, RP, RT>(db8, sm, buf, q0, ia, j, g, lane, gsp, ib - wk0 <= 0, gst, gtm,
-                                   gst.thr, gst.thr2, tj, kWaveRows * wave + lr);
+                const BiasSpan gsp{RP ? uniform_i(md.pkind) : 0, md.pb_lo, md.pb_hi, md.pthr, 0u};
+                const BiasSpan gst{0, md.tb_lo, md.tb_hi, md.thr, md.thr2};
+                grads_a<D, RP, RT>(db8, sm, buf, q0, iq0, j, g, lane, gsp, md.pneg != 0, gst,
+                                   RT ? uniform_i(md.tm) : 0, md.thr, md.thr2, tj,
+                                   kWaveRows * wave + lr);
             }
         }
         if (t + 1 < ntiles) store_tile(buf ^ 1, tfirst + t + 1);
