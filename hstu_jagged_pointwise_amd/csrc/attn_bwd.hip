@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     static_assert(sizeof(sm.q) + sizeof(sm.dout) >= 4 * (D / 32) * 16 * 64 * sizeof(float),
                   "reduction buffer");
 
-    const int wk0 = k0 + kWaveRows * wave, wk1 = imin(wk0 + kWaveRows, khi);
+    const int wk0 = k0 + kWaveRows * wave;
     const int j = wk0 + lr;
     const bool key_ok = j < khi;
     int lo = 1, hi = 0;  // rows that see key j: lo <= i <= hi
