@@ -60,8 +60,7 @@ struct Grad {
 __device__ __forceinline__ Grad silu_grad(float t, float dp) {
     const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
     const float pv = t * sg;
-    const float xs = -kLn2 * pv;
-    return Grad{pv, dp * (fmaf(-xs, sg, xs) + sg)};
+    return Grad{pv, dp * fmaf(kLn2, fmaf(pv, sg, -pv), sg)};
 }
 
 // The layer backward's pre-activations for one lane's part of a gradient row (C layout of D / 32
@@ -223,11 +222,13 @@ struct SmemA {
 //   TM 0: time bias absent or one bucket; 1: two buckets, b1 where |dt| >= thr; 2 / 3: per-element
 //      bucket class with 32-bit / 64-bit times.
 // One wavefront's 32 x 32 block: queries q0 + (8r + 4g + c) of the tile (C layout), its key per
-// lane; u0 is the Toeplitz slot of the block's first query for this lane.
+// lane; u0 is the Toeplitz slot of the block's first query for this lane.  The modes only form
+// the scores t = -log2(e) S in place; the sigmoid and gradient arithmetic that follows is common
+// (silu_grad_all), so the mode branches rejoin with one register set.
 template <int D, int PM, int TM>
-__device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>& sm, int buf,
-                                           int q0, int u0, int g, float alpha2, const TimeSel tb,
-                                           uint32_t tj, int kl) {
+__device__ __forceinline__ void scores_a(f32x16& s, const SmemA<D>& sm, int buf, int q0, int u0,
+                                         int g, float alpha2, const TimeSel tb, uint32_t tj,
+                                         int kl) {
     const TimePick pick(tb, tj);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -241,23 +242,31 @@ __device__ __forceinline__ void epilogue_a(f32x16& s, f32x16& dp, const SmemA<D>
             if (PM == 1) b += sm.rp[buf][u0 + 8 * r + c];
             if (TM == 2) b += sm.wt[bucket_class(absdiff_u32(tj, tq4[c]))];
             if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(sm.kt64[kl], sm.tq64[buf][ii + c]))];
-            const Grad gr = silu_grad(fmaf(alpha2, s[e], b), dp[e]);
-            s[e] = gr.p;
-            dp[e] = gr.ds;
+            s[e] = fmaf(alpha2, s[e], b);
         }
     }
 }
 
 template <int D, int PM>
-__device__ __forceinline__ void epilogue_a_tm(int tm, f32x16& s, f32x16& dp, const SmemA<D>& sm,
-                                              int buf, int q0, int u0, int g, float alpha2,
-                                              const TimeSel tb, uint32_t tj, int kl) {
+__device__ __forceinline__ void scores_a_tm(int tm, f32x16& s, const SmemA<D>& sm, int buf, int q0,
+                                            int u0, int g, float alpha2, const TimeSel tb,
+                                            uint32_t tj, int kl) {
     switch (tm) {
-        case 0: epilogue_a<D, PM, 0>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
-        case 1: epilogue_a<D, PM, 1>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
-        case 4: epilogue_a<D, PM, 4>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
-        case 2: epilogue_a<D, PM, 2>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
-        default: epilogue_a<D, PM, 3>(s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 0: scores_a<D, PM, 0>(s, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 1: scores_a<D, PM, 1>(s, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 4: scores_a<D, PM, 4>(s, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        case 2: scores_a<D, PM, 2>(s, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+        default: scores_a<D, PM, 3>(s, sm, buf, q0, u0, g, alpha2, tb, tj, kl); break;
+    }
+}
+
+// P' and dS N of all sixteen elements from the scores and dP (silu_grad).
+__device__ __forceinline__ void silu_grad_all(f32x16& s, f32x16& dp) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const Grad gr = silu_grad(s[e], dp[e]);
+        s[e] = gr.p;
+        dp[e] = gr.ds;
     }
 }
 
@@ -594,8 +603,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             tb.thr = md.thr;
             tb.thr2 = md.thr2;
             tb.later = md.later != 0;
-            if (pm) epilogue_a_tm<D, 1>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
-            else epilogue_a_tm<D, 0>(tm, s, dp, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
+            if (pm) scores_a_tm<D, 1>(tm, s, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
+            else scores_a_tm<D, 0>(tm, s, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
+            silu_grad_all(s, dp);
             if (kind == kPartial) mask_queries(s, dp, g, iq0, lo, hi);
             bf16x8 pb[2], db8[2];
 #pragma unroll
