@@ -155,43 +155,69 @@ __device__ __forceinline__ void sched_mfma_2lds() {
     __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
 }
 
-// Bias modes of one (wavefront, query tile) of the dK/dV pass: decided once per tile for all eight
-// wavefronts by eight lanes of wavefront 0 (with the tile's tables) and read by each wavefront,
-// instead of every wavefront deriving them from the tile's ranges itself.
-struct TileModes {
-    int kind;                 // classify_key_tile
-    int pm;                   // position bias: 0 one bucket (folded into b0 .. b2), 1 per element
-    int tm;                   // time mode, as TimeSel::set
-    int later;                // TimeSel
-    float b0, b1, b2;
-    uint32_t thr, thr2;
-    int pkind, pb_lo, pb_hi;  // position span (bias-gradient sums)
-    uint32_t pthr;
-    int pneg;                 // every i - j of the tile <= 0
-    int tb_lo, tb_hi;         // time span (bias-gradient sums)
+// Bias modes of one (wavefront, query tile) of the dK/dV pass, the same for every head: the tile
+// kind, the position and time modes with their buckets and thresholds.  With the stored-dS
+// workspace the modes pass (bwd_modes_kernel) writes them for every (sequence, key block, query
+// tile) ahead of the dK/dV pass, which copies each tile's eight records into LDS with its rows;
+// without it eight lanes of wavefront 0 decide them from the tile's times.  Each wavefront turns
+// its record into bias values with its head's tables (mode_timesel).
+struct ModeRec {
+    uint32_t bits;  // kind | pm << 2 | tm << 3 | later << 6 | pkind << 7 | pneg << 9
+    uint32_t bk;    // position buckets lo | hi << 8, time buckets lo << 16 | hi << 24
+    uint32_t thr, thr2;  // time thresholds (modes 1 and 4)
+    uint32_t pthr;       // position threshold (two position buckets)
+    uint32_t pad[3];
 };
+static_assert(sizeof(ModeRec) == 32, "eight records make one 256-byte copy");
 
-// TimeSel::set for one lane's own (wavefront, tile) into a TileModes record (no wavefront-uniform
-// values assumed).
-__device__ __forceinline__ int time_mode(const BiasSpan& st, bool fit, float bpos, const float* wtb,
-                                         bool later, uint32_t kmax_rel, TileModes& m) {
-    m.b0 = m.b1 = m.b2 = bpos;
-    m.thr = m.thr2 = 0xffffffffu;
-    m.later = 1;
-    if (st.kind == 0) {
-        m.b0 = m.b1 = m.b2 = bpos + wtb[st.b_lo];
-        return 0;
+// The record of key group [mk0, mk1) (key times tkmin .. tkmax; kfit: all fit in 32 bits relative
+// to the sequence's first time; kmax_rel: tkmax so) against query rows mq0 .. mq1 (times
+// tlo .. thi; qfit as kfit) of a sequence of n rows with nc contexts and nh = n - candidates.
+//   pm: position bias one bucket (0) or per element (1); pkind, buckets, pthr, pneg: the position
+//   span for the bias-gradient sums (pneg: every i - j <= 0).
+//   tm (as TimeSel::set): 0 one time bucket, 1 / 4 two / three buckets by threshold (key minus
+//   query has one sign; later: key times not below query times), 2 / 3 per-element class with
+//   32-bit / 64-bit times.
+__device__ __forceinline__ ModeRec make_mode_rec(bool rp, bool rt, int mk0, int mk1, int mq0,
+                                                 int mq1, int n, int nc, int nh, int64_t tkmin,
+                                                 int64_t tkmax, bool kfit, uint32_t kmax_rel,
+                                                 int64_t tlo, int64_t thi, bool qfit) {
+    ModeRec m{};
+    const uint32_t kind = mk0 < mk1 && mq0 < n ? classify_key_tile(mk0, mk1, mq0, n, nc, nh, kWaveRows)
+                                               : kEmpty;
+    uint32_t pm = 0, tm = 0, later = 1, pkind = 0, pneg = 0, pb_lo = 0, pb_hi = 0, tb_lo = 0,
+             tb_hi = 0;
+    m.thr = m.thr2 = m.pthr = 0xffffffffu;
+    if (rp) {
+        const BiasSpan sp = bias_span((int64_t)mq0 - (mk1 - 1), (int64_t)mq1 - mk0);
+        pkind = (uint32_t)sp.kind;
+        pb_lo = (uint32_t)sp.b_lo;
+        pb_hi = (uint32_t)sp.b_hi;
+        m.pthr = sp.thr;
+        pneg = mq1 - mk0 <= 0 ? 1u : 0u;
+        pm = sp.kind != 0 ? 1u : 0u;
     }
-    if (!fit) return 3;
-    if (st.kind == 2) return 2;
-    if (!later && (uint64_t)kmax_rel + (st.kind == 1 ? st.thr : st.thr2) > 0xffffffffull) return 2;
-    m.b0 = bpos + wtb[st.b_lo];
-    m.b1 = bpos + wtb[st.b_lo + 1];
-    m.b2 = bpos + wtb[st.b_hi];
-    m.thr = st.thr;
-    m.thr2 = st.thr2;
-    m.later = later ? 1 : 0;
-    return st.kind == 1 ? 1 : 4;
+    if (rt) {
+        const int64_t dlo = tkmin - thi;
+        const BiasSpan st = bias_span(dlo, tkmax - tlo);
+        tb_lo = (uint32_t)st.b_lo;
+        tb_hi = (uint32_t)st.b_hi;
+        const bool lat = dlo >= 0;
+        if (st.kind == 0) tm = 0;
+        else if (!(kfit && qfit)) tm = 3;
+        else if (st.kind == 2) tm = 2;
+        else if (!lat && (uint64_t)kmax_rel + (st.kind == 1 ? st.thr : st.thr2) > 0xffffffffull)
+            tm = 2;
+        else {
+            tm = st.kind == 1 ? 1u : 4u;
+            m.thr = st.thr;
+            m.thr2 = st.thr2;
+            later = lat ? 1u : 0u;
+        }
+    }
+    m.bits = kind | pm << 2 | tm << 3 | later << 6 | pkind << 7 | pneg << 9;
+    m.bk = pb_lo | pb_hi << 8 | tb_lo << 16 | tb_hi << 24;
+    return m;
 }
 
 template <int D>
@@ -202,7 +228,7 @@ struct SmemA {
     float rp[2][kToep + 1];
     uint32_t tq[2][kTile];
     int64_t tq64[2][kTile];
-    TileModes modes[2][8];               // by tile buffer, 4 * query half + key group
+    ModeRec modes[2][8];                 // by tile buffer, 4 * query half + key group
     int64_t kgmin[4], kgmax[4];          // key times of each key group: range, whether all fit
     uint32_t kgmax_rel[4];               // in 32 bits relative to the sequence's first time
     int kgfit[4];
@@ -216,6 +242,30 @@ struct SmemA {
     alignas(256) bf16 kb[kBlk * D];      // the unit's keys and values, swizzled like the tiles
     bf16 vb[kBlk * D];
 };
+
+// A record's bias values for this head: TimeSel with the position bias folded in when it is one
+// bucket (bits, bk, thresholds wavefront-uniform).
+template <int D, bool RP, bool RT>
+__device__ __forceinline__ TimeSel mode_timesel(uint32_t bits, uint32_t bk, uint32_t thr,
+                                                uint32_t thr2, const SmemA<D>& sm) {
+    const uint32_t pm = (bits >> 2) & 1u, tm = (bits >> 3) & 7u;
+    const float bpos = RP && pm == 0 ? sm.wp[bk & 0xffu] : 0.0f;
+    TimeSel tb;
+    tb.set_const(bpos);
+    if (RT) {
+        const int lo = (int)((bk >> 16) & 0xffu), hi = (int)(bk >> 24);
+        if (tm == 0) tb.set_const(bpos + sm.wtb[lo]);
+        else if (tm == 1 || tm == 4) {
+            tb.b0 = bpos + sm.wtb[lo];
+            tb.b1 = bpos + sm.wtb[imin(lo + 1, kNumBuckets - 1)];
+            tb.b2 = bpos + sm.wtb[hi];
+            tb.thr = thr;
+            tb.thr2 = thr2;
+            tb.later = ((bits >> 6) & 1u) != 0;
+        }
+    }
+    return tb;
+}
 
 // Bias modes of a (wavefront, tile) as in the forward:
 //   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
@@ -489,21 +539,42 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     }
     const buffer_rsrc dsrs = bytes_rsrc(dsb, ds_size);
     int64_t tqr = 0;
+    // stored-dS workspace: the unit's mode records (one 256-byte block per tile, from the modes
+    // pass) and the sequence's relative and raw query times, copied into LDS with each tile
+    i32x4 mrs{}, trs{}, tsrs{};
+    if constexpr (DS) {
+        const int kb = k0 / kBlk;
+        const ModeRec* mb = static_cast<const ModeRec*>(p.modes) +
+                            8 * (p.ds_off[wu.seq] / ((int64_t)kDsChunk * p.heads) +
+                                 ds_chunks_before(kb, n, nc, nh));
+        mrs = rsrc_words(mb, (int64_t)ntiles * 8 * (int64_t)sizeof(ModeRec));
+        trs = rsrc_words(RT ? p.tq_rel + tok0 : nullptr, RT ? (int64_t)n * 4 : 0);
+        tsrs = rsrc_words(RT ? p.ts + tok0 : nullptr, RT ? (int64_t)n * 8 : 0);
+    }
     // starts the copy of a query tile's Q and dO rows into buffer buf and loads its timestamps
+    // (stored-dS workspace: copies its records and times too, one 256-byte copy per wavefront
+    // 0 .. 3; rows past the sequence end read as zero)
     auto load_tile = [&](int buf, int tile) {
         const int i0 = tile * kTile;
-        if (RT && tid < kTile) {  // first: see the forward kernel's load_tile
+        if constexpr (DS) {
+            if (tid < 64) copy4_lds_asm(mrs, lds_addr(&sm.modes[buf][0]), (tile - tfirst) * 256 + 4 * lane);
+            else if (RT && tid < 128) copy4_lds_asm(trs, lds_addr(&sm.tq[buf][0]), i0 * 4 + 4 * lane);
+            else if (RT && tid < 256) {
+                const int hf = (tid >> 6) - 2;
+                copy4_lds_asm(tsrs, lds_addr(&sm.tq64[buf][32 * hf]), i0 * 8 + 256 * hf + 4 * lane);
+            }
+        } else if (RT && tid < kTile) {  // first: see the forward kernel's load_tile
             const int i = i0 + tid;
             tqr = i < n ? p.ts[tok0 + i] : tbase;
         }
         qdma.issue_asm(qrs, sm.q[buf], (int)((int64_t)i0 * ld * 2));
         ddma.issue_asm(drs, sm.dout[buf], (int)((int64_t)i0 * p.ld_out * 2));
     };
-    // the tile's small tables: query times, the bias modes of its eight (wavefront, tile) blocks,
+    // the tile's small tables: (without the workspace) query times and the eight mode records;
     // position bias by (i - j)
     auto store_tile = [&](int buf, int tile) {
         const int i0 = tile * kTile;
-        if (tid < kTile) {  // exactly wavefront 0
+        if (!DS && tid < kTile) {  // exactly wavefront 0
             TimeRange tr{};
             if (RT) {
                 const bool real = i0 + tid < n;
@@ -515,37 +586,10 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 const int w = tid & 3, hq = tid >> 2;
                 const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
                 const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
-                TileModes m{};
-                m.kind = mk0 < khi && mq0 < n ? classify_key_tile(mk0, mk1, mq0, n, nc, nh, kWaveRows)
-                                              : kEmpty;
-                float bpos = 0.0f;
-                if (RP) {
-                    const BiasSpan sp = bias_span((int64_t)mq0 - (mk1 - 1), (int64_t)mq1 - mk0);
-                    m.pkind = sp.kind;
-                    m.pb_lo = sp.b_lo;
-                    m.pb_hi = sp.b_hi;
-                    m.pthr = sp.thr;
-                    m.pneg = mq1 - mk0 <= 0 ? 1 : 0;
-                    if (sp.kind == 0) bpos = sm.wp[sp.b_lo];
-                    else m.pm = 1;
-                }
-                if (RT) {
-                    // key minus query: in the two- and three-bucket modes all differences of the
-                    // block have one sign, and each pair takes one comparison of the query time
-                    // with a per-lane limit (TimePick)
-                    const int64_t tlo = hq ? tr.lo[1] : tr.lo[0], thi = hq ? tr.hi[1] : tr.hi[0];
-                    const int64_t dlo = sm.kgmin[w] - thi;
-                    const BiasSpan st = bias_span(dlo, sm.kgmax[w] - tlo);
-                    m.tm = time_mode(st, sm.kgfit[w] && tr.fit, bpos, sm.wtb, dlo >= 0,
-                                     sm.kgmax_rel[w], m);
-                    m.tb_lo = st.b_lo;
-                    m.tb_hi = st.b_hi;
-                } else {
-                    m.b0 = m.b1 = m.b2 = bpos;
-                    m.thr = m.thr2 = 0xffffffffu;
-                    m.later = 1;
-                }
-                sm.modes[buf][tid] = m;
+                sm.modes[buf][tid] = make_mode_rec(
+                    RP, RT, mk0, mk1, mq0, mq1, n, nc, nh, sm.kgmin[w], sm.kgmax[w],
+                    sm.kgfit[w] != 0, sm.kgmax_rel[w], hq ? tr.lo[1] : tr.lo[0],
+                    hq ? tr.hi[1] : tr.hi[0], tr.fit);
             }
         }
         if (RP)
@@ -580,8 +624,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1, i0 = (tfirst + t) * kTile, iq0 = i0 + q0;
         if (t + 1 < ntiles) load_tile(buf ^ 1, tfirst + t + 1);
-        const TileModes& md = sm.modes[buf][mslot];
-        const int kind = uniform_i(md.kind);
+        const ModeRec& md = sm.modes[buf][mslot];
+        const uint32_t mbits = (uint32_t)uniform_i((int)md.bits);
+        const int kind = (int)(mbits & 3u);
         if (kind != kEmpty) {
             f32x16 s = f32x16{}, dp = f32x16{};
             // this lane's Q row (dO: + sizeof(sm.q)) and key row (V: + sizeof(sm.kb)) at ks = 0,
@@ -595,14 +640,9 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
                 dp = mfma32(lds_b128(xq + (uint32_t)sizeof(sm.q)), lds_b128(xk + (uint32_t)sizeof(sm.kb)), dp);
             }
             sched_mfma_2lds<D / 8, kReadAhead>();
-            const int pm = RP ? uniform_i(md.pm) : 0, tm = RT ? uniform_i(md.tm) : 0;
-            TimeSel tb;
-            tb.b0 = md.b0;
-            tb.b1 = md.b1;
-            tb.b2 = md.b2;
-            tb.thr = md.thr;
-            tb.thr2 = md.thr2;
-            tb.later = md.later != 0;
+            const int pm = RP ? (int)((mbits >> 2) & 1u) : 0, tm = RT ? (int)((mbits >> 3) & 7u) : 0;
+            const uint32_t mbk = (uint32_t)uniform_i((int)md.bk);
+            const TimeSel tb = mode_timesel<D, RP, RT>(mbits, mbk, md.thr, md.thr2, sm);
             if (pm) scores_a_tm<D, 1>(tm, s, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
             else scores_a_tm<D, 0>(tm, s, sm, buf, q0, u0, g, alpha2, tb, tj, kWaveRows * wave + lr);
             silu_grad_all(s, dp);
@@ -649,10 +689,13 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dkdv_kernel(const AttnParams
             // from the stored values, after the products are issued (their vector work overlaps
             // the matrix instructions, and S and dP in fp32 are no longer held)
             if constexpr (DS && (RP || RT)) {
-                const BiasSpan gsp{RP ? uniform_i(md.pkind) : 0, md.pb_lo, md.pb_hi, md.pthr, 0u};
-                const BiasSpan gst{0, md.tb_lo, md.tb_hi, md.thr, md.thr2};
-                grads_a<D, RP, RT>(db8, sm, buf, q0, iq0, j, g, lane, gsp, md.pneg != 0, gst,
-                                   RT ? uniform_i(md.tm) : 0, md.thr, md.thr2, tj,
+                const uint32_t gb = (uint32_t)uniform_i((int)md.bits);
+                const uint32_t gk = (uint32_t)uniform_i((int)md.bk);
+                const BiasSpan gsp{RP ? (int)((gb >> 7) & 3u) : 0, (int)(gk & 0xffu),
+                                   (int)((gk >> 8) & 0xffu), md.pthr, 0u};
+                const BiasSpan gst{0, (int)((gk >> 16) & 0xffu), (int)(gk >> 24), md.thr, md.thr2};
+                grads_a<D, RP, RT>(db8, sm, buf, q0, iq0, j, g, lane, gsp, ((gb >> 9) & 1u) != 0,
+                                   gst, RT ? (int)((gb >> 3) & 7u) : 0, md.thr, md.thr2, tj,
                                    kWaveRows * wave + lr);
             }
         }
@@ -1454,10 +1497,72 @@ __global__ void zero_f32_list_kernel(const ZeroList z) {
         p[i] = 0.0f;
 }
 
+// The modes pass of the stored-dS backward: for each (sequence, 128-key block) -- the head-0
+// units of the dK/dV unit list; the records do not depend on the head -- the mode record of every
+// (query tile, wavefront) the dK/dV pass visits (one wavefront per tile: the tile's time range,
+// then eight lanes), and the times of the block's own rows relative to the sequence's first time.
+template <bool RP, bool RT>
+__global__ __launch_bounds__(256) void bwd_modes_kernel(const AttnParams p) {
+    __shared__ int64_t kmin[4], kmax[4];
+    __shared__ uint32_t kmaxr[4];
+    __shared__ int kfit[4];
+    const WorkUnit wu = p.units[blockIdx.x];
+    if (wu.head != 0) return;  // uniform over the workgroup
+    const SeqInfo si = p.seqs[wu.seq];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = si.n, nc = si.nc, nh = si.nh, k0 = wu.row0;
+    const int64_t tok0 = si.start;
+    const int khi = imin(k0 + kBlk, n);
+    int qlo, qhi;
+    rows_for_keys(k0, khi, n, nc, nh, &qlo, &qhi);
+    const int tfirst = qlo / kTile, ntiles = cdiv(qhi, kTile) - tfirst;
+    const int64_t tbase = RT ? p.ts[tok0] : 0;
+    if (RT) {
+        // key group `wave`: keys k0 + 32 wave + (lane % 32), as the dK/dV pass reads them
+        const int j = k0 + kWaveRows * wave + (lane & 31);
+        const bool key_ok = j < khi;
+        const int64_t t = key_ok ? p.ts[tok0 + j] : tbase;
+        const bool fit = __all(rel_time_fits(t, tbase));
+        int64_t lo, hi;
+        wave_time_minmax(t, key_ok, tbase, lo, hi);
+        if (lane == 0) {
+            kmin[wave] = lo;
+            kmax[wave] = hi;
+            kmaxr[wave] = rel_time_u32(hi, tbase);
+            kfit[wave] = fit ? 1 : 0;
+        }
+        for (int r = tid; r < kBlk; r += 256)  // every row lies in exactly one key block
+            if (k0 + r < n) p.tq_rel[tok0 + k0 + r] = rel_time_u32(p.ts[tok0 + k0 + r], tbase);
+    }
+    __syncthreads();
+    ModeRec* out = static_cast<ModeRec*>(p.modes) +
+                   8 * (p.ds_off[wu.seq] / ((int64_t)kDsChunk * p.heads) +
+                        ds_chunks_before(k0 / kBlk, n, nc, nh));
+    for (int t = wave; t < ntiles; t += 4) {
+        const int i0 = (tfirst + t) * kTile;
+        TimeRange tr{};
+        if (RT) {
+            const bool real = i0 + lane < n;
+            tr = wave_time_range(real ? p.ts[tok0 + i0 + lane] : tbase, real, tbase);
+        }
+        if (lane < 8) {  // lane 4 hq + w: key group w, query half hq
+            const int w = lane & 3, hq = lane >> 2;
+            const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
+            const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
+            out[8 * t + lane] = make_mode_rec(RP, RT, mk0, mk1, mq0, mq1, n, nc, nh, kmin[w],
+                                              kmax[w], kfit[w] != 0, kmaxr[w],
+                                              hq ? tr.lo[1] : tr.lo[0], hq ? tr.hi[1] : tr.hi[0],
+                                              tr.fit);
+        }
+    }
+}
+
 template <int D, bool RP, bool RT>
 hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
     if constexpr (D >= 64)
         if (p.ds) {
+            if (!p.modes || (RT && !p.tq_rel)) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((bwd_modes_kernel<RP, RT>), dim3(p.num_units), dim3(256), 0, s, p);
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, RP, RT, true>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
             return hipGetLastError();
         }

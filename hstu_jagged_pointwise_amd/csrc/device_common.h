@@ -533,6 +533,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)reinterpret_cast<uintptr_t>(p));
 }
 
+// Lane l copies 4 bytes at byte offset voff to LDS address lds + 4 l.
+__device__ __forceinline__ void copy4_lds_asm(i32x4 rs, uint32_t lds, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+#else
+    (void)rs;
+    (void)lds;
+    (void)voff;
+#endif
+}
+
 // Lane l copies 16 bytes at byte offset voff to LDS address lds + 16 l.
 __device__ __forceinline__ void copy16_lds_asm(i32x4 rs, uint32_t lds, int voff) {
 #if defined(__HIP_DEVICE_COMPILE__)

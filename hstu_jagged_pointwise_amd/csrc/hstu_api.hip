@@ -275,6 +275,24 @@ size_t part_bytes(const hstu_plan_t* plan) {
 // Stored dS of the bf16 backward (0 when the plan does not use it).
 size_t ds_bytes(const hstu_plan_t* plan) { return align_up(size_t(plan->ds_elems) * 2, 256); }
 
+// The stored-dS dK/dV pass's bias-mode records (256 bytes per chunk of one head: one 32-byte
+// record per wavefront of the 128-key x 64-query block) and the query times relative to each
+// sequence's first (4 bytes per token), after the dS (and in op 2 after the gradient tables).
+size_t rec_bytes(const hstu_plan_t* plan) {
+    if (plan->ds_elems <= 0) return 0;
+    const int64_t chunks = plan->ds_elems / (int64_t(hstu::kDsChunk) * plan->shape.num_heads);
+    return align_up(size_t(chunks) * 256, 256);
+}
+size_t modes_bytes(const hstu_plan_t* plan) {
+    if (plan->ds_elems <= 0) return 0;
+    return rec_bytes(plan) + align_up(size_t(plan->shape.total_tokens) * 4, 256);
+}
+// Points p's mode records and relative times at `at` (the layout of modes_bytes).
+void set_modes(const hstu_plan_t* plan, char* at, hstu::AttnParams* p) {
+    p->modes = at;
+    p->tq_rel = reinterpret_cast<uint32_t*>(at + rec_bytes(plan));
+}
+
 // The bias-table gradients the stored-dS dK/dV pass sums for the dQ pass to hand out: two
 // [H][128] fp32 tables after the stored dS.
 size_t grad_bytes(const hstu_plan_t* plan) {
@@ -602,7 +620,7 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
     switch (op) {
         case 0: return part_bytes(plan);
         case 1: return align_up(thd * elem_size(a.dtype), 256) + part_bytes(plan);
-        case 2: return ds_bytes(plan) + grad_bytes(plan);
+        case 2: return ds_bytes(plan) + grad_bytes(plan) + modes_bytes(plan);
         case 3: {
             (void)d_model;  // Z and A depend on H*d only
             return align_up(4 * thd * 2, 256) + align_up(thd * 2, 256) + part_bytes(plan);
@@ -612,7 +630,7 @@ size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model
             (void)d_model;
             // Z, H (pre-activation), dH: T x 4Hd bf16; A, G, dA: T x Hd bf16; dG: T x Hd fp32
             return 3 * align_up(4 * thd * 2, 256) + 3 * align_up(thd * 2, 256) +
-                   align_up(thd * 4, 256) + std::max(part_bytes(plan), ds_bytes(plan));
+                   align_up(thd * 4, 256) + std::max(part_bytes(plan), ds_bytes(plan) + modes_bytes(plan));
         }
         default: return 0;
     }
@@ -738,6 +756,7 @@ hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t
     p.dv = dv;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.ds) {  // this pass sums the bias-table gradients into the workspace
+        set_modes(plan, static_cast<char*>(ws) + ds_bytes(plan) + grad_bytes(plan), &p);
         float* grads = reinterpret_cast<float*>(static_cast<char*>(ws) + ds_bytes(plan));
         const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
         p.gpos = args->rab_pos ? grads : nullptr;
@@ -977,6 +996,7 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         if (plan->ds_elems > 0) {  // the dK/dV pass then sums the bias-table gradients
             p.ds = tail;
             p.ds_off = plan->d_ds_off;
+            set_modes(plan, tail + ds_bytes(plan), &p);
             p.gpos = drab_pos;
             p.gts = drab_ts;
         }

@@ -57,6 +57,12 @@ struct AttnParams {
     // either may be NULL) and the dQ pass does not.
     float* gpos;
     float* gts;
+    // With ds: the bias-mode records the dK/dV pass launch writes in a pass of its own before
+    // the products (32 bytes per sequence, 128-key block, query tile and wavefront: dS chunk
+    // count / heads x 256 bytes) and the query times relative to each sequence's first (uint32
+    // per token; with a time bias only).
+    void* modes;
+    uint32_t* tq_rel;
     // Layer backward: when nonzero, dQ, dK and dV leave multiplied by SiLU'(h), the derivative of
     // the projection's SiLU at its pre-activation h (bf16), found gate_delta bytes after each
     // output element (dQ, dK, dV are blocks of dH, and H has the same layout).

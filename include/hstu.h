@@ -155,12 +155,15 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
  * 2 = hstu_attn_bwd, 3 = hstu_layer_fwd, 4 = hstu_layer_bwd, 5 = hstu_attn_fwd_cached (d_model
  * is the model width; it does not change the result at present).  The forward ops, and op 4,
  * include 4 * head_dim bytes per row per partial slot of split row blocks (fwd_item_rows rows:
- * 512 * head_dim bytes for 128-row items; 0 when the plan splits none).  Op 2, and op 4 when larger than the partial slots, is the stored dS of the bf16
- * backward with head_dim 64 or 128: per sequence and head, each 128-key block holds one
- * 128 x 64 bf16 chunk per 64-query tile of the queries that see it (their range rounded out to
- * 128), about 2 bytes per visible pair plus the blocks on the diagonal (0 for fp32, head_dim 32,
- * or a sequence of 8M tokens or more); op 2 adds 2 * H * 128 fp32 (rounded up to 256 bytes) for
- * the bias-table gradients that pass sums. */
+ * 512 * head_dim bytes for 128-row items; 0 when the plan splits none).  Op 2, and op 4 when
+ * larger than the partial slots, is the stored dS of the bf16 backward with head_dim 64 or 128:
+ * per sequence and head, each 128-key block holds one 128 x 64 bf16 chunk per 64-query tile of
+ * the queries that see it (their range rounded out to 128), about 2 bytes per visible pair plus
+ * the blocks on the diagonal (0 for fp32, head_dim 32, or a sequence of 8M tokens or more),
+ * followed by the dK/dV pass's bias-mode records (256 bytes per chunk of one head, rounded up to
+ * 256 bytes) and the query times relative to each sequence's first (4 bytes per token, rounded
+ * up to 256 bytes); op 2 puts 2 * H * 128 fp32 (rounded up to 256 bytes) between the dS and the
+ * records for the bias-table gradients that pass sums. */
 size_t hstu_workspace_bytes(const hstu_plan_t* plan, int32_t op, int32_t d_model);
 
 /* Attention forward (equation (2) above).  q, k, v: THD inputs; out: dense THD output.

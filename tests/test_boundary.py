@@ -210,11 +210,14 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
     # dK/dV pass sums (rounded up to 256 bytes)
     ds = 3 * 2 * 128 * 128 * 2
     grads = 2 * 2 * 128 * 4
-    assert hj.hstu_workspace_bytes(plan, hj.OP_BWD) == ds + grads
+    # the dK/dV pass's mode records: 256 bytes per chunk of one head (3 sequences x 2 chunks),
+    # then the relative query times, 4 bytes per token, each rounded up to 256 bytes
+    modes = 3 * 2 * 256 + 256
+    assert hj.hstu_workspace_bytes(plan, hj.OP_BWD) == ds + grads + modes
     # layer backward: Z, H and dH (T x 4Hd bf16), A, G, dA (T x Hd bf16), dG (T x Hd fp32),
-    # then the stored dS (no partial slots here)
+    # then the stored dS and the mode records (no partial slots here)
     hd = 2 * 64
-    want = 3 * (30 * 4 * hd * 2) + 3 * (30 * hd * 2) + 30 * hd * 4 + ds
+    want = 3 * (30 * 4 * hd * 2) + 3 * (30 * hd * 2) + 30 * hd * 4 + ds + modes
     assert hj.hstu_workspace_bytes(plan, hj.OP_LAYER_BWD, 512) == want
     plan.close()
     # no stored dS for fp32 or head_dim 32; npad rounds each length up to 128
@@ -228,7 +231,8 @@ def test_calls_on_host_only_plan_and_mismatched_sizes():
     # chunks of 128 keys x 64 queries: the 128-token sequence's block (a context block) spans its
     # 2 query tiles; the 129-token sequence's first block (contexts) all 4, its second block the
     # query tiles from its own first key on, 2; two heads
-    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == 2 * (2 + 4 + 2) * 128 * 64 * 2 + 2 * 2 * 128 * 4
+    assert hj.hstu_workspace_bytes(p3, hj.OP_BWD) == (2 * (2 + 4 + 2) * 128 * 64 * 2 + 2 * 2 * 128 * 4
+                                                     + (2 + 4 + 2) * 256 + 1280)
     p3.close()
 
 
