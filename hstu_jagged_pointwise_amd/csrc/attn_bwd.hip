@@ -1176,9 +1176,10 @@ constexpr int kStages = 4;
 // chunk of the unit's first query tile and 64..127 the next chunk (two consecutive chunks of the
 // tile's key block, geometry.h); the tile's 64 keys are rows 64 * (key tile & 1) .. + 63 of
 // both chunks (row_bytes adds that offset).
+template <int THREADS>
 struct DsPairDma {
     static constexpr int C = kBlk / 8;  // 16-byte chunks per LDS row
-    static constexpr int W = kThreadsA / 64;
+    static constexpr int W = THREADS / 64;
     static constexpr int N = C / W;
     int off[N];
     int wave;
@@ -1237,33 +1238,57 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     const bf16* dss = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq];  // the sequence's chunks
     // byte size as rows_rsrc computes it (rows past the end read as zero)
     const i32x4 krs = rsrc_words(kg, n > 0 ? ((int64_t)(n - 1) * ld + D) * 2 : 0);
-    const TileDma<D, kThreads> kdma(tid, ld);
-    const DsPairDma dsdma(tid);
+    // The second key half's four wavefronts issue every copy (their address arithmetic runs on
+    // the scalar unit, which the CU's wavefronts share); the first half only waits at the barrier.
+    constexpr int kCopiers = kThreadsA / 2;
+    const int ctid = tid - kCopiers;  // valid in the copying wavefronts
+    const TileDma<D, kCopiers> kdma(ctid, ld);
+    const DsPairDma<kCopiers> dsdma(ctid);
     const TrOperand<D> trop(lane);
     const TrBlock<kBlk> dsop(lane, wave);
 
     // The copies of list entry t form a group (its K and dS rows); groups are issued in order.
-    constexpr int kPerTile = TileDma<D, kThreads>::N + DsPairDma::N;
-    // the unit's two query tiles are two consecutive chunks of the key tile's block
-    auto issue_group = [&](int t) {
-        const int kt = ktl.tile(t), kb = kt >> 1, j0 = kt * kTile;
-        kdma.issue_asm(krs, sm.k[t % kStages], (int)((int64_t)j0 * ld * 2));
-        const bf16* pair = dss + (int64_t)kDsChunk *
-            ((int64_t)p.heads * ds_chunks_before(kb, n, nc, nh) + (int64_t)h * ds_chunks(kb, n, nc, nh) +
-             (r0 / kTile - ds_first_qtile(kb, nc)));
-        dsdma.issue_asm(rsrc_words(pair, 2 * kDsChunk * 2), sm.ds[t % kStages], (kt & 1) * kTile * kTile * 2);
+    constexpr int kPerTile = TileDma<D, kCopiers>::N + DsPairDma<kCopiers>::N;
+    static_assert(2 * kPerTile < 64, "vmcnt");
+    // the unit's two query tiles are two consecutive chunks of the key tile's block; the block's
+    // first chunk follows from the previous block's (chunks_before(kb + 1) = chunks_before(kb) +
+    // chunks(kb)) as the list walks the blocks in order
+    int kb_at = -2;
+    int64_t cb_at = 0, pair_at = 0;
+    auto pair_of = [&](int kb) {
+        if (kb != kb_at) {
+            cb_at = kb == kb_at + 1 ? cb_at + ds_chunks(kb_at, n, nc, nh) : ds_chunks_before(kb, n, nc, nh);
+            kb_at = kb;
+            pair_at = (int64_t)kDsChunk * ((int64_t)p.heads * cb_at + (int64_t)h * ds_chunks(kb, n, nc, nh) +
+                                           (r0 / kTile - ds_first_qtile(kb, nc)));
+        }
+        return pair_at;
     };
-    // waits for this thread's copies of group t, with groups t + 1 .. t + k still in flight
-    auto wait_group = [&](int t) { wait_vmcnt_upto(imin(kStages - 2, ntiles - 1 - t) * kPerTile); };
+    auto issue_group = [&](int t) {
+        const int kt = ktl.tile(t), j0 = kt * kTile;
+        kdma.issue_asm(krs, sm.k[t % kStages], (int)((int64_t)j0 * ld * 2));
+        dsdma.issue_asm(rsrc_words(dss + pair_of(kt >> 1), 2 * kDsChunk * 2), sm.ds[t % kStages],
+                        (kt & 1) * kTile * kTile * 2);
+    };
+    // a copying wavefront waits for its copies of group t, with groups t + 1 .. t + k still in
+    // flight
+    auto wait_group = [&](int t) {
+        const int later = imin(kStages - 2, ntiles - 1 - t);
+        if (later >= 2) wait_vmcnt<2 * kPerTile>();
+        else if (later == 1) wait_vmcnt<kPerTile>();
+        else wait_vmcnt<0>();
+    };
+    static_assert(kStages == 4, "wait_group covers two later groups");
 
-    for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_group(t);
+    if (kh == 1)
+        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_group(t);
 
     const int k0 = kWaveRows * kh;
     for (int t = 0; t < ntiles; ++t) {
         const int st = t % kStages, jk0 = ktl.tile(t) * kTile + k0;
-        wait_group(t);    // this thread's copies of entry t have landed
-        lds_barrier();    // everyone's; entry t - 1 is done with
-        if (t + kStages - 1 < ntiles) issue_group(t + kStages - 1);
+        if (kh == 1) wait_group(t);  // this thread's copies of entry t have landed
+        lds_barrier();               // everyone's; entry t - 1 is done with
+        if (kh == 1 && t + kStages - 1 < ntiles) issue_group(t + kStages - 1);
         const int kind = wlo < rhi && jk0 < n ? classify_row_tile(wlo, whi, jk0, n, nc, nh, kWaveRows)
                                               : kEmpty;
         if (kind == kEmpty) continue;
