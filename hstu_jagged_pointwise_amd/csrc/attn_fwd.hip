@@ -56,7 +56,8 @@ struct FwdSmem {
 //   TM 0: time bias absent or one bucket (inside tb.b0); 1: two buckets, tb.b1 where
 //      |dt| >= thr; 4: three buckets (tb.b2 where |dt| >= thr2); 2: per-element bucket class,
 //      32-bit relative times; 3: the same with 64-bit times.
-// s[x] holds the 32-key block kb0 + x of the tile (x < NKB).
+// s[x] holds the 32-key block kb0 + x of the tile (x < NKB); on return, the scores
+// t = -log2(e) (alpha q.k + bias) that silu_scaled takes.
 template <int D, int PM, int TM, int NKB>
 __device__ __forceinline__ void epilogue(f32x16 (&s)[NKB], const FwdSmem<D>& sm, int buf, int u0,
                                          int g, float alpha2, const TimeSel tb, uint32_t ti,
@@ -77,7 +78,7 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[NKB], const FwdSmem<D>& sm,
                 if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
                 if (TM == 2) b += sm.wt[bucket_class(absdiff_sad(ti, tq[c]))];
                 if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
-                s[x][e] = silu_scaled(fmaf(alpha2, s[x][e], b));
+                s[x][e] = fmaf(alpha2, s[x][e], b);
             }
         }
     }
@@ -283,6 +284,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             } else tb.set_const(bpos);
             if (pm) epilogue_tm<D, 1, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
             else epilogue_tm<D, 0, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
+            // the mode branches only form the scores; the SiLU is common code after them
+#pragma unroll
+            for (int x = 0; x < NKB; ++x)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[x][e] = silu_scaled(s[x][e]);
             if (kind == kPartial) mask_keys<NKB>(s, g, j0, lim, dg, kh);
 #pragma unroll
             for (int st = 0; st < 2 * NKB; ++st) {
