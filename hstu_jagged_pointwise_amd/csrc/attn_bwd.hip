@@ -1523,18 +1523,23 @@ __global__ void zero_f32_list_kernel(const ZeroList z) {
 }
 
 // The modes pass of the stored-dS backward: for each (sequence, 128-key block) -- the head-0
-// units of the dK/dV unit list; the records do not depend on the head -- the mode record of every
-// (query tile, wavefront) the dK/dV pass visits (one wavefront per tile: the tile's time range,
-// then eight lanes), and the times of the block's own rows relative to the sequence's first time.
+// units of the dK/dV unit list, every heads-th entry (the plan lists a block's heads one after
+// another, in head order); the records do not depend on the head -- the mode record of every
+// (query tile, wavefront) the dK/dV pass visits, and the times of the block's own rows relative to
+// the sequence's first time.  Eight wavefronts take the tiles round robin; each loads the
+// timestamps of up to eight of its tiles at once (one load latency per batch), then per tile
+// takes the time range (DPP) and eight lanes write the records.
+constexpr int kModesThreads = 512;
 template <bool RP, bool RT>
-__global__ __launch_bounds__(256) void bwd_modes_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kModesThreads) void bwd_modes_kernel(const AttnParams p) {
     __shared__ int64_t kmin[4], kmax[4];
     __shared__ uint32_t kmaxr[4];
     __shared__ int kfit[4];
-    const WorkUnit wu = p.units[blockIdx.x];
-    if (wu.head != 0) return;  // uniform over the workgroup
+    const WorkUnit wu = p.units[(int64_t)blockIdx.x * p.heads];
+    if (wu.head != 0) return;  // not a block's first entry: nothing to do (uniform)
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kWaves = kModesThreads / 64;
     const int n = si.n, nc = si.nc, nh = si.nh, k0 = wu.row0;
     const int64_t tok0 = si.start;
     const int khi = imin(k0 + kBlk, n);
@@ -1542,7 +1547,7 @@ __global__ __launch_bounds__(256) void bwd_modes_kernel(const AttnParams p) {
     rows_for_keys(k0, khi, n, nc, nh, &qlo, &qhi);
     const int tfirst = qlo / kTile, ntiles = cdiv(qhi, kTile) - tfirst;
     const int64_t tbase = RT ? p.ts[tok0] : 0;
-    if (RT) {
+    if (RT && wave < 4) {
         // key group `wave`: keys k0 + 32 wave + (lane % 32), as the dK/dV pass reads them
         const int j = k0 + kWaveRows * wave + (lane & 31);
         const bool key_ok = j < khi;
@@ -1556,28 +1561,38 @@ __global__ __launch_bounds__(256) void bwd_modes_kernel(const AttnParams p) {
             kmaxr[wave] = rel_time_u32(hi, tbase);
             kfit[wave] = fit ? 1 : 0;
         }
-        for (int r = tid; r < kBlk; r += 256)  // every row lies in exactly one key block
-            if (k0 + r < n) p.tq_rel[tok0 + k0 + r] = rel_time_u32(p.ts[tok0 + k0 + r], tbase);
     }
+    if (RT)  // every row lies in exactly one key block
+        for (int r = tid; r < kBlk; r += kModesThreads)
+            if (k0 + r < n) p.tq_rel[tok0 + k0 + r] = rel_time_u32(p.ts[tok0 + k0 + r], tbase);
     __syncthreads();
     ModeRec* out = static_cast<ModeRec*>(p.modes) +
                    8 * (p.ds_off[wu.seq] / ((int64_t)kDsChunk * p.heads) +
                         ds_chunks_before(k0 / kBlk, n, nc, nh));
-    for (int t = wave; t < ntiles; t += 4) {
-        const int i0 = (tfirst + t) * kTile;
-        TimeRange tr{};
-        if (RT) {
-            const bool real = i0 + lane < n;
-            tr = wave_time_range(real ? p.ts[tok0 + i0 + lane] : tbase, real, tbase);
+    constexpr int kBatch = 8;
+    for (int tb = wave; tb < ntiles; tb += kWaves * kBatch) {  // tiles tb + kWaves * b
+        int64_t tq[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int i = (tfirst + tb + kWaves * b) * kTile + lane;
+            tq[b] = RT && tb + kWaves * b < ntiles && i < n ? p.ts[tok0 + i] : tbase;
         }
-        if (lane < 8) {  // lane 4 hq + w: key group w, query half hq
-            const int w = lane & 3, hq = lane >> 2;
-            const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
-            const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
-            out[8 * t + lane] = make_mode_rec(RP, RT, mk0, mk1, mq0, mq1, n, nc, nh, kmin[w],
-                                              kmax[w], kfit[w] != 0, kmaxr[w],
-                                              hq ? tr.lo[1] : tr.lo[0], hq ? tr.hi[1] : tr.hi[0],
-                                              tr.fit);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int t = tb + kWaves * b;
+            if (t >= ntiles) break;  // wavefront-uniform
+            const int i0 = (tfirst + t) * kTile;
+            TimeRange tr{};
+            if (RT) tr = wave_time_range(tq[b], i0 + lane < n, tbase);
+            if (lane < 8) {  // lane 4 hq + w: key group w, query half hq
+                const int w = lane & 3, hq = lane >> 2;
+                const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
+                const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
+                out[8 * t + lane] = make_mode_rec(RP, RT, mk0, mk1, mq0, mq1, n, nc, nh, kmin[w],
+                                                  kmax[w], kfit[w] != 0, kmaxr[w],
+                                                  hq ? tr.lo[1] : tr.lo[0],
+                                                  hq ? tr.hi[1] : tr.hi[0], tr.fit);
+            }
         }
     }
 }
@@ -1587,7 +1602,7 @@ hipError_t launch_dkdv_t(const AttnParams& p, hipStream_t s) {
     if constexpr (D >= 64)
         if (p.ds) {
             if (!p.modes || (RT && !p.tq_rel)) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((bwd_modes_kernel<RP, RT>), dim3(p.num_units), dim3(256), 0, s, p);
+            hipLaunchKernelGGL((bwd_modes_kernel<RP, RT>), dim3(p.num_units / p.heads), dim3(kModesThreads), 0, s, p);
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, RP, RT, true>), dim3(p.num_units), dim3(kThreadsA), 0, s, p);
             return hipGetLastError();
         }

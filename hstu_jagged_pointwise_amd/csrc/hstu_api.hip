@@ -524,7 +524,9 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
         }
     }
     // row blocks in the XCD launch order (the dQ pass reads each (sequence, head)'s K rows from
-    // one L2); key blocks longest first (their costs differ widely and the longest bound the pass)
+    // one L2); key blocks longest first (their costs differ widely and the longest bound the pass),
+    // a stable sort, so each block's heads stay together in head order (the stored-dS modes pass
+    // takes every heads-th entry)
     order_for_xcds(plan->fwd);
     sort_longest_first(plan->bwd);
     return finish_plan(plan, flags, out);
