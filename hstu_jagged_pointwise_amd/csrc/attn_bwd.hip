@@ -1527,14 +1527,18 @@ __global__ void zero_f32_list_kernel(const ZeroList z) {
 // another, in head order); the records do not depend on the head -- the mode record of every
 // (query tile, wavefront) the dK/dV pass visits, and the times of the block's own rows relative to
 // the sequence's first time.  Eight wavefronts take the tiles round robin; each loads the
-// timestamps of up to eight of its tiles at once (one load latency per batch), then per tile
-// takes the time range (DPP) and eight lanes write the records.
+// timestamps of up to eight of its tiles at once (one load latency per batch), takes their time
+// ranges (DPP, one tile after another), and then all 64 lanes write the batch's records (lane
+// 8 b + r: tile b, record r).
 constexpr int kModesThreads = 512;
 template <bool RP, bool RT>
 __global__ __launch_bounds__(kModesThreads) void bwd_modes_kernel(const AttnParams p) {
     __shared__ int64_t kmin[4], kmax[4];
     __shared__ uint32_t kmaxr[4];
     __shared__ int kfit[4];
+    constexpr int kBatch = 8;
+    __shared__ int64_t qlo_s[kModesThreads / 64][kBatch][2], qhi_s[kModesThreads / 64][kBatch][2];
+    __shared__ int qfit_s[kModesThreads / 64][kBatch];
     const WorkUnit wu = p.units[(int64_t)blockIdx.x * p.heads];
     if (wu.head != 0) return;  // not a block's first entry: nothing to do (uniform)
     const SeqInfo si = p.seqs[wu.seq];
@@ -1569,31 +1573,40 @@ __global__ __launch_bounds__(kModesThreads) void bwd_modes_kernel(const AttnPara
     ModeRec* out = static_cast<ModeRec*>(p.modes) +
                    8 * (p.ds_off[wu.seq] / ((int64_t)kDsChunk * p.heads) +
                         ds_chunks_before(k0 / kBlk, n, nc, nh));
-    constexpr int kBatch = 8;
     for (int tb = wave; tb < ntiles; tb += kWaves * kBatch) {  // tiles tb + kWaves * b
-        int64_t tq[kBatch];
+        if (RT) {
+            int64_t tq[kBatch];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int i = (tfirst + tb + kWaves * b) * kTile + lane;
-            tq[b] = RT && tb + kWaves * b < ntiles && i < n ? p.ts[tok0 + i] : tbase;
-        }
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int t = tb + kWaves * b;
-            if (t >= ntiles) break;  // wavefront-uniform
-            const int i0 = (tfirst + t) * kTile;
-            TimeRange tr{};
-            if (RT) tr = wave_time_range(tq[b], i0 + lane < n, tbase);
-            if (lane < 8) {  // lane 4 hq + w: key group w, query half hq
-                const int w = lane & 3, hq = lane >> 2;
-                const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
-                const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
-                out[8 * t + lane] = make_mode_rec(RP, RT, mk0, mk1, mq0, mq1, n, nc, nh, kmin[w],
-                                                  kmax[w], kfit[w] != 0, kmaxr[w],
-                                                  hq ? tr.lo[1] : tr.lo[0],
-                                                  hq ? tr.hi[1] : tr.hi[0], tr.fit);
+            for (int b = 0; b < kBatch; ++b) {
+                const int i = (tfirst + tb + kWaves * b) * kTile + lane;
+                tq[b] = tb + kWaves * b < ntiles && i < n ? p.ts[tok0 + i] : tbase;
             }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int t = tb + kWaves * b;
+                if (t >= ntiles) break;  // wavefront-uniform
+                const TimeRange tr = wave_time_range(tq[b], (tfirst + t) * kTile + lane < n, tbase);
+                if (lane == 0) {
+                    qlo_s[wave][b][0] = tr.lo[0];
+                    qlo_s[wave][b][1] = tr.lo[1];
+                    qhi_s[wave][b][0] = tr.hi[0];
+                    qhi_s[wave][b][1] = tr.hi[1];
+                    qfit_s[wave][b] = tr.fit ? 1 : 0;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes
+            __builtin_amdgcn_wave_barrier();
         }
+        const int b = lane >> 3, r = lane & 7, t = tb + kWaves * b;
+        if (t < ntiles) {  // record r (4 hq + w: key group w, query half hq) of tile t
+            const int w = r & 3, hq = r >> 2, i0 = (tfirst + t) * kTile;
+            const int mk0 = k0 + kWaveRows * w, mk1 = imin(mk0 + kWaveRows, khi);
+            const int mq0 = i0 + kWaveRows * hq, mq1 = imin(mq0 + kWaveRows, n) - 1;
+            out[8 * t + r] = make_mode_rec(
+                RP, RT, mk0, mk1, mq0, mq1, n, nc, nh, kmin[w], kmax[w], kfit[w] != 0, kmaxr[w],
+                RT ? qlo_s[wave][b][hq] : 0, RT ? qhi_s[wave][b][hq] : 0, RT && qfit_s[wave][b] != 0);
+        }
+        __builtin_amdgcn_wave_barrier();  // the batch's ranges are read before the next batch
     }
 }
 
