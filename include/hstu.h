@@ -202,6 +202,8 @@ hstu_status_t hstu_attn_fwd_noalloc(const hstu_plan_t* plan, const hstu_attn_arg
  * bytes (it may be NULL when that is 0): the dK/dV pass stores dS there (bf16, dS * max_seqlen)
  * for every pair it visits and sums the bias-table gradients from it (fp32, before rounding),
  * and the dQ pass reads dS back instead of recomputing S and dP and copies the gradients out.
+ * With ws the dK/dV half is two launches: a short pass that writes the per-tile bias-mode
+ * records and relative query times into ws, then the dK/dV pass that reads them.
  * Same as hstu_attn_bwd_dkdv followed by hstu_attn_bwd_dq with the same ws. */
 hstu_status_t hstu_attn_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* args,
                             const void* q, const void* k, const void* v, const void* dout,
