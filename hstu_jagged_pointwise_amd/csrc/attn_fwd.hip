@@ -356,8 +356,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             for (int r = 0; r < 4; ++r)
                 *reinterpret_cast<f32x4*>(pg + 32 * db + 8 * r + 4 * g) =
                     f32x4{o[db][4 * r], o[db][4 * r + 1], o[db][4 * r + 2], o[db][4 * r + 3]};
-    } else if (row_ok) {
-        bf16* og = static_cast<bf16*>(p.out) + (tok0 + i) * p.ld_out + h * D;
+    } else if (wu.part < 0) {
+        // this wavefront's 32 rows go through LDS (the idle V tiles, swizzled like a tile) so
+        // that each store instruction writes whole row segments
+        bf16* stage = sm.v[0] + (size_t)rg * kWaveRows * D;
         const float oscale = -kLn2 * p.inv_n;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -366,8 +368,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                 bf16x4 w;
 #pragma unroll
                 for (int c = 0; c < 4; ++c) w[c] = (bf16)(o[db][4 * r + c] * oscale);
-                *reinterpret_cast<bf16x4*>(og + 32 * db + 8 * r + 4 * g) = w;
+                *reinterpret_cast<bf16x4*>(stage + tile_off<D>(lr, 32 * db + 8 * r + 4 * g)) = w;
             }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        constexpr int kChunks = D / 8, kRowsPer = 64 / kChunks;  // 16-byte chunks per row
+#pragma unroll
+        for (int it = 0; it < kWaveRows / kRowsPer; ++it) {
+            const int row = kRowsPer * it + lane / kChunks, ch = lane % kChunks;
+            if (wlo + row < rhi) {
+                const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + tile_off<D>(row, 8 * ch));
+                *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + (tok0 + wlo + row) * p.ld_out +
+                                           h * D + 8 * ch) = v;
+            }
+        }
     }
 }
 
