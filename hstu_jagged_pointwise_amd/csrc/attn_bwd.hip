@@ -1212,6 +1212,11 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     __shared__ __attribute__((aligned(16))) SmemC<D> sm;
     static_assert(sizeof(SmemC<D>) <= 160 * 1024, "LDS");
 
+    if (blockIdx.x == 0)  // the bias-table gradients the dK/dV pass summed, to the outputs
+        for (int e = threadIdx.x; e < p.heads * kNumBuckets; e += kThreads) {
+            if (p.drab_pos && p.gpos && p.drab_pos != p.gpos) p.drab_pos[e] = p.gpos[e];
+            if (p.drab_ts && p.gts && p.drab_ts != p.gts) p.drab_ts[e] = p.gts[e];
+        }
     const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lr = lane & 31;
@@ -1539,6 +1544,12 @@ __global__ __launch_bounds__(kModesThreads) void bwd_modes_kernel(const AttnPara
     constexpr int kBatch = 8;
     __shared__ int64_t qlo_s[kModesThreads / 64][kBatch][2], qhi_s[kModesThreads / 64][kBatch][2];
     __shared__ int qfit_s[kModesThreads / 64][kBatch];
+    if (blockIdx.x == 0) {  // the bias-table gradient sums of the dK/dV pass start from zero
+        for (int e = threadIdx.x; e < p.heads * kNumBuckets; e += kModesThreads) {
+            if (p.gpos) p.gpos[e] = 0.0f;
+            if (p.gts) p.gts[e] = 0.0f;
+        }
+    }
     const WorkUnit wu = p.units[(int64_t)blockIdx.x * p.heads];
     if (wu.head != 0) return;  // not a block's first entry: nothing to do (uniform)
     const SeqInfo si = p.seqs[wu.seq];

@@ -757,13 +757,13 @@ hstu_status_t hstu_attn_bwd_dkdv(const hstu_plan_t* plan, const hstu_attn_args_t
     p.dk = dk;
     p.dv = dv;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (p.ds) {  // this pass sums the bias-table gradients into the workspace
+    if (p.ds) {  // this pass sums the bias-table gradients into the workspace (the modes pass,
+                 // which runs first, clears them)
         set_modes(plan, static_cast<char*>(ws) + ds_bytes(plan) + grad_bytes(plan), &p);
         float* grads = reinterpret_cast<float*>(static_cast<char*>(ws) + ds_bytes(plan));
         const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
         p.gpos = args->rab_pos ? grads : nullptr;
         p.gts = args->rab_ts ? grads + nb : nullptr;
-        if (checked(hstu::launch_zero_f32(grads, 2 * nb, s), s) != hipSuccess) return HSTU_ERR_HIP;
     }
     return hip_status(args->dtype == HSTU_BF16 ? checked(hstu::launch_attn_bwd_dkdv_bf16(p, s), s)
                                                : checked(hstu::launch_attn_bwd_dkdv_f32(p, s), s));
@@ -789,13 +789,11 @@ hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t nb = int64_t(args->num_heads) * hstu::kNumBuckets;
     hipError_t e = hipSuccess;
-    if (p.ds) {  // the dK/dV pass summed the bias-table gradients into the workspace
-        const float* grads =
-            reinterpret_cast<const float*>(static_cast<const char*>(ws) + ds_bytes(plan));
-        if (p.drab_pos)
-            e = hipMemcpyAsync(p.drab_pos, grads, nb * 4, hipMemcpyDeviceToDevice, s);
-        if (e == hipSuccess && p.drab_ts)
-            e = hipMemcpyAsync(p.drab_ts, grads + nb, nb * 4, hipMemcpyDeviceToDevice, s);
+    if (p.ds) {  // the dK/dV pass summed the bias-table gradients into the workspace; the dQ
+                 // pass's first workgroup copies them to the outputs
+        float* grads = reinterpret_cast<float*>(static_cast<char*>(ws) + ds_bytes(plan));
+        p.gpos = p.drab_pos ? grads : nullptr;
+        p.gts = p.drab_ts ? grads + nb : nullptr;
     } else {
         if (p.drab_pos) e = checked(hstu::launch_zero_f32(p.drab_pos, nb, s), s);
         if (e == hipSuccess && p.drab_ts) e = checked(hstu::launch_zero_f32(p.drab_ts, nb, s), s);
