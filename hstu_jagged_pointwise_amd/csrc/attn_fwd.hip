@@ -35,27 +35,55 @@ constexpr int kRows = 4 * kWaveRows;  // 128 query rows per unit
 constexpr int kBN = kKeyTile;         // 64 keys per tile
 constexpr int kToep = kRows + kBN - 1;  // 191 distinct i - j per (unit, tile)
 
+// Time bias by the bit pattern of a float distance.  For an integer distance 1 <= x < 2^24 the
+// float's exponent and first three fraction bits, (bits >> 20) = 8 * (127 + e) + m3, name a
+// class of width 2^(e-3) that lies inside one bucket (the bucket rule is exact on quarter octaves
+// and the identity below 16), so ((bits >> 18) & 0x1ffc) is a byte offset into a table of
+// kFloatClasses entries that starts kFloatClassBase bytes after the bucket table's entry for
+// distance 0 -- which is where the pattern of +-0.0 points.  Three instructions from two float
+// times to a table address, against seven for the integer class (bucket_class).
+constexpr int kFloatClasses = 192;               // exponents 0 .. 23
+constexpr int kFloatClassBase = (127 * 8) * 4;   // byte offset of the class of 1.0f
+constexpr int64_t kFloatExact = 1 << 24;         // time differences below this: exact floats
+
 template <int D>
 struct FwdSmem {
-    // Small tables first, so their offsets fit the 16-bit LDS instruction offset field.  Bias
+    // Small tables first, so their offsets fit the 16-bit LDS instruction offset field (the
+    // Toeplitz table at offset 0, so its per-element reads need no address arithmetic).  Bias
     // values are stored multiplied by -log2(e) (see silu_scaled).
-    float wt[kNumClasses];              // time bias by bucket class
+    float rp[2][kToep + 1];             // position bias by (i - j) for the tile
     float wp[kNumBuckets];              // position bias by bucket
     float wtb[kNumBuckets];             // time bias by bucket
-    float rp[2][kToep + 1];             // position bias by (i - j) for the tile
+    float wt[kNumClasses];              // time bias by bucket class
     uint32_t tk[2][kBN];                // key timestamps, biased 32-bit relative
     int64_t tk64[2][kBN];               // key timestamps (fallback)
     int64_t tkmin[2], tkmax[2];         // time range of the tile's real keys
     int fits[2];
+    char pad_[kFloatClassBase - sizeof(float) * (kNumBuckets + kNumClasses) -
+              sizeof(uint32_t) * 2 * kBN - sizeof(int64_t) * (2 * kBN + 4) - sizeof(int) * 2];
+    float wtf[kFloatClasses];           // time bias by float class (see kFloatClassBase)
     alignas(16) bf16 k[2][kBN * D];     // swizzled tiles (tile_off)
     bf16 v[2][kBN * D];
 };
+
+// Time bias of the distance between two biased 32-bit relative times whose difference is below
+// 2^24 in magnitude (see kFloatClassBase): the byte offset from the bucket table, then the
+// lookup.
+__device__ __forceinline__ uint32_t float_class_offset(uint32_t ti, uint32_t tk) {
+    return (__float_as_uint((float)(int32_t)(ti - tk)) >> 18) & 0x1ffcu;
+}
+template <int D>
+__device__ __forceinline__ float float_class_at(const FwdSmem<D>& sm, uint32_t off) {
+    return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(sm.wtb) + off);
+}
 
 // Bias handling of one (wavefront, tile), decided once per tile from the distance ranges:
 //   PM 0: position bias absent or one bucket (inside b0/b1); 1: Toeplitz table per element.
 //   TM 0: time bias absent or one bucket (inside tb.b0); 1: two buckets, tb.b1 where
 //      |dt| >= thr; 4: three buckets (tb.b2 where |dt| >= thr2); 2: per-element bucket class,
-//      32-bit relative times; 3: the same with 64-bit times.
+//      32-bit relative times; 3: the same with 64-bit times; 5: per-element float class
+//      (float_class_offset) when every time difference of the tile is below 2^24.
+// In the per-element time modes tb.b0 is the position bucket's bias, zero when PM is 1.
 // s[x] holds the 32-key block kb0 + x of the tile (x < NKB); on return, the scores
 // t = -log2(e) (alpha q.k + bias) that silu_scaled takes.
 template <int D, int PM, int TM, int NKB>
@@ -63,6 +91,34 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[NKB], const FwdSmem<D>& sm,
                                          int g, float alpha2, const TimeSel tb, uint32_t ti,
                                          int64_t ti64, int kb0) {
     const TimePick pick(tb, ti);
+    constexpr bool kPerElem = TM == 2 || TM == 3 || TM == 5;
+    if constexpr (TM == 5) {
+        // per 32-key block: the 16 table addresses, then all 16 lookups (with the Toeplitz
+        // reads), then the sums -- so the lookups are in flight together
+#pragma unroll
+        for (int x = 0; x < NKB; ++x) {
+            const int kb = kb0 + x;
+            uint32_t a[16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const u32x4 tq = *reinterpret_cast<const u32x4*>(&sm.tk[buf][32 * kb + 8 * r + 4 * g]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) a[4 * r + c] = float_class_offset(ti, tq[c]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            float bt[16], bp[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                bt[e] = float_class_at(sm, a[e]);
+                if (PM == 1) bp[e] = sm.rp[buf][u0 + 32 * kb + 8 * (e >> 2) + (e & 3)];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                s[x][e] = fmaf(alpha2, s[x][e], (PM == 1 ? bp[e] : tb.b0) + bt[e]);
+        }
+        return;
+    }
 #pragma unroll
     for (int x = 0; x < NKB; ++x) {
         const int kb = kb0 + x;
@@ -74,10 +130,13 @@ __device__ __forceinline__ void epilogue(f32x16 (&s)[NKB], const FwdSmem<D>& sm,
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 4 * r + c;
-                float b = pick.get<TM>(tq[c]);
-                if (PM == 1) b += sm.rp[buf][u0 + 32 * kb + 8 * r + c];
-                if (TM == 2) b += sm.wt[bucket_class(absdiff_sad(ti, tq[c]))];
-                if (TM == 3) b += sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
+                float bt;  // time part
+                if (TM == 2) bt = sm.wt[bucket_class(absdiff_sad(ti, tq[c]))];
+                else if (TM == 3) bt = sm.wt[bucket_class(absdiff_sat(ti64, sm.tk64[buf][jj + c]))];
+                else bt = pick.get<TM>(tq[c]);
+                float b;
+                if (PM == 1) b = sm.rp[buf][u0 + 32 * kb + 8 * r + c] + bt;
+                else b = kPerElem ? tb.b0 + bt : bt;
                 s[x][e] = fmaf(alpha2, s[x][e], b);
             }
         }
@@ -92,6 +151,7 @@ __device__ __forceinline__ void epilogue_tm(int tm, f32x16 (&s)[NKB], const FwdS
         case 0: epilogue<D, PM, 0, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
         case 1: epilogue<D, PM, 1, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
         case 4: epilogue<D, PM, 4, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
+        case 5: epilogue<D, PM, 5, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
         case 2: epilogue<D, PM, 2, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
         default: epilogue<D, PM, 3, NKB>(s, sm, buf, u0, g, alpha2, tb, ti, ti64, kb0); break;
     }
@@ -122,6 +182,8 @@ __device__ __forceinline__ void mask_keys(f32x16 (&s)[NKB], int g, int j0, int l
 template <int D, bool RP, bool RT, bool CACHED, bool KH>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+    static_assert(offsetof(FwdSmem<D>, wtf) == offsetof(FwdSmem<D>, wtb) + kFloatClassBase,
+                  "float-class table placement");
 
     constexpr int kItemRows = KH ? 2 * kWaveRows : kRows;
     constexpr int NKB = KH ? 1 : 2;                  // 32-key blocks per wavefront and tile
@@ -162,9 +224,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
     auto load_tile = [&](int buf, int tile) {
         const int j0 = tile * kBN;
         const int row_bytes = (int)((int64_t)j0 * ld * 2);
-        if (RT && tid < kBN) {
+        if (RT && tid < kBN) {  // keys past the end take the last key's time (within the tile's range)
             const int j = j0 + tid;
-            tkr = j < nk ? tsk[j] : tbase;
+            tkr = tsk[j < nk ? j : nk - 1];
         }
         dma.issue_asm(krs, sm.k[buf], row_bytes);
         dma.issue_asm(vrs, sm.v[buf], row_bytes);
@@ -202,6 +264,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
             sm.wt[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of_class(e)];
         for (int e = tid; e < kNumBuckets; e += kThreads)
             sm.wtb[e] = -kLog2e * p.rab_ts[h * kNumBuckets + e];
+        for (int e = tid; e < kFloatClasses; e += kThreads)  // a member of float class e
+            sm.wtf[e] = -kLog2e * p.rab_ts[h * kNumBuckets + bucket_of(((8u + (e & 7)) << (e >> 3)) >> 3)];
     }
 
     // this wavefront's rows and this lane's row
@@ -281,6 +345,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const AttnParams 
                 const int64_t dlo = timin - uniform64(sm.tkmax[buf]);
                 const BiasSpan st = bias_span(dlo, timax - uniform64(sm.tkmin[buf]));
                 tm = tb.set(st, wave_qfit && uniform_i(sm.fits[buf]), bpos, sm.wtb, dlo >= 0, timax_rel);
+                // every |t_i - t_j| of the tile below 2^24: exact as a float
+                if (tm == 2 && dlo > -kFloatExact && timax - uniform64(sm.tkmin[buf]) < kFloatExact) tm = 5;
             } else tb.set_const(bpos);
             if (pm) epilogue_tm<D, 1, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
             else epilogue_tm<D, 0, NKB>(tm, s, sm, buf, u0, g, alpha2, tb, ti, ti64, kh);
