@@ -40,8 +40,9 @@ constexpr int kToep = kRows + kBN - 1;  // 191 distinct i - j per (unit, tile)
 // class of width 2^(e-3) that lies inside one bucket (the bucket rule is exact on quarter octaves
 // and the identity below 16), so ((bits >> 18) & 0x1ffc) is a byte offset into a table of
 // kFloatClasses entries that starts kFloatClassBase bytes after the bucket table's entry for
-// distance 0 -- which is where the pattern of +-0.0 points.  Three instructions from two float
-// times to a table address, against seven for the integer class (bucket_class).
+// distance 0 -- which is where the pattern of +-0.0 points.  Four instructions from two 32-bit
+// times to a table address (subtract, convert, shift, mask; the sign bit is masked off),
+// against eight for |difference| and the integer class (bucket_class).
 constexpr int kFloatClasses = 192;               // exponents 0 .. 23
 constexpr int kFloatClassBase = (127 * 8) * 4;   // byte offset of the class of 1.0f
 constexpr int64_t kFloatExact = 1 << 24;         // time differences below this: exact floats
