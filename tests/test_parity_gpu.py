@@ -129,6 +129,37 @@ def test_bwd_wide_timestamps_take_64bit_path():
     _bwd_check(w, "bf16")
 
 
+def _one_hot_values(T, H, d):
+    v = np.zeros((T, H, d), np.float32)
+    v[np.arange(T), :, np.arange(T) % d] = 1.0
+    return v
+
+
+@pytest.mark.parametrize("gap", [1 << 12, 1 << 18, (1 << 24) // 48])
+def test_fwd_bias_buckets_one_hot(gap):
+    # Scores from the bias tables alone (alpha = 0), neighbouring buckets with far-apart biases,
+    # and one-hot value rows, so that each output element holds the probabilities of two or three
+    # keys: a key that took a wrong position or time bucket moves its output element by far more
+    # than the tolerance.  Time gaps of up to 2^24 / 24 per token put the tiles near the diagonal
+    # on both sides of the 2^24 limit of the float-class time bias (page 1, section 2.1.2:
+    # rab^{p,t} of the bucketized |i - j| and |t_i - t_j|).
+    lengths = [300, 129, 700, 64]
+    w = hs.make_inputs(lengths, 2, 128, dtype="bf16", seed=31, rab=True, alpha=0.0)
+    T = w["total_tokens"]
+    w["v"] = _one_hot_values(T, 2, 128)
+    rng = np.random.default_rng(gap)
+    ts = np.empty(T, np.int64)
+    off = w["seq_offsets"]
+    for b in range(len(lengths)):
+        ts[off[b]:off[b + 1]] = 1_700_000_000 + np.cumsum(rng.integers(1, 2 * gap, off[b + 1] - off[b]))
+    w["timestamps"] = ts
+    buckets = np.arange(128, dtype=np.float32)
+    w["rab_ts"] = np.stack([(buckets % 7) * 0.8 - 2.4, 2.0 - (buckets % 5) * 0.9]).astype(np.float32)
+    w["rab_pos"] = np.stack([1.5 * np.cos(buckets), 1.5 * np.sin(1.3 * buckets)]).astype(np.float32)
+    say(f"fwd one-hot bias buckets gap={gap}")
+    check("O", run_fwd(w), oracle.attn_fwd(w), "bf16")
+
+
 def test_fwd_empty_and_single():
     w = hs.make_inputs([0, 1, 0, 0, 1], 2, 32, dtype="bf16", seed=3, rab=True, num_targets=1,
                        max_seqlen=8)
