@@ -502,6 +502,29 @@ def _bwd_check(w, dtype):
             check(name, host(g[name]), ref[name], "bf16" if dtype == "bf16" else "fp32")
 
 
+@pytest.mark.parametrize("gap", [1 << 12, (1 << 24) // 48])
+def test_bwd_bias_buckets_strong(gap):
+    # Neighbouring buckets with far-apart biases (the scores depend strongly on which bucket each
+    # pair takes) at time gaps on both sides of the float-class limit; contexts and candidates in
+    # the mask, so the dK/dV pass meets its one-, two- and three-bucket and per-element modes
+    # (page 1, section 2.1.2: rab^{p,t} and its gradients).
+    lengths = [300, 129, 700]
+    w = hs.make_inputs(lengths, 2, 64, dtype="bf16", seed=41, rab=True, alpha=0.3,
+                       num_contexts=3, num_targets=9, backward=True)
+    T = w["total_tokens"]
+    rng = np.random.default_rng(gap + 1)
+    ts = np.empty(T, np.int64)
+    off = w["seq_offsets"]
+    for b in range(len(lengths)):
+        ts[off[b]:off[b + 1]] = 1_700_000_000 + np.cumsum(rng.integers(1, 2 * gap, off[b + 1] - off[b]))
+    w["timestamps"] = ts
+    buckets = np.arange(128, dtype=np.float32)
+    w["rab_ts"] = np.stack([(buckets % 7) * 0.8 - 2.4, 2.0 - (buckets % 5) * 0.9]).astype(np.float32)
+    w["rab_pos"] = np.stack([1.5 * np.cos(buckets), 1.5 * np.sin(1.3 * buckets)]).astype(np.float32)
+    say(f"bwd strong bias buckets gap={gap}")
+    _bwd_check(w, "bf16")
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("mask", [0, 2, 3, 4])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
