@@ -228,7 +228,7 @@ def hstu_plan_info(plan: Plan) -> dict:
 
 
 def hstu_plan_units(plan: Plan, op: int) -> np.ndarray:
-    """op 0 / 1: (count, 4) work units; op 2: (count, 8) bf16 forward items."""
+    """op 0 / 1 / 3: (count, 4) work units; op 2: (count, 8) bf16 forward items."""
     lib = load_library()
     count = ctypes.c_int64()
     _check(lib.hstu_plan_units(ctypes.c_void_p(plan.handle), int(op), None, 0, ctypes.byref(count)))

@@ -1166,14 +1166,17 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_kernel(const AttnParams p
 // ---------------------------------------------------------------------------------------------
 // The dK/dV pass has written dS * N for every pair it visits (AttnParams::ds, rows = keys) and
 // summed the bias-table gradients, so per key tile this pass only copies the K rows and the
-// 64 x 128 dS block of its rows into LDS and runs dQ^T += K^T dS^T.  With so little arithmetic
-// per tile the copies set the pace: a ring of kStages tiles keeps kStages - 1 of them in flight.
+// 64 x 256 dS block of its rows into LDS and runs dQ^T += K^T dS^T.  With so little arithmetic
+// per tile the copies set the pace: a ring of kDqStages tiles keeps kDqStages - 1 of them in
+// flight.  Units of 256 query rows (the plan's dQ list), one 32-row group per wavefront (eight),
+// every wavefront over all 64 keys of each tile: no partial sums to combine at the end, and each
+// K tile copied serves 256 rows.
+constexpr int kDqRows = 8 * kWaveRows;
+constexpr int kDqStages = 3;
 
-constexpr int kStages = 4;
-
-// Copies the 64 x 128 dS block of one key tile and the unit's 128 query rows into an LDS tile
+// Copies the 64 x 128 dS block of one key tile and 128 consecutive query rows into an LDS tile
 // laid out like a 128-column operand tile (TileDma<kBlk>): its columns 0..63 are the 64-query
-// chunk of the unit's first query tile and 64..127 the next chunk (two consecutive chunks of the
+// chunk of the rows' first query tile and 64..127 the next chunk (two consecutive chunks of the
 // tile's key block, geometry.h); the tile's 64 keys are rows 64 * (key tile & 1) .. + 63 of
 // both chunks (row_bytes adds that offset).
 template <int THREADS>
@@ -1202,8 +1205,8 @@ struct DsPairDma {
 
 template <int D>
 struct SmemC {
-    alignas(16) bf16 k[kStages][kTile * D];   // swizzled tiles (tile_off)
-    bf16 ds[kStages][kTile * kBlk];           // dS^T rows j0 .. j0 + 63, the unit's 128 columns
+    alignas(16) bf16 k[kDqStages][kTile * D];      // swizzled tiles (tile_off)
+    bf16 ds[kDqStages][2][kTile * kBlk];           // dS^T rows j0 .. j0 + 63, per 128-row half
 };
 
 template <int D>
@@ -1220,12 +1223,12 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     const WorkUnit wu = p.units[blockIdx.x];
     const SeqInfo si = p.seqs[wu.seq];
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, lr = lane & 31;
-    const int wave = uniform_i((tid >> 6) & 3), kh = uniform_i(tid >> 8);  // row group, key half
+    const int wave = uniform_i(tid >> 6), hf = wave >> 2;  // row group; 128-row half
     const int n = si.n, nc = si.nc, nh = si.nh, r0 = wu.row0, h = wu.head;
     const int64_t tok0 = si.start, ld = p.ld_in;
     const bf16* __restrict__ kg = static_cast<const bf16*>(p.k) + tok0 * ld + h * D;
 
-    const int rhi = imin(r0 + kBlk, n);
+    const int rhi = imin(r0 + kDqRows, n);
     const KeyTiles ktl = key_tiles_for_rows(r0, rhi, nc, nh);
     const int ntiles = ktl.count();
     const int wlo = r0 + kWaveRows * wave, whi = imin(wlo + kWaveRows, rhi);
@@ -1243,109 +1246,86 @@ __global__ __launch_bounds__(kThreadsA, 1) void bwd_dq_stored_kernel(const AttnP
     const bf16* dss = static_cast<const bf16*>(p.ds) + p.ds_off[wu.seq];  // the sequence's chunks
     // byte size as rows_rsrc computes it (rows past the end read as zero)
     const i32x4 krs = rsrc_words(kg, n > 0 ? ((int64_t)(n - 1) * ld + D) * 2 : 0);
-    // The second key half's four wavefronts issue every copy (their address arithmetic runs on
-    // the scalar unit, which the CU's wavefronts share); the first half only waits at the barrier.
-    constexpr int kCopiers = kThreadsA / 2;
-    const int ctid = tid - kCopiers;  // valid in the copying wavefronts
-    const TileDma<D, kCopiers> kdma(ctid, ld);
-    const DsPairDma<kCopiers> dsdma(ctid);
+    const TileDma<D, kThreads> kdma(tid, ld);
+    const DsPairDma<kThreads> dsdma(tid);
     const TrOperand<D> trop(lane);
-    const TrBlock<kBlk> dsop(lane, wave);
+    const TrBlock<kBlk> dsop(lane, wave & 3);
 
-    // The copies of list entry t form a group (its K and dS rows); groups are issued in order.
-    constexpr int kPerTile = TileDma<D, kCopiers>::N + DsPairDma<kCopiers>::N;
-    static_assert(2 * kPerTile < 64, "vmcnt");
-    // the unit's two query tiles are two consecutive chunks of the key tile's block; the block's
-    // first chunk follows from the previous block's (chunks_before(kb + 1) = chunks_before(kb) +
-    // chunks(kb)) as the list walks the blocks in order
-    int kb_at = -2;
-    int64_t cb_at = 0, pair_at = 0;
-    auto pair_of = [&](int kb) {
-        if (kb != kb_at) {
-            cb_at = kb == kb_at + 1 ? cb_at + ds_chunks(kb_at, n, nc, nh) : ds_chunks_before(kb, n, nc, nh);
-            kb_at = kb;
-            pair_at = (int64_t)kDsChunk * ((int64_t)p.heads * cb_at + (int64_t)h * ds_chunks(kb, n, nc, nh) +
-                                           (r0 / kTile - ds_first_qtile(kb, nc)));
-        }
-        return pair_at;
-    };
+    // The copies of list entry t form a group (its K rows and both halves' dS); groups are issued
+    // in order, every group with the same number of copies: a half whose 128 rows have no chunks
+    // in the tile's key block (none of them sees the block) copies from an empty range, which
+    // reads zeros, and its wavefronts skip the tile.
+    constexpr int kPerTile = TileDma<D, kThreads>::N + 2 * DsPairDma<kThreads>::N;
+    static_assert(kPerTile < 64, "vmcnt");
+    // first chunk of the tile's key block for this head and the block's chunk count, kept while
+    // the list walks the blocks in order (chunks_before(kb + 1) = chunks_before(kb) + chunks(kb))
+    int kb_at = -2, nch_at = 0, q0_at = 0;
+    int64_t head_at = 0, cb_at = 0;
     auto issue_group = [&](int t) {
-        const int kt = ktl.tile(t), j0 = kt * kTile;
-        kdma.issue_asm(krs, sm.k[t % kStages], (int)((int64_t)j0 * ld * 2));
-        dsdma.issue_asm(rsrc_words(dss + pair_of(kt >> 1), 2 * kDsChunk * 2), sm.ds[t % kStages],
-                        (kt & 1) * kTile * kTile * 2);
+        const int kt = ktl.tile(t), j0 = kt * kTile, kb = kt >> 1;
+        if (kb != kb_at) {
+            cb_at = kb == kb_at + 1 ? cb_at + nch_at : ds_chunks_before(kb, n, nc, nh);
+            kb_at = kb;
+            nch_at = ds_chunks(kb, n, nc, nh);
+            q0_at = ds_first_qtile(kb, nc);
+            head_at = (int64_t)kDsChunk * ((int64_t)p.heads * cb_at + (int64_t)h * nch_at);
+        }
+        kdma.issue_asm(krs, sm.k[t % kDqStages], (int)((int64_t)j0 * ld * 2));
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int c = (r0 + kBlk * half) / kTile - q0_at;  // the half's first chunk
+            const bool has = c >= 0 && c + 2 <= nch_at;
+            dsdma.issue_asm(rsrc_words(dss + (has ? head_at + (int64_t)kDsChunk * c : 0), has ? 2 * kDsChunk * 2 : 0),
+                            sm.ds[t % kDqStages][half], (kt & 1) * kTile * kTile * 2);
+        }
     };
-    // a copying wavefront waits for its copies of group t, with groups t + 1 .. t + k still in
-    // flight
+    // waits for this thread's copies of group t, with group t + 1 still in flight
     auto wait_group = [&](int t) {
-        const int later = imin(kStages - 2, ntiles - 1 - t);
-        if (later >= 2) wait_vmcnt<2 * kPerTile>();
-        else if (later == 1) wait_vmcnt<kPerTile>();
+        if (t + 1 < ntiles) wait_vmcnt<kPerTile>();
         else wait_vmcnt<0>();
     };
-    static_assert(kStages == 4, "wait_group covers two later groups");
+    static_assert(kDqStages == 3, "wait_group covers one later group");
 
-    if (kh == 1)
-        for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue_group(t);
+    for (int t = 0; t < kDqStages - 1 && t < ntiles; ++t) issue_group(t);
 
-    const int k0 = kWaveRows * kh;
     for (int t = 0; t < ntiles; ++t) {
-        const int st = t % kStages, jk0 = ktl.tile(t) * kTile + k0;
-        if (kh == 1) wait_group(t);  // this thread's copies of entry t have landed
-        lds_barrier();               // everyone's; entry t - 1 is done with
-        if (kh == 1 && t + kStages - 1 < ntiles) issue_group(t + kStages - 1);
-        const int kind = wlo < rhi && jk0 < n ? classify_row_tile(wlo, whi, jk0, n, nc, nh, kWaveRows)
-                                              : kEmpty;
+        const int st = t % kDqStages, jk0 = ktl.tile(t) * kTile;
+        wait_group(t);  // this thread's copies of entry t have landed
+        lds_barrier();  // everyone's; entry t - 1 is done with
+        if (t + kDqStages - 1 < ntiles) issue_group(t + kDqStages - 1);
+        const int kind = wlo < rhi && jk0 < n ? classify_row_tile(wlo, whi, jk0, n, nc, nh, kTile) : kEmpty;
         if (kind == kEmpty) continue;
-        bf16x8 b8[2];  // dS (times N) of keys jk0 + 16sl + key(k) for this lane's row
+        bf16x8 b8[4];  // dS (times N) of keys jk0 + 16sl + key(k) for this lane's row
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) b8[sl] = dsop.read(sm.ds[st], 2 * kh + sl);
+        for (int sl = 0; sl < 4; ++sl) b8[sl] = dsop.read(sm.ds[st][hf], sl);
         if (kind == kPartial) {  // entries the dK/dV pass did not write for this row
-            f32x16 dp;
 #pragma unroll
-            for (int x = 0; x < 16; ++x) dp[x] = (float)b8[x >> 3][x & 7];
-            mask_keys_b(dp, g, jk0, lim, dg);
+            for (int x2 = 0; x2 < 2; ++x2) {
+                f32x16 dp;
 #pragma unroll
-            for (int sl = 0; sl < 2; ++sl) {
-                float td[8];
+                for (int x = 0; x < 16; ++x) dp[x] = (float)b8[2 * x2 + (x >> 3)][x & 7];
+                mask_keys_b(dp, g, jk0 + 32 * x2, lim, dg);
 #pragma unroll
-                for (int x = 0; x < 8; ++x) td[x] = dp[8 * sl + x];
-                b8[sl] = pack8(td);
+                for (int sl = 0; sl < 2; ++sl) {
+                    float td[8];
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) td[x] = dp[8 * sl + x];
+                    b8[2 * x2 + sl] = pack8(td);
+                }
             }
         }
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
+        for (int sl = 0; sl < 4; ++sl)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
-                dqt[db] = mfma32(trop.read(sm.k[st], 2 * kh + sl, db), b8[sl], dqt[db]);
-    }
-    __syncthreads();  // every wavefront is done with the K ring (the last wait_group left no copy
-                      // in flight)
-
-    bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
-    GateRow<D> gq;
-    if (p.gate_delta != 0 && row_ok && kh == 0) gq.load(dqg, g, p.gate_delta);
-    // add the second key half's partial dQ into the first's through the K ring, laid out
-    // [row group][db][element][lane]
-    static_assert(sizeof(sm.k) >= 4 * (D / 32) * 16 * 64 * sizeof(float), "reduction buffer");
-    {
-        float* mine = reinterpret_cast<float*>(&sm.k[0][0]) + ((size_t)wave * (D / 32) * 16) * 64 + lane;
-        if (kh == 1)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mine[(db * 16 + e) * 64] = dqt[db][e];
-        __syncthreads();
-        if (kh == 0)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) dqt[db][e] += mine[(db * 16 + e) * 64];
+                dqt[db] = mfma32(trop.read(sm.k[st], sl, db), b8[sl], dqt[db]);
     }
 
-    if (row_ok && kh == 0) {
-        const float sq = p.alpha * p.inv_n;
-        store_grad_row<D>(dqg, dqt, g, sq, p.gate_delta, gq);
+    if (row_ok) {
+        bf16* dqg = static_cast<bf16*>(p.dq) + (tok0 + i) * p.ld_grad + h * D;
+        GateRow<D> gq;
+        if (p.gate_delta != 0) gq.load(dqg, g, p.gate_delta);
+        store_grad_row<D>(dqg, dqt, g, p.alpha * p.inv_n, p.gate_delta, gq);
     }
 }
 

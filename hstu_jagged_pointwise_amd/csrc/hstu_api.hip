@@ -32,6 +32,7 @@ struct hstu_plan {
     int64_t fwd_tiles = -1;    // computed on first hstu_plan_info (-1: not yet)
     std::vector<SeqInfo> seqs;
     std::vector<WorkUnit> fwd, bwd;
+    std::vector<WorkUnit> dqs;   // bf16: 256-row blocks of the stored-dS dQ pass
     std::vector<FwdItem> items;  // bf16 forward launch (row blocks, the longest split by key tiles)
     std::vector<FixItem> fix;
     int32_t item_rows = 128;     // rows per forward item: 128, or 64 (key-half layout)
@@ -48,6 +49,7 @@ struct hstu_plan {
     const SeqInfo* d_seqs = nullptr;
     const WorkUnit* d_fwd = nullptr;
     const WorkUnit* d_bwd = nullptr;
+    const WorkUnit* d_dqs = nullptr;
     const FwdItem* d_items = nullptr;
     const FixItem* d_fix = nullptr;
     const CacheSeq* d_cache = nullptr;
@@ -366,17 +368,18 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
     plan_ds_layout(plan);
 
     if (!host_only) {
-        constexpr int kArrays = 7;
+        constexpr int kArrays = 8;
         const size_t sizes[kArrays] = {sizeof(SeqInfo) * plan->seqs.size(),
                                        sizeof(WorkUnit) * plan->fwd.size(),
                                        sizeof(WorkUnit) * plan->bwd.size(),
                                        sizeof(FwdItem) * plan->items.size(),
                                        sizeof(FixItem) * plan->fix.size(),
                                        sizeof(CacheSeq) * plan->cache.size(),
-                                       sizeof(int64_t) * plan->ds_off.size()};
+                                       sizeof(int64_t) * plan->ds_off.size(),
+                                       sizeof(WorkUnit) * plan->dqs.size()};
         const void* srcs[kArrays] = {plan->seqs.data(), plan->fwd.data(), plan->bwd.data(),
                                      plan->items.data(), plan->fix.data(), plan->cache.data(),
-                                     plan->ds_off.data()};
+                                     plan->ds_off.data(), plan->dqs.data()};
         size_t offs[kArrays], total = 0;
         for (int i = 0; i < kArrays; ++i) {
             offs[i] = total;
@@ -416,6 +419,7 @@ hstu_status_t finish_plan(hstu_plan_t* plan, uint32_t flags, hstu_plan_t** out) 
         plan->d_fix = reinterpret_cast<const FixItem*>(base + offs[4]);
         plan->d_cache = reinterpret_cast<const CacheSeq*>(base + offs[5]);
         plan->d_ds_off = reinterpret_cast<const int64_t*>(base + offs[6]);
+        plan->d_dqs = reinterpret_cast<const WorkUnit*>(base + offs[7]);
         plan->on_device = true;
     }
     *out = plan;
@@ -514,6 +518,12 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
             hstu::KeyTiles kt = hstu::key_tiles_for_rows(r0, rhi, s.nc, s.nh);
             for (int h = 0; h < H; ++h) plan->fwd.push_back(WorkUnit{b, h, r0, kt.count()});
         }
+        // stored-dS dQ (bf16): 256-row blocks
+        if (bf16)
+            for (int r0 = 0; r0 < s.n; r0 += 2 * plan->fwd_rows) {
+                hstu::KeyTiles kt = hstu::key_tiles_for_rows(r0, std::min(r0 + 2 * plan->fwd_rows, s.n), s.nc, s.nh);
+                for (int h = 0; h < H; ++h) plan->dqs.push_back(WorkUnit{b, h, r0, kt.count()});
+            }
         // dK/dV: key blocks
         for (int k0 = 0; k0 < s.n; k0 += plan->bwd_keys) {
             int qlo, qhi;
@@ -528,6 +538,7 @@ hstu_status_t hstu_plan_create(const hstu_attn_args_t* args, const int64_t* off,
     // a stable sort, so each block's heads stay together in head order (the stored-dS modes pass
     // takes every heads-th entry)
     order_for_xcds(plan->fwd);
+    order_for_xcds(plan->dqs);
     sort_longest_first(plan->bwd);
     return finish_plan(plan, flags, out);
 }
@@ -590,7 +601,7 @@ hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info) {
 hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* units, int64_t cap,
                               int64_t* count) {
     if (!plan || !count) return HSTU_ERR_NULL_ARG;
-    if (op != 0 && op != 1 && op != 2) return HSTU_ERR_BAD_SHAPE;
+    if (op < 0 || op > 3) return HSTU_ERR_BAD_SHAPE;
     if (op == 2) {
         *count = (int64_t)plan->items.size();
         if (cap > 0 && !units) return HSTU_ERR_NULL_ARG;
@@ -602,7 +613,7 @@ hstu_status_t hstu_plan_units(const hstu_plan_t* plan, int32_t op, int32_t* unit
         }
         return HSTU_OK;
     }
-    const std::vector<WorkUnit>& u = op == 0 ? plan->fwd : plan->bwd;
+    const std::vector<WorkUnit>& u = op == 0 ? plan->fwd : op == 1 ? plan->bwd : plan->dqs;
     *count = (int64_t)u.size();
     if (cap > 0 && !units) return HSTU_ERR_NULL_ARG;
     int64_t m = std::min<int64_t>(cap, (int64_t)u.size());
@@ -782,6 +793,10 @@ hstu_status_t hstu_attn_bwd_dq(const hstu_plan_t* plan, const hstu_attn_args_t* 
         st = ds_workspace(plan, ws, ws_bytes, &p.ds);
         if (st != HSTU_OK) return st;
         p.ds_off = p.ds ? plan->d_ds_off : nullptr;
+        if (p.ds) {  // the stored-dS pass runs over 256-row blocks
+            p.units = plan->d_dqs;
+            p.num_units = (int32_t)plan->dqs.size();
+        }
     }
     p.dq = dq;
     p.drab_pos = args->rab_pos ? drab_pos : nullptr;
@@ -1003,8 +1018,8 @@ hstu_status_t hstu_layer_bwd(const hstu_plan_t* plan, const hstu_attn_args_t* ar
         e = checked(hstu::launch_attn_bwd_dkdv_bf16(p, s), s);
     }
     if (e == hipSuccess) {
-        p.units = plan->d_fwd;
-        p.num_units = (int32_t)plan->fwd.size();
+        p.units = p.ds ? plan->d_dqs : plan->d_fwd;  // the stored-dS pass runs over 256-row blocks
+        p.num_units = (int32_t)(p.ds ? plan->dqs.size() : plan->fwd.size());
         p.drab_pos = drab_pos;
         p.drab_ts = drab_ts;
         e = checked(hstu::launch_attn_bwd_dq_bf16(p, s), s);

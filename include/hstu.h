@@ -143,8 +143,9 @@ void hstu_plan_destroy_on(hstu_plan_t* plan, void* stream);
 /* Fills *info. */
 hstu_status_t hstu_plan_info(const hstu_plan_t* plan, hstu_plan_info_t* info);
 
-/* Copies the work list of `op` (0 = forward / dQ, 1 = dK/dV) to host memory as int32 quadruples
- * {sequence, head, first row (or key), cost} in launch order; op 2 gives the bf16 forward items
+/* Copies the work list of `op` (0 = forward / recomputing dQ, 1 = dK/dV, 3 = the stored-dS dQ
+ * pass's 256-row blocks) to host memory as int32 quadruples {sequence, head, first row (or key),
+ * cost} in launch order; op 2 gives the bf16 forward items
  * as int32 octets {sequence, head, first row, cost, first tile, end tile, partial slot or -1, 0}
  * (row blocks of fwd_item_rows rows; tiles index the row block's list of visible key tiles).  Writes at most `cap` items and
  * returns the total count through *count. */

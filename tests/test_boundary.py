@@ -255,7 +255,10 @@ def test_plan_covers_every_block_once_in_launch_order(dtype):
                                                            w["num_targets"])
     rows = info["fwd_row_block"]
     assert rows == (128 if dtype == "bf16" else 64)
-    for op, block in ((0, rows), (1, info["bwd_key_block"])):
+    ops = [(0, rows), (1, info["bwd_key_block"])]
+    if dtype == "bf16":
+        ops.append((3, 2 * rows))  # the stored-dS dQ pass: 256-row blocks, the same order rules
+    for op, block in ops:
         u = hj.hstu_plan_units(plan, op)
         if op == 1:
             assert np.all(np.diff(u[:, 3]) <= 0)             # key blocks: longest first
